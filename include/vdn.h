@@ -1,0 +1,197 @@
+/*
+ * vdn.h -- C-ABI of the MI355X (gfx950) Video DeltaNet attention library.
+ *
+ * The operator is the video-to-video attention of "Video DeltaNet: A
+ * Video-Native Hybrid Attention for Livestream Video Generation" (arXiv
+ * 2609.20744): a local window Softmax with two boundary anchors, a
+ * bidirectional Video Delta Attention (VDA) linear memory started from a
+ * text state, and a gated merge through separate output projections.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    contiguous in the layouts given (row-major, last index fastest).  The
+ *    library never allocates device memory: scratch space is the caller's
+ *    `workspace` of at least vdn_workspace_bytes() bytes (256-byte aligned).
+ *  - Token layout is frame-major: token row l = f*N + n for frame f in
+ *    [0,F) and spatial token n in [0,N); L = F*N.
+ *  - `dt` gives the element type of q, k, v, k_text, v_text, W_s, W_l, out
+ *    and the branch outputs: VDN_F32 (float) or VDN_BF16 (bfloat16).  The
+ *    gates beta, alpha, beta_text, g_s, g_l, gamma are always float; all
+ *    states (S_text, P_fwd, P_rev) are always float.
+ *  - Inputs are read only and may alias each other; outputs must not alias
+ *    inputs, each other, or the workspace.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*,
+ *    NULL = the legacy default stream); the library does not synchronise.
+ *    vdn_attn_fwd may fork one internal stream through events and always
+ *    joins it back onto `stream` before returning.
+ *  - Every argument check runs on the host before the first HIP call.  A
+ *    failing check returns an error code and launches nothing.  The message
+ *    of the last error on the calling thread is vdn_last_error().
+ *  - Results are deterministic: no floating-point atomics.
+ *  - Supported: d_k == d_v in {16, 32, 64, 128}; F >= 2; F % chunk_frames
+ *    == 0; 1 <= N; 0 <= T; B, H >= 1.  Other shapes return
+ *    VDN_ERR_INVALID_ARG or VDN_ERR_UNSUPPORTED.
+ */
+#ifndef VDN_H_
+#define VDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VDN_OK = 0,
+  VDN_ERR_INVALID_ARG = -1,   /* null pointer, bad size or inconsistent shape */
+  VDN_ERR_UNSUPPORTED = -2,   /* valid but not implemented (head dim, dtype)  */
+  VDN_ERR_WORKSPACE = -3,     /* workspace smaller than vdn_workspace_bytes() */
+  VDN_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed   */
+} vdn_status;
+
+typedef enum { VDN_F32 = 0, VDN_BF16 = 1 } vdn_dtype;
+
+/* Problem sizes.  L = F*N video tokens per (b, h); D is the model width of
+ * the projected output (D must equal H*d_v when no projections are given). */
+typedef struct {
+  int B, H, F, N, T, d_k, d_v, D;
+} vdn_dims;
+
+/* Operator hyper-parameters; vdn_default_params() fills the page's values.
+ *  softmax_scale   : logit scale; <= 0 selects 1/sqrt(d_k) (not printed on
+ *                    the page; the standard choice).
+ *  rms_eps         : epsilon of the RMSNorm on the linear readout (1e-6).
+ *  text_init_scale : each directional scan starts from this multiple of the
+ *                    text state; 0.5 makes the two summed readouts count the
+ *                    prompt exactly once (method, bidirectional linear
+ *                    attention).
+ *  chunk_frames    : latent frames per VAE temporal chunk (5).
+ *  window_chunks   : a query chunk sees this many chunks on each side (1).
+ *  anchors         : 1 = frames 0 and F-1 are boundary anchors with
+ *                    four-way connectivity, 0 = no anchors.            */
+typedef struct {
+  float softmax_scale;
+  float rms_eps;
+  float text_init_scale;
+  int chunk_frames;
+  int window_chunks;
+  int anchors;
+} vdn_params;
+
+/* Fills *p with the defaults listed above. */
+void vdn_default_params(vdn_params* p);
+
+/*
+ * vdn_attn_fwd -- the whole VDN attention forward.
+ *
+ * Method, hybrid attention (paper: local Softmax window and boundary
+ * anchors; bidirectional linear attention; branch calibration):
+ *   Ohat_s = g_s * Softmax-window/anchor attention(q, k, v)
+ *   Ohat_l = g_l * gamma * O_l / sqrt(mean_dv(O_l^2) + rms_eps),
+ *            O_l = q^T (M_fwd + M_rev), the two VDA directional memories
+ *   out    = Ohat_s W_s + Ohat_l W_l      (heads concatenated, h*d_v + j)
+ *
+ *  q, k, v     [B,H,L,d]   dt      queries/keys/values, frame-major
+ *  beta        [B,H,L]     float   VDA write gate per token (>= 0)
+ *  alpha       [B,H,F,d_k] float   VDA channel-wise decay per frame, (0,1]
+ *  k_text, v_text [B,H,T,d] dt     text tokens (may be NULL when T == 0)
+ *  beta_text   [B,H,T]     float   write gate of the text tokens
+ *  g_s, g_l    [B,H,L]     float   post-sigmoid output gates
+ *  gamma       [d_v]       float   RMSNorm weight; NULL = all ones
+ *  W_s, W_l    [H*d_v, D]  dt      output projections; both NULL = identity
+ *                                  (then D == H*d_v and out = Ohat_s+Ohat_l)
+ *  out         [B,L,D]     dt
+ *  ohat_s, ohat_l [B,L,H,d_v] dt   optional: if non-NULL the gated branch
+ *                                  outputs are written there as well.
+ */
+vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v,
+                        const float* beta, const float* alpha,
+                        const void* k_text, const void* v_text, const float* beta_text,
+                        const float* g_s, const float* g_l, const float* gamma,
+                        const void* W_s, const void* W_l,
+                        void* out, void* ohat_s, void* ohat_l,
+                        void* workspace, size_t workspace_bytes,
+                        const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                        void* stream);
+
+/*
+ * vda_scan_fwd -- forward VDA scan, read at chunk boundaries.
+ *
+ * Paper, Video Delta Attention (joint frame objective and its closed form)
+ * and system section (chunk-wise scans; the prompt state as a leading
+ * virtual frame; the small-matrix inverse in FP32):
+ *   A_f = K_f^T diag(beta_f) K_f,  W_f = K_f^T diag(beta_f) V_f,
+ *   T_f = (I + A_f)^{-1} diag(alpha_f),  U_f = (I + A_f)^{-1} W_f,
+ *   anchor frames (when enabled) decay only: T_f = diag(alpha_f), U_f = 0,
+ *   S_text = (I + A_text)^{-1} W_text,
+ *   P_fwd[0] = text_init_scale * S_text,
+ *   P_fwd[c+1] = (maps of frames c*cf .. c*cf+cf-1 applied in order) P_fwd[c].
+ *
+ *  k, v [B,H,L,d] dt; beta [B,H,L]; alpha [B,H,F,d_k]; text as above.
+ *  P_fwd      [B,H,C+1,d_k,d_v] float   (C = F / chunk_frames)
+ *  S_text_out [B,H,d_k,d_v]     float   nullable
+ */
+vdn_status vda_scan_fwd(const void* k, const void* v, const float* beta, const float* alpha,
+                        const void* k_text, const void* v_text, const float* beta_text,
+                        float* P_fwd, float* S_text_out,
+                        void* workspace, size_t workspace_bytes,
+                        const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                        void* stream);
+
+/*
+ * vda_scan_rev -- reverse VDA scan with the same per-frame maps:
+ *   P_rev[C] = text_init_scale * S_text,
+ *   P_rev[c] = (maps of frames c*cf+cf-1 .. c*cf applied in that order) P_rev[c+1],
+ * so P_rev[c] summarises frames >= c*cf.  Arguments as vda_scan_fwd.
+ */
+vdn_status vda_scan_rev(const void* k, const void* v, const float* beta, const float* alpha,
+                        const void* k_text, const void* v_text, const float* beta_text,
+                        float* P_rev, float* S_text_out,
+                        void* workspace, size_t workspace_bytes,
+                        const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                        void* stream);
+
+/*
+ * vdn_window_softmax_fwd -- the Softmax branch alone.
+ *
+ * Paper, method, local Softmax window: query frame t in chunk c sees every
+ * token of the frames whose chunk is within window_chunks of c, plus (with
+ * anchors) frames 0 and F-1; frames 0 and F-1 see every frame; each frame is
+ * counted once.  out = g_s * softmax(scale * q k^T) v over those keys.
+ *
+ *  q, k, v [B,H,L,d] dt;  g_s [B,H,L] float, NULL = 1
+ *  out [B,L,H,d_v] dt;  lse [B,H,L] float natural-log normaliser, nullable
+ */
+vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v, const float* g_s,
+                                  void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes,
+                                  const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                                  void* stream);
+
+/* Workspace bytes that suffice for every entry point above at these sizes;
+ * 0 if the arguments are invalid. */
+size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
+
+/*
+ * vdn_window_plan -- host-only helper: the frame roles the kernels use.
+ *  vis   [F*F] row = query frame, 1 = key frame visible to Softmax (nullable)
+ *  i_fwd, ws, i_rev, we [F] (each nullable): query frame t reads
+ *        P_fwd[i_fwd[t]] decayed over frames ws[t]..t and P_rev[i_rev[t]]
+ *        decayed over frames t..we[t].
+ * Host memory, caller owned.  No device is touched.
+ */
+vdn_status vdn_window_plan(int F, const vdn_params* p, uint8_t* vis,
+                           int32_t* i_fwd, int32_t* ws, int32_t* i_rev, int32_t* we);
+
+/* Static text of a status code. */
+const char* vdn_status_string(vdn_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* vdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDN_H_ */

@@ -487,6 +487,48 @@ def vdn_attn(inp: dict, p: Params = DEFAULT, linear_form: str = "scan"):
     return heads
 
 
+def head_rows(q, k, v, beta, alpha, k_text, v_text, beta_text, g_s, g_l, rows,
+              gamma=None, p: Params = DEFAULT, want_softmax: bool = True):
+    """The same per-head definitions evaluated only at the token rows `rows`
+    (frame-major indices), for checks at sizes where every row is too slow.
+
+    The chunk-boundary states are computed in full (they are O(F) updates);
+    the Softmax and linear readouts only for the chosen rows.  Returns a
+    dict with S_text, P_fwd, P_rev and, per chosen row, O_s, Ohat_s, lse,
+    O_l, Ohat_l.
+    """
+    L, dk = q.shape
+    dv = v.shape[1]
+    F = alpha.shape[0]
+    N = L // F
+    rows = np.asarray(rows, np.int64)
+    Kf = np.asarray(k, np.float64).reshape(F, N, dk)
+    Vf = np.asarray(v, np.float64).reshape(F, N, dv)
+    bf = np.asarray(beta, np.float64).reshape(F, N)
+    a = np.asarray(alpha, np.float64)
+    S_text = text_state(k_text, v_text, beta_text, dk, dv)
+    P_fwd, P_rev = scan_states(Kf, Vf, bf, a, S_text, p)
+    M_fwd, M_rev = directional_memory_scan(P_fwd, P_rev, a, p)
+    n = len(rows)
+    out = {"S_text": S_text, "P_fwd": P_fwd, "P_rev": P_rev,
+           "O_l": np.zeros((n, dv)), "Ohat_l": np.zeros((n, dv))}
+    if want_softmax:
+        out.update(O_s=np.zeros((n, dv)), Ohat_s=np.zeros((n, dv)), lse=np.zeros(n))
+    frames = rows // N
+    for t in np.unique(frames):
+        sel = np.nonzero(frames == t)[0]
+        qr = np.asarray(q, np.float64)[rows[sel]]
+        O_l, Oh_l = linear_branch(qr[None], M_fwd[t][None], M_rev[t][None],
+                                  np.asarray(g_l, np.float64)[rows[sel]][None], gamma, p)
+        out["O_l"][sel], out["Ohat_l"][sel] = O_l[0], Oh_l[0]
+        if want_softmax:
+            O_s, lse = softmax_rows(qr, int(t), Kf, Vf, p)
+            out["O_s"][sel] = O_s
+            out["Ohat_s"][sel] = np.asarray(g_s, np.float64)[rows[sel]][:, None] * O_s
+            out["lse"][sel] = lse
+    return out
+
+
 # --------------------------------------------------------------------------
 # Algorithmic work counts (used for reporting only)
 # --------------------------------------------------------------------------

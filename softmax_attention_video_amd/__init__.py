@@ -1,0 +1,309 @@
+"""MI355X-native Video DeltaNet (VDN) attention forward.
+
+A thin ctypes binding over the HIP library libvdn.so (C-ABI in include/vdn.h).
+Every step of the operator runs in the library's gfx950 kernels; this module
+only checks tensor shapes/dtypes, allocates the workspace through torch and
+passes raw device pointers and the current stream.  There is no fallback: if
+the library is missing, every call raises.
+
+Entry points (same names as the C-ABI):
+  attn_fwd(...)               -> out            (vdn_attn_fwd)
+  scan_fwd(...), scan_rev(...) -> P, S_text     (vda_scan_fwd / vda_scan_rev)
+  window_softmax_fwd(...)     -> out, lse       (vdn_window_softmax_fwd)
+  window_plan(F, params)      -> host tables    (vdn_window_plan)
+  workspace_bytes(...)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvdn.so")
+
+VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE, VDN_ERR_HIP = 0, -1, -2, -3, -4
+VDN_F32, VDN_BF16 = 0, 1
+
+EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
+           "vdn_window_softmax_fwd", "vdn_workspace_bytes", "vdn_window_plan",
+           "vdn_status_string", "vdn_last_error")
+
+
+class VdnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "H", "F", "N", "T", "d_k", "d_v", "D")]
+
+
+class CParams(ctypes.Structure):
+    _fields_ = [("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("text_init_scale", ctypes.c_float), ("chunk_frames", ctypes.c_int),
+                ("window_chunks", ctypes.c_int), ("anchors", ctypes.c_int)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Params:
+    """Operator hyper-parameters (defaults: 5-frame chunks, +-1 chunk window,
+    anchors on, scale 1/sqrt(d_k) (0 = default), eps 1e-6, text split 1/2)."""
+    softmax_scale: float = 0.0
+    rms_eps: float = 1e-6
+    text_init_scale: float = 0.5
+    chunk_frames: int = 5
+    window_chunks: int = 1
+    anchors: int = 1
+
+    def c(self) -> CParams:
+        return CParams(self.softmax_scale, self.rms_eps, self.text_init_scale,
+                       self.chunk_frames, self.window_chunks, self.anchors)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not found: build it with "
+                           "`python -m softmax_attention_video_amd._build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dp, pp = ctypes.POINTER(Dims), ctypes.POINTER(CParams)
+    L.vdn_default_params.argtypes = [pp]
+    L.vdn_default_params.restype = None
+    L.vdn_attn_fwd.argtypes = [P] * 17 + [S, dp, pp, I, P]
+    L.vdn_attn_fwd.restype = I
+    for n in ("vda_scan_fwd", "vda_scan_rev"):
+        getattr(L, n).argtypes = [P] * 10 + [S, dp, pp, I, P]
+        getattr(L, n).restype = I
+    L.vdn_window_softmax_fwd.argtypes = [P] * 7 + [S, dp, pp, I, P]
+    L.vdn_window_softmax_fwd.restype = I
+    L.vdn_workspace_bytes.argtypes = [dp, pp, I]
+    L.vdn_workspace_bytes.restype = S
+    L.vdn_window_plan.argtypes = [I, pp, P, P, P, P, P]
+    L.vdn_window_plan.restype = I
+    L.vdn_status_string.argtypes = [I]
+    L.vdn_status_string.restype = ctypes.c_char_p
+    L.vdn_last_error.argtypes = []
+    L.vdn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != VDN_OK:
+        L = lib()
+        raise VdnError(status, f"{L.vdn_status_string(status).decode()}: "
+                               f"{L.vdn_last_error().decode()}")
+
+
+def default_params() -> Params:
+    c = CParams()
+    lib().vdn_default_params(ctypes.byref(c))
+    return Params(c.softmax_scale, c.rms_eps, c.text_init_scale, c.chunk_frames,
+                  c.window_chunks, c.anchors)
+
+
+def window_plan(F: int, params: Params | None = None):
+    """Host tables (vis [F,F] uint8, i_fwd, ws, i_rev, we [F] int32)."""
+    p = (params or Params()).c()
+    vis = np.zeros((F, F), np.uint8)
+    t = [np.zeros(F, np.int32) for _ in range(4)]
+    _check(lib().vdn_window_plan(F, ctypes.byref(p), vis.ctypes.data,
+                                 *[a.ctypes.data for a in t]))
+    return vis, *t
+
+
+def workspace_bytes(dims: Dims, params: Params | None = None, dtype: int = VDN_BF16) -> int:
+    p = (params or Params()).c()
+    return int(lib().vdn_workspace_bytes(ctypes.byref(dims), ctypes.byref(p), dtype))
+
+
+# ----------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return VDN_BF16
+    if t.dtype == torch.float32:
+        return VDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t, name, dtype=None, shape=None, device=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    del torch
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(dims, params, code, device, workspace):
+    torch = _torch()
+    need = workspace_bytes(dims, params, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace of {workspace.numel()} bytes < {need}")
+    return workspace
+
+
+def attn_fwd(q, k, v, beta, alpha, k_text, v_text, beta_text, g_s, g_l, gamma=None,
+             W_s=None, W_l=None, out=None, ohat_s=None, ohat_l=None,
+             params: Params | None = None, workspace=None, stream=None):
+    """Full VDN attention forward (vdn_attn_fwd).
+
+    q, k, v [B,H,L,d] (bf16 or fp32, frame-major); beta, g_s, g_l [B,H,L] fp32;
+    alpha [B,H,F,d] fp32; k_text, v_text [B,H,T,d]; beta_text [B,H,T] fp32;
+    gamma [d] fp32 or None; W_s, W_l [H*d, D] or None (identity).
+    Returns out [B,L,D] (or [B,L,H*d] without projections).
+    """
+    torch = _torch()
+    params = params or Params()
+    B, H, L, d = q.shape
+    F = alpha.shape[2]
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    N = L // F
+    T = k_text.shape[2] if k_text is not None else 0
+    dt = q.dtype
+    code = _dtype_code(q)
+    dev = q.device
+    Dm = W_s.shape[1] if W_s is not None else H * d
+    dims = Dims(B, H, F, N, T, d, d, Dm)
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty((B, L, Dm), dtype=dt, device=dev)
+    ws = _workspace(dims, params, code, dev, workspace)
+    p = params.c()
+    args = [
+        _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
+        _ptr(v, "v", dt, (B, H, L, d), dev), _ptr(beta, "beta", f32, (B, H, L), dev),
+        _ptr(alpha, "alpha", f32, (B, H, F, d), dev),
+        _ptr(k_text, "k_text", dt, (B, H, T, d), dev, allow_none=T == 0),
+        _ptr(v_text, "v_text", dt, (B, H, T, d), dev, allow_none=T == 0),
+        _ptr(beta_text, "beta_text", f32, (B, H, T), dev, allow_none=T == 0),
+        _ptr(g_s, "g_s", f32, (B, H, L), dev), _ptr(g_l, "g_l", f32, (B, H, L), dev),
+        _ptr(gamma, "gamma", f32, (d,), dev, allow_none=True),
+        _ptr(W_s, "W_s", dt, (H * d, Dm), dev, allow_none=True),
+        _ptr(W_l, "W_l", dt, (H * d, Dm), dev, allow_none=True),
+        _ptr(out, "out", dt, (B, L, Dm), dev),
+        _ptr(ohat_s, "ohat_s", dt, (B, L, H, d), dev, allow_none=True),
+        _ptr(ohat_l, "ohat_l", dt, (B, L, H, d), dev, allow_none=True),
+        ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+    ]
+    _check(lib().vdn_attn_fwd(*args, ctypes.byref(dims), ctypes.byref(p), code,
+                              _stream(stream, dev)))
+    return out
+
+
+def _scan(which, k, v, beta, alpha, k_text, v_text, beta_text, params, workspace, stream,
+          P=None, S_text=None):
+    torch = _torch()
+    params = params or Params()
+    B, H, L, d = k.shape
+    F = alpha.shape[2]
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    N = L // F
+    T = k_text.shape[2] if k_text is not None else 0
+    dt = k.dtype
+    code = _dtype_code(k)
+    dev = k.device
+    C = F // params.chunk_frames
+    dims = Dims(B, H, F, N, T, d, d, H * d)
+    f32 = torch.float32
+    if P is None:
+        P = torch.empty((B, H, C + 1, d, d), dtype=f32, device=dev)
+    if S_text is None:
+        S_text = torch.empty((B, H, d, d), dtype=f32, device=dev)
+    ws = _workspace(dims, params, code, dev, workspace)
+    p = params.c()
+    fn = lib().vda_scan_fwd if which == "fwd" else lib().vda_scan_rev
+    _check(fn(_ptr(k, "k", dt, (B, H, L, d), dev), _ptr(v, "v", dt, (B, H, L, d), dev),
+              _ptr(beta, "beta", f32, (B, H, L), dev), _ptr(alpha, "alpha", f32, (B, H, F, d), dev),
+              _ptr(k_text, "k_text", dt, (B, H, T, d), dev, allow_none=T == 0),
+              _ptr(v_text, "v_text", dt, (B, H, T, d), dev, allow_none=T == 0),
+              _ptr(beta_text, "beta_text", f32, (B, H, T), dev, allow_none=T == 0),
+              _ptr(P, "P", f32, (B, H, C + 1, d, d), dev),
+              _ptr(S_text, "S_text", f32, (B, H, d, d), dev),
+              ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+              ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return P, S_text
+
+
+def scan_fwd(k, v, beta, alpha, k_text, v_text, beta_text, params=None, workspace=None,
+             stream=None, P=None, S_text=None):
+    """Forward VDA chunk-boundary states P_fwd [B,H,C+1,d,d] and S_text (vda_scan_fwd)."""
+    return _scan("fwd", k, v, beta, alpha, k_text, v_text, beta_text, params, workspace,
+                 stream, P, S_text)
+
+
+def scan_rev(k, v, beta, alpha, k_text, v_text, beta_text, params=None, workspace=None,
+             stream=None, P=None, S_text=None):
+    """Reverse VDA chunk-boundary states P_rev [B,H,C+1,d,d] and S_text (vda_scan_rev)."""
+    return _scan("rev", k, v, beta, alpha, k_text, v_text, beta_text, params, workspace,
+                 stream, P, S_text)
+
+
+def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=None,
+                       params: Params | None = None, workspace=None, stream=None):
+    """Window/anchor Softmax branch (vdn_window_softmax_fwd).
+    Returns (out [B,L,H,d], lse [B,H,L] or None)."""
+    torch = _torch()
+    params = params or Params()
+    B, H, L, d = q.shape
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    N = L // F
+    dt = q.dtype
+    code = _dtype_code(q)
+    dev = q.device
+    dims = Dims(B, H, F, N, 0, d, d, H * d)
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=dt, device=dev)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=dev) if want_lse else None
+    ws = _workspace(dims, params, code, dev, workspace)
+    p = params.c()
+    _check(lib().vdn_window_softmax_fwd(
+        _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
+        _ptr(v, "v", dt, (B, H, L, d), dev),
+        _ptr(g_s, "g_s", torch.float32, (B, H, L), dev, allow_none=True),
+        _ptr(out, "out", dt, (B, L, H, d), dev),
+        _ptr(lse, "lse", torch.float32, (B, H, L), dev, allow_none=True),
+        ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+        ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return out, lse

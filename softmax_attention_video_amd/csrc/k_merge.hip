@@ -1,0 +1,163 @@
+// Gated merge of the two branches through separate output projections.
+//
+// Paper ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream
+// Video Generation"), method, branch calibration: each branch has its own
+// output projection and the two projected outputs are added, so
+//   out[M, Dm] = Ohat_s[M, K] W_s[K, Dm] + Ohat_l[M, K] W_l[K, Dm]
+// with M = B*L tokens and K = H*d_v (heads concatenated).  This is one GEMM
+// over the concatenated contraction [Ohat_s | Ohat_l] [W_s ; W_l].
+//
+// bf16 path: both operands K-contiguous (the projections are transposed
+// once per call into the workspace, W^T [Dm, K]), 128 x 128 output tiles,
+// 256 threads, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The
+// product is formed as out^T blocks so each lane owns 4 consecutive output
+// features of one token (8-byte stores).
+#include "vdn_common.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+__global__ __launch_bounds__(256) void merge_gemm_bf16_kernel(const bf16_t* __restrict__ a0,
+                                                              const bf16_t* __restrict__ a1,
+                                                              const bf16_t* __restrict__ bt0,
+                                                              const bf16_t* __restrict__ bt1,
+                                                              bf16_t* __restrict__ out,
+                                                              long long M, int K, int N) {
+  constexpr int BM = 128, BN = 128, BK = 64, P = BK + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t As[BM * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * P];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  const long long m0 = (long long)blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int K2 = 2 * K;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  for (int k0 = 0; k0 < K2; k0 += BK) {
+    __syncthreads();
+#pragma unroll
+    for (int c = tid; c < BM * BK / 8; c += 256) {
+      const int r = c / (BK / 8), c8 = c % (BK / 8);
+      const int kc = k0 + c8 * 8;
+      u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+      const long long m = m0 + r;
+      const int n = n0 + r;
+      if (kc < K) {
+        if (m < M) va = ld16(a0 + (size_t)m * K + kc);
+        if (n < N) vb = ld16(bt0 + (size_t)n * K + kc);
+      } else if (kc < K2) {
+        if (m < M) va = ld16(a1 + (size_t)m * K + (kc - K));
+        if (n < N) vb = ld16(bt1 + (size_t)n * K + (kc - K));
+      }
+      st16(&As[r * P + c8 * 8], va);
+      st16(&Bs[r * P + c8 * 8], vb);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 bm[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        bm[mb] = as_bf16x8(ld16(&As[(wm * 64 + mb * 32 + l32) * P + ks * 16 + hg * 8]));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x8 an = as_bf16x8(ld16(&Bs[(wn * 64 + nb * 32 + l32) * P + ks * 16 + hg * 8]));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32x32x16(an, bm[mb], acc[nb][mb]);
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const long long m = m0 + wm * 64 + mb * 32 + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int n = n0 + wn * 64 + nb * 32 + 8 * i4 + 4 * hg;
+        if (n >= N) continue;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[nb][mb][i4 * 4 + 0], acc[nb][mb][i4 * 4 + 1]);
+        pk[1] = pack_bf16x2(acc[nb][mb][i4 * 4 + 2], acc[nb][mb][i4 * 4 + 3]);
+        *reinterpret_cast<u32x2*>(out + (size_t)m * N + n) = pk;
+      }
+  }
+}
+
+hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const uint16_t* w0t,
+                                  const uint16_t* w1t, uint16_t* out, long long M, int K, int Dm,
+                                  hipStream_t s) {
+  if (M == 0 || Dm == 0) return hipSuccess;
+  dim3 grid((unsigned)((Dm + 127) / 128), (unsigned)((M + 127) / 128));
+  merge_gemm_bf16_kernel<<<grid, 256, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm);
+  return hipGetLastError();
+}
+
+// ---- generic SIMT GEMM (fp32 storage or odd shapes): 16x16 tiles ----
+template <typename T>
+__global__ __launch_bounds__(256) void merge_gemm_simt_kernel(const T* __restrict__ a0,
+                                                              const T* __restrict__ a1,
+                                                              const T* __restrict__ w0,
+                                                              const T* __restrict__ w1,
+                                                              T* __restrict__ out, long long M,
+                                                              int K, int N) {
+  __shared__ float As[16][17];
+  __shared__ float Ws[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const long long m = (long long)blockIdx.y * 16 + ty;
+  const int n = blockIdx.x * 16 + tx;
+  float acc = 0.f;
+  for (int part = 0; part < 2; ++part) {
+    const T* a = part ? a1 : a0;
+    const T* w = part ? w1 : w0;
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      __syncthreads();
+      const long long am = (long long)blockIdx.y * 16 + ty;
+      As[ty][tx] = (am < M && k0 + tx < K) ? Elem<T>::load(a, (size_t)am * K + k0 + tx) : 0.f;
+      Ws[ty][tx] = (k0 + ty < K && n < N) ? Elem<T>::load(w, (size_t)(k0 + ty) * N + n) : 0.f;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc = fmaf(As[ty][k], Ws[k][tx], acc);
+    }
+  }
+  if (m < M && n < N) Elem<T>::store(out, (size_t)m * N + n, acc);
+}
+
+template <typename T>
+hipError_t launch_merge_gemm_simt(const T* a0, const T* a1, const T* w0, const T* w1, T* out,
+                                  long long M, int K, int Dm, hipStream_t s) {
+  if (M == 0 || Dm == 0) return hipSuccess;
+  dim3 grid((unsigned)((Dm + 15) / 16), (unsigned)((M + 15) / 16));
+  merge_gemm_simt_kernel<T><<<grid, 256, 0, s>>>(a0, a1, w0, w1, out, M, K, Dm);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void add_kernel(const T* __restrict__ a, const T* __restrict__ b, T* __restrict__ out,
+                           long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) Elem<T>::store(out, i, Elem<T>::load(a, i) + Elem<T>::load(b, i));
+}
+
+template <typename T>
+hipError_t launch_add(const T* a, const T* b, T* out, long long n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  add_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, b, out, n);
+  return hipGetLastError();
+}
+
+template hipError_t launch_merge_gemm_simt<float>(const float*, const float*, const float*,
+                                                  const float*, float*, long long, int, int,
+                                                  hipStream_t);
+template hipError_t launch_merge_gemm_simt<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
+                                                   const bf16_t*, bf16_t*, long long, int, int,
+                                                   hipStream_t);
+template hipError_t launch_add<float>(const float*, const float*, float*, long long, hipStream_t);
+template hipError_t launch_add<bf16_t>(const bf16_t*, const bf16_t*, bf16_t*, long long, hipStream_t);
+
+}  // namespace vdn

@@ -1,0 +1,201 @@
+// VDA chunk composition and the bidirectional chunk prefix scans.
+//
+// Paper ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream
+// Video Generation"), system section, chunk-wise scans: each frame is an
+// affine map S -> T_f S + U_f, and attention only reads memory at VAE-chunk
+// boundaries, so the maps of each chunk are composed into one (T_c, U_c) and
+// the shorter chunk sequence is scanned in both directions; the prompt state
+// enters as the leading virtual frame.  Method, bidirectional linear
+// attention: each directional scan starts from text_init_scale * S_text.
+//
+//   forward : T_c = T_{e} ... T_{s},  U_c = T_e(...(T_{s+1} U_s + U_{s+1})...) + U_e
+//   reverse : the same frames applied from e down to s
+//   P_fwd[0] = a S_text,  P_fwd[c+1] = T_c P_fwd[c] + U_c
+//   P_rev[C] = a S_text,  P_rev[c]   = T_c P_rev[c+1] + U_c
+//
+// Every map acts column by column on the state, so the work splits over
+// 32-column blocks: the composition runs one workgroup per
+// (b, h, direction, chunk, column block of [T_c | U_c]) and the scan one per
+// (b, h, direction, column block of P).  The left factor (a D x D fp32
+// matrix) is staged in LDS; the 32 state columns stay in LDS between steps.
+#include "vdn_common.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+constexpr int kCB = 32;   // state columns per workgroup
+
+// Y_out[:, 0:32] = Ts * Y_in[:, 0:32] (+ add[:, 0:32] if add != nullptr).
+// Ts: [D][D+1] in LDS; Y_in/Y_out: [D][32] in LDS; add: row-major, pitch ldadd.
+template <int D>
+__device__ __forceinline__ void apply_left(const float* Ts, const float* Y_in, float* Y_out,
+                                           const float* add, int ldadd, int ncols) {
+  constexpr int RPT = (D + 31) / 32;
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
+  float acc[RPT][4];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+  for (int k = 0; k < D; ++k) {
+    const f32x4 y = *reinterpret_cast<const f32x4*>(&Y_in[k * kCB + tx * 4]);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int row = ty + 32 * r;
+      const float t = row < D ? Ts[row * (D + 1) + k] : 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(t, y[c], acc[r][c]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int row = ty + 32 * r;
+    if (row >= D) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = tx * 4 + c;
+      float v = acc[r][c];
+      if (add && col < ncols) v += add[(size_t)row * ldadd + col];
+      Y_out[row * kCB + col] = v;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_matrix(float* Ts, const float* src) {
+  for (int e = threadIdx.x; e < D * D; e += blockDim.x) Ts[(e / D) * (D + 1) + (e % D)] = src[e];
+}
+
+// ---- composition: grid = B*H * 2 * C * (2D/32) ----
+template <int D>
+__global__ __launch_bounds__(256) void vda_chunk_compose_kernel(Geometry g, const float* __restrict__ Tf,
+                                                                const float* __restrict__ Uf,
+                                                                float* __restrict__ Tc,
+                                                                float* __restrict__ Uc, int dirs_mask) {
+  __shared__ __attribute__((aligned(16))) float smem[D * (D + 1) + 2 * D * kCB];
+  float* Ts = smem;                        // D x (D+1)
+  float* Y1 = smem + D * (D + 1);          // D x 32 (16-byte aligned: D*(D+1) % 4 == 0)
+  float* Y0 = Y1 + D * kCB;                // D x 32
+  constexpr int NCBH = (D + kCB - 1) / kCB;   // column blocks per half of [T | U]
+  constexpr int NCB = 2 * NCBH;
+  int id = blockIdx.x;
+  const int cb = id % NCB; id /= NCB;
+  const int c = id % g.C; id /= g.C;
+  const int dir = id % 2;
+  const int bh = id / 2;
+  if (!((dirs_mask >> dir) & 1)) return;
+  const size_t DD = (size_t)D * D;
+  // columns [lc0, lc0 + ncols) of T (cb < NCBH) or of U
+  const bool upart = cb >= NCBH;
+  const int lc0 = (cb % NCBH) * kCB;
+  const int ncols = min(kCB, D - lc0);
+  const int s = c * g.cf, e = s + g.cf - 1;
+  const int first = dir == 0 ? s : e;
+  const int step = dir == 0 ? 1 : -1;
+  const float* fbase_T = Tf + (size_t)bh * g.F * DD;
+  const float* fbase_U = Uf + (size_t)bh * g.F * DD;
+
+  // Y0 = columns of the first frame's map
+  {
+    const float* src = (upart ? fbase_U : fbase_T) + (size_t)first * DD;
+    for (int i = threadIdx.x; i < D * kCB; i += blockDim.x) {
+      const int row = i / kCB, col = i % kCB;
+      Y0[i] = col < ncols ? src[(size_t)row * D + lc0 + col] : 0.f;
+    }
+  }
+  float* yin = Y0;
+  float* yout = Y1;
+  for (int n = 1; n < g.cf; ++n) {
+    const int f = first + step * n;
+    __syncthreads();
+    stage_matrix<D>(Ts, fbase_T + (size_t)f * DD);
+    __syncthreads();
+    apply_left<D>(Ts, yin, yout, upart ? fbase_U + (size_t)f * DD + lc0 : nullptr, D, ncols);
+    float* t = yin; yin = yout; yout = t;
+  }
+  __syncthreads();
+  float* dst = (upart ? Uc : Tc) + (((size_t)bh * 2 + dir) * g.C + c) * DD;
+  for (int i = threadIdx.x; i < D * kCB; i += blockDim.x) {
+    const int row = i / kCB, col = i % kCB;
+    if (col < ncols) dst[(size_t)row * D + lc0 + col] = yin[i];
+  }
+}
+
+hipError_t launch_vda_chunk_compose(const Geometry& g, const float* Tf, const float* Uf, float* Tc,
+                                    float* Uc, int dirs_mask, hipStream_t s) {
+  const int NCB = 2 * ((g.D + kCB - 1) / kCB);
+  const unsigned grid = (unsigned)(g.B * g.H * 2 * g.C * NCB);
+  switch (g.D) {
+    case 16: vda_chunk_compose_kernel<16><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
+    case 32: vda_chunk_compose_kernel<32><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
+    case 64: vda_chunk_compose_kernel<64><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
+    case 128: vda_chunk_compose_kernel<128><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---- prefix scan: grid = B*H * 2 * (D/32 rounded up) ----
+template <int D>
+__global__ __launch_bounds__(256) void vda_chunk_scan_kernel(Geometry g, const float* __restrict__ Tc,
+                                                             const float* __restrict__ Uc,
+                                                             const float* __restrict__ S_text,
+                                                             float init_scale, float* __restrict__ P_fwd,
+                                                             float* __restrict__ P_rev) {
+  __shared__ __attribute__((aligned(16))) float smem[D * (D + 1) + 2 * D * kCB];
+  float* Ts = smem;
+  float* Y0 = smem + D * (D + 1);
+  float* Y1 = Y0 + D * kCB;
+  constexpr int NCB = (D + kCB - 1) / kCB;
+  int id = blockIdx.x;
+  const int cb = id % NCB; id /= NCB;
+  const int dir = id % 2;
+  const int bh = id / 2;
+  float* P = dir == 0 ? P_fwd : P_rev;
+  if (!P) return;
+  const size_t DD = (size_t)D * D;
+  const int col0 = cb * kCB;
+  const int ncols = min(kCB, D - col0);
+  const float* St = S_text + (size_t)bh * DD;
+  float* Pb = P + (size_t)bh * (g.C + 1) * DD;
+  for (int i = threadIdx.x; i < D * kCB; i += blockDim.x) {
+    const int row = i / kCB, col = i % kCB;
+    const float v = col < ncols ? init_scale * St[(size_t)row * D + col0 + col] : 0.f;
+    Y0[i] = v;
+    if (col < ncols) Pb[(size_t)(dir == 0 ? 0 : g.C) * DD + (size_t)row * D + col0 + col] = v;
+  }
+  float* yin = Y0;
+  float* yout = Y1;
+  for (int n = 0; n < g.C; ++n) {
+    const int c = dir == 0 ? n : g.C - 1 - n;
+    const size_t mo = (((size_t)bh * 2 + dir) * g.C + c) * DD;
+    __syncthreads();
+    stage_matrix<D>(Ts, Tc + mo);
+    __syncthreads();
+    apply_left<D>(Ts, yin, yout, Uc + mo + col0, D, ncols);
+    __syncthreads();
+    const int slot = dir == 0 ? c + 1 : c;
+    for (int i = threadIdx.x; i < D * kCB; i += blockDim.x) {
+      const int row = i / kCB, col = i % kCB;
+      if (col < ncols) Pb[(size_t)slot * DD + (size_t)row * D + col0 + col] = yout[i];
+    }
+    float* t = yin; yin = yout; yout = t;
+  }
+}
+
+hipError_t launch_vda_chunk_scan(const Geometry& g, const float* Tc, const float* Uc,
+                                 const float* S_text, float init_scale, float* P_fwd, float* P_rev,
+                                 hipStream_t s) {
+  const int NCB = (g.D + kCB - 1) / kCB;
+  const unsigned grid = (unsigned)(g.B * g.H * 2 * NCB);
+  switch (g.D) {
+    case 16: vda_chunk_scan_kernel<16><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
+    case 32: vda_chunk_scan_kernel<32><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
+    case 64: vda_chunk_scan_kernel<64><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
+    case 128: vda_chunk_scan_kernel<128><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vdn

@@ -1,0 +1,133 @@
+// VDA readout and linear-branch epilogue.
+//
+// Paper ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream
+// Video Generation"), method, bidirectional linear attention: at readout
+// time the state just outside the query frame's window is gathered from each
+// directional scan, the accumulated channel-wise decay across the skipped
+// local span is applied, the query is evaluated against the resulting
+// memory and the two readouts are added.  Branch calibration: the linear
+// readout is RMS-normalised and passed through its own output gate.
+// System section (VDA-Gather, VDA-Epilogue): gather + decay bridge, then
+// RMSNorm + gating + layout conversion, here fused into one kernel.
+//
+// For query frame t in chunk c (non-anchor):
+//   i_fwd = max(c - wc, 0), ws = i_fwd * cf, i_rev = min(c + wc + 1, C),
+//   we = min(i_rev * cf, F) - 1;  anchor frames: 0, 0, C, F - 1.
+//   M_t = diag(prod_{f=ws..t} alpha_f) P_fwd[i_fwd] + diag(prod_{f=t..we} alpha_f) P_rev[i_rev]
+//   O_l = q M_t;  out = g_l * gamma * O_l / sqrt(mean(O_l^2) + eps)   in [B, L, H, D]
+#include "vdn_common.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+__device__ __forceinline__ void readout_indices(const Geometry& g, int t, int& i_f, int& ws,
+                                                int& i_r, int& we) {
+  if (g.anchors && (t == 0 || t == g.F - 1)) {
+    i_f = 0; ws = 0; i_r = g.C; we = g.F - 1;
+    return;
+  }
+  const int c = t / g.cf;
+  i_f = c - g.wc < 0 ? 0 : c - g.wc;
+  ws = i_f * g.cf;
+  i_r = c + g.wc + 1 > g.C ? g.C : c + g.wc + 1;
+  we = (i_r * g.cf < g.F ? i_r * g.cf : g.F) - 1;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vda_readout_simt_kernel(Geometry g, const T* __restrict__ q,
+                                                               const float* __restrict__ alpha,
+                                                               const float* __restrict__ P_fwd,
+                                                               const float* __restrict__ P_rev,
+                                                               const float* __restrict__ g_l,
+                                                               const float* __restrict__ gamma,
+                                                               float eps, T* __restrict__ out) {
+  constexpr int TPG = 16;          // threads per token
+  constexpr int CPT = D / TPG;     // output columns per thread
+  constexpr int TOK = 256 / TPG;   // tokens per pass
+  __shared__ __attribute__((aligned(16))) float Ms[D * D];
+  __shared__ float Qs[TOK][D + 1];
+  __shared__ float dfs[D], drs[D];
+
+  const int t = blockIdx.x % g.F;
+  const int bh = blockIdx.x / g.F;
+  const int tid = threadIdx.x;
+  int i_f, ws, i_r, we;
+  readout_indices(g, t, i_f, ws, i_r, we);
+  const float* al = alpha + (size_t)bh * g.F * D;
+  for (int k = tid; k < D; k += 256) {
+    float df = 1.f, dr = 1.f;
+    for (int f = ws; f <= t; ++f) df *= al[(size_t)f * D + k];
+    for (int f = t; f <= we; ++f) dr *= al[(size_t)f * D + k];
+    dfs[k] = df;
+    drs[k] = dr;
+  }
+  __syncthreads();
+  const size_t DD = (size_t)D * D;
+  const float* pf = P_fwd + ((size_t)bh * (g.C + 1) + i_f) * DD;
+  const float* pr = P_rev + ((size_t)bh * (g.C + 1) + i_r) * DD;
+  for (int e = tid; e < D * D; e += 256) {
+    const int k = e / D;
+    Ms[e] = dfs[k] * pf[e] + drs[k] * pr[e];
+  }
+
+  const int grp = tid / TPG, sub = tid % TPG;
+  float gm[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) gm[j] = gamma ? gamma[sub * CPT + j] : 1.f;
+  const int bidx = bh / g.H, h = bh % g.H;
+  const size_t tok0 = (size_t)bh * g.L + (size_t)t * g.N;   // row of token 0 of frame t
+  for (int n0 = 0; n0 < g.N; n0 += TOK) {
+    __syncthreads();
+    for (int e = tid; e < TOK * D; e += 256) {
+      const int r = e / D, c = e % D;
+      Qs[r][c] = (n0 + r < g.N) ? Elem<T>::load(q, (tok0 + n0 + r) * D + c) : 0.f;
+    }
+    __syncthreads();
+    float o[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) o[j] = 0.f;
+    for (int k = 0; k < D; ++k) {
+      const float qk = Qs[grp][k];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) o[j] = fmaf(qk, Ms[k * D + sub * CPT + j], o[j]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) ss = fmaf(o[j], o[j], ss);
+#pragma unroll
+    for (int m = TPG / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPG);
+    const int n = n0 + grp;
+    if (n < g.N) {
+      const float r = rsqrtf(ss / (float)D + eps);
+      const size_t l = (size_t)t * g.N + n;
+      const float gate = g_l[(size_t)bh * g.L + l] * r;
+      const size_t ob = (((size_t)bidx * g.L + l) * g.H + h) * D + sub * CPT;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) Elem<T>::store(out, ob + j, o[j] * gate * gm[j]);
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_vda_readout(const Geometry& g, const T* q, const float* alpha, const float* P_fwd,
+                              const float* P_rev, const float* g_l, const float* gamma, float eps,
+                              T* out, hipStream_t s) {
+  const unsigned grid = (unsigned)(g.B * g.H * g.F);
+  switch (g.D) {
+    case 16: vda_readout_simt_kernel<T, 16><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    case 32: vda_readout_simt_kernel<T, 32><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    case 64: vda_readout_simt_kernel<T, 64><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    case 128: vda_readout_simt_kernel<T, 128><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_vda_readout<float>(const Geometry&, const float*, const float*,
+                                              const float*, const float*, const float*,
+                                              const float*, float, float*, hipStream_t);
+template hipError_t launch_vda_readout<bf16_t>(const Geometry&, const bf16_t*, const float*,
+                                               const float*, const float*, const float*,
+                                               const float*, float, bf16_t*, hipStream_t);
+
+}  // namespace vdn

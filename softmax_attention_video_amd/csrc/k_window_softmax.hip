@@ -1,0 +1,439 @@
+// Window + boundary-anchor Softmax branch of VDN attention.
+//
+// Paper ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream
+// Video Generation"), method, local Softmax window: a query chunk of
+// chunk_frames latent frames sees itself and window_chunks chunks on each
+// side; with anchors every frame also sees frames 0 and F-1 and those two
+// frames see every frame; each key frame counts once.
+//
+// Work decomposition.  All non-anchor query frames of one chunk share one
+// key set, so a "chunk group" is the contiguous query range of a chunk minus
+// its anchor frames, and its keys are at most three contiguous token spans
+// (anchor 0, the window, anchor F-1).  An "anchor group" is one anchor frame,
+// whose keys are the whole sequence.  Groups are cut into query tiles; one
+// workgroup owns one tile and streams the key spans through LDS with an
+// online softmax (no mask tensor, no gathered copies).
+//
+// XCD-aware order: MI355X deals workgroups round-robin to its 8 XCDs, so
+// blockIdx b runs on XCD b % 8.  Each XCD gets a contiguous slice of groups
+// (consecutive chunks of the same head share 2/3 of their key windows in
+// that XCD's L2), anchor groups (7x longer at 120 frames) first.
+#include "vdn_common.h"
+#include "vdn_internal.h"
+
+#include <math.h>
+
+namespace vdn {
+
+SoftmaxWork window_work(const Geometry& g, int bq) {
+  SoftmaxWork w{};
+  w.GA = g.anchors ? 2 * g.B * g.H : 0;
+  w.GC = g.B * g.H * g.C;
+  w.tA = (g.N + bq - 1) / bq;
+  w.tC = (g.cf * g.N + bq - 1) / bq;
+  w.pa = (w.GA + kNumXcd - 1) / kNumXcd;
+  w.pc = (w.GC + kNumXcd - 1) / kNumXcd;
+  int mx = 0;
+  for (int x = 0; x < kNumXcd; ++x) {
+    int na = w.GA - x * w.pa;
+    na = na < 0 ? 0 : (na > w.pa ? w.pa : na);
+    int nc = w.GC - x * w.pc;
+    nc = nc < 0 ? 0 : (nc > w.pc ? w.pc : nc);
+    int items = na * w.tA + nc * w.tC;
+    mx = items > mx ? items : mx;
+  }
+  w.grid = mx * kNumXcd;
+  return w;
+}
+
+struct Item {
+  int bh;            // b * H + h
+  int q_begin, q_end;
+  int nspan;
+  int kb0, ke0, kb1, ke1, kb2, ke2;   // up to three key spans [kb, ke) in tokens
+};
+
+// Key tiles of BK over the (up to three) spans, flattened: tile j of the
+// walk starts at key ks and holds nk valid keys.
+template <int BK>
+struct SpanWalk {
+  int n0, n01, n;      // cumulative tile counts
+  int kb0, ke0, kb1, ke1, kb2, ke2;
+  __device__ __forceinline__ SpanWalk(const Item& it) {
+    kb0 = it.kb0; ke0 = it.ke0;
+    kb1 = it.nspan > 1 ? it.kb1 : 0; ke1 = it.nspan > 1 ? it.ke1 : 0;
+    kb2 = it.nspan > 2 ? it.kb2 : 0; ke2 = it.nspan > 2 ? it.ke2 : 0;
+    n0 = (ke0 - kb0 + BK - 1) / BK;
+    n01 = n0 + (ke1 - kb1 + BK - 1) / BK;
+    n = n01 + (ke2 - kb2 + BK - 1) / BK;
+  }
+  __device__ __forceinline__ void tile(int j, int& ks, int& nk) const {
+    int b, e;
+    if (j < n0) { b = kb0 + j * BK; e = ke0; }
+    else if (j < n01) { b = kb1 + (j - n0) * BK; e = ke1; }
+    else { b = kb2 + (j - n01) * BK; e = ke2; }
+    ks = b;
+    nk = min(BK, e - b);
+  }
+};
+
+// Decode workgroup id -> (query range, key spans).  Returns false if idle.
+__device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork& w, int bq,
+                                            int bid, Item& it, int& q0) {
+  const int x = bid % kNumXcd;
+  int k = bid / kNumXcd;
+  const int a0 = x * w.pa;
+  int na = w.GA - a0;
+  na = na < 0 ? 0 : (na > w.pa ? w.pa : na);
+  const long long N = g.N;
+  if (k < na * w.tA) {
+    const int ga = a0 + k / w.tA;
+    const int tile = k % w.tA;
+    it.bh = ga >> 1;
+    const int f = (ga & 1) ? g.F - 1 : 0;
+    it.q_begin = (int)(f * N);
+    it.q_end = (int)((f + 1) * N);
+    it.nspan = 1;
+    it.kb0 = 0;
+    it.ke0 = (int)g.L;
+    it.kb1 = it.ke1 = it.kb2 = it.ke2 = 0;
+    q0 = it.q_begin + tile * bq;
+    return true;
+  }
+  k -= na * w.tA;
+  const int gc = x * w.pc + k / w.tC;
+  const int tile = k % w.tC;
+  if (gc >= w.GC || gc >= (x + 1) * w.pc) return false;
+  it.bh = gc / g.C;
+  const int c = gc % g.C;
+  int f0 = c * g.cf, f1 = (c + 1) * g.cf;
+  if (f1 > g.F) f1 = g.F;
+  if (g.anchors) {
+    if (f0 == 0) f0 = 1;
+    if (f1 == g.F) f1 = g.F - 1;
+  }
+  if (f1 <= f0) return false;
+  it.q_begin = (int)(f0 * N);
+  it.q_end = (int)(f1 * N);
+  int lo = c - g.wc;
+  lo = (lo < 0 ? 0 : lo) * g.cf;
+  int hi = (c + g.wc + 1) * g.cf;
+  hi = hi > g.F ? g.F : hi;
+  // spans in ascending key order: [anchor 0] window [anchor F-1]
+  const int nN = (int)N;
+  const bool a_lo = g.anchors && lo > 0, a_hi = g.anchors && hi < g.F;
+  it.kb0 = a_lo ? 0 : lo * nN;
+  it.ke0 = a_lo ? nN : hi * nN;
+  it.kb1 = a_lo ? lo * nN : (g.F - 1) * nN;
+  it.ke1 = a_lo ? hi * nN : g.F * nN;
+  it.kb2 = (g.F - 1) * nN;
+  it.ke2 = g.F * nN;
+  it.nspan = 1 + (a_lo ? 1 : 0) + (a_hi ? 1 : 0);
+  q0 = it.q_begin + tile * bq;
+  return q0 < it.q_end;
+}
+
+// -------------------------------------------------------------------------
+// bf16 MFMA flash kernel.  256 threads = 4 waves; a wave owns 32 queries.
+//   S^T (keys x queries) = K Q^T  on v_mfma_f32_32x32x16_bf16;
+//   O^T (dv x queries)  += V^T P^T, with V pre-transposed to [D, L].
+// In the S^T accumulator a lane holds one query (lane % 32) and 16 keys, so
+// the row max / sum are in-lane plus one exchange with lane ^ 32.  K rows
+// are loaded in a permuted order so that lane half g holds keys 16g..16g+15
+// of each 32-key block in register order; those registers then feed the PV
+// product directly as its B operand, matching 16 contiguous bytes of V^T.
+// -------------------------------------------------------------------------
+struct WinArgs {
+  Geometry g;
+  SoftmaxWork w;
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* vt;
+  const float* g_s;
+  bf16_t* out;
+  float* lse;
+  float scale_log2;
+};
+
+__device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
+
+template <int D>
+__global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
+  constexpr int BQ = 128, BK = 64;
+  constexpr int KP = D + 8;    // padded pitches (bf16 elements) against bank conflicts
+  constexpr int VP = BK + 8;
+  constexpr int NKK = D / 16;  // k-steps of QK^T
+  constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[BK * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[D * VP];
+
+  const Geometry& g = a.g;
+  Item it;
+  int q0;
+  if (!decode_item(g, a.w, BQ, blockIdx.x, it, q0)) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const long long L = g.L;
+  const bf16_t* Q = a.q + (size_t)it.bh * L * D;
+  const bf16_t* K = a.k + (size_t)it.bh * L * D;
+  const bf16_t* Vt = a.vt + (size_t)it.bh * L * D;
+
+  const int qrow = q0 + wave * 32 + l32;
+  const bool qvalid = qrow < it.q_end;
+  bf16x8 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 v = {0, 0, 0, 0};
+    if (qvalid) v = ld16(Q + (size_t)qrow * D + kk * 16 + hg * 8);
+    qf[kk] = as_bf16x8(v);
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) o[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int krow_perm = key_perm(l32);
+
+  const SpanWalk<BK> walk(it);
+  for (int j = 0; j < walk.n; ++j) {
+    {
+      int ks, nk;
+      walk.tile(j, ks, nk);
+      __syncthreads();
+#pragma unroll
+      for (int c = tid; c < BK * D / 8; c += 256) {
+        const int r = c / (D / 8), c8 = c % (D / 8);
+        u32x4 v = {0, 0, 0, 0};
+        if (r < nk) v = ld16(K + (size_t)(ks + r) * D + c8 * 8);
+        st16(&Ks[r * KP + c8 * 8], v);
+      }
+#pragma unroll
+      for (int c = tid; c < D * BK / 8; c += 256) {
+        const int r = c / (BK / 8), c8 = c % (BK / 8);
+        u32x4 v = {0, 0, 0, 0};
+        if (c8 * 8 < nk) v = ld16(Vt + (size_t)r * L + ks + c8 * 8);
+        st16(&Vs[r * VP + c8 * 8], v);
+      }
+      __syncthreads();
+
+      f32x16 s[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        s[kb2] = f32x16{};
+        const bf16_t* krow = &Ks[(kb2 * 32 + krow_perm) * KP + hg * 8];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) s[kb2] = mfma32x32x16(as_bf16x8(ld16(krow + kk * 16)), qf[kk], s[kb2]);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb2 * 32 + hg * 16 + i;
+          const float v = key < nk ? s[kb2][i] * a.scale_log2 : -INFINITY;
+          s[kb2][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = half_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(s[kb2][i] - m_new);
+          s[kb2][i] = p;
+          lsum += p;
+        }
+      l_run = l_run * corr + lsum;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) o[b] *= corr;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bf16x8 pb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(s[kb2][h2 * 8 + j]);
+#pragma unroll
+          for (int b = 0; b < NDB; ++b) {
+            const bf16_t* vrow = &Vs[(b * 32 + l32) * VP + kb2 * 32 + hg * 16 + h2 * 8];
+            o[b] = mfma32x32x16(as_bf16x8(ld16(vrow)), pb, o[b]);
+          }
+        }
+    }
+  }
+
+  const float l_tot = half_sum(l_run);
+  if (!qvalid) return;
+  const float inv = 1.f / l_tot;
+  const int bidx = it.bh / g.H, h = it.bh % g.H;
+  const float gate = a.g_s ? a.g_s[(size_t)it.bh * L + qrow] : 1.f;
+  const float sc = inv * gate;
+  bf16_t* orow = a.out + (((size_t)bidx * L + qrow) * g.H + h) * D;
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int dv = b * 32 + 8 * i4 + 4 * hg;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[b][i4 * 4 + 0] * sc, o[b][i4 * 4 + 1] * sc);
+      pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc, o[b][i4 * 4 + 3] * sc);
+      *reinterpret_cast<u32x2*>(orow + dv) = pk;
+    }
+  if (a.lse && hg == 0) a.lse[(size_t)it.bh * L + qrow] = m_run * kLn2 + logf(l_tot);
+}
+
+bool window_softmax_mfma_ok(const Geometry& g) {
+  return (g.D == 64 || g.D == 128) && (g.N % 16 == 0);
+}
+
+hipError_t launch_window_softmax_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* vt, const float* g_s, uint16_t* out,
+                                      float* lse, float scale, hipStream_t s) {
+  WinArgs a;
+  a.g = g;
+  a.w = window_work(g, 128);
+  a.q = q; a.k = k; a.vt = vt; a.g_s = g_s; a.out = out; a.lse = lse;
+  a.scale_log2 = scale * kLog2e;
+  if (a.w.grid == 0) return hipSuccess;
+  if (g.D == 128)
+    window_softmax_mfma_kernel<128><<<a.w.grid, 256, 0, s>>>(a);
+  else
+    window_softmax_mfma_kernel<64><<<a.w.grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------------------
+// [rows, cols] -> [cols, rows] per batch, bf16, through a 64x64 LDS tile.
+// Used to lay V out key-contiguous for the PV product.
+// -------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src,
+                                                             bf16_t* __restrict__ dst,
+                                                             long long rows, int cols) {
+  __shared__ bf16_t t[64][65];
+  const long long r0 = (long long)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const size_t boff = (size_t)blockIdx.z * rows * cols;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const long long gr = r0 + r;
+    const int gc = c0 + tx;
+    t[r][tx] = (gr < rows && gc < cols) ? src[boff + gr * cols + gc] : (bf16_t)0;
+  }
+  __syncthreads();
+  for (int c = ty; c < 64; c += 4) {
+    const int gc = c0 + c;
+    const long long gr = r0 + tx;
+    if (gc < cols && gr < rows) dst[boff + (size_t)gc * rows + gr] = t[tx][c];
+  }
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, long long rows, int cols,
+                                 long long batch, hipStream_t s) {
+  if (rows == 0 || cols == 0 || batch == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols + 63) / 64), (unsigned)batch);
+  transpose_bf16_kernel<<<grid, 256, 0, s>>>(src, dst, rows, cols);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------------------
+// Generic SIMT kernel (fp32 storage, any D <= 128, any N): one thread per
+// query, keys staged through LDS 32 at a time, fp32 online softmax.
+// -------------------------------------------------------------------------
+template <typename T, int DMAX>
+__global__ __launch_bounds__(128) void window_softmax_simt_kernel(Geometry g, SoftmaxWork w,
+                                                                  const T* __restrict__ qp,
+                                                                  const T* __restrict__ kp,
+                                                                  const T* __restrict__ vp,
+                                                                  const float* __restrict__ g_s,
+                                                                  T* __restrict__ out,
+                                                                  float* __restrict__ lse,
+                                                                  float scale_log2) {
+  constexpr int BQ = 128, BK = 32;
+  __shared__ float Ks[BK][DMAX + 1];
+  __shared__ float Vs[BK][DMAX + 1];
+  Item it;
+  int q0;
+  if (!decode_item(g, w, BQ, blockIdx.x, it, q0)) return;
+  const int D = g.D;
+  const long long L = g.L;
+  const int qrow = q0 + threadIdx.x;
+  const bool qvalid = qrow < it.q_end;
+  const size_t base = (size_t)it.bh * L * D;
+  float qv[DMAX], ov[DMAX];
+#pragma unroll
+  for (int j = 0; j < DMAX; ++j) {
+    qv[j] = (j < D && qvalid) ? Elem<T>::load(qp, base + (size_t)qrow * D + j) : 0.f;
+    ov[j] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  const SpanWalk<BK> walk(it);
+  for (int jt = 0; jt < walk.n; ++jt) {
+    {
+      int ks, nk;
+      walk.tile(jt, ks, nk);
+      __syncthreads();
+      for (int e = threadIdx.x; e < BK * D; e += blockDim.x) {
+        const int r = e / D, c = e % D;
+        Ks[r][c] = r < nk ? Elem<T>::load(kp, base + (size_t)(ks + r) * D + c) : 0.f;
+        Vs[r][c] = r < nk ? Elem<T>::load(vp, base + (size_t)(ks + r) * D + c) : 0.f;
+      }
+      __syncthreads();
+      for (int r = 0; r < nk; ++r) {
+        float dot = 0.f;
+#pragma unroll
+        for (int j = 0; j < DMAX; ++j)
+          if (j < D) dot = fmaf(qv[j], Ks[r][j], dot);
+        const float sv = dot * scale_log2;
+        const float m_new = fmaxf(m_run, sv);
+        const float corr = exp2f(m_run - m_new);
+        const float p = exp2f(sv - m_new);
+        l_run = l_run * corr + p;
+#pragma unroll
+        for (int j = 0; j < DMAX; ++j)
+          if (j < D) ov[j] = ov[j] * corr + p * Vs[r][j];
+        m_run = m_new;
+      }
+    }
+  }
+  if (!qvalid) return;
+  const int bidx = it.bh / g.H, h = it.bh % g.H;
+  const float gate = g_s ? g_s[(size_t)it.bh * L + qrow] : 1.f;
+  const float sc = gate / l_run;
+  const size_t ob = (((size_t)bidx * L + qrow) * g.H + h) * D;
+#pragma unroll
+  for (int j = 0; j < DMAX; ++j)
+    if (j < D) Elem<T>::store(out, ob + j, ov[j] * sc);
+  if (lse) lse[(size_t)it.bh * L + qrow] = m_run * kLn2 + logf(l_run);
+}
+
+template <typename T>
+hipError_t launch_window_softmax_simt(const Geometry& g, const T* q, const T* k, const T* v,
+                                      const float* g_s, T* out, float* lse, float scale,
+                                      hipStream_t s) {
+  const SoftmaxWork w = window_work(g, 128);
+  if (w.grid == 0) return hipSuccess;
+  const float sl2 = scale * kLog2e;
+  if (g.D <= 16)
+    window_softmax_simt_kernel<T, 16><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+  else if (g.D <= 32)
+    window_softmax_simt_kernel<T, 32><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+  else if (g.D <= 64)
+    window_softmax_simt_kernel<T, 64><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+  else
+    window_softmax_simt_kernel<T, 128><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+  return hipGetLastError();
+}
+
+template hipError_t launch_window_softmax_simt<float>(const Geometry&, const float*, const float*,
+                                                      const float*, const float*, float*, float*,
+                                                      float, hipStream_t);
+template hipError_t launch_window_softmax_simt<bf16_t>(const Geometry&, const bf16_t*,
+                                                       const bf16_t*, const bf16_t*, const float*,
+                                                       bf16_t*, float*, float, hipStream_t);
+
+}  // namespace vdn

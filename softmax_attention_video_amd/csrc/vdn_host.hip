@@ -1,0 +1,348 @@
+// C-ABI of the VDN attention library: argument checks, workspace layout and
+// launch sequencing.  Every check runs on the host before the first HIP call.
+#include "../../include/vdn.h"
+#include "vdn_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+vdn_status fail(vdn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+#define VDN_HIP(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(VDN_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));          \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace carve-up (offsets in bytes, each 256-aligned).
+struct Layout {
+  size_t vt, wt0, wt1, Tf, Uf, St, Tc, Uc, Pf, Pr, ohs, ohl, total;
+};
+
+Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt) {
+  const size_t es = dt == VDN_BF16 ? 2 : 4;
+  const size_t BH = (size_t)g.B * g.H, DD = (size_t)g.D * g.D;
+  Layout l{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+  l.vt = take(dt == VDN_BF16 ? BH * g.L * g.D * es : 0);
+  l.wt0 = take(dt == VDN_BF16 ? (size_t)g.H * g.D * Dm * es : 0);
+  l.wt1 = take(dt == VDN_BF16 ? (size_t)g.H * g.D * Dm * es : 0);
+  l.Tf = take(BH * g.F * DD * 4);
+  l.Uf = take(BH * g.F * DD * 4);
+  l.St = take(BH * DD * 4);
+  l.Tc = take(BH * 2 * g.C * DD * 4);
+  l.Uc = take(BH * 2 * g.C * DD * 4);
+  l.Pf = take(BH * (g.C + 1) * DD * 4);
+  l.Pr = take(BH * (g.C + 1) * DD * 4);
+  l.ohs = take(BH * g.L * g.D * es);
+  l.ohl = take(BH * g.L * g.D * es);
+  l.total = o;
+  return l;
+}
+
+vdn_params defaults() {
+  vdn_params p;
+  p.softmax_scale = 0.f;
+  p.rms_eps = 1e-6f;
+  p.text_init_scale = 0.5f;
+  p.chunk_frames = 5;
+  p.window_chunks = 1;
+  p.anchors = 1;
+  return p;
+}
+
+// Shape / parameter checks shared by all entry points.
+vdn_status check_geometry(const vdn_dims* d, const vdn_params* p, vdn_dtype dt, vdn::Geometry* g) {
+  if (!d) return fail(VDN_ERR_INVALID_ARG, "dims is NULL");
+  if (!p) return fail(VDN_ERR_INVALID_ARG, "params is NULL");
+  if (dt != VDN_F32 && dt != VDN_BF16) return fail(VDN_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (d->B < 1 || d->H < 1) return fail(VDN_ERR_INVALID_ARG, "B=%d H=%d must be >= 1", d->B, d->H);
+  if (d->F < 2) return fail(VDN_ERR_INVALID_ARG, "F=%d must be >= 2", d->F);
+  if (d->N < 1) return fail(VDN_ERR_INVALID_ARG, "N=%d must be >= 1", d->N);
+  if (d->T < 0) return fail(VDN_ERR_INVALID_ARG, "T=%d must be >= 0", d->T);
+  if (p->chunk_frames < 1) return fail(VDN_ERR_INVALID_ARG, "chunk_frames=%d must be >= 1", p->chunk_frames);
+  if (p->window_chunks < 0) return fail(VDN_ERR_INVALID_ARG, "window_chunks=%d must be >= 0", p->window_chunks);
+  if (p->anchors != 0 && p->anchors != 1) return fail(VDN_ERR_INVALID_ARG, "anchors=%d must be 0 or 1", p->anchors);
+  if (d->F % p->chunk_frames != 0)
+    return fail(VDN_ERR_INVALID_ARG, "F=%d is not a multiple of chunk_frames=%d", d->F, p->chunk_frames);
+  if (!(p->rms_eps >= 0.f) || !isfinite(p->text_init_scale) || !isfinite(p->softmax_scale))
+    return fail(VDN_ERR_INVALID_ARG, "rms_eps / text_init_scale / softmax_scale not finite or negative eps");
+  if (d->d_k != d->d_v) return fail(VDN_ERR_UNSUPPORTED, "d_k=%d != d_v=%d", d->d_k, d->d_v);
+  if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "head dim %d not in {16,32,64,128}", d->d_k);
+  const long long L = (long long)d->F * d->N;
+  const long long rows = (long long)d->B * d->H * L;
+  if (L > (1ll << 31) - 1 || rows > (1ll << 40))
+    return fail(VDN_ERR_INVALID_ARG, "sequence too long (L=%lld)", L);
+  if (d->N > (1 << 26)) return fail(VDN_ERR_INVALID_ARG, "N=%d too large", d->N);
+  g->B = d->B; g->H = d->H; g->F = d->F; g->N = d->N; g->T = d->T; g->D = d->d_k;
+  g->cf = p->chunk_frames; g->wc = p->window_chunks; g->anchors = p->anchors;
+  g->C = d->F / p->chunk_frames;
+  g->L = L;
+  return VDN_OK;
+}
+
+float softmax_scale(const vdn_params* p, int D) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.f / sqrtf((float)D);
+}
+
+#define NEED(ptr) \
+  if (!(ptr)) return fail(VDN_ERR_INVALID_ARG, "%s is NULL", #ptr)
+
+// VDA stages a1-a4 into the workspace; P pointers may be workspace or caller buffers.
+vdn_status run_scan(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, const void* k,
+                    const void* v, const float* beta, const float* alpha, const void* kt,
+                    const void* vt, const float* bt, char* ws, const Layout& lay, float* P_fwd,
+                    float* P_rev, hipStream_t s) {
+  float* Tf = (float*)(ws + lay.Tf);
+  float* Uf = (float*)(ws + lay.Uf);
+  float* St = (float*)(ws + lay.St);
+  float* Tc = (float*)(ws + lay.Tc);
+  float* Uc = (float*)(ws + lay.Uc);
+  if (dt == VDN_BF16)
+    VDN_HIP(vdn::launch_vda_frame_solve<uint16_t>(g, (const uint16_t*)k, (const uint16_t*)v, beta,
+                                                  alpha, (const uint16_t*)kt, (const uint16_t*)vt,
+                                                  bt, Tf, Uf, St, s));
+  else
+    VDN_HIP(vdn::launch_vda_frame_solve<float>(g, (const float*)k, (const float*)v, beta, alpha,
+                                               (const float*)kt, (const float*)vt, bt, Tf, Uf, St,
+                                               s));
+  const int dirs = (P_fwd ? 1 : 0) | (P_rev ? 2 : 0);
+  VDN_HIP(vdn::launch_vda_chunk_compose(g, Tf, Uf, Tc, Uc, dirs, s));
+  VDN_HIP(vdn::launch_vda_chunk_scan(g, Tc, Uc, St, p->text_init_scale, P_fwd, P_rev, s));
+  return VDN_OK;
+}
+
+vdn_status run_softmax(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, const void* q,
+                       const void* k, const void* v, const float* g_s, void* out, float* lse,
+                       char* ws, const Layout& lay, hipStream_t s) {
+  const float sc = softmax_scale(p, g.D);
+  if (dt == VDN_BF16 && vdn::window_softmax_mfma_ok(g)) {
+    uint16_t* vt = (uint16_t*)(ws + lay.vt);
+    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)v, vt, g.L, g.D, (long long)g.B * g.H, s));
+    VDN_HIP(vdn::launch_window_softmax_mfma(g, (const uint16_t*)q, (const uint16_t*)k, vt, g_s,
+                                            (uint16_t*)out, lse, sc, s));
+  } else if (dt == VDN_BF16) {
+    VDN_HIP(vdn::launch_window_softmax_simt<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k,
+                                                      (const uint16_t*)v, g_s, (uint16_t*)out, lse,
+                                                      sc, s));
+  } else {
+    VDN_HIP(vdn::launch_window_softmax_simt<float>(g, (const float*)q, (const float*)k,
+                                                   (const float*)v, g_s, (float*)out, lse, sc, s));
+  }
+  return VDN_OK;
+}
+
+vdn_status check_workspace(void* ws, size_t bytes, size_t need) {
+  if (bytes < need)
+    return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", bytes, need);
+  if (need && !ws) return fail(VDN_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)ws & 255) return fail(VDN_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  return VDN_OK;
+}
+
+vdn_status scan_entry(const void* k, const void* v, const float* beta, const float* alpha,
+                      const void* k_text, const void* v_text, const float* beta_text, float* P_fwd,
+                      float* P_rev, float* S_text_out, void* workspace, size_t workspace_bytes,
+                      const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(k); NEED(v); NEED(beta); NEED(alpha);
+  if (g.T > 0) { NEED(k_text); NEED(v_text); NEED(beta_text); }
+  if (!P_fwd && !P_rev) return fail(VDN_ERR_INVALID_ARG, "output state pointer is NULL");
+  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt);
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != VDN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  st = run_scan(g, p, dt, k, v, beta, alpha, k_text, v_text, beta_text, ws, lay, P_fwd, P_rev, s);
+  if (st != VDN_OK) return st;
+  if (S_text_out)
+    VDN_HIP(hipMemcpyAsync(S_text_out, ws + lay.St, (size_t)g.B * g.H * g.D * g.D * 4,
+                           hipMemcpyDeviceToDevice, s));
+  return VDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void vdn_default_params(vdn_params* p) {
+  if (p) *p = defaults();
+}
+
+const char* vdn_status_string(vdn_status s) {
+  switch (s) {
+    case VDN_OK: return "VDN_OK";
+    case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG";
+    case VDN_ERR_UNSUPPORTED: return "VDN_ERR_UNSUPPORTED";
+    case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE";
+    case VDN_ERR_HIP: return "VDN_ERR_HIP";
+  }
+  return "unknown vdn_status";
+}
+
+const char* vdn_last_error(void) { return g_err; }
+
+size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
+  vdn::Geometry g;
+  if (check_geometry(dims, p, dt, &g) != VDN_OK) return 0;
+  const int Dm = dims->D > 0 ? dims->D : g.H * g.D;
+  return make_layout(g, Dm, dt).total;
+}
+
+vdn_status vdn_window_plan(int F, const vdn_params* p, uint8_t* vis, int32_t* i_fwd, int32_t* ws,
+                           int32_t* i_rev, int32_t* we) {
+  g_err[0] = 0;
+  if (!p) return fail(VDN_ERR_INVALID_ARG, "params is NULL");
+  if (F < 2) return fail(VDN_ERR_INVALID_ARG, "F=%d must be >= 2", F);
+  if (p->chunk_frames < 1 || p->window_chunks < 0 || (p->anchors != 0 && p->anchors != 1))
+    return fail(VDN_ERR_INVALID_ARG, "bad chunk_frames/window_chunks/anchors");
+  if (F % p->chunk_frames != 0)
+    return fail(VDN_ERR_INVALID_ARG, "F=%d is not a multiple of chunk_frames=%d", F, p->chunk_frames);
+  const int cf = p->chunk_frames, wc = p->window_chunks, C = F / cf;
+  for (int t = 0; t < F; ++t) {
+    const bool anc = p->anchors && (t == 0 || t == F - 1);
+    const int c = t / cf;
+    int lo = c - wc < 0 ? 0 : c - wc;
+    int hi = c + wc + 1 > C ? C : c + wc + 1;     // chunk range [lo, hi)
+    if (vis) {
+      for (int f = 0; f < F; ++f) {
+        const int cfr = f / cf;
+        bool v = anc || (cfr >= lo && cfr < hi) || (p->anchors && (f == 0 || f == F - 1));
+        vis[(size_t)t * F + f] = v ? 1 : 0;
+      }
+    }
+    int a = anc ? 0 : lo, b = anc ? C : hi;
+    if (i_fwd) i_fwd[t] = a;
+    if (ws) ws[t] = a * cf;
+    if (i_rev) i_rev[t] = b;
+    if (we) we[t] = (b * cf < F ? b * cf : F) - 1;
+  }
+  return VDN_OK;
+}
+
+vdn_status vda_scan_fwd(const void* k, const void* v, const float* beta, const float* alpha,
+                        const void* k_text, const void* v_text, const float* beta_text,
+                        float* P_fwd, float* S_text_out, void* workspace, size_t workspace_bytes,
+                        const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream) {
+  if (!P_fwd) { g_err[0] = 0; return fail(VDN_ERR_INVALID_ARG, "P_fwd is NULL"); }
+  return scan_entry(k, v, beta, alpha, k_text, v_text, beta_text, P_fwd, nullptr, S_text_out,
+                    workspace, workspace_bytes, dims, p, dt, stream);
+}
+
+vdn_status vda_scan_rev(const void* k, const void* v, const float* beta, const float* alpha,
+                        const void* k_text, const void* v_text, const float* beta_text,
+                        float* P_rev, float* S_text_out, void* workspace, size_t workspace_bytes,
+                        const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream) {
+  if (!P_rev) { g_err[0] = 0; return fail(VDN_ERR_INVALID_ARG, "P_rev is NULL"); }
+  return scan_entry(k, v, beta, alpha, k_text, v_text, beta_text, nullptr, P_rev, S_text_out,
+                    workspace, workspace_bytes, dims, p, dt, stream);
+}
+
+vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v, const float* g_s,
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                                  void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(q); NEED(k); NEED(v); NEED(out);
+  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt);
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != VDN_OK) return st;
+  return run_softmax(g, p, dt, q, k, v, g_s, out, lse, (char*)workspace, lay, (hipStream_t)stream);
+}
+
+vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float* beta,
+                        const float* alpha, const void* k_text, const void* v_text,
+                        const float* beta_text, const float* g_s, const float* g_l,
+                        const float* gamma, const void* W_s, const void* W_l, void* out,
+                        void* ohat_s, void* ohat_l, void* workspace, size_t workspace_bytes,
+                        const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(q); NEED(k); NEED(v); NEED(beta); NEED(alpha); NEED(g_s); NEED(g_l); NEED(out);
+  if (g.T > 0) { NEED(k_text); NEED(v_text); NEED(beta_text); }
+  if ((W_s == nullptr) != (W_l == nullptr))
+    return fail(VDN_ERR_INVALID_ARG, "W_s and W_l must both be given or both be NULL");
+  const bool proj = W_s != nullptr;
+  const int Dm = dims->D;
+  if (Dm < 1) return fail(VDN_ERR_INVALID_ARG, "D=%d must be >= 1", Dm);
+  if (!proj && Dm != g.H * g.D)
+    return fail(VDN_ERR_INVALID_ARG, "without projections D=%d must equal H*d_v=%d", Dm, g.H * g.D);
+  const Layout lay = make_layout(g, Dm, dt);
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != VDN_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* ohs = ohat_s ? ohat_s : (void*)(ws + lay.ohs);
+  void* ohl = ohat_l ? ohat_l : (void*)(ws + lay.ohl);
+  float* Pf = (float*)(ws + lay.Pf);
+  float* Pr = (float*)(ws + lay.Pr);
+
+  // Linear branch (a1-a6)
+  st = run_scan(g, p, dt, k, v, beta, alpha, k_text, v_text, beta_text, ws, lay, Pf, Pr, s);
+  if (st != VDN_OK) return st;
+  if (dt == VDN_BF16)
+    VDN_HIP(vdn::launch_vda_readout<uint16_t>(g, (const uint16_t*)q, alpha, Pf, Pr, g_l, gamma,
+                                              p->rms_eps, (uint16_t*)ohl, s));
+  else
+    VDN_HIP(vdn::launch_vda_readout<float>(g, (const float*)q, alpha, Pf, Pr, g_l, gamma,
+                                           p->rms_eps, (float*)ohl, s));
+  // Softmax branch (a7)
+  st = run_softmax(g, p, dt, q, k, v, g_s, ohs, nullptr, ws, lay, s);
+  if (st != VDN_OK) return st;
+  // Merge (a8)
+  const long long M = (long long)g.B * g.L;
+  const int K = g.H * g.D;
+  if (!proj) {
+    if (dt == VDN_BF16)
+      VDN_HIP(vdn::launch_add<uint16_t>((const uint16_t*)ohs, (const uint16_t*)ohl,
+                                        (uint16_t*)out, M * K, s));
+    else
+      VDN_HIP(vdn::launch_add<float>((const float*)ohs, (const float*)ohl, (float*)out, M * K, s));
+  } else if (dt == VDN_BF16 && Dm % 8 == 0) {
+    uint16_t* w0t = (uint16_t*)(ws + lay.wt0);
+    uint16_t* w1t = (uint16_t*)(ws + lay.wt1);
+    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_s, w0t, K, Dm, 1, s));
+    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_l, w1t, K, Dm, 1, s));
+    VDN_HIP(vdn::launch_merge_gemm_bf16((const uint16_t*)ohs, (const uint16_t*)ohl, w0t, w1t,
+                                        (uint16_t*)out, M, K, Dm, s));
+  } else if (dt == VDN_BF16) {
+    VDN_HIP(vdn::launch_merge_gemm_simt<uint16_t>((const uint16_t*)ohs, (const uint16_t*)ohl,
+                                                  (const uint16_t*)W_s, (const uint16_t*)W_l,
+                                                  (uint16_t*)out, M, K, Dm, s));
+  } else {
+    VDN_HIP(vdn::launch_merge_gemm_simt<float>((const float*)ohs, (const float*)ohl,
+                                               (const float*)W_s, (const float*)W_l, (float*)out,
+                                               M, K, Dm, s));
+  }
+  return VDN_OK;
+}
+
+}  // extern "C"

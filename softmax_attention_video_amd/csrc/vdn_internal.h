@@ -1,0 +1,80 @@
+// Host-visible kernel launchers of the VDN library (internal; not the C-ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vdn {
+
+// Frame geometry of one call.  D = d_k = d_v.
+struct Geometry {
+  int B, H, F, N, T, D;
+  int cf;        // chunk_frames
+  int wc;        // window_chunks
+  int anchors;   // 0 / 1
+  int C;         // F / cf
+  long long L;   // F * N
+};
+
+// Work split of the window Softmax over query groups (see window_work()).
+struct SoftmaxWork {
+  int GA, GC;    // anchor-frame groups, chunk groups
+  int tA, tC;    // query tiles per anchor group / chunk group
+  int pa, pc;    // groups per XCD slice
+  int grid;      // total workgroups
+};
+
+constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dealt round-robin
+
+SoftmaxWork window_work(const Geometry& g, int bq);
+
+// ---- window Softmax (Softmax branch) ----
+// q,k [B,H,L,D]; vt [B,H,D,L] (bf16 path only); out [B,L,H,D]; lse [B,H,L].
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, long long rows, int cols,
+                                 long long batch, hipStream_t s);
+hipError_t launch_window_softmax_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* vt, const float* g_s, uint16_t* out,
+                                      float* lse, float scale, hipStream_t s);
+template <typename T>
+hipError_t launch_window_softmax_simt(const Geometry& g, const T* q, const T* k, const T* v,
+                                      const float* g_s, T* out, float* lse, float scale,
+                                      hipStream_t s);
+bool window_softmax_mfma_ok(const Geometry& g);
+
+// ---- VDA frame statistics + solve (per frame and the text frame) ----
+// Tf [B,H,F,D,D], Uf [B,H,F,D,D], S_text [B,H,D,D] (all fp32).
+template <typename T>
+hipError_t launch_vda_frame_solve(const Geometry& g, const T* k, const T* v, const float* beta,
+                                  const float* alpha, const T* k_text, const T* v_text,
+                                  const float* beta_text, float* Tf, float* Uf, float* S_text,
+                                  hipStream_t s);
+
+// ---- chunk composition and chunk prefix scans ----
+// Tc, Uc [B,H,2,C,D,D] (dir 0 = forward, 1 = reverse)
+hipError_t launch_vda_chunk_compose(const Geometry& g, const float* Tf, const float* Uf,
+                                    float* Tc, float* Uc, int dirs_mask, hipStream_t s);
+// P [B,H,C+1,D,D] for each requested direction (nullable).
+hipError_t launch_vda_chunk_scan(const Geometry& g, const float* Tc, const float* Uc,
+                                 const float* S_text, float init_scale, float* P_fwd,
+                                 float* P_rev, hipStream_t s);
+
+// ---- readout: gather + decay bridge + q.M + RMSNorm + gate ----
+// out [B,L,H,D] (element type T)
+template <typename T>
+hipError_t launch_vda_readout(const Geometry& g, const T* q, const float* alpha,
+                              const float* P_fwd, const float* P_rev, const float* g_l,
+                              const float* gamma, float eps, T* out, hipStream_t s);
+
+// ---- merge ----
+// out[M,Dm] = A0[M,K] W0[K,Dm] + A1[M,K] W1[K,Dm]   (bf16 path via W^T)
+hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const uint16_t* w0t,
+                                  const uint16_t* w1t, uint16_t* out, long long M, int K, int Dm,
+                                  hipStream_t s);
+template <typename T>
+hipError_t launch_merge_gemm_simt(const T* a0, const T* a1, const T* w0, const T* w1, T* out,
+                                  long long M, int K, int Dm, hipStream_t s);
+template <typename T>
+hipError_t launch_add(const T* a, const T* b, T* out, long long n, hipStream_t s);
+
+}  // namespace vdn

@@ -1,0 +1,84 @@
+"""Helpers shared by the GPU parity tests (no test functions here)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+DEV = "cuda:0"
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(cfg):
+    import torch
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def to_dev(a, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(dtype)
+
+
+def gpu_tensors(cfg, inp):
+    """Upload the generator's (already rounded) arrays; bf16 casts are exact."""
+    import torch
+    dt = torch_dtype(cfg)
+    t = {}
+    for key in ("q", "k", "v", "k_text", "v_text"):
+        t[key] = to_dev(inp[key], dt)
+    for key in ("beta", "alpha", "beta_text", "g_s", "g_l", "gamma"):
+        t[key] = to_dev(inp[key], torch.float32)
+    t["W_s"] = to_dev(inp["W_s"], dt) if inp.get("W_s") is not None else None
+    t["W_l"] = to_dev(inp["W_l"], dt) if inp.get("W_l") is not None else None
+    return t
+
+
+def to_np(x):
+    return None if x is None else x.float().cpu().numpy().astype(np.float64)
+
+
+def rel_l2(got, exp) -> float:
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    assert got.shape == exp.shape, (got.shape, exp.shape)
+    assert np.isfinite(got).all(), "non-finite values in GPU output"
+    den = np.linalg.norm(exp)
+    return float(np.linalg.norm(got - exp) / (den if den > 0 else 1.0))
+
+
+def run_library(cfg, t, params=None, with_parts=True):
+    """Run every entry point once on the same inputs; returns numpy float64."""
+    import torch
+    import softmax_attention_video_amd as vdn
+    B, H, L, d = t["q"].shape
+    F = t["alpha"].shape[2]
+    dt = torch_dtype(cfg)
+    ohs = torch.empty((B, L, H, d), dtype=dt, device=DEV)
+    ohl = torch.empty((B, L, H, d), dtype=dt, device=DEV)
+    args = (t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["k_text"], t["v_text"],
+            t["beta_text"], t["g_s"], t["g_l"])
+    out = vdn.attn_fwd(*args, gamma=t["gamma"], W_s=t["W_s"], W_l=t["W_l"], ohat_s=ohs,
+                       ohat_l=ohl, params=params)
+    res = {"out": out, "Ohat_s": ohs, "Ohat_l": ohl}
+    if with_parts:
+        sargs = (t["k"], t["v"], t["beta"], t["alpha"], t["k_text"], t["v_text"], t["beta_text"])
+        res["P_fwd"], res["S_text"] = vdn.scan_fwd(*sargs, params=params)
+        res["P_rev"], _ = vdn.scan_rev(*sargs, params=params)
+        res["sm"], res["lse"] = vdn.window_softmax_fwd(t["q"], t["k"], t["v"], F, g_s=t["g_s"],
+                                                       want_lse=True, params=params)
+    torch.cuda.synchronize()
+    return {k: to_np(v) for k, v in res.items()}
+
+
+def oracle_params(params):
+    from oracle import vdn_oracle as O
+    if params is None:
+        return O.Params()
+    return O.Params(chunk_frames=params.chunk_frames, window_chunks=params.window_chunks,
+                    anchors=bool(params.anchors),
+                    softmax_scale=params.softmax_scale if params.softmax_scale > 0 else None,
+                    rms_eps=params.rms_eps, text_init_scale=params.text_init_scale)

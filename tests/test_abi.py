@@ -1,0 +1,163 @@
+"""C-ABI tests that need no GPU: exports, host-side argument checks, and the
+frame-role tables of vdn_window_plan bit-exact against the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import softmax_attention_video_amd as vdn
+from oracle import vdn_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "vdn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:vdn|vda)_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_header_symbol():
+    L = vdn.lib()
+    names = _header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(vdn.EXPORTS)
+
+
+def test_default_params():
+    p = vdn.default_params()
+    assert (p.chunk_frames, p.window_chunks, p.anchors) == (5, 1, 1)
+    assert p.text_init_scale == 0.5 and p.softmax_scale == 0.0
+    assert abs(p.rms_eps - 1e-6) < 1e-12
+
+
+def test_status_strings():
+    L = vdn.lib()
+    for code, name in [(0, b"VDN_OK"), (-1, b"VDN_ERR_INVALID_ARG"), (-2, b"VDN_ERR_UNSUPPORTED"),
+                       (-3, b"VDN_ERR_WORKSPACE"), (-4, b"VDN_ERR_HIP")]:
+        assert L.vdn_status_string(code) == name
+
+
+@pytest.mark.parametrize("F", list(range(2, 61)))
+@pytest.mark.parametrize("params", [O.Params(), O.Params(chunk_frames=3, window_chunks=2),
+                                    O.Params(anchors=False), O.Params(chunk_frames=1, window_chunks=0),
+                                    O.Params(chunk_frames=2, window_chunks=3)])
+def test_window_plan_bit_exact(F, params):
+    if F % params.chunk_frames:
+        with pytest.raises(vdn.VdnError) as e:
+            vdn.window_plan(F, vdn.Params(chunk_frames=params.chunk_frames))
+        assert e.value.status == vdn.VDN_ERR_INVALID_ARG
+        return
+    vp = vdn.Params(chunk_frames=params.chunk_frames, window_chunks=params.window_chunks,
+                    anchors=int(params.anchors))
+    vis, i_f, ws, i_r, we = vdn.window_plan(F, vp)
+    np.testing.assert_array_equal(vis, O.visibility(F, params))
+    for got, exp in zip((i_f, ws, i_r, we), O.scan_indices(F, params)):
+        np.testing.assert_array_equal(got, exp)
+
+
+def test_window_plan_rejects_bad_args():
+    with pytest.raises(vdn.VdnError):
+        vdn.window_plan(1)
+    with pytest.raises(vdn.VdnError):
+        vdn.window_plan(20, vdn.Params(anchors=2))
+
+
+# ---- argument validation: every failing check returns before any HIP call ----
+def _call_attn(dims, params=None, dt=vdn.VDN_BF16, ws_bytes=1 << 40, null=(), W=True):
+    L = vdn.lib()
+    p = (params or vdn.Params()).c()
+    fake = ctypes.c_void_p(0x100000)
+    ptrs = [fake] * 16
+    names = ["q", "k", "v", "beta", "alpha", "k_text", "v_text", "beta_text", "g_s", "g_l",
+             "gamma", "W_s", "W_l", "out", "ohat_s", "ohat_l"]
+    for n in null:
+        ptrs[names.index(n)] = None
+    if not W:
+        ptrs[names.index("W_s")] = ptrs[names.index("W_l")] = None
+    return L.vdn_attn_fwd(*ptrs, fake, ctypes.c_size_t(ws_bytes),
+                          ctypes.byref(dims) if dims is not None else None,
+                          ctypes.byref(p), dt, None)
+
+
+def _dims(**kw):
+    d = dict(B=1, H=2, F=20, N=16, T=4, d_k=64, d_v=64, D=128)
+    d.update(kw)
+    return vdn.Dims(*[d[k] for k in ("B", "H", "F", "N", "T", "d_k", "d_v", "D")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(F=1), vdn.VDN_ERR_INVALID_ARG),
+    (dict(F=22), vdn.VDN_ERR_INVALID_ARG),          # not a multiple of 5
+    (dict(N=0), vdn.VDN_ERR_INVALID_ARG),
+    (dict(B=0), vdn.VDN_ERR_INVALID_ARG),
+    (dict(H=0), vdn.VDN_ERR_INVALID_ARG),
+    (dict(T=-1), vdn.VDN_ERR_INVALID_ARG),
+    (dict(D=0), vdn.VDN_ERR_INVALID_ARG),
+    (dict(d_k=48, d_v=48), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(d_k=64, d_v=32), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(d_k=256, d_v=256), vdn.VDN_ERR_UNSUPPORTED),
+])
+def test_attn_invalid_dims(kw, code):
+    assert _call_attn(_dims(**kw)) == code
+    assert vdn.lib().vdn_last_error() != b""
+
+
+def test_attn_null_pointers_and_pairs():
+    assert _call_attn(None) == vdn.VDN_ERR_INVALID_ARG
+    for n in ("q", "k", "v", "beta", "alpha", "g_s", "g_l", "out", "k_text", "v_text",
+              "beta_text"):
+        assert _call_attn(_dims(), null=(n,)) == vdn.VDN_ERR_INVALID_ARG, n
+    # only one projection
+    assert _call_attn(_dims(), null=("W_l",)) == vdn.VDN_ERR_INVALID_ARG
+    # identity merge needs D == H * d_v
+    assert _call_attn(_dims(D=100), W=False) == vdn.VDN_ERR_INVALID_ARG
+
+
+def test_attn_unknown_dtype_and_params():
+    assert _call_attn(_dims(), dt=7) == vdn.VDN_ERR_UNSUPPORTED
+    assert _call_attn(_dims(), params=vdn.Params(chunk_frames=0)) == vdn.VDN_ERR_INVALID_ARG
+    assert _call_attn(_dims(), params=vdn.Params(window_chunks=-1)) == vdn.VDN_ERR_INVALID_ARG
+    assert _call_attn(_dims(), params=vdn.Params(rms_eps=-1.0)) == vdn.VDN_ERR_INVALID_ARG
+
+
+def test_attn_workspace_too_small():
+    need = vdn.workspace_bytes(_dims())
+    assert need > 0
+    assert _call_attn(_dims(), ws_bytes=need - 1) == vdn.VDN_ERR_WORKSPACE
+
+
+def test_workspace_bytes_zero_for_invalid():
+    assert vdn.workspace_bytes(_dims(F=21)) == 0
+    assert vdn.workspace_bytes(_dims(d_k=48, d_v=48)) == 0
+
+
+def test_scan_and_softmax_validation():
+    L = vdn.lib()
+    p = vdn.Params().c()
+    fake = ctypes.c_void_p(0x100000)
+    d = _dims()
+    for fn in (L.vda_scan_fwd, L.vda_scan_rev):
+        # no output state
+        assert fn(*[fake] * 7, None, None, fake, ctypes.c_size_t(1 << 40), ctypes.byref(d),
+                  ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+        # workspace too small
+        assert fn(*[fake] * 9, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p),
+                  vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+    assert L.vdn_window_softmax_fwd(None, fake, fake, None, fake, None, fake,
+                                    ctypes.c_size_t(1 << 40), ctypes.byref(d), ctypes.byref(p),
+                                    vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    assert L.vdn_window_softmax_fwd(fake, fake, fake, None, fake, None, fake,
+                                    ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p),
+                                    vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 20, 16)
+    with pytest.raises(ValueError):
+        vdn.window_softmax_fwd(q, q, q, F=20)

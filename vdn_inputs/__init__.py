@@ -46,7 +46,7 @@ class Config:
     N: int
     T: int
     seed: int
-    beta: str = "sigmoid"       # "uniform" | "sigmoid" | "zero"
+    beta: str = "sigmoid"       # "uniform" | "sigmoid" | "zero" (video tokens only)
     gates: str = "token"        # "token" | "head"
     alpha: str = "u0.9"         # "u0.9" | "unit" | "u01"
     dup_frac: float = 0.0
@@ -118,7 +118,7 @@ def _beta(cfg, tid, b, h, n):
     g = _rng(cfg, tid, b, h)
     if cfg.beta == "uniform":
         return g.random(n, dtype=np.float32)
-    if cfg.beta == "zero":
+    if cfg.beta == "zero" and tid == "beta":   # video write gate only
         return np.zeros(n, np.float32)
     z = g.standard_normal(n, dtype=np.float32).astype(np.float64)
     return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)

@@ -185,6 +185,21 @@ size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype 
 vdn_status vdn_window_plan(int F, const vdn_params* p, uint8_t* vis,
                            int32_t* i_fwd, int32_t* ws, int32_t* i_rev, int32_t* we);
 
+/*
+ * Kernel timer (instrumentation for roofline measurements).
+ * vdn_timer_enable(n): the next n launches of the window Softmax kernel made
+ *   by this thread (through vdn_attn_fwd or vdn_window_softmax_fwd) are each
+ *   bracketed by a pair of HIP events recorded on the stream the kernel runs
+ *   on.  The library creates the events (no device memory is allocated).
+ * vdn_timer_read(ms, cap): waits for the recorded events and writes up to
+ *   cap per-launch durations in milliseconds to host array ms; returns the
+ *   number written (negative vdn_status on error).
+ * vdn_timer_disable(): stops recording and destroys the events.
+ */
+vdn_status vdn_timer_enable(int n);
+int vdn_timer_read(float* ms, int cap);
+void vdn_timer_disable(void);
+
 /* Static text of a status code. */
 const char* vdn_status_string(vdn_status s);
 /* Message of the last failing call on this thread ("" if none). */

@@ -29,7 +29,8 @@ VDN_F32, VDN_BF16 = 0, 1
 
 EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_window_softmax_fwd", "vdn_workspace_bytes", "vdn_window_plan",
-           "vdn_status_string", "vdn_last_error")
+           "vdn_status_string", "vdn_last_error", "vdn_timer_enable", "vdn_timer_read",
+           "vdn_timer_disable")
 
 
 class VdnError(RuntimeError):
@@ -95,6 +96,12 @@ def lib() -> ctypes.CDLL:
     L.vdn_status_string.restype = ctypes.c_char_p
     L.vdn_last_error.argtypes = []
     L.vdn_last_error.restype = ctypes.c_char_p
+    L.vdn_timer_enable.argtypes = [I]
+    L.vdn_timer_enable.restype = I
+    L.vdn_timer_read.argtypes = [P, I]
+    L.vdn_timer_read.restype = I
+    L.vdn_timer_disable.argtypes = []
+    L.vdn_timer_disable.restype = None
     _lib = L
     return L
 
@@ -121,6 +128,25 @@ def window_plan(F: int, params: Params | None = None):
     _check(lib().vdn_window_plan(F, ctypes.byref(p), vis.ctypes.data,
                                  *[a.ctypes.data for a in t]))
     return vis, *t
+
+
+class KernelTimer:
+    """Per-launch durations of the window Softmax kernel, from HIP events the
+    library records around each launch on its stream (vdn_timer_*)."""
+
+    def __init__(self, n: int):
+        self.n = n
+        _check(lib().vdn_timer_enable(n))
+
+    def read(self) -> np.ndarray:
+        ms = np.zeros(self.n, np.float32)
+        k = lib().vdn_timer_read(ms.ctypes.data, self.n)
+        if k < 0:
+            _check(k)
+        return ms[:k].astype(np.float64)
+
+    def close(self):
+        lib().vdn_timer_disable()
 
 
 def workspace_bytes(dims: Dims, params: Params | None = None, dtype: int = VDN_BF16) -> int:

@@ -31,6 +31,20 @@ vdn_status fail(vdn_status s, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Per-thread kernel timer (see vdn_timer_enable).
+struct KernelTimer {
+  hipEvent_t* ev = nullptr;
+  int cap = 0, used = 0;
+};
+thread_local KernelTimer g_timer;
+
+hipError_t timer_mark(hipStream_t s, bool begin) {
+  if (!g_timer.ev || g_timer.used >= g_timer.cap) return hipSuccess;
+  hipError_t e = hipEventRecord(g_timer.ev[2 * g_timer.used + (begin ? 0 : 1)], s);
+  if (!begin) ++g_timer.used;
+  return e;
+}
+
 // Workspace carve-up (offsets in bytes, each 256-aligned).
 struct Layout {
   size_t vt, wt0, wt1, Tf, Uf, St, Tc, Uc, Pf, Pr, ohs, ohl, total;
@@ -138,15 +152,21 @@ vdn_status run_softmax(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt
   if (dt == VDN_BF16 && vdn::window_softmax_mfma_ok(g)) {
     uint16_t* vt = (uint16_t*)(ws + lay.vt);
     VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)v, vt, g.L, g.D, (long long)g.B * g.H, s));
+    VDN_HIP(timer_mark(s, true));
     VDN_HIP(vdn::launch_window_softmax_mfma(g, (const uint16_t*)q, (const uint16_t*)k, vt, g_s,
                                             (uint16_t*)out, lse, sc, s));
+    VDN_HIP(timer_mark(s, false));
   } else if (dt == VDN_BF16) {
+    VDN_HIP(timer_mark(s, true));
     VDN_HIP(vdn::launch_window_softmax_simt<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k,
                                                       (const uint16_t*)v, g_s, (uint16_t*)out, lse,
                                                       sc, s));
+    VDN_HIP(timer_mark(s, false));
   } else {
+    VDN_HIP(timer_mark(s, true));
     VDN_HIP(vdn::launch_window_softmax_simt<float>(g, (const float*)q, (const float*)k,
                                                    (const float*)v, g_s, (float*)out, lse, sc, s));
+    VDN_HIP(timer_mark(s, false));
   }
   return VDN_OK;
 }
@@ -203,6 +223,47 @@ const char* vdn_status_string(vdn_status s) {
 }
 
 const char* vdn_last_error(void) { return g_err; }
+
+void vdn_timer_disable(void) {
+  if (g_timer.ev) {
+    for (int i = 0; i < 2 * g_timer.cap; ++i) (void)hipEventDestroy(g_timer.ev[i]);
+    delete[] g_timer.ev;
+  }
+  g_timer = KernelTimer{};
+}
+
+vdn_status vdn_timer_enable(int n) {
+  g_err[0] = 0;
+  vdn_timer_disable();
+  if (n < 1 || n > (1 << 20)) return fail(VDN_ERR_INVALID_ARG, "timer capacity %d out of range", n);
+  g_timer.ev = new hipEvent_t[2 * (size_t)n];
+  for (int i = 0; i < 2 * n; ++i) {
+    hipError_t e = hipEventCreate(&g_timer.ev[i]);
+    if (e != hipSuccess) {
+      g_timer.cap = i / 2;   // destroy what was created
+      for (int j = i; j < 2 * n; ++j) g_timer.ev[j] = nullptr;
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_timer.ev[j]);
+      delete[] g_timer.ev;
+      g_timer = KernelTimer{};
+      return fail(VDN_ERR_HIP, "hipEventCreate failed: %s", hipGetErrorString(e));
+    }
+  }
+  g_timer.cap = n;
+  g_timer.used = 0;
+  return VDN_OK;
+}
+
+int vdn_timer_read(float* ms, int cap) {
+  g_err[0] = 0;
+  if (!ms) return fail(VDN_ERR_INVALID_ARG, "ms is NULL");
+  const int n = g_timer.used < cap ? g_timer.used : cap;
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev[2 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess) return fail(VDN_ERR_HIP, "timer read failed: %s", hipGetErrorString(e));
+  }
+  return n;
+}
 
 size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
   vdn::Geometry g;

@@ -134,7 +134,9 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
 }
 
 // -------------------------------------------------------------------------
-// bf16 MFMA flash kernel.  256 threads = 4 waves; a wave owns 32 queries.
+// bf16 MFMA flash kernel.  256 threads = 4 waves; a wave owns 64 queries as
+// two 32-query blocks, so every K / V^T fragment read from LDS feeds two
+// MFMAs (half the LDS traffic of one block per wave).
 //   S^T (keys x queries) = K Q^T  on v_mfma_f32_32x32x16_bf16;
 //   O^T (dv x queries)  += V^T P^T, with V pre-transposed to [D, L].
 // In the S^T accumulator a lane holds one query (lane % 32) and 16 keys, so
@@ -142,6 +144,16 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
 // are loaded in a permuted order so that lane half g holds keys 16g..16g+15
 // of each 32-key block in register order; those registers then feed the PV
 // product directly as its B operand, matching 16 contiguous bytes of V^T.
+//
+// Pipeline: the next key tile is fetched from global memory into registers
+// while the current one is computed from LDS, then written into the other
+// LDS buffer; one barrier per tile.
+//
+// Online softmax with a lazy rescale: O and l are kept relative to a
+// running reference max m; the reference only moves (and O, l are rescaled)
+// when a tile's max exceeds it by more than kRescaleLog2 (log2 units), so
+// unnormalised probabilities stay below 2^kRescaleLog2.  This is exact: the
+// final O / l does not depend on the reference.
 // -------------------------------------------------------------------------
 struct WinArgs {
   Geometry g;
@@ -155,17 +167,22 @@ struct WinArgs {
   float scale_log2;
 };
 
+constexpr int kWinBQ = 256;          // queries per workgroup
+constexpr float kRescaleLog2 = 8.f;
+
 __device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
 template <int D>
 __global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
-  constexpr int BQ = 128, BK = 64;
+  constexpr int BQ = kWinBQ, BK = 64, QB = 2;
   constexpr int KP = D + 8;    // padded pitches (bf16 elements) against bank conflicts
   constexpr int VP = BK + 8;
   constexpr int NKK = D / 16;  // k-steps of QK^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[BK * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[D * VP];
+  constexpr int KCH = BK * D / 8 / 256;   // 16-byte chunks per thread per tile
+  constexpr int VCH = D * BK / 8 / 256;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BK * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * VP];
 
   const Geometry& g = a.g;
   Item it;
@@ -178,113 +195,164 @@ __global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
   const bf16_t* Q = a.q + (size_t)it.bh * L * D;
   const bf16_t* K = a.k + (size_t)it.bh * L * D;
   const bf16_t* Vt = a.vt + (size_t)it.bh * L * D;
+  const float sl2 = a.scale_log2;
 
-  const int qrow = q0 + wave * 32 + l32;
-  const bool qvalid = qrow < it.q_end;
-  bf16x8 qf[NKK];
+  bf16x8 qf[QB][NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    u32x4 v = {0, 0, 0, 0};
-    if (qvalid) v = ld16(Q + (size_t)qrow * D + kk * 16 + hg * 8);
-    qf[kk] = as_bf16x8(v);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = q0 + wave * 64 + qb * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 v = {0, 0, 0, 0};
+      if (qrow < it.q_end) v = ld16(Q + (size_t)qrow * D + kk * 16 + hg * 8);
+      qf[qb][kk] = as_bf16x8(v);
+    }
   }
 
-  f32x16 o[NDB];
+  f32x16 o[QB][NDB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) o[b] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) o[qb][b] = f32x16{};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
   const int krow_perm = key_perm(l32);
-
   const SpanWalk<BK> walk(it);
-  for (int j = 0; j < walk.n; ++j) {
-    {
-      int ks, nk;
-      walk.tile(j, ks, nk);
-      __syncthreads();
-#pragma unroll
-      for (int c = tid; c < BK * D / 8; c += 256) {
-        const int r = c / (D / 8), c8 = c % (D / 8);
-        u32x4 v = {0, 0, 0, 0};
-        if (r < nk) v = ld16(K + (size_t)(ks + r) * D + c8 * 8);
-        st16(&Ks[r * KP + c8 * 8], v);
-      }
-#pragma unroll
-      for (int c = tid; c < D * BK / 8; c += 256) {
-        const int r = c / (BK / 8), c8 = c % (BK / 8);
-        u32x4 v = {0, 0, 0, 0};
-        if (c8 * 8 < nk) v = ld16(Vt + (size_t)r * L + ks + c8 * 8);
-        st16(&Vs[r * VP + c8 * 8], v);
-      }
-      __syncthreads();
 
-      f32x16 s[2];
+  u32x4 kreg[KCH], vreg[VCH];
+  auto gload = [&](int j) {
+    int ks, nk;
+    walk.tile(j, ks, nk);
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        s[kb2] = f32x16{};
-        const bf16_t* krow = &Ks[(kb2 * 32 + krow_perm) * KP + hg * 8];
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / (D / 8), c8 = c % (D / 8);
+      kreg[i] = u32x4{0, 0, 0, 0};
+      if (r < nk) kreg[i] = ld16(K + (size_t)(ks + r) * D + c8 * 8);
+    }
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) s[kb2] = mfma32x32x16(as_bf16x8(ld16(krow + kk * 16)), qf[kk], s[kb2]);
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / (BK / 8), c8 = c % (BK / 8);
+      vreg[i] = u32x4{0, 0, 0, 0};
+      if (c8 * 8 < nk) vreg[i] = ld16(Vt + (size_t)r * L + ks + c8 * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i;
+      st16(&Ks[buf][(c / (D / 8)) * KP + (c % (D / 8)) * 8], kreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + 256 * i;
+      st16(&Vs[buf][(c / (BK / 8)) * VP + (c % (BK / 8)) * 8], vreg[i]);
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int j = 0; j < walk.n; ++j) {
+    int ks, nk;
+    walk.tile(j, ks, nk);
+    if (j + 1 < walk.n) gload(j + 1);
+    const bf16_t* Kb = Ks[j & 1];
+    const bf16_t* Vb = Vs[j & 1];
+
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {   // two 32-key halves: QK -> softmax -> PV
+      f32x16 s[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+      const bf16_t* krow = Kb + (kb2 * 32 + krow_perm) * KP + hg * 8;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 af = as_bf16x8(ld16(krow + kk * 16));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(af, qf[qb][kk], s[qb]);
       }
-      float mx = -INFINITY;
+      if (nk < BK) {   // partial tile: keys past nk do not exist
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int i = 0; i < 16; ++i)
+          if (kb2 * 32 + hg * 16 + i >= nk) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb2 * 32 + hg * 16 + i;
-          const float v = key < nk ? s[kb2][i] * a.scale_log2 : -INFINITY;
-          s[kb2][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(s[kb2][i] - m_new);
-          s[kb2][i] = p;
-          lsum += p;
-        }
-      l_run = l_run * corr + lsum;
-#pragma unroll
-      for (int b = 0; b < NDB; ++b) o[b] *= corr;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          bf16x8 pb;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(s[kb2][h2 * 8 + j]);
-#pragma unroll
-          for (int b = 0; b < NDB; ++b) {
-            const bf16_t* vrow = &Vs[(b * 32 + l32) * VP + kb2 * 32 + hg * 16 + h2 * 8];
-            o[b] = mfma32x32x16(as_bf16x8(ld16(vrow)), pb, o[b]);
+            for (int qb = 0; qb < QB; ++qb) s[qb][i] = -INFINITY;
           }
+      }
+      float mx[QB];
+      bool need = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float m = s[qb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, s[qb][i]);
+        mx[qb] = half_max(m) * sl2;
+        need |= mx[qb] > m_run[qb] + kRescaleLog2;
+      }
+      if (__any(need)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = fmaxf(m_run[qb], mx[qb]);
+          const float corr = fast_exp2(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_run[qb] *= corr;
+#pragma unroll
+          for (int b = 0; b < NDB; ++b) o[qb][b] *= corr;
+        }
+      }
+      bf16x8 pb[QB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float nm = -m_run[qb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(s[qb][i], sl2, nm));
+          lsum += p;
+          pb[qb][i >> 3][i & 7] = static_cast<__bf16>(p);
+        }
+        l_run[qb] += lsum;
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const bf16x8 vf = as_bf16x8(ld16(Vb + (b * 32 + l32) * VP + kb2 * 32 + hg * 16 + h2 * 8));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][b] = mfma32x32x16(vf, pb[qb][h2], o[qb][b]);
         }
     }
+    if (j + 1 < walk.n) lstore((j + 1) & 1);
+    __syncthreads();
   }
 
-  const float l_tot = half_sum(l_run);
-  if (!qvalid) return;
-  const float inv = 1.f / l_tot;
   const int bidx = it.bh / g.H, h = it.bh % g.H;
-  const float gate = a.g_s ? a.g_s[(size_t)it.bh * L + qrow] : 1.f;
-  const float sc = inv * gate;
-  bf16_t* orow = a.out + (((size_t)bidx * L + qrow) * g.H + h) * D;
 #pragma unroll
-  for (int b = 0; b < NDB; ++b)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = half_sum(l_run[qb]);
+    const int qrow = q0 + wave * 64 + qb * 32 + l32;
+    if (qrow >= it.q_end) continue;
+    const float gate = a.g_s ? a.g_s[(size_t)it.bh * L + qrow] : 1.f;
+    const float sc = gate / l_tot;
+    bf16_t* orow = a.out + (((size_t)bidx * L + qrow) * g.H + h) * D;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int dv = b * 32 + 8 * i4 + 4 * hg;
-      u32x2 pk;
-      pk[0] = pack_bf16x2(o[b][i4 * 4 + 0] * sc, o[b][i4 * 4 + 1] * sc);
-      pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc, o[b][i4 * 4 + 3] * sc);
-      *reinterpret_cast<u32x2*>(orow + dv) = pk;
-    }
-  if (a.lse && hg == 0) a.lse[(size_t)it.bh * L + qrow] = m_run * kLn2 + logf(l_tot);
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int dv = b * 32 + 8 * i4 + 4 * hg;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[qb][b][i4 * 4 + 0] * sc, o[qb][b][i4 * 4 + 1] * sc);
+        pk[1] = pack_bf16x2(o[qb][b][i4 * 4 + 2] * sc, o[qb][b][i4 * 4 + 3] * sc);
+        *reinterpret_cast<u32x2*>(orow + dv) = pk;
+      }
+    if (a.lse && hg == 0) a.lse[(size_t)it.bh * L + qrow] = m_run[qb] * kLn2 + logf(l_tot);
+  }
 }
 
 bool window_softmax_mfma_ok(const Geometry& g) {
@@ -296,7 +364,7 @@ hipError_t launch_window_softmax_mfma(const Geometry& g, const uint16_t* q, cons
                                       float* lse, float scale, hipStream_t s) {
   WinArgs a;
   a.g = g;
-  a.w = window_work(g, 128);
+  a.w = window_work(g, kWinBQ);
   a.q = q; a.k = k; a.vt = vt; a.g_s = g_s; a.out = out; a.lse = lse;
   a.scale_log2 = scale * kLog2e;
   if (a.w.grid == 0) return hipSuccess;

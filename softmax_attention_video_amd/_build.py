@@ -33,9 +33,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source extra flags.  The window Softmax kernel keeps MFMA results in
+# arch VGPRs so its softmax arithmetic reads S without AGPR moves.
+EXTRA = {"k_window_softmax.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

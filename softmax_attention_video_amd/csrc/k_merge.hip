@@ -8,78 +8,114 @@
 // over the concatenated contraction [Ohat_s | Ohat_l] [W_s ; W_l].
 //
 // bf16 path: both operands K-contiguous (the projections are transposed
-// once per call into the workspace, W^T [Dm, K]), 128 x 128 output tiles,
-// 256 threads, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The
-// product is formed as out^T blocks so each lane owns 4 consecutive output
-// features of one token (8-byte stores).
+// once per call into the workspace, W^T [Dm, K]), 256 x 256 output tiles
+// (4 waves of 128 x 128), 32-deep K steps through double-buffered LDS with
+// the next step's global loads in flight, v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation.  The product is formed as out^T blocks so each lane owns 4
+// consecutive output features of one token (8-byte stores).
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
 namespace vdn {
+
+constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
 
 __global__ __launch_bounds__(256) void merge_gemm_bf16_kernel(const bf16_t* __restrict__ a0,
                                                               const bf16_t* __restrict__ a1,
                                                               const bf16_t* __restrict__ bt0,
                                                               const bf16_t* __restrict__ bt1,
                                                               bf16_t* __restrict__ out,
-                                                              long long M, int K, int N) {
-  constexpr int BM = 128, BN = 128, BK = 64, P = BK + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * P];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
-  const long long m0 = (long long)blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-  const int K2 = 2 * K;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+                                                              long long M, int K, int N,
+                                                              int tiles_m, int tiles_n) {
+  constexpr int BM = kGBM, BN = kGBN, BK = kGBK;
+  constexpr int P = BK + 8;   // 80-byte rows: 16 consecutive rows hit distinct LDS banks
+  constexpr int CH = BM * BK / 8 / 256;   // 16-byte chunks per thread per operand tile
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * P];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * P];
 
-  for (int k0 = 0; k0 < K2; k0 += BK) {
-    __syncthreads();
+  // XCD-aware order: XCD x (= blockIdx % 8) walks a contiguous run of tiles,
+  // N-fastest, so the tiles sharing one row panel of A run in one L2.
+  const long long ntiles = (long long)tiles_m * tiles_n;
+  const long long per = (ntiles + kNumXcd - 1) / kNumXcd;
+  const long long tl = (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
+  if (blockIdx.x / kNumXcd >= per || tl >= ntiles) return;
+  const long long m0 = (tl / tiles_n) * BM;
+  const int n0 = (int)(tl % tiles_n) * BN;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;   // wave tile: 128 x 128
+  const int K2 = 2 * K;
+  const int nkt = (K2 + BK - 1) / BK;
+
+  f32x16 acc[4][4];
 #pragma unroll
-    for (int c = tid; c < BM * BK / 8; c += 256) {
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  u32x4 ra[CH], rb[CH];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i;
       const int r = c / (BK / 8), c8 = c % (BK / 8);
-      const int kc = k0 + c8 * 8;
-      u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+      const int kc = kt * BK + c8 * 8;
       const long long m = m0 + r;
       const int n = n0 + r;
+      ra[i] = u32x4{0, 0, 0, 0};
+      rb[i] = u32x4{0, 0, 0, 0};
       if (kc < K) {
-        if (m < M) va = ld16(a0 + (size_t)m * K + kc);
-        if (n < N) vb = ld16(bt0 + (size_t)n * K + kc);
+        if (m < M) ra[i] = ld16(a0 + (size_t)m * K + kc);
+        if (n < N) rb[i] = ld16(bt0 + (size_t)n * K + kc);
       } else if (kc < K2) {
-        if (m < M) va = ld16(a1 + (size_t)m * K + (kc - K));
-        if (n < N) vb = ld16(bt1 + (size_t)n * K + (kc - K));
+        if (m < M) ra[i] = ld16(a1 + (size_t)m * K + (kc - K));
+        if (n < N) rb[i] = ld16(bt1 + (size_t)n * K + (kc - K));
       }
-      st16(&As[r * P + c8 * 8], va);
-      st16(&Bs[r * P + c8 * 8], vb);
     }
-    __syncthreads();
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i;
+      const int off = (c / (BK / 8)) * P + (c % (BK / 8)) * 8;
+      st16(&As[buf][off], ra[i]);
+      st16(&Bs[buf][off], rb[i]);
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) gload(kt + 1);
+    const bf16_t* Ab = As[kt & 1];
+    const bf16_t* Bb = Bs[kt & 1];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 bm[2];
+      bf16x8 fm[4], fn[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        bm[mb] = as_bf16x8(ld16(&As[(wm * 64 + mb * 32 + l32) * P + ks * 16 + hg * 8]));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const bf16x8 an = as_bf16x8(ld16(&Bs[(wn * 64 + nb * 32 + l32) * P + ks * 16 + hg * 8]));
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32x32x16(an, bm[mb], acc[nb][mb]);
+      for (int i = 0; i < 4; ++i) {
+        fm[i] = as_bf16x8(ld16(Ab + (wm * 128 + i * 32 + l32) * P + ks * 16 + hg * 8));
+        fn[i] = as_bf16x8(ld16(Bb + (wn * 128 + i * 32 + l32) * P + ks * 16 + hg * 8));
       }
-    }
-  }
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const long long m = m0 + wm * 64 + mb * 32 + l32;
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32x32x16(fn[nb], fm[mb], acc[nb][mb]);
+    }
+    if (kt + 1 < nkt) lstore((kt + 1) & 1);
+    __syncthreads();
+  }
+  // acc[nb][mb] holds out^T: lane = token (l32), registers = 4 consecutive features
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const long long m = m0 + wm * 128 + mb * 32 + l32;
     if (m >= M) continue;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int n = n0 + wn * 64 + nb * 32 + 8 * i4 + 4 * hg;
+        const int n = n0 + wn * 128 + nb * 32 + 8 * i4 + 4 * hg;
         if (n >= N) continue;
         u32x2 pk;
         pk[0] = pack_bf16x2(acc[nb][mb][i4 * 4 + 0], acc[nb][mb][i4 * 4 + 1]);
@@ -93,8 +129,10 @@ hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const 
                                   const uint16_t* w1t, uint16_t* out, long long M, int K, int Dm,
                                   hipStream_t s) {
   if (M == 0 || Dm == 0) return hipSuccess;
-  dim3 grid((unsigned)((Dm + 127) / 128), (unsigned)((M + 127) / 128));
-  merge_gemm_bf16_kernel<<<grid, 256, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm);
+  const int tm = (int)((M + kGBM - 1) / kGBM), tn = (Dm + kGBN - 1) / kGBN;
+  const long long nt = (long long)tm * tn;
+  const long long grid = ((nt + kNumXcd - 1) / kNumXcd) * kNumXcd;
+  merge_gemm_bf16_kernel<<<(unsigned)grid, 256, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm, tm, tn);
   return hipGetLastError();
 }
 

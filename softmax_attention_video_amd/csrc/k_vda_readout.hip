@@ -108,6 +108,108 @@ __global__ __launch_bounds__(256) void vda_readout_simt_kernel(Geometry g, const
   }
 }
 
+// bf16 path (D = 64, 128): one workgroup per (b, h, query frame).  M_t is
+// built once in fp32, stored transposed in LDS as bf16 hi + lo parts, and
+// O_l^T = M^T Q^T runs on v_mfma_f32_32x32x16_bf16 (hi and lo products
+// accumulate in fp32, so M keeps ~16 extra mantissa bits).  A lane ends up
+// holding one token and half of its dv values: the RMS is an in-lane sum of
+// squares plus one exchange with lane ^ 32.
+template <int D>
+__global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const bf16_t* __restrict__ q,
+                                                               const float* __restrict__ alpha,
+                                                               const float* __restrict__ P_fwd,
+                                                               const float* __restrict__ P_rev,
+                                                               const float* __restrict__ g_l,
+                                                               const float* __restrict__ gamma,
+                                                               float eps, bf16_t* __restrict__ out) {
+  constexpr int MP = D + 8;        // pitch of M^T (bf16)
+  constexpr int NKK = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t mh[D * MP];
+  __shared__ __attribute__((aligned(16))) bf16_t ml[D * MP];
+  __shared__ float dfs[D], drs[D];
+
+  const int t = blockIdx.x % g.F;
+  const int bh = blockIdx.x / g.F;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  int i_f, ws, i_r, we;
+  readout_indices(g, t, i_f, ws, i_r, we);
+  const float* al = alpha + (size_t)bh * g.F * D;
+  for (int k = tid; k < D; k += 256) {
+    float df = 1.f, dr = 1.f;
+    for (int f = ws; f <= t; ++f) df *= al[(size_t)f * D + k];
+    for (int f = t; f <= we; ++f) dr *= al[(size_t)f * D + k];
+    dfs[k] = df;
+    drs[k] = dr;
+  }
+  __syncthreads();
+  const size_t DD = (size_t)D * D;
+  const float* pf = P_fwd + ((size_t)bh * (g.C + 1) + i_f) * DD;
+  const float* pr = P_rev + ((size_t)bh * (g.C + 1) + i_r) * DD;
+  for (int e4 = tid; e4 < D * D / 4; e4 += 256) {
+    const int k = e4 / (D / 4), j0 = (e4 % (D / 4)) * 4;
+    const f32x4 a4 = *reinterpret_cast<const f32x4*>(pf + (size_t)k * D + j0);
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(pr + (size_t)k * D + j0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float mv = dfs[k] * a4[c] + drs[k] * b4[c];
+      const bf16_t hi = f32_to_bf16(mv);
+      mh[(j0 + c) * MP + k] = hi;
+      ml[(j0 + c) * MP + k] = f32_to_bf16(mv - bf16_to_f32(hi));
+    }
+  }
+  __syncthreads();
+
+  float gm[NDB][16];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) gm[b][i] = gamma ? gamma[b * 32 + mfma32_row(i, hg)] : 1.f;
+  const int bidx = bh / g.H, h = bh % g.H;
+  const size_t tok0 = (size_t)bh * g.L + (size_t)t * g.N;
+  for (int n0 = wave * 32; n0 < g.N; n0 += 128) {
+    const int n = n0 + l32;
+    const bool valid = n < g.N;
+    bf16x8 qf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 v = {0, 0, 0, 0};
+      if (valid) v = ld16(q + (tok0 + n) * D + kk * 16 + hg * 8);
+      qf[kk] = as_bf16x8(v);
+    }
+    f32x16 o[NDB];
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) {
+      o[b] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int off = (b * 32 + l32) * MP + kk * 16 + hg * 8;
+        o[b] = mfma32x32x16(as_bf16x8(ld16(&mh[off])), qf[kk], o[b]);
+        o[b] = mfma32x32x16(as_bf16x8(ld16(&ml[off])), qf[kk], o[b]);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fmaf(o[b][i], o[b][i], ss);
+    ss = half_sum(ss);
+    if (!valid) continue;
+    const size_t l = (size_t)t * g.N + n;
+    const float sc = g_l[(size_t)bh * g.L + l] * rsqrtf(ss / (float)D + eps);
+    bf16_t* orow = out + (((size_t)bidx * g.L + l) * g.H + h) * D;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[b][i4 * 4 + 0] * sc * gm[b][i4 * 4 + 0], o[b][i4 * 4 + 1] * sc * gm[b][i4 * 4 + 1]);
+        pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc * gm[b][i4 * 4 + 2], o[b][i4 * 4 + 3] * sc * gm[b][i4 * 4 + 3]);
+        *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * i4 + 4 * hg) = pk;
+      }
+  }
+}
+
 template <typename T>
 hipError_t launch_vda_readout(const Geometry& g, const T* q, const float* alpha, const float* P_fwd,
                               const float* P_rev, const float* g_l, const float* gamma, float eps,
@@ -123,11 +225,23 @@ hipError_t launch_vda_readout(const Geometry& g, const T* q, const float* alpha,
   return hipGetLastError();
 }
 
+template <>
+hipError_t launch_vda_readout<bf16_t>(const Geometry& g, const bf16_t* q, const float* alpha,
+                                      const float* P_fwd, const float* P_rev, const float* g_l,
+                                      const float* gamma, float eps, bf16_t* out, hipStream_t s) {
+  const unsigned grid = (unsigned)(g.B * g.H * g.F);
+  switch (g.D) {
+    case 16: vda_readout_simt_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    case 32: vda_readout_simt_kernel<bf16_t, 32><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    case 64: vda_readout_mfma_kernel<64><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    case 128: vda_readout_mfma_kernel<128><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template hipError_t launch_vda_readout<float>(const Geometry&, const float*, const float*,
                                               const float*, const float*, const float*,
                                               const float*, float, float*, hipStream_t);
-template hipError_t launch_vda_readout<bf16_t>(const Geometry&, const bf16_t*, const float*,
-                                               const float*, const float*, const float*,
-                                               const float*, float, bf16_t*, hipStream_t);
 
 }  // namespace vdn

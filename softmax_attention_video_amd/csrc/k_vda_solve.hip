@@ -13,11 +13,17 @@
 // Our design: one workgroup (256 threads, a 16 x 16 thread grid) per
 // (b, h, frame), frame index F being the text frame.  Thread (tr, tc) owns
 // rows tr*R..tr*R+R-1 of the augmented matrix [I + A | W] in columns
-// tc*R..tc*R+R-1 of each half (R = D / 16), i.e. 2 R^2 fp32 registers.  The
-// statistics are accumulated straight into that ownership, so A and W never
-// leave registers.  I + A is symmetric positive definite (eigenvalues >= 1),
-// so the elimination needs no pivoting; each pivot step broadcasts the pivot
-// row and column through double-buffered LDS with one barrier.
+// tc*R..tc*R+R-1 of each half (R = D / 16), i.e. 2 R^2 fp32 registers.
+// I + A is symmetric positive definite (eigenvalues >= 1), so the
+// elimination needs no pivoting; each pivot step broadcasts the pivot row
+// and column through double-buffered LDS with one barrier.
+//
+// Statistics: the bf16 kernel (D = 64, 128) contracts over tokens on
+// v_mfma_f32_32x32x16_bf16.  Tokens must be the contracted (lane-contiguous)
+// index, so each 64-token tile is transposed into LDS ([channel][token]).
+// beta * K is formed in fp32 and split into bf16 hi + lo parts, so A and W
+// carry ~16 more mantissa bits than a single bf16 product.  The generic
+// kernel (fp32 storage, any D) accumulates in fp32 on the VALU.
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
@@ -38,6 +44,136 @@ struct SolveArgs {
   float* S_text;
 };
 
+struct GJShared {
+  float colbuf[2][128];
+  float rowM[2][128];
+  float rowW[2][128];
+};
+
+// Anchor frames are excluded from both scans: decay only (T = diag(alpha), U = 0).
+template <int D>
+__device__ __forceinline__ void emit_anchor(const Geometry& g, const float* alpha, float* Tf,
+                                            float* Uf, int bh, int fr) {
+  const size_t DD = (size_t)D * D;
+  const float* al = alpha + ((size_t)bh * g.F + fr) * D;
+  float* Tout = Tf + ((size_t)bh * g.F + fr) * DD;
+  float* Uout = Uf + ((size_t)bh * g.F + fr) * DD;
+  for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
+    const int i = e / D, j = e % D;
+    Tout[e] = (i == j) ? al[j] : 0.f;
+    Uout[e] = 0.f;
+  }
+}
+
+// In-place Gauss-Jordan on [I + A | W] held as (m | w) in the thread-grid
+// ownership; on return m = (I + A)^{-1} and w = (I + A)^{-1} W.
+template <int D>
+__device__ __forceinline__ void gauss_jordan(float (&m)[D / 16][D / 16], float (&w)[D / 16][D / 16],
+                                             GJShared& sh, int tr, int tc) {
+  constexpr int R = D / 16;
+  for (int kb = 0; kb < 16; ++kb) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int k = kb * R + r;
+      const int buf = k & 1;
+      if (tc == kb) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) sh.colbuf[buf][tr * R + i] = m[i][r];
+      }
+      if (tr == kb) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          sh.rowM[buf][tc * R + j] = m[r][j];
+          sh.rowW[buf][tc * R + j] = w[r][j];
+        }
+      }
+      __syncthreads();
+      const float p = 1.f / sh.rowM[buf][k];
+      float cik[R], rkj[R], rkw[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) cik[i] = sh.colbuf[buf][tr * R + i] * p;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        rkj[j] = sh.rowM[buf][tc * R + j];
+        rkw[j] = sh.rowW[buf][tc * R + j];
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          m[i][j] = fmaf(-cik[i], rkj[j], m[i][j]);
+          w[i][j] = fmaf(-cik[i], rkw[j], w[i][j]);
+        }
+      if (tr == kb) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          m[r][j] = rkj[j] * p;
+          w[r][j] = rkw[j] * p;
+        }
+      }
+      if (tc == kb) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) m[i][r] = -cik[i];
+      }
+      if (tr == kb && tc == kb) m[r][r] = p;
+    }
+  }
+}
+
+// Write T = X diag(alpha), U = X W for a video frame, or S_text = X W.
+template <int D>
+__device__ __forceinline__ void emit_solution(const Geometry& g, const float* alpha, float* Tf,
+                                              float* Uf, float* S_text, int bh, int fr, bool text,
+                                              const float (&m)[D / 16][D / 16],
+                                              const float (&w)[D / 16][D / 16], int tr, int tc) {
+  constexpr int R = D / 16;
+  const size_t DD = (size_t)D * D;
+  if (text) {
+    float* S = S_text + (size_t)bh * DD;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int j = 0; j < R; ++j) S[(size_t)(tr * R + i) * D + tc * R + j] = w[i][j];
+    return;
+  }
+  const float* al = alpha + ((size_t)bh * g.F + fr) * D;
+  float* Tout = Tf + ((size_t)bh * g.F + fr) * DD;
+  float* Uout = Uf + ((size_t)bh * g.F + fr) * DD;
+  float aj[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) aj[j] = al[tc * R + j];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const size_t e = (size_t)(tr * R + i) * D + tc * R + j;
+      Tout[e] = m[i][j] * aj[j];
+      Uout[e] = w[i][j];
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void frame_tokens(const SolveArgs<T>& a, int bh, int fr, bool text,
+                                             const T*& kp, const T*& vp, const float*& bp,
+                                             long long& ntok) {
+  const Geometry& g = a.g;
+  if (text) {
+    ntok = g.T;
+    kp = a.k_text + (size_t)bh * g.T * g.D;
+    vp = a.v_text + (size_t)bh * g.T * g.D;
+    bp = a.beta_text + (size_t)bh * g.T;
+  } else {
+    ntok = g.N;
+    const size_t off = (size_t)bh * g.L + (size_t)fr * g.N;
+    kp = a.k + off * g.D;
+    vp = a.v + off * g.D;
+    bp = a.beta + off;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel: fp32 VALU statistics.
+// ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void vda_frame_solve_kernel(SolveArgs<T> a) {
   constexpr int R = D / 16;
@@ -45,46 +181,21 @@ __global__ __launch_bounds__(256) void vda_frame_solve_kernel(SolveArgs<T> a) {
   __shared__ float Ks[TT][D + 1];
   __shared__ float Vs[TT][D + 1];
   __shared__ float Bs[TT];
-  __shared__ float colbuf[2][D];
-  __shared__ float rowM[2][D];
-  __shared__ float rowW[2][D];
+  __shared__ GJShared sh;
 
   const Geometry& g = a.g;
   const int fr = blockIdx.x % (g.F + 1);
   const int bh = blockIdx.x / (g.F + 1);
   const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
   const bool text = (fr == g.F);
-  const size_t DD = (size_t)D * D;
-
   if (!text && g.anchors && (fr == 0 || fr == g.F - 1)) {
-    // Anchor frames are excluded from both scans: decay only.
-    const float* al = a.alpha + ((size_t)bh * g.F + fr) * D;
-    float* Tout = a.Tf + ((size_t)bh * g.F + fr) * DD;
-    float* Uout = a.Uf + ((size_t)bh * g.F + fr) * DD;
-    for (int e = tid; e < D * D; e += 256) {
-      const int i = e / D, j = e % D;
-      Tout[e] = (i == j) ? al[j] : 0.f;
-      Uout[e] = 0.f;
-    }
+    emit_anchor<D>(g, a.alpha, a.Tf, a.Uf, bh, fr);
     return;
   }
-
-  const T* kp;
-  const T* vp;
+  const T *kp, *vp;
   const float* bp;
   long long ntok;
-  if (text) {
-    ntok = g.T;
-    kp = a.k_text + (size_t)bh * g.T * D;
-    vp = a.v_text + (size_t)bh * g.T * D;
-    bp = a.beta_text + (size_t)bh * g.T;
-  } else {
-    ntok = g.N;
-    const size_t off = (size_t)bh * g.L + (size_t)fr * g.N;
-    kp = a.k + off * D;
-    vp = a.v + off * D;
-    bp = a.beta + off;
-  }
+  frame_tokens(a, bh, fr, text, kp, vp, bp, ntok);
 
   float m[R][R], w[R][R];
 #pragma unroll
@@ -94,8 +205,6 @@ __global__ __launch_bounds__(256) void vda_frame_solve_kernel(SolveArgs<T> a) {
       m[i][j] = 0.f;
       w[i][j] = 0.f;
     }
-
-  // ---- statistics: m += beta k k^T, w += beta k v^T over the tokens ----
   for (long long t0 = 0; t0 < ntok; t0 += TT) {
     const int nt = (int)min((long long)TT, ntok - t0);
     __syncthreads();
@@ -128,79 +237,138 @@ __global__ __launch_bounds__(256) void vda_frame_solve_kernel(SolveArgs<T> a) {
 #pragma unroll
     for (int i = 0; i < R; ++i) m[i][i] += 1.f;
   }
+  gauss_jordan<D>(m, w, sh, tr, tc);
+  emit_solution<D>(g, a.alpha, a.Tf, a.Uf, a.S_text, bh, fr, text, m, w, tr, tc);
+}
 
-  // ---- in-place Gauss-Jordan on [I + A | W] -> [(I + A)^{-1} | (I + A)^{-1} W] ----
-  for (int kb = 0; kb < 16; ++kb) {
+// ---------------------------------------------------------------------------
+// bf16 kernel: MFMA statistics (D = 64, 128).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf16_t> a) {
+  constexpr int R = D / 16;
+  constexpr int TT = 64;            // tokens per tile
+  constexpr int TP = TT + 8;        // transposed tile pitch (bf16)
+  constexpr int NB = D / 32;        // 32-blocks per matrix side
+  constexpr int BPW = 2 * NB * NB / 4;   // output blocks per wave (A and W)
+  constexpr int XP = D + 1;         // fp32 transfer pitch
+  constexpr int PAIRS = TT / 2 * (D / 8) / 256;   // (token pair, 8-channel chunk) per thread
+  struct StatsTiles {
+    bf16_t kt[D * TP];    // K^T
+    bf16_t kh[D * TP];    // (beta K)^T, bf16 high part
+    bf16_t kl[D * TP];    // (beta K)^T, bf16 low part
+    bf16_t vt[D * TP];    // V^T
+  };
+  union Smem {
+    StatsTiles st;
+    float xfer[D * XP];
+  };
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ GJShared sh;
+
+  const Geometry& g = a.g;
+  const int fr = blockIdx.x % (g.F + 1);
+  const int bh = blockIdx.x / (g.F + 1);
+  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const bool text = (fr == g.F);
+  if (!text && g.anchors && (fr == 0 || fr == g.F - 1)) {
+    emit_anchor<D>(g, a.alpha, a.Tf, a.Uf, bh, fr);
+    return;
+  }
+  const bf16_t *kp, *vp;
+  const float* bp;
+  long long ntok;
+  frame_tokens(a, bh, fr, text, kp, vp, bp, ntok);
+
+  f32x16 acc[BPW];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int k = kb * R + r;
-      const int buf = k & 1;
-      if (tc == kb) {
+  for (int i = 0; i < BPW; ++i) acc[i] = f32x16{};
+
+  for (long long t0 = 0; t0 < ntok; t0 += TT) {
+    const int nt = (int)min((long long)TT, ntok - t0);
+    __syncthreads();
+    // transpose 64 tokens into [channel][token], two tokens per 4-byte write
 #pragma unroll
-        for (int i = 0; i < R; ++i) colbuf[buf][tr * R + i] = m[i][r];
+    for (int i = 0; i < PAIRS; ++i) {
+      const int pc = tid + 256 * i;
+      const int p = pc % (TT / 2), c8 = pc / (TT / 2);
+      const int t_a = 2 * p, t_b = 2 * p + 1;
+      u32x4 ka = {0, 0, 0, 0}, kb = {0, 0, 0, 0}, va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+      float ba = 0.f, bb = 0.f;
+      if (t_a < nt) {
+        ka = ld16(kp + (size_t)(t0 + t_a) * D + c8 * 8);
+        va = ld16(vp + (size_t)(t0 + t_a) * D + c8 * 8);
+        ba = bp[t0 + t_a];
       }
-      if (tr == kb) {
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          rowM[buf][tc * R + j] = m[r][j];
-          rowW[buf][tc * R + j] = w[r][j];
-        }
-      }
-      __syncthreads();
-      const float p = 1.f / rowM[buf][k];
-      float cik[R], rkj[R], rkw[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) cik[i] = colbuf[buf][tr * R + i] * p;
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        rkj[j] = rowM[buf][tc * R + j];
-        rkw[j] = rowW[buf][tc * R + j];
+      if (t_b < nt) {
+        kb = ld16(kp + (size_t)(t0 + t_b) * D + c8 * 8);
+        vb = ld16(vp + (size_t)(t0 + t_b) * D + c8 * 8);
+        bb = bp[t0 + t_b];
       }
 #pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          m[i][j] = fmaf(-cik[i], rkj[j], m[i][j]);
-          w[i][j] = fmaf(-cik[i], rkw[j], w[i][j]);
-        }
-      if (tr == kb) {
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          m[r][j] = rkj[j] * p;
-          w[r][j] = rkw[j] * p;
-        }
+      for (int jj = 0; jj < 8; ++jj) {
+        const uint32_t sh16 = (jj & 1) * 16;
+        const uint32_t xa = (ka[jj >> 1] >> sh16) & 0xFFFFu, xb = (kb[jj >> 1] >> sh16) & 0xFFFFu;
+        const uint32_t ya = (va[jj >> 1] >> sh16) & 0xFFFFu, yb = (vb[jj >> 1] >> sh16) & 0xFFFFu;
+        const float fa = ba * bf16_to_f32((bf16_t)xa), fb = bb * bf16_to_f32((bf16_t)xb);
+        const bf16_t ha = f32_to_bf16(fa), hb = f32_to_bf16(fb);
+        const bf16_t la = f32_to_bf16(fa - bf16_to_f32(ha)), lb = f32_to_bf16(fb - bf16_to_f32(hb));
+        const int off = (c8 * 8 + jj) * TP + t_a;
+        *reinterpret_cast<uint32_t*>(&sm.st.kt[off]) = xa | (xb << 16);
+        *reinterpret_cast<uint32_t*>(&sm.st.vt[off]) = ya | (yb << 16);
+        *reinterpret_cast<uint32_t*>(&sm.st.kh[off]) = (uint32_t)ha | ((uint32_t)hb << 16);
+        *reinterpret_cast<uint32_t*>(&sm.st.kl[off]) = (uint32_t)la | ((uint32_t)lb << 16);
       }
-      if (tc == kb) {
+    }
+    __syncthreads();
 #pragma unroll
-        for (int i = 0; i < R; ++i) m[i][r] = -cik[i];
+    for (int ks = 0; ks < TT / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int bi = wave * BPW + i;
+        const bool wblk = bi >= NB * NB;                 // block of W (else of A)
+        const int mb = (bi % (NB * NB)) / NB, nb = bi % NB;
+        const int col = ks * 16 + hg * 8;
+        const bf16x8 ah = as_bf16x8(ld16(&sm.st.kh[(mb * 32 + l32) * TP + col]));
+        const bf16x8 al = as_bf16x8(ld16(&sm.st.kl[(mb * 32 + l32) * TP + col]));
+        const bf16_t* bsrc = wblk ? sm.st.vt : sm.st.kt;
+        const bf16x8 bo = as_bf16x8(ld16(&bsrc[(nb * 32 + l32) * TP + col]));
+        acc[i] = mfma32x32x16(ah, bo, acc[i]);
+        acc[i] = mfma32x32x16(al, bo, acc[i]);
       }
-      if (tr == kb && tc == kb) m[r][r] = p;
     }
   }
 
-  // ---- emit T = X diag(alpha), U = X W (or S_text) ----
-  if (text) {
-    float* S = a.S_text + (size_t)bh * DD;
+  // accumulators -> GJ ownership, A first then W, through one fp32 buffer
+  float m[R][R], w[R][R];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int bi = wave * BPW + i;
+      if ((bi >= NB * NB) != (pass == 1)) continue;
+      const int mb = (bi % (NB * NB)) / NB, nb = bi % NB;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sm.xfer[(mb * 32 + mfma32_row(r, hg)) * XP + nb * 32 + l32] = acc[i][r];
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int j = 0; j < R; ++j) S[(size_t)(tr * R + i) * D + tc * R + j] = w[i][j];
-    return;
+      for (int j = 0; j < R; ++j) {
+        const float x = sm.xfer[(tr * R + i) * XP + tc * R + j];
+        if (pass == 0) m[i][j] = x; else w[i][j] = x;
+      }
   }
-  const float* al = a.alpha + ((size_t)bh * g.F + fr) * D;
-  float* Tout = a.Tf + ((size_t)bh * g.F + fr) * DD;
-  float* Uout = a.Uf + ((size_t)bh * g.F + fr) * DD;
-  float aj[R];
+  if (tr == tc) {
 #pragma unroll
-  for (int j = 0; j < R; ++j) aj[j] = al[tc * R + j];
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const size_t e = (size_t)(tr * R + i) * D + tc * R + j;
-      Tout[e] = m[i][j] * aj[j];
-      Uout[e] = w[i][j];
-    }
+    for (int i = 0; i < R; ++i) m[i][i] += 1.f;
+  }
+  gauss_jordan<D>(m, w, sh, tr, tc);
+  emit_solution<D>(g, a.alpha, a.Tf, a.Uf, a.S_text, bh, fr, text, m, w, tr, tc);
 }
 
 template <typename T>
@@ -220,13 +388,27 @@ hipError_t launch_vda_frame_solve(const Geometry& g, const T* k, const T* v, con
   return hipGetLastError();
 }
 
+template <>
+hipError_t launch_vda_frame_solve<bf16_t>(const Geometry& g, const bf16_t* k, const bf16_t* v,
+                                          const float* beta, const float* alpha,
+                                          const bf16_t* k_text, const bf16_t* v_text,
+                                          const float* beta_text, float* Tf, float* Uf,
+                                          float* S_text, hipStream_t s) {
+  SolveArgs<bf16_t> a{g, k, v, beta, alpha, k_text, v_text, beta_text, Tf, Uf, S_text};
+  const unsigned grid = (unsigned)(g.B * g.H * (g.F + 1));
+  switch (g.D) {
+    case 16: vda_frame_solve_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(a); break;
+    case 32: vda_frame_solve_kernel<bf16_t, 32><<<grid, 256, 0, s>>>(a); break;
+    case 64: vda_frame_solve_mfma_kernel<64><<<grid, 256, 0, s>>>(a); break;
+    case 128: vda_frame_solve_mfma_kernel<128><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template hipError_t launch_vda_frame_solve<float>(const Geometry&, const float*, const float*,
                                                   const float*, const float*, const float*,
                                                   const float*, const float*, float*, float*,
                                                   float*, hipStream_t);
-template hipError_t launch_vda_frame_solve<bf16_t>(const Geometry&, const bf16_t*, const bf16_t*,
-                                                   const float*, const float*, const bf16_t*,
-                                                   const bf16_t*, const float*, float*, float*,
-                                                   float*, hipStream_t);
 
 }  // namespace vdn

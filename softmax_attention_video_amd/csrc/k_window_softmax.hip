@@ -134,9 +134,11 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
 }
 
 // -------------------------------------------------------------------------
-// bf16 MFMA flash kernel.  256 threads = 4 waves; a wave owns 64 queries as
-// two 32-query blocks, so every K / V^T fragment read from LDS feeds two
-// MFMAs (half the LDS traffic of one block per wave).
+// bf16 MFMA flash kernel.  512 threads = 8 waves of 32 queries each (256
+// queries per workgroup), two waves per SIMD: while one wave runs its
+// softmax arithmetic on the VALU the other keeps the matrix core busy.
+// The kernel is compiled with MFMA results in arch VGPRs (not AGPRs) so the
+// softmax reads S without accumulator-register moves.
 //   S^T (keys x queries) = K Q^T  on v_mfma_f32_32x32x16_bf16;
 //   O^T (dv x queries)  += V^T P^T, with V pre-transposed to [D, L].
 // In the S^T accumulator a lane holds one query (lane % 32) and 16 keys, so
@@ -145,9 +147,9 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
 // of each 32-key block in register order; those registers then feed the PV
 // product directly as its B operand, matching 16 contiguous bytes of V^T.
 //
-// Pipeline: the next key tile is fetched from global memory into registers
-// while the current one is computed from LDS, then written into the other
-// LDS buffer; one barrier per tile.
+// Pipeline: the next 128-key tile is fetched from global memory into
+// registers while the current one is computed from LDS, then written into
+// the other LDS buffer; one barrier per tile.
 //
 // Online softmax with a lazy rescale: O and l are kept relative to a
 // running reference max m; the reference only moves (and O, l are rescaled)
@@ -167,20 +169,21 @@ struct WinArgs {
   float scale_log2;
 };
 
-constexpr int kWinBQ = 256;          // queries per workgroup
+constexpr int kWinNW = 8, kWinQB = 1;      // waves per workgroup, 32-query blocks per wave
+constexpr int kWinBQ = kWinNW * kWinQB * 32;  // queries per workgroup
 constexpr float kRescaleLog2 = 8.f;
 
 __device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
 template <int D>
-__global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
-  constexpr int BQ = kWinBQ, BK = 64, QB = 2;
+__global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArgs a) {
+  constexpr int BQ = kWinBQ, BK = 128, QB = kWinQB, NT = kWinNW * 64;
   constexpr int KP = D + 8;    // padded pitches (bf16 elements) against bank conflicts
   constexpr int VP = BK + 8;
   constexpr int NKK = D / 16;  // k-steps of QK^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  constexpr int KCH = BK * D / 8 / 256;   // 16-byte chunks per thread per tile
-  constexpr int VCH = D * BK / 8 / 256;
+  constexpr int KCH = BK * D / 8 / NT;   // 16-byte chunks per thread per tile
+  constexpr int VCH = D * BK / 8 / NT;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BK * KP];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * VP];
 
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
   bf16x8 qf[QB][NKK];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = q0 + wave * 64 + qb * 32 + l32;
+    const int qrow = q0 + wave * (QB * 32) + qb * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
@@ -229,14 +232,14 @@ __global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
     walk.tile(j, ks, nk);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int r = c / (D / 8), c8 = c % (D / 8);
       kreg[i] = u32x4{0, 0, 0, 0};
       if (r < nk) kreg[i] = ld16(K + (size_t)(ks + r) * D + c8 * 8);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int r = c / (BK / 8), c8 = c % (BK / 8);
       vreg[i] = u32x4{0, 0, 0, 0};
       if (c8 * 8 < nk) vreg[i] = ld16(Vt + (size_t)r * L + ks + c8 * 8);
@@ -245,12 +248,12 @@ __global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       st16(&Ks[buf][(c / (D / 8)) * KP + (c % (D / 8)) * 8], kreg[i]);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       st16(&Vs[buf][(c / (BK / 8)) * VP + (c % (BK / 8)) * 8], vreg[i]);
     }
   };
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
     const bf16_t* Vb = Vs[j & 1];
 
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {   // two 32-key halves: QK -> softmax -> PV
+    for (int kb2 = 0; kb2 < BK / 32; ++kb2) {   // 32-key blocks: QK -> softmax -> PV
       f32x16 s[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(256) void window_softmax_mfma_kernel(WinArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = half_sum(l_run[qb]);
-    const int qrow = q0 + wave * 64 + qb * 32 + l32;
+    const int qrow = q0 + wave * (QB * 32) + qb * 32 + l32;
     if (qrow >= it.q_end) continue;
     const float gate = a.g_s ? a.g_s[(size_t)it.bh * L + qrow] : 1.f;
     const float sc = gate / l_tot;
@@ -369,9 +372,9 @@ hipError_t launch_window_softmax_mfma(const Geometry& g, const uint16_t* q, cons
   a.scale_log2 = scale * kLog2e;
   if (a.w.grid == 0) return hipSuccess;
   if (g.D == 128)
-    window_softmax_mfma_kernel<128><<<a.w.grid, 256, 0, s>>>(a);
+    window_softmax_mfma_kernel<128><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
   else
-    window_softmax_mfma_kernel<64><<<a.w.grid, 256, 0, s>>>(a);
+    window_softmax_mfma_kernel<64><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

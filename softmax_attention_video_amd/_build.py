@@ -33,9 +33,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-# Per-source extra flags.  The window Softmax kernel keeps MFMA results in
-# arch VGPRs so its softmax arithmetic reads S without AGPR moves.
-EXTRA = {"k_window_softmax.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags: the window Softmax and merge GEMM kernels keep MFMA
+# results in arch VGPRs (two waves per SIMD fit in 256 registers; the
+# softmax arithmetic reads S without accumulator-register moves).
+EXTRA = {"k_window_softmax.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "k_merge.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

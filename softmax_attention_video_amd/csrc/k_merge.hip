@@ -8,19 +8,23 @@
 // over the concatenated contraction [Ohat_s | Ohat_l] [W_s ; W_l].
 //
 // bf16 path: both operands K-contiguous (the projections are transposed
-// once per call into the workspace, W^T [Dm, K]), 256 x 256 output tiles
-// (4 waves of 128 x 128), 32-deep K steps through double-buffered LDS with
-// the next step's global loads in flight, v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation.  The product is formed as out^T blocks so each lane owns 4
+// once per call into the workspace, W^T [Dm, K]), 256 x 256 output tiles,
+// 64-deep K steps through double-buffered LDS with the next step's global
+// loads in flight, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The product is formed as out^T blocks so each lane owns 4
 // consecutive output features of one token (8-byte stores).
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
 namespace vdn {
 
-constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
-
-__global__ __launch_bounds__(256) void merge_gemm_bf16_kernel(const bf16_t* __restrict__ a0,
+constexpr int kGBM = 256, kGBN = 256, kGBK = 64;
+// 8 waves (two per SIMD): wave (wm 0..3, wn 0..1) owns a 64 x 128 block of
+// the 256 x 256 tile.  Operand panels are read with buffer loads whose
+// descriptors end at the last row of A / W^T, so rows past M or N read as
+// zero without branches; K must be a multiple of the 64-deep K step.  The
+// LDS fragments of the next 16-deep step are loaded while the current
+// step's MFMAs run.
+__global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __restrict__ a0,
                                                               const bf16_t* __restrict__ a1,
                                                               const bf16_t* __restrict__ bt0,
                                                               const bf16_t* __restrict__ bt1,
@@ -28,88 +32,88 @@ __global__ __launch_bounds__(256) void merge_gemm_bf16_kernel(const bf16_t* __re
                                                               long long M, int K, int N,
                                                               int tiles_m, int tiles_n) {
   constexpr int BM = kGBM, BN = kGBN, BK = kGBK;
-  constexpr int P = BK + 8;   // 80-byte rows: 16 consecutive rows hit distinct LDS banks
-  constexpr int CH = BM * BK / 8 / 256;   // 16-byte chunks per thread per operand tile
+  constexpr int P = BK + 8;
+  constexpr int CH = BM * BK / 8 / 512;
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * P];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * P];
-
-  // XCD-aware order: XCD x (= blockIdx % 8) walks a contiguous run of tiles,
-  // N-fastest, so the tiles sharing one row panel of A run in one L2.
   const long long ntiles = (long long)tiles_m * tiles_n;
   const long long per = (ntiles + kNumXcd - 1) / kNumXcd;
   const long long tl = (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
   if (blockIdx.x / kNumXcd >= per || tl >= ntiles) return;
   const long long m0 = (tl / tiles_n) * BM;
   const int n0 = (int)(tl % tiles_n) * BN;
-
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;   // wave tile: 128 x 128
-  const int K2 = 2 * K;
-  const int nkt = (K2 + BK - 1) / BK;
-
-  f32x16 acc[4][4];
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nkt = 2 * K / BK;   // K % BK == 0
+  // descriptors over this tile's row panels (rows past M / N read as zero)
+  const rsrc_t ra0 = make_rsrc(a0 + (size_t)m0 * K, rsrc_bytes(a0 + (size_t)m0 * K, a0 + (size_t)M * K));
+  const rsrc_t ra1 = make_rsrc(a1 + (size_t)m0 * K, rsrc_bytes(a1 + (size_t)m0 * K, a1 + (size_t)M * K));
+  const rsrc_t rb0 = make_rsrc(bt0 + (size_t)n0 * K, rsrc_bytes(bt0 + (size_t)n0 * K, bt0 + (size_t)N * K));
+  const rsrc_t rb1 = make_rsrc(bt1 + (size_t)n0 * K, rsrc_bytes(bt1 + (size_t)n0 * K, bt1 + (size_t)N * K));
+  uint32_t voff[CH];
+  int soff[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 512 * i;
+    const int r = c / (BK / 8), c8 = c % (BK / 8);
+    voff[i] = (uint32_t)((r * K + c8 * 8) * 2);
+    soff[i] = (r * P + c8 * 8);
+  }
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  u32x4 ra[CH], rb[CH];
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  u32x4 pa[CH], pb[CH];
   auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+    const bool second = k0 >= K;
+    const uint32_t kb = (uint32_t)((second ? k0 - K : k0) * 2);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / (BK / 8), c8 = c % (BK / 8);
-      const int kc = kt * BK + c8 * 8;
-      const long long m = m0 + r;
-      const int n = n0 + r;
-      ra[i] = u32x4{0, 0, 0, 0};
-      rb[i] = u32x4{0, 0, 0, 0};
-      if (kc < K) {
-        if (m < M) ra[i] = ld16(a0 + (size_t)m * K + kc);
-        if (n < N) rb[i] = ld16(bt0 + (size_t)n * K + kc);
-      } else if (kc < K2) {
-        if (m < M) ra[i] = ld16(a1 + (size_t)m * K + (kc - K));
-        if (n < N) rb[i] = ld16(bt1 + (size_t)n * K + (kc - K));
-      }
+      pa[i] = buf_ld16(second ? ra1 : ra0, voff[i], kb);
+      pb[i] = buf_ld16(second ? rb1 : rb0, voff[i], kb);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      const int off = (c / (BK / 8)) * P + (c % (BK / 8)) * 8;
-      st16(&As[buf][off], ra[i]);
-      st16(&Bs[buf][off], rb[i]);
+      st16(&As[buf][soff[i]], pa[i]);
+      st16(&Bs[buf][soff[i]], pb[i]);
     }
   };
-
   gload(0);
   lstore(0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     if (kt + 1 < nkt) gload(kt + 1);
-    const bf16_t* Ab = As[kt & 1];
-    const bf16_t* Bb = Bs[kt & 1];
+    const bf16_t* Ab = As[kt & 1] + (wm * 64 + l32) * P + hg * 8;
+    const bf16_t* Bb = Bs[kt & 1] + (wn * 128 + l32) * P + hg * 8;
+    bf16x8 fm[2][2], fn[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fm[0][i] = as_bf16x8(ld16(Ab + i * 32 * P));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fn[0][i] = as_bf16x8(ld16(Bb + i * 32 * P));
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fm[4], fn[4];
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fm[i] = as_bf16x8(ld16(Ab + (wm * 128 + i * 32 + l32) * P + ks * 16 + hg * 8));
-        fn[i] = as_bf16x8(ld16(Bb + (wn * 128 + i * 32 + l32) * P + ks * 16 + hg * 8));
+        for (int i = 0; i < 2; ++i) fm[nxt][i] = as_bf16x8(ld16(Ab + i * 32 * P + (ks + 1) * 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fn[nxt][i] = as_bf16x8(ld16(Bb + i * 32 * P + (ks + 1) * 16));
       }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32x32x16(fn[nb], fm[mb], acc[nb][mb]);
+        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32x32x16(fn[cur][nb], fm[cur][mb], acc[nb][mb]);
     }
     if (kt + 1 < nkt) lstore((kt + 1) & 1);
     __syncthreads();
   }
-  // acc[nb][mb] holds out^T: lane = token (l32), registers = 4 consecutive features
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const long long m = m0 + wm * 128 + mb * 32 + l32;
+  for (int mb = 0; mb < 2; ++mb) {
+    const long long m = m0 + wm * 64 + mb * 32 + l32;
     if (m >= M) continue;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -132,7 +136,7 @@ hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const 
   const int tm = (int)((M + kGBM - 1) / kGBM), tn = (Dm + kGBN - 1) / kGBN;
   const long long nt = (long long)tm * tn;
   const long long grid = ((nt + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  merge_gemm_bf16_kernel<<<(unsigned)grid, 256, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm, tm, tn);
+  merge_gemm_bf16_kernel<<<(unsigned)grid, 512, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm, tm, tn);
   return hipGetLastError();
 }
 

@@ -121,15 +121,156 @@ __global__ __launch_bounds__(256) void vda_chunk_compose_kernel(Geometry g, cons
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 MFMA chain kernel (D = 64, 128): Y <- L_s Y (+ A_s), s = 0..S-1, on a
+// 32-column block of Y, with v_mfma_f32_32x32x2f32.  Wave w owns rows
+// 32w..32w+31: its slice of each left factor L_s goes straight from global
+// memory into registers (the next step's slice is fetched while the current
+// product runs), so the left factors never pass through LDS.  Y is kept
+// transposed in LDS (Yt[n][k]) so both MFMA operands are k-contiguous; the
+// contracted index is permuted identically on both operands (lane half g
+// takes k = k0 + 4g .. k0 + 4g + 3 of each 8-wide group).
+//
+// Mode compose: grid (b, h, dir, chunk, part in {T, U}, column block);
+//   Y0 = first frame's T or U columns, L_s = T of the next frames, A_s = U
+//   of the next frames for part U; the final Y is T_c / U_c.
+// Mode scan: grid (b, h, dir, column block); Y0 = init_scale * S_text,
+//   L_s = T_c, A_s = U_c in scan order; Y is written to P after every step.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void vda_chain_mfma_kernel(Geometry g, const float* __restrict__ Tf,
+                                                             const float* __restrict__ Uf,
+                                                             float* __restrict__ Tc, float* __restrict__ Uc,
+                                                             const float* __restrict__ S_text,
+                                                             float init_scale, float* __restrict__ P_fwd,
+                                                             float* __restrict__ P_rev, int mode,
+                                                             int dirs_mask) {
+  constexpr int NB = D / 32;            // row blocks (waves doing MFMA work)
+  constexpr int NCB = D / 32;           // 32-column blocks of Y
+  constexpr int YP = D + 4;             // pitch of Yt (floats)
+  constexpr int NK8 = D / 8;            // 8-wide k groups
+  __shared__ __attribute__((aligned(16))) float Yt[32 * YP];
+  const size_t DD = (size_t)D * D;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  int id = blockIdx.x;
+  const int cb = id % NCB; id /= NCB;
+  int part = 0, c = 0, dir, bh;
+  if (mode == 0) {
+    part = id % 2; id /= 2;
+    c = id % g.C; id /= g.C;
+  }
+  dir = id % 2;
+  bh = id / 2;
+  if (!((dirs_mask >> dir) & 1)) return;
+  const int col0 = cb * 32;
+  int nsteps;
+  const float *L0, *A0 = nullptr;
+  ptrdiff_t lstride;       // elements between consecutive left factors (signed: reverse order)
+  const float* ysrc;
+  float yscale = 1.f;
+  float* out_final = nullptr;
+  float* Pb = nullptr;
+  if (mode == 0) {
+    const int s0 = c * g.cf, e0 = s0 + g.cf - 1;
+    const int first = dir == 0 ? s0 : e0;
+    const int step = dir == 0 ? 1 : -1;
+    nsteps = g.cf - 1;
+    lstride = (ptrdiff_t)step * (ptrdiff_t)DD;
+    L0 = Tf + ((size_t)bh * g.F + first + step) * DD;
+    if (part == 1) A0 = Uf + ((size_t)bh * g.F + first + step) * DD;
+    ysrc = (part == 0 ? Tf : Uf) + ((size_t)bh * g.F + first) * DD;
+    out_final = (part == 0 ? Tc : Uc) + (((size_t)bh * 2 + dir) * g.C + c) * DD;
+  } else {
+    float* P = dir == 0 ? P_fwd : P_rev;
+    nsteps = g.C;
+    const int c0 = dir == 0 ? 0 : g.C - 1;
+    lstride = (dir == 0 ? 1 : -1) * (ptrdiff_t)DD;
+    L0 = Tc + (((size_t)bh * 2 + dir) * g.C + c0) * DD;
+    A0 = Uc + (((size_t)bh * 2 + dir) * g.C + c0) * DD;
+    ysrc = S_text + (size_t)bh * DD;
+    yscale = init_scale;
+    Pb = P + (size_t)bh * (g.C + 1) * DD;
+  }
+  // Y0 -> Yt (transposed), and the initial P slot in scan mode
+  for (int e = tid; e < D * 32; e += 256) {
+    const int k = e / 32, n = e % 32;
+    const float y = yscale * ysrc[(size_t)k * D + col0 + n];
+    Yt[n * YP + k] = y;
+    if (Pb) Pb[(size_t)(dir == 0 ? 0 : g.C) * DD + (size_t)k * D + col0 + n] = y;
+  }
+  const bool mw = wave < NB;           // waves holding a row block
+  const int mrow = wave * 32 + l32;    // this lane's row of the left factor
+  f32x4 lf[NK8], lnext[NK8];
+  auto load_left = [&](const float* Lm, f32x4 (&dst)[NK8]) {
+#pragma unroll
+    for (int j = 0; j < NK8; ++j)
+      dst[j] = mw ? *reinterpret_cast<const f32x4*>(Lm + (size_t)mrow * D + 8 * j + 4 * hg) : f32x4{};
+  };
+  if (nsteps > 0) load_left(L0, lf);
+  for (int st = 0; st < nsteps; ++st) {
+    const float* Lm = L0 + st * lstride;
+    if (st + 1 < nsteps) load_left(Lm + lstride, lnext);
+    __syncthreads();                      // Yt holds the current Y
+    f32x16 acc = f32x16{};
+    if (mw) {
+#pragma unroll
+      for (int j = 0; j < NK8; ++j) {
+        const f32x4 yb = *reinterpret_cast<const f32x4*>(&Yt[l32 * YP + 8 * j + 4 * hg]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = mfma32x32x2f32(lf[j][q], yb[q], acc);
+      }
+      if (A0) {
+        const float* Am = A0 + st * lstride;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += Am[(size_t)(wave * 32 + mfma32_row(i, hg)) * D + col0 + l32];
+      }
+    }
+    __syncthreads();                      // everyone has read the old Y
+    if (mw) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 v = {acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
+        *reinterpret_cast<f32x4*>(&Yt[l32 * YP + wave * 32 + 8 * i4 + 4 * hg]) = v;
+      }
+      if (Pb) {
+        const int slot = dir == 0 ? st + 1 : g.C - 1 - st;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          Pb[(size_t)slot * DD + (size_t)(wave * 32 + mfma32_row(i, hg)) * D + col0 + l32] = acc[i];
+      }
+      if (out_final && st + 1 == nsteps) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          out_final[(size_t)(wave * 32 + mfma32_row(i, hg)) * D + col0 + l32] = acc[i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NK8; ++j) lf[j] = lnext[j];
+  }
+  if (out_final && nsteps == 0) {   // single-frame chunk: the map itself
+    __syncthreads();
+    for (int e = tid; e < D * 32; e += 256) {
+      const int k = e / 32, n = e % 32;
+      out_final[(size_t)k * D + col0 + n] = Yt[n * YP + k];
+    }
+  }
+}
+
 hipError_t launch_vda_chunk_compose(const Geometry& g, const float* Tf, const float* Uf, float* Tc,
                                     float* Uc, int dirs_mask, hipStream_t s) {
+  if (g.D == 64 || g.D == 128) {
+    const unsigned grid = (unsigned)(g.B * g.H * 2 * g.C * 2 * (g.D / 32));
+    if (g.D == 128)
+      vda_chain_mfma_kernel<128><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, nullptr, 0.f, nullptr, nullptr, 0, dirs_mask);
+    else
+      vda_chain_mfma_kernel<64><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, nullptr, 0.f, nullptr, nullptr, 0, dirs_mask);
+    return hipGetLastError();
+  }
   const int NCB = 2 * ((g.D + kCB - 1) / kCB);
   const unsigned grid = (unsigned)(g.B * g.H * 2 * g.C * NCB);
   switch (g.D) {
     case 16: vda_chunk_compose_kernel<16><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
     case 32: vda_chunk_compose_kernel<32><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
-    case 64: vda_chunk_compose_kernel<64><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
-    case 128: vda_chunk_compose_kernel<128><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, dirs_mask); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -186,13 +327,20 @@ __global__ __launch_bounds__(256) void vda_chunk_scan_kernel(Geometry g, const f
 hipError_t launch_vda_chunk_scan(const Geometry& g, const float* Tc, const float* Uc,
                                  const float* S_text, float init_scale, float* P_fwd, float* P_rev,
                                  hipStream_t s) {
+  const int dirs = (P_fwd ? 1 : 0) | (P_rev ? 2 : 0);
+  if (g.D == 64 || g.D == 128) {
+    const unsigned grid = (unsigned)(g.B * g.H * 2 * (g.D / 32));
+    if (g.D == 128)
+      vda_chain_mfma_kernel<128><<<grid, 256, 0, s>>>(g, nullptr, nullptr, const_cast<float*>(Tc), const_cast<float*>(Uc), S_text, init_scale, P_fwd, P_rev, 1, dirs);
+    else
+      vda_chain_mfma_kernel<64><<<grid, 256, 0, s>>>(g, nullptr, nullptr, const_cast<float*>(Tc), const_cast<float*>(Uc), S_text, init_scale, P_fwd, P_rev, 1, dirs);
+    return hipGetLastError();
+  }
   const int NCB = (g.D + kCB - 1) / kCB;
   const unsigned grid = (unsigned)(g.B * g.H * 2 * NCB);
   switch (g.D) {
     case 16: vda_chunk_scan_kernel<16><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
     case 32: vda_chunk_scan_kernel<32><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
-    case 64: vda_chunk_scan_kernel<64><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
-    case 128: vda_chunk_scan_kernel<128><<<grid, 256, 0, s>>>(g, Tc, Uc, S_text, init_scale, P_fwd, P_rev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -49,6 +49,23 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Raw buffer loads (gfx9 buffer descriptor: stride 0, num_records = bytes,
+// word 3 = 0x00020000).  A 16-byte load whose range lies past num_records
+// returns zeros, so tile loads need no bounds branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+// Largest byte count a descriptor can cover starting at `base` of a tensor
+// whose end is `end` (clamped to 2^31 - 16).
+__device__ __forceinline__ uint32_t rsrc_bytes(const void* base, const void* end) {
+  const long long n = (const char*)end - (const char*)base;
+  return (uint32_t)(n < 0 ? 0 : (n > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : n));
+}
+
 // v_mfma_f32_32x32x16_bf16.  Operand layout (wave64): lane l supplies row
 // (l % 32) of A / column (l % 32) of B with 8 consecutive k-slots of its half
 // (l / 32).  A and B use the same k-slot mapping, so any bijection of the 16

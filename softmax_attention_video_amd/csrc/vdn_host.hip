@@ -387,7 +387,7 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
                                         (uint16_t*)out, M * K, s));
     else
       VDN_HIP(vdn::launch_add<float>((const float*)ohs, (const float*)ohl, (float*)out, M * K, s));
-  } else if (dt == VDN_BF16 && Dm % 8 == 0) {
+  } else if (dt == VDN_BF16 && Dm % 8 == 0 && K % 64 == 0) {
     uint16_t* w0t = (uint16_t*)(ws + lay.wt0);
     uint16_t* w1t = (uint16_t*)(ws + lay.wt1);
     VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_s, w0t, K, Dm, 1, s));

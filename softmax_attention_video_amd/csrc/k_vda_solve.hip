@@ -285,33 +285,44 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
 #pragma unroll
   for (int i = 0; i < BPW; ++i) acc[i] = f32x16{};
 
-  for (long long t0 = 0; t0 < ntok; t0 += TT) {
+  // raw tile data for (token pair, 8-channel chunk) units, prefetched one
+  // tile ahead so the global loads overlap the previous tile's MFMAs
+  u32x4 pk_a[PAIRS], pk_b[PAIRS], pv_a[PAIRS], pv_b[PAIRS];
+  float pb_a[PAIRS], pb_b[PAIRS];
+  auto fetch = [&](long long t0) {
     const int nt = (int)min((long long)TT, ntok - t0);
-    __syncthreads();
-    // transpose 64 tokens into [channel][token], two tokens per 4-byte write
 #pragma unroll
     for (int i = 0; i < PAIRS; ++i) {
       const int pc = tid + 256 * i;
       const int p = pc % (TT / 2), c8 = pc / (TT / 2);
       const int t_a = 2 * p, t_b = 2 * p + 1;
-      u32x4 ka = {0, 0, 0, 0}, kb = {0, 0, 0, 0}, va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-      float ba = 0.f, bb = 0.f;
+      pk_a[i] = pk_b[i] = pv_a[i] = pv_b[i] = u32x4{0, 0, 0, 0};
+      pb_a[i] = pb_b[i] = 0.f;
       if (t_a < nt) {
-        ka = ld16(kp + (size_t)(t0 + t_a) * D + c8 * 8);
-        va = ld16(vp + (size_t)(t0 + t_a) * D + c8 * 8);
-        ba = bp[t0 + t_a];
+        pk_a[i] = ld16(kp + (size_t)(t0 + t_a) * D + c8 * 8);
+        pv_a[i] = ld16(vp + (size_t)(t0 + t_a) * D + c8 * 8);
+        pb_a[i] = bp[t0 + t_a];
       }
       if (t_b < nt) {
-        kb = ld16(kp + (size_t)(t0 + t_b) * D + c8 * 8);
-        vb = ld16(vp + (size_t)(t0 + t_b) * D + c8 * 8);
-        bb = bp[t0 + t_b];
+        pk_b[i] = ld16(kp + (size_t)(t0 + t_b) * D + c8 * 8);
+        pv_b[i] = ld16(vp + (size_t)(t0 + t_b) * D + c8 * 8);
+        pb_b[i] = bp[t0 + t_b];
       }
+    }
+  };
+  // transpose into [channel][token], two tokens per 4-byte write
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < PAIRS; ++i) {
+      const int pc = tid + 256 * i;
+      const int p = pc % (TT / 2), c8 = pc / (TT / 2);
+      const int t_a = 2 * p;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const uint32_t sh16 = (jj & 1) * 16;
-        const uint32_t xa = (ka[jj >> 1] >> sh16) & 0xFFFFu, xb = (kb[jj >> 1] >> sh16) & 0xFFFFu;
-        const uint32_t ya = (va[jj >> 1] >> sh16) & 0xFFFFu, yb = (vb[jj >> 1] >> sh16) & 0xFFFFu;
-        const float fa = ba * bf16_to_f32((bf16_t)xa), fb = bb * bf16_to_f32((bf16_t)xb);
+        const uint32_t xa = (pk_a[i][jj >> 1] >> sh16) & 0xFFFFu, xb = (pk_b[i][jj >> 1] >> sh16) & 0xFFFFu;
+        const uint32_t ya = (pv_a[i][jj >> 1] >> sh16) & 0xFFFFu, yb = (pv_b[i][jj >> 1] >> sh16) & 0xFFFFu;
+        const float fa = pb_a[i] * bf16_to_f32((bf16_t)xa), fb = pb_b[i] * bf16_to_f32((bf16_t)xb);
         const bf16_t ha = f32_to_bf16(fa), hb = f32_to_bf16(fb);
         const bf16_t la = f32_to_bf16(fa - bf16_to_f32(ha)), lb = f32_to_bf16(fb - bf16_to_f32(hb));
         const int off = (c8 * 8 + jj) * TP + t_a;
@@ -321,7 +332,14 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
         *reinterpret_cast<uint32_t*>(&sm.st.kl[off]) = (uint32_t)la | ((uint32_t)lb << 16);
       }
     }
+  };
+
+  if (ntok > 0) fetch(0);
+  for (long long t0 = 0; t0 < ntok; t0 += TT) {
     __syncthreads();
+    stage();
+    __syncthreads();
+    if (t0 + TT < ntok) fetch(t0 + TT);
 #pragma unroll
     for (int ks = 0; ks < TT / 16; ++ks) {
 #pragma unroll

@@ -403,11 +403,48 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __res
   }
 }
 
+// Same transpose with 16-byte global accesses (rows % 8 == 0, cols % 8 == 0).
+__global__ __launch_bounds__(256) void transpose16_bf16_kernel(const bf16_t* __restrict__ src,
+                                                               bf16_t* __restrict__ dst,
+                                                               long long rows, int cols) {
+  __shared__ bf16_t t[64][66];
+  const long long r0 = (long long)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const size_t boff = (size_t)blockIdx.z * rows * cols;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = threadIdx.x + 256 * i;
+    const int r = ch >> 3, c8 = (ch & 7) * 8;
+    u32x4 v = {0, 0, 0, 0};
+    if (r0 + r < rows && c0 + c8 < cols) v = ld16(src + boff + (size_t)(r0 + r) * cols + c0 + c8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[r][c8 + 2 * j] = (bf16_t)(v[j] & 0xFFFFu);
+      t[r][c8 + 2 * j + 1] = (bf16_t)(v[j] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = threadIdx.x + 256 * i;
+    const int c = ch >> 3, r8 = (ch & 7) * 8;
+    if (c0 + c >= cols || r0 + r8 >= rows) continue;
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = (uint32_t)t[r8 + 2 * j][c] | ((uint32_t)t[r8 + 2 * j + 1][c] << 16);
+    st16(dst + boff + (size_t)(c0 + c) * rows + r0 + r8, v);
+  }
+}
+
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, long long rows, int cols,
                                  long long batch, hipStream_t s) {
   if (rows == 0 || cols == 0 || batch == 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols + 63) / 64), (unsigned)batch);
-  transpose_bf16_kernel<<<grid, 256, 0, s>>>(src, dst, rows, cols);
+  if (rows % 8 == 0 && cols % 8 == 0)
+    transpose16_bf16_kernel<<<grid, 256, 0, s>>>(src, dst, rows, cols);
+  else
+    transpose_bf16_kernel<<<grid, 256, 0, s>>>(src, dst, rows, cols);
   return hipGetLastError();
 }
 

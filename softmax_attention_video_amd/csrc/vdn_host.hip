@@ -45,6 +45,32 @@ hipError_t timer_mark(hipStream_t s, bool begin) {
   return e;
 }
 
+// Per-thread, per-device side stream and fork/join events for running the
+// VDA linear branch concurrently with the window Softmax.  Created on first
+// use at default priority; they live until the thread exits.
+struct SideStream {
+  int device = -1;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+thread_local SideStream g_side[16];
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    if ((e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    ss.device = dev;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 // Workspace carve-up (offsets in bytes, each 256-aligned).
 struct Layout {
   size_t vt, wt0, wt1, Tf, Uf, St, Tc, Uc, Pf, Pr, ohs, ohl, total;
@@ -366,18 +392,29 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   float* Pf = (float*)(ws + lay.Pf);
   float* Pr = (float*)(ws + lay.Pr);
 
-  // Linear branch (a1-a6)
-  st = run_scan(g, p, dt, k, v, beta, alpha, k_text, v_text, beta_text, ws, lay, Pf, Pr, s);
+  // Linear branch (a1-a6) on the side stream, forked from and joined back
+  // into the caller's stream; the window Softmax (a7) runs on the caller's
+  // stream meanwhile.  The two branches touch disjoint workspace regions.
+  SideStream* ss = nullptr;
+  VDN_HIP(side_stream(&ss));
+  VDN_HIP(hipEventRecord(ss->fork, s));
+  VDN_HIP(hipStreamWaitEvent(ss->stream, ss->fork, 0));
+  st = run_scan(g, p, dt, k, v, beta, alpha, k_text, v_text, beta_text, ws, lay, Pf, Pr, ss->stream);
+  if (st == VDN_OK) {
+    const hipError_t e = dt == VDN_BF16
+        ? vdn::launch_vda_readout<uint16_t>(g, (const uint16_t*)q, alpha, Pf, Pr, g_l, gamma,
+                                            p->rms_eps, (uint16_t*)ohl, ss->stream)
+        : vdn::launch_vda_readout<float>(g, (const float*)q, alpha, Pf, Pr, g_l, gamma,
+                                         p->rms_eps, (float*)ohl, ss->stream);
+    if (e != hipSuccess) st = fail(VDN_ERR_HIP, "readout launch failed: %s", hipGetErrorString(e));
+  }
+  // join is recorded even after a failure, so the caller's stream never
+  // runs ahead of work already queued on the side stream
+  const hipError_t ej = hipEventRecord(ss->join, ss->stream);
+  if (st == VDN_OK) st = run_softmax(g, p, dt, q, k, v, g_s, ohs, nullptr, ws, lay, s);
+  const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, ss->join, 0) : ej;
   if (st != VDN_OK) return st;
-  if (dt == VDN_BF16)
-    VDN_HIP(vdn::launch_vda_readout<uint16_t>(g, (const uint16_t*)q, alpha, Pf, Pr, g_l, gamma,
-                                              p->rms_eps, (uint16_t*)ohl, s));
-  else
-    VDN_HIP(vdn::launch_vda_readout<float>(g, (const float*)q, alpha, Pf, Pr, g_l, gamma,
-                                           p->rms_eps, (float*)ohl, s));
-  // Softmax branch (a7)
-  st = run_softmax(g, p, dt, q, k, v, g_s, ohs, nullptr, ws, lay, s);
-  if (st != VDN_OK) return st;
+  if (ew != hipSuccess) return fail(VDN_ERR_HIP, "side-stream join failed: %s", hipGetErrorString(ew));
   // Merge (a8)
   const long long M = (long long)g.B * g.L;
   const int K = g.H * g.D;

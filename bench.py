@@ -99,6 +99,45 @@ def cpu_baseline(cfg, target_s: float = 15.0) -> dict:
     }
 
 
+COPY_KERNEL_TAG = "MulFunctor"      # torch.mul(x, 1, out=y): reads and writes its size once
+SOFTMAX_KERNEL_TAG = "window_softmax_mfma_kernel"
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, config: str, calib_bytes: int) -> dict:
+    """HBM bytes per window-Softmax launch from two rocprofv3 --pmc CSVs.
+
+    FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch.  Each is scaled
+    by factor = known bytes / counter bytes of the calibration copy kernel
+    (a torch elementwise copy of calib_bytes that reads and writes its size
+    once), measured in the same run.
+    """
+    import csv
+    import statistics
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0
+        return vals
+
+    out = {}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        v = per_dispatch(path, counter)
+        copies = [b for (k, _), b in v.items() if COPY_KERNEL_TAG in k]
+        sm = [b for (k, _), b in v.items() if SOFTMAX_KERNEL_TAG in k]
+        if not copies or not sm:
+            raise SystemExit(f"{path}: calibration copy or softmax dispatches missing")
+        factor = calib_bytes / statistics.median(copies)
+        out[name] = {"counter_bytes_per_launch": statistics.median(sm), "copy_factor": factor,
+                     "bytes_per_launch": statistics.median(sm) * factor, "launches": len(sm)}
+    out["bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    out["config"] = config
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,7 +145,20 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="h3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one elementwise copy of this many MiB before timing "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 counter CSVs into the traffic JSON and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        res = traffic_from_counters(*args.traffic_from, config=args.config,
+                                    calib_bytes=(args.calib_copy_mib or 1024) << 20)
+        path = os.path.join(ROOT, "profiles", f"window_softmax_{args.config}_traffic.json")
+        with open(path, "w") as fh:
+            json.dump(res, fh, indent=1)
+        print(json.dumps(res))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "multi-GPU (head-sharded) path is not built.", file=sys.stderr)
@@ -116,7 +168,6 @@ def main() -> int:
     import torch
 
     import softmax_attention_video_amd as vdn
-    from oracle import vdn_oracle as O
     from vdn_inputs import CONFIGS, full_inputs
 
     cfg = CONFIGS[args.config]
@@ -148,6 +199,13 @@ def main() -> int:
                      t["beta_text"], t["g_s"], t["g_l"], gamma=t["gamma"], W_s=t["W_s"],
                      W_l=t["W_l"], out=out, workspace=ws)
 
+    if args.calib_copy_mib:
+        n = (args.calib_copy_mib << 20) // 4
+        xa = torch.ones(n, dtype=torch.float32, device=dev)
+        xb = torch.empty_like(xa)
+        torch.mul(xa, 1.0, out=xb)
+        torch.cuda.synchronize()
+        del xa, xb
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -167,7 +225,7 @@ def main() -> int:
           f"{k_ms.mean():.3f} ms (min {k_ms.min():.3f}, max {k_ms.max():.3f})",
           file=sys.stderr, flush=True)
 
-    pairs = O.visible_pairs(cfg.F)
+    pairs = int(vdn.window_plan(cfg.F)[0].sum())     # visible (query, key) frame pairs
     fl = flop_counts(cfg, pairs)
     tok_s = B * L / (ms_step / 1e3)
     tflops = fl["total"] / (ms_step / 1e3) / 1e12

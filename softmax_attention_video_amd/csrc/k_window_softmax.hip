@@ -54,26 +54,30 @@ struct Item {
 };
 
 // Key tiles of BK over the (up to three) spans, flattened: tile j of the
-// walk starts at key ks and holds nk valid keys.
+// walk starts at key ks and holds nk valid keys.  The lookup is plain
+// arithmetic on the span index (no selects of struct members), which keeps
+// the walk in scalar registers instead of private memory.
 template <int BK>
 struct SpanWalk {
   int n0, n01, n;      // cumulative tile counts
-  int kb0, ke0, kb1, ke1, kb2, ke2;
+  int o0, o1, o2;      // key start of tile j in span i is j * BK + o_i
+  int e0, e1, e2;      // span ends
   __device__ __forceinline__ SpanWalk(const Item& it) {
-    kb0 = it.kb0; ke0 = it.ke0;
-    kb1 = it.nspan > 1 ? it.kb1 : 0; ke1 = it.nspan > 1 ? it.ke1 : 0;
-    kb2 = it.nspan > 2 ? it.kb2 : 0; ke2 = it.nspan > 2 ? it.ke2 : 0;
-    n0 = (ke0 - kb0 + BK - 1) / BK;
+    const int kb1 = it.nspan > 1 ? it.kb1 : 0, ke1 = it.nspan > 1 ? it.ke1 : 0;
+    const int kb2 = it.nspan > 2 ? it.kb2 : 0, ke2 = it.nspan > 2 ? it.ke2 : 0;
+    n0 = (it.ke0 - it.kb0 + BK - 1) / BK;
     n01 = n0 + (ke1 - kb1 + BK - 1) / BK;
     n = n01 + (ke2 - kb2 + BK - 1) / BK;
+    o0 = it.kb0;
+    o1 = kb1 - n0 * BK;
+    o2 = kb2 - n01 * BK;
+    e0 = it.ke0; e1 = ke1; e2 = ke2;
   }
   __device__ __forceinline__ void tile(int j, int& ks, int& nk) const {
-    int b, e;
-    if (j < n0) { b = kb0 + j * BK; e = ke0; }
-    else if (j < n01) { b = kb1 + (j - n0) * BK; e = ke1; }
-    else { b = kb2 + (j - n01) * BK; e = ke2; }
-    ks = b;
-    nk = min(BK, e - b);
+    const int s1 = j >= n0, s2 = j >= n01;
+    ks = j * BK + o0 + (o1 - o0) * s1 + (o2 - o1) * s2;
+    const int e = e0 + (e1 - e0) * s1 + (e2 - e1) * s2;
+    nk = min(BK, e - ks);
   }
 };
 
@@ -135,27 +139,28 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
 
 // -------------------------------------------------------------------------
 // bf16 MFMA flash kernel.  512 threads = 8 waves of 32 queries each (256
-// queries per workgroup), two waves per SIMD: while one wave runs its
-// softmax arithmetic on the VALU the other keeps the matrix core busy.
-// The kernel is compiled with MFMA results in arch VGPRs (not AGPRs) so the
-// softmax reads S without accumulator-register moves.
+// queries per workgroup), two waves per SIMD.  The kernel is compiled with
+// MFMA results in arch VGPRs (not AGPRs) so the softmax reads S without
+// accumulator-register moves.
 //   S^T (keys x queries) = K Q^T  on v_mfma_f32_32x32x16_bf16;
 //   O^T (dv x queries)  += V^T P^T, with V pre-transposed to [D, L].
-// In the S^T accumulator a lane holds one query (lane % 32) and 16 keys, so
-// the row max / sum are in-lane plus one exchange with lane ^ 32.  K rows
-// are loaded in a permuted order so that lane half g holds keys 16g..16g+15
-// of each 32-key block in register order; those registers then feed the PV
-// product directly as its B operand, matching 16 contiguous bytes of V^T.
+// In the S^T accumulator a lane holds one query (lane % 32) and 16 keys.  K
+// rows are loaded in a permuted order so that lane half g holds keys
+// 16g..16g+15 of each 32-key block in register order; those registers then
+// feed the PV product directly as its B operand, matching 16 contiguous
+// bytes of V^T.
 //
-// Pipeline: the next 128-key tile is fetched from global memory into
-// registers while the current one is computed from LDS, then written into
-// the other LDS buffer; one barrier per tile.
+// Software pipeline per 32-key block b: the QK^T MFMAs of block b+1 are
+// issued while the VALU turns S_b into P_b, then PV of block b.  Key tiles
+// (96 keys at D = 128, 128 at D = 64) are staged global -> registers -> LDS
+// one piece per block, with one workgroup barrier per tile.
 //
-// Online softmax with a lazy rescale: O and l are kept relative to a
-// running reference max m; the reference only moves (and O, l are rescaled)
-// when a tile's max exceeds it by more than kRescaleLog2 (log2 units), so
-// unnormalised probabilities stay below 2^kRescaleLog2.  This is exact: the
-// final O / l does not depend on the reference.
+// Online softmax with a lazy reference: O and l are kept relative to a
+// running reference m; P is computed against it and the reference only
+// moves (rescaling O and l, recomputing P) when a lane's partial row sum of
+// the block exceeds kLazySum, which bounds every probability it holds.  No
+// per-block row max is needed on the common path.  This is exact: the final
+// O / l does not depend on the reference.
 // -------------------------------------------------------------------------
 struct WinArgs {
   Geometry g;
@@ -169,23 +174,26 @@ struct WinArgs {
   float scale_log2;
 };
 
-constexpr int kWinNW = 8, kWinQB = 1;      // waves per workgroup, 32-query blocks per wave
-constexpr int kWinBQ = kWinNW * kWinQB * 32;  // queries per workgroup
-constexpr float kRescaleLog2 = 8.f;
+constexpr int kWinNW = 8;                  // waves per workgroup, 32 queries each
+constexpr int kWinBQ = kWinNW * 32;        // queries per workgroup
+constexpr float kLazySum = 256.f;
 
 __device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
 template <int D>
 __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArgs a) {
-  constexpr int BQ = kWinBQ, BK = 128, QB = kWinQB, NT = kWinNW * 64;
+  // 96-key tiles at D = 128 keep two K and three V buffers within LDS.
+  constexpr int BQ = kWinBQ, BK = D == 128 ? 96 : 128, NT = kWinNW * 64;
   constexpr int KP = D + 8;    // padded pitches (bf16 elements) against bank conflicts
   constexpr int VP = BK + 8;
   constexpr int NKK = D / 16;  // k-steps of QK^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  constexpr int NB = BK / 32;  // 32-key blocks per tile
   constexpr int KCH = BK * D / 8 / NT;   // 16-byte chunks per thread per tile
   constexpr int VCH = D * BK / 8 / NT;
+  static_assert(KCH * NT * 8 == BK * D && VCH * NT * 8 == D * BK, "tile split");
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BK * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * VP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[3][D * VP];
 
   const Geometry& g = a.g;
   Item it;
@@ -200,147 +208,168 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   const bf16_t* Vt = a.vt + (size_t)it.bh * L * D;
   const float sl2 = a.scale_log2;
 
-  bf16x8 qf[QB][NKK];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = q0 + wave * (QB * 32) + qb * 32 + l32;
+  bf16x8 qf[NKK];
+  {
+    const int qrow = q0 + wave * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
       if (qrow < it.q_end) v = ld16(Q + (size_t)qrow * D + kk * 16 + hg * 8);
-      qf[qb][kk] = as_bf16x8(v);
+      qf[kk] = as_bf16x8(v);
     }
   }
-
-  f32x16 o[QB][NDB];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int b = 0; b < NDB; ++b) o[qb][b] = f32x16{};
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-  }
+  for (int b = 0; b < NDB; ++b) o[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
   const int krow_perm = key_perm(l32);
   const SpanWalk<BK> walk(it);
 
-  u32x4 kreg[KCH], vreg[VCH];
-  auto gload = [&](int j) {
+  // Tile staging.  A tile is KCH K chunks and VCH V^T chunks of 16 bytes
+  // per thread, cut into NB pieces; one piece is stored to LDS and the same
+  // piece of the following tile is requested per 32-key block, so the
+  // workgroup's vector-memory requests are spread over the tile instead of
+  // arriving in one burst.  Loads are raw buffer loads: per-lane byte offsets
+  // are loop invariant, the tile position goes into the descriptor base; K
+  // rows past the tile's valid keys fall outside the descriptor and read as
+  // zero, V^T columns past them are steered out of range the same way.
+  constexpr int CH = KCH + VCH, CPP = CH / NB;
+  static_assert(CPP * NB == CH, "pieces");
+  u32x4 creg[CH];
+  const uint32_t vt_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
+  auto load_piece = [&](int p, int j) {   // tiles past the walk read as zeros
     int ks, nk;
     walk.tile(j, ks, nk);
+    if (j >= walk.n) ks = 0, nk = 0;
+    const rsrc_t krs = make_rsrc(K + (size_t)ks * D, (uint32_t)nk * D * 2);
+    const rsrc_t vrs = make_rsrc(Vt + ks, vt_bytes - (uint32_t)ks * 2);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + NT * i;
-      const int r = c / (D / 8), c8 = c % (D / 8);
-      kreg[i] = u32x4{0, 0, 0, 0};
-      if (r < nk) kreg[i] = ld16(K + (size_t)(ks + r) * D + c8 * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + NT * i;
-      const int r = c / (BK / 8), c8 = c % (BK / 8);
-      vreg[i] = u32x4{0, 0, 0, 0};
-      if (c8 * 8 < nk) vreg[i] = ld16(Vt + (size_t)r * L + ks + c8 * 8);
+    for (int q = p * CPP; q < (p + 1) * CPP; ++q) {
+      if (q < KCH) {
+        const int c = tid + NT * q;
+        creg[q] = buf_ld16(krs, (uint32_t)((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2);
+      } else {
+        const int c = tid + NT * (q - KCH);
+        const int r = c / (BK / 8), c8 = c % (BK / 8);
+        const uint32_t off = (uint32_t)(r * L + c8 * 8) * 2;
+        creg[q] = buf_ld16(vrs, c8 * 8 < nk ? off : 0x80000000u);
+      }
     }
   };
-  auto lstore = [&](int buf) {
+  auto store_piece = [&](int p, int j) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + NT * i;
-      st16(&Ks[buf][(c / (D / 8)) * KP + (c % (D / 8)) * 8], kreg[i]);
+    for (int q = p * CPP; q < (p + 1) * CPP; ++q) {
+      if (q < KCH) {
+        const int c = tid + NT * q;
+        st16(&Ks[j & 1][(c / (D / 8)) * KP + (c % (D / 8)) * 8], creg[q]);
+      } else {
+        const int c = tid + NT * (q - KCH);
+        st16(&Vs[j % 3][(c / (BK / 8)) * VP + (c % (BK / 8)) * 8], creg[q]);
+      }
     }
+  };
+  // S^T of one 32-key block: lane half hg holds keys 16 hg .. 16 hg + 15.
+  auto qk = [&](const bf16_t* Kb, int blk) {
+    f32x16 s = {};
+    const bf16_t* krow = Kb + (blk * 32 + krow_perm) * KP + hg * 8;
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + NT * i;
-      st16(&Vs[buf][(c / (BK / 8)) * VP + (c % (BK / 8)) * 8], vreg[i]);
+    for (int kk = 0; kk < NKK; ++kk) s = mfma32x32x16(as_bf16x8(ld16(krow + kk * 16)), qf[kk], s);
+    return s;
+  };
+  // P of one block relative to the running reference m_run.  The lane's
+  // partial row sum bounds every p it holds, so while it stays <= 2^8 no p
+  // can overflow and the reference may stay.  Otherwise (also on the first
+  // block, where m_run = -inf makes every p infinite) the block max moves the
+  // reference, O and l are rescaled, and P is recomputed.
+  auto probs = [&](const f32x16& s, bool valid, bf16x8* pb) {
+    float ls = 0.f;
+    {
+      const float nm = valid ? -m_run : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[i], sl2, nm));
+        ls += p;
+        pb[i >> 3][i & 7] = static_cast<__bf16>(p);
+      }
     }
+    if (__any(!(ls <= kLazySum))) {
+      float m = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, s[i]);
+      m = valid ? m : -INFINITY;
+      const float m_new = fmaxf(m_run, half_max(m) * sl2);
+      const float corr = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) o[b] *= corr;
+      const float nm = valid ? -m_run : -INFINITY;
+      ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[i], sl2, nm));
+        ls += p;
+        pb[i >> 3][i & 7] = static_cast<__bf16>(p);
+      }
+    }
+    l_run += ls;
   };
 
-  gload(0);
-  lstore(0);
+#pragma unroll
+  for (int p = 0; p < NB; ++p) load_piece(p, 0);
+#pragma unroll
+  for (int p = 0; p < NB; ++p) store_piece(p, 0);
   __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NB; ++p) load_piece(p, 1);
+  store_piece(0, 1);
+  load_piece(0, 2);
+  int ks, nk;
+  walk.tile(0, ks, nk);
+  f32x16 s_cur = qk(Ks[0], 0);
+  bool v_cur = hg * 16 < nk;
   for (int j = 0; j < walk.n; ++j) {
-    int ks, nk;
-    walk.tile(j, ks, nk);
-    if (j + 1 < walk.n) gload(j + 1);
     const bf16_t* Kb = Ks[j & 1];
-    const bf16_t* Vb = Vs[j & 1];
-
+    const bf16_t* Vb = Vs[j % 3];
+    const bf16_t* Kn = Ks[(j + 1) & 1];
+    int ks1 = 0, nk1 = 0;
+    if (j + 1 < walk.n) walk.tile(j + 1, ks1, nk1);
 #pragma unroll
-    for (int kb2 = 0; kb2 < BK / 32; ++kb2) {   // 32-key blocks: QK -> softmax -> PV
-      f32x16 s[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
-      const bf16_t* krow = Kb + (kb2 * 32 + krow_perm) * KP + hg * 8;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 af = as_bf16x8(ld16(krow + kk * 16));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(af, qf[qb][kk], s[qb]);
-      }
-      if (nk < BK) {   // partial tile: keys past nk do not exist
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb2 * 32 + hg * 16 + i >= nk) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][i] = -INFINITY;
-          }
-      }
-      float mx[QB];
-      bool need = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float m = s[qb][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) m = fmaxf(m, s[qb][i]);
-        mx[qb] = half_max(m) * sl2;
-        need |= mx[qb] > m_run[qb] + kRescaleLog2;
-      }
-      if (__any(need)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float m_new = fmaxf(m_run[qb], mx[qb]);
-          const float corr = fast_exp2(m_run[qb] - m_new);
-          m_run[qb] = m_new;
-          l_run[qb] *= corr;
-#pragma unroll
-          for (int b = 0; b < NDB; ++b) o[qb][b] *= corr;
-        }
-      }
-      bf16x8 pb[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float nm = -m_run[qb];
-        float lsum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[qb][i], sl2, nm));
-          lsum += p;
-          pb[qb][i >> 3][i & 7] = static_cast<__bf16>(p);
-        }
-        l_run[qb] += lsum;
-      }
+    for (int kb2 = 0; kb2 < NB; ++kb2) {
+      // (1) S of the next block on the matrix core, P of this block on the VALU
+      const f32x16 s_next = kb2 + 1 < NB ? qk(Kb, kb2 + 1) : qk(Kn, 0);
+      const bool v_next = kb2 + 1 < NB ? (kb2 + 1) * 32 + hg * 16 < nk : hg * 16 < nk1;
+      bf16x8 pb[2];
+      probs(s_cur, v_cur, pb);
+      // (2) O += V P of this block
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int b = 0; b < NDB; ++b) {
           const bf16x8 vf = as_bf16x8(ld16(Vb + (b * 32 + l32) * VP + kb2 * 32 + hg * 16 + h2 * 8));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][b] = mfma32x32x16(vf, pb[qb][h2], o[qb][b]);
+          o[b] = mfma32x32x16(vf, pb[h2], o[b]);
         }
+      s_cur = s_next;
+      v_cur = v_next;
+      // Stage piece p of the next tile (of the one after, on the last
+      // block); one barrier per tile, once the next tile is complete.  K
+      // tiles are read one block ahead of V tiles, so K needs two buffers
+      // and V three.
+      {
+        const int p = (kb2 + 1) % NB;
+        const int st = j + 1 + (kb2 == NB - 1 ? 1 : 0);
+        store_piece(p, st);   // unconditional: keeps the vector-memory wait counts exact
+        if (kb2 == NB - 2) lds_barrier();
+        load_piece(p, st + 1);
+      }
     }
-    if (j + 1 < walk.n) lstore((j + 1) & 1);
-    __syncthreads();
+    nk = nk1;
   }
 
   const int bidx = it.bh / g.H, h = it.bh % g.H;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = half_sum(l_run[qb]);
-    const int qrow = q0 + wave * (QB * 32) + qb * 32 + l32;
-    if (qrow >= it.q_end) continue;
+  const float l_tot = half_sum(l_run);
+  const int qrow = q0 + wave * 32 + l32;
+  if (qrow < it.q_end) {
     const float gate = a.g_s ? a.g_s[(size_t)it.bh * L + qrow] : 1.f;
     const float sc = gate / l_tot;
     bf16_t* orow = a.out + (((size_t)bidx * L + qrow) * g.H + h) * D;
@@ -350,16 +379,18 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
       for (int i4 = 0; i4 < 4; ++i4) {
         const int dv = b * 32 + 8 * i4 + 4 * hg;
         u32x2 pk;
-        pk[0] = pack_bf16x2(o[qb][b][i4 * 4 + 0] * sc, o[qb][b][i4 * 4 + 1] * sc);
-        pk[1] = pack_bf16x2(o[qb][b][i4 * 4 + 2] * sc, o[qb][b][i4 * 4 + 3] * sc);
+        pk[0] = pack_bf16x2(o[b][i4 * 4 + 0] * sc, o[b][i4 * 4 + 1] * sc);
+        pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc, o[b][i4 * 4 + 3] * sc);
         *reinterpret_cast<u32x2*>(orow + dv) = pk;
       }
-    if (a.lse && hg == 0) a.lse[(size_t)it.bh * L + qrow] = m_run[qb] * kLn2 + logf(l_tot);
+    if (a.lse && hg == 0) a.lse[(size_t)it.bh * L + qrow] = m_run * kLn2 + logf(l_tot);
   }
 }
 
 bool window_softmax_mfma_ok(const Geometry& g) {
-  return (g.D == 64 || g.D == 128) && (g.N % 16 == 0);
+  // 16-key granularity of the masks; V^T of one head addressed by a single
+  // 32-bit buffer descriptor
+  return (g.D == 64 || g.D == 128) && (g.N % 16 == 0) && (long long)g.D * g.L * 2 <= 0x7FFFFFF0ll;
 }
 
 hipError_t launch_window_softmax_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,

@@ -135,7 +135,19 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, config: str, calib_byt
                      "bytes_per_launch": statistics.median(sm) * factor, "launches": len(sm)}
     out["bytes_per_launch"] = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
     out["config"] = config
+    out["kernel_source_sha256"] = softmax_source_digest()
     return out
+
+
+def softmax_source_digest() -> str:
+    """Digest of the sources the window-Softmax kernel is compiled from; a
+    stored traffic figure is only reported while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("k_window_softmax.hip", "vdn_common.h", "vdn_internal.h"):
+        with open(os.path.join(ROOT, "softmax_attention_video_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def main() -> int:
@@ -235,7 +247,9 @@ def main() -> int:
     prof = os.path.join(ROOT, "profiles", f"window_softmax_{cfg.name}_traffic.json")
     if os.path.exists(prof):
         with open(prof) as fh:
-            traffic = json.load(fh).get("bytes_per_launch")
+            rec = json.load(fh)
+        if rec.get("kernel_source_sha256") == softmax_source_digest():
+            traffic = rec.get("bytes_per_launch")
 
     res = {
         "metric": "VDN attention fwd video tokens/s (1 GPU)",

@@ -9,43 +9,61 @@
 //
 // bf16 path: both operands K-contiguous (the projections are transposed
 // once per call into the workspace, W^T [Dm, K]), 256 x 256 output tiles,
-// 64-deep K steps through double-buffered LDS with the next step's global
-// loads in flight, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The product is formed as out^T blocks so each lane owns 4
-// consecutive output features of one token (8-byte stores).
+// 64-deep K steps through double-buffered LDS with the next steps' global
+// loads in flight, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The
+// product is formed as out^T blocks so each lane owns 4 consecutive output
+// features of one token (8-byte stores).
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
 namespace vdn {
 
 constexpr int kGBM = 256, kGBN = 256, kGBK = 64;
+constexpr int kGroupRows = 4;
 // 8 waves (two per SIMD): wave (wm 0..3, wn 0..1) owns a 64 x 128 block of
 // the 256 x 256 tile.  Operand panels are read with buffer loads whose
 // descriptors end at the last row of A / W^T, so rows past M or N read as
 // zero without branches; K must be a multiple of the 64-deep K step.  The
 // LDS fragments of the next 16-deep step are loaded while the current
-// step's MFMAs run.
+// step's MFMAs run, and each 16-deep step stores one 16-byte chunk per
+// operand of the next K step to LDS and requests the same chunk of the one
+// after, so vector-memory requests are spread over the K step (scheduling
+// barriers keep the compiler from regrouping them).  One LDS-only barrier
+// per K step.
+//
+// Tile order: XCD x (blockIdx % 8) owns a contiguous range of row tiles and
+// walks it in groups of kGroupRows rows, column by column inside a group, so
+// the workgroups resident on one XCD share A row panels and W^T column
+// panels in that XCD's L2.
 __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __restrict__ a0,
                                                               const bf16_t* __restrict__ a1,
                                                               const bf16_t* __restrict__ bt0,
                                                               const bf16_t* __restrict__ bt1,
                                                               bf16_t* __restrict__ out,
                                                               long long M, int K, int N,
-                                                              int tiles_m, int tiles_n) {
+                                                              int tiles_m, int tiles_n, int rpx) {
   constexpr int BM = kGBM, BN = kGBN, BK = kGBK;
   constexpr int P = BK + 8;
-  constexpr int CH = BM * BK / 8 / 512;
+  constexpr int CH = BM * BK / 8 / 512;   // 16-byte chunks per thread per operand and K step (4)
+  constexpr int NSUB = BK / 16;           // 16-deep MFMA steps per K step (4)
+  static_assert(CH == NSUB, "one chunk of each operand staged per MFMA step");
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * P];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * P];
-  const long long ntiles = (long long)tiles_m * tiles_n;
-  const long long per = (ntiles + kNumXcd - 1) / kNumXcd;
-  const long long tl = (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
-  if (blockIdx.x / kNumXcd >= per || tl >= ntiles) return;
-  const long long m0 = (tl / tiles_n) * BM;
-  const int n0 = (int)(tl % tiles_n) * BN;
+  // XCD-aware grouped order: XCD x owns row tiles [x rpx, (x+1) rpx) and walks
+  // them in groups of kGroupRows rows, column by column inside a group.
+  const int x = blockIdx.x % kNumXcd;
+  const int t = blockIdx.x / kNumXcd;
+  const int gsz = kGroupRows * tiles_n;
+  const int grp = t / gsz, rem = t % gsz;
+  const int col = rem / kGroupRows;
+  const int row = x * rpx + grp * kGroupRows + rem % kGroupRows;
+  const int row_end = min((x + 1) * rpx, tiles_m);
+  if (row >= row_end) return;
+  const long long m0 = (long long)row * BM;
+  const int n0 = col * BN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
   const int nkt = 2 * K / BK;   // K % BK == 0
-  // descriptors over this tile's row panels (rows past M / N read as zero)
   const rsrc_t ra0 = make_rsrc(a0 + (size_t)m0 * K, rsrc_bytes(a0 + (size_t)m0 * K, a0 + (size_t)M * K));
   const rsrc_t ra1 = make_rsrc(a1 + (size_t)m0 * K, rsrc_bytes(a1 + (size_t)m0 * K, a1 + (size_t)M * K));
   const rsrc_t rb0 = make_rsrc(bt0 + (size_t)n0 * K, rsrc_bytes(bt0 + (size_t)n0 * K, bt0 + (size_t)N * K));
@@ -65,28 +83,26 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   u32x4 pa[CH], pb[CH];
-  auto gload = [&](int kt) {
+  auto load_piece = [&](int i, int kt) {   // K steps past the end re-read the last one
+    kt = min(kt, nkt - 1);
     const int k0 = kt * BK;
     const bool second = k0 >= K;
     const uint32_t kb = (uint32_t)((second ? k0 - K : k0) * 2);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      pa[i] = buf_ld16(second ? ra1 : ra0, voff[i], kb);
-      pb[i] = buf_ld16(second ? rb1 : rb0, voff[i], kb);
-    }
+    pa[i] = buf_ld16(second ? ra1 : ra0, voff[i], kb);
+    pb[i] = buf_ld16(second ? rb1 : rb0, voff[i], kb);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      st16(&As[buf][soff[i]], pa[i]);
-      st16(&Bs[buf][soff[i]], pb[i]);
-    }
+  auto store_piece = [&](int i, int buf) {
+    st16(&As[buf][soff[i]], pa[i]);
+    st16(&Bs[buf][soff[i]], pb[i]);
   };
-  gload(0);
-  lstore(0);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) load_piece(i, 0);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) store_piece(i, 0);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) load_piece(i, 1);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) gload(kt + 1);
     const bf16_t* Ab = As[kt & 1] + (wm * 64 + l32) * P + hg * 8;
     const bf16_t* Bb = Bs[kt & 1] + (wn * 128 + l32) * P + hg * 8;
     bf16x8 fm[2][2], fn[2][4];
@@ -95,9 +111,9 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) fn[0][i] = as_bf16x8(ld16(Bb + i * 32 * P));
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < NSUB; ++ks) {
       const int cur = ks & 1, nxt = cur ^ 1;
-      if (ks + 1 < BK / 16) {
+      if (ks + 1 < NSUB) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) fm[nxt][i] = as_bf16x8(ld16(Ab + i * 32 * P + (ks + 1) * 16));
 #pragma unroll
@@ -107,9 +123,12 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32x32x16(fn[cur][nb], fm[cur][mb], acc[nb][mb]);
+      // stage chunk ks of the next K step, request it for the one after
+      store_piece(ks, (kt + 1) & 1);
+      load_piece(ks, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nkt) lstore((kt + 1) & 1);
-    __syncthreads();
+    lds_barrier();
   }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -134,12 +153,12 @@ hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const 
                                   hipStream_t s) {
   if (M == 0 || Dm == 0) return hipSuccess;
   const int tm = (int)((M + kGBM - 1) / kGBM), tn = (Dm + kGBN - 1) / kGBN;
-  const long long nt = (long long)tm * tn;
-  const long long grid = ((nt + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  merge_gemm_bf16_kernel<<<(unsigned)grid, 512, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm, tm, tn);
+  const int rpx = (tm + kNumXcd - 1) / kNumXcd;
+  const int groups = (rpx + kGroupRows - 1) / kGroupRows;
+  const long long grid = (long long)kNumXcd * groups * kGroupRows * tn;
+  merge_gemm_bf16_kernel<<<(unsigned)grid, 512, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm, tm, tn, rpx);
   return hipGetLastError();
 }
-
 // ---- generic SIMT GEMM (fp32 storage or odd shapes): 16x16 tiles ----
 template <typename T>
 __global__ __launch_bounds__(256) void merge_gemm_simt_kernel(const T* __restrict__ a0,

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
 
   // Tile staging.  A tile is KCH K chunks and VCH V^T chunks of 16 bytes
   // per thread, cut into NB pieces; one piece is stored to LDS and the same
-  // piece of the following tile is requested per 32-key block, so the
+  // piece of the tile two ahead is requested per 32-key block, so the
   // workgroup's vector-memory requests are spread over the tile instead of
   // arriving in one burst.  Loads are raw buffer loads: per-lane byte offsets
   // are loop invariant, the tile position goes into the descriptor base; K
@@ -235,9 +235,9 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   // zero, V^T columns past them are steered out of range the same way.
   constexpr int CH = KCH + VCH, CPP = CH / NB;
   static_assert(CPP * NB == CH, "pieces");
-  u32x4 creg[CH];
+  u32x4 cA[CH], cB[CH];   // staging registers of even / odd tiles
   const uint32_t vt_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
-  auto load_piece = [&](int p, int j) {   // tiles past the walk read as zeros
+  auto load_piece = [&](u32x4* creg, int p, int j) {   // tiles past the walk read as zeros
     int ks, nk;
     walk.tile(j, ks, nk);
     if (j >= walk.n) ks = 0, nk = 0;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
       }
     }
   };
-  auto store_piece = [&](int p, int j) {
+  auto store_piece = [&](const u32x4* creg, int p, int j) {
 #pragma unroll
     for (int q = p * CPP; q < (p + 1) * CPP; ++q) {
       if (q < KCH) {
@@ -316,19 +316,23 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   };
 
 #pragma unroll
-  for (int p = 0; p < NB; ++p) load_piece(p, 0);
+  for (int p = 0; p < NB; ++p) load_piece(cA, p, 0);
 #pragma unroll
-  for (int p = 0; p < NB; ++p) store_piece(p, 0);
+  for (int p = 0; p < NB; ++p) store_piece(cA, p, 0);
+#pragma unroll
+  for (int p = 0; p < NB; ++p) load_piece(cB, p, 1);
+  store_piece(cB, 0, 1);
+#pragma unroll
+  for (int p = 0; p < NB; ++p) load_piece(cA, p, 2);
+  load_piece(cB, 0, 3);
   __syncthreads();
-#pragma unroll
-  for (int p = 0; p < NB; ++p) load_piece(p, 1);
-  store_piece(0, 1);
-  load_piece(0, 2);
   int ks, nk;
   walk.tile(0, ks, nk);
   f32x16 s_cur = qk(Ks[0], 0);
   bool v_cur = hg * 16 < nk;
-  for (int j = 0; j < walk.n; ++j) {
+  // Pieces are requested two tiles ahead of their LDS store, in the register
+  // set of the tile's parity.
+  auto tile_body = [&](int j, u32x4* c_near, u32x4* c_far) {
     const bf16_t* Kb = Ks[j & 1];
     const bf16_t* Vb = Vs[j % 3];
     const bf16_t* Kn = Ks[(j + 1) & 1];
@@ -354,16 +358,23 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
       // Stage piece p of the next tile (of the one after, on the last
       // block); one barrier per tile, once the next tile is complete.  K
       // tiles are read one block ahead of V tiles, so K needs two buffers
-      // and V three.
+      // and V three.  Stores and loads are unconditional (tiles past the
+      // walk are zeros), which keeps the vector-memory wait counts exact.
       {
         const int p = (kb2 + 1) % NB;
-        const int st = j + 1 + (kb2 == NB - 1 ? 1 : 0);
-        store_piece(p, st);   // unconditional: keeps the vector-memory wait counts exact
+        const bool far = kb2 == NB - 1;
+        const int st = j + 1 + (far ? 1 : 0);
+        u32x4* c = far ? c_far : c_near;
+        store_piece(c, p, st);
         if (kb2 == NB - 2) lds_barrier();
-        load_piece(p, st + 1);
+        load_piece(c, p, st + 2);
       }
     }
     nk = nk1;
+  };
+  for (int j = 0; j < walk.n; j += 2) {
+    tile_body(j, cB, cA);
+    if (j + 1 < walk.n) tile_body(j + 1, cA, cB);
   }
 
   const int bidx = it.bh / g.H, h = it.bh % g.H;

@@ -52,7 +52,7 @@ def algorithmic_bytes(cfg) -> float:
     return float(qkv + gates + states + w + out)
 
 
-def cpu_baseline(cfg, target_s: float = 15.0) -> dict:
+def cpu_baseline(cfg, target_s: float = 30.0) -> dict:
     """The oracle, untouched, on a bounded sample: head (0, 0) in full for its
     chunk-boundary states plus S sampled query rows, and the merge for those
     rows; scaled to the whole layer in tokens/s."""

@@ -32,7 +32,11 @@ import numpy as np
 
 # tensor ids of the seed sequence
 _ID = dict(q=0, k=1, v=2, beta=3, alpha=4, k_text=5, v_text=6, beta_text=7,
-           g_s=8, g_l=9, W_s=10, W_l=11, dup=12)
+           g_s=8, g_l=9, W_s=10, W_l=11, dup=12, prep_q=13, prep_k=14, prep_v=15,
+           prep_ws=16, prep_wt=17)
+
+# latent grid (rows x columns) of one frame for each configuration, N = rows * columns
+GRIDS = {"tiny": (4, 4), "small": (16, 16), "medium": (24, 16), "h3": (48, 32), "long": (32, 24)}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -207,4 +211,37 @@ def full_inputs(cfg: Config, threads: int | None = None) -> dict:
         list(ex.map(one, [(b, h) for b in range(B) for h in range(H)]))
     out["gamma"] = np.ones(cfg.d, np.float32)
     out["W_s"], out["W_l"] = proj_weights(cfg)
+    return out
+
+
+def prep_head_inputs(cfg: Config, b: int, h: int) -> dict:
+    """Raw projection outputs of one (b, h) for the linear branch's feature
+    map: q, k, v [L, d] frame-major rows ~ N(0, 1), rounded to cfg.dtype."""
+    return {key: _store(cfg, _normal(cfg, "prep_" + key, b, h, (cfg.L, cfg.d))) for key in ("q", "k", "v")}
+
+
+def prep_filters(cfg: Config, kernel_h: int = 3, kernel_w: int = 3, taps: int = 5):
+    """Depthwise filters: spatial [H, d, kh, kw] ~ N(0, 1/(kh kw)), temporal
+    [H, d, taps] ~ N(0, 1/taps), float32."""
+    ws = _rng(cfg, "prep_ws").standard_normal((cfg.H, cfg.d, kernel_h, kernel_w)) / np.sqrt(kernel_h * kernel_w)
+    wt = _rng(cfg, "prep_wt").standard_normal((cfg.H, cfg.d, taps)) / np.sqrt(taps)
+    return ws.astype(np.float32), wt.astype(np.float32)
+
+
+def prep_inputs(cfg: Config, threads: int | None = None) -> dict:
+    """Stacked raw features q, k, v [B, H, L, d] (float32 holding cfg.dtype
+    values); the feature map consumes them token-major, i.e. transposed to
+    [B, L, H, d]."""
+    B, H = cfg.B, cfg.H
+    out = {k: np.empty((B, H, cfg.L, cfg.d), np.float32) for k in ("q", "k", "v")}
+
+    def one(bh):
+        b, h = bh
+        r = prep_head_inputs(cfg, b, h)
+        for k in out:
+            out[k][b, h] = r[k]
+
+    n = threads or min(16, len(os.sched_getaffinity(0)))
+    with _cf.ThreadPoolExecutor(max_workers=max(1, n)) as ex:
+        list(ex.map(one, [(b, h) for b in range(B) for h in range(H)]))
     return out

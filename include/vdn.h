@@ -170,6 +170,49 @@ vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v, c
                                   const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
                                   void* stream);
 
+/*
+ * vda_prep_fwd -- VDA-Prep, the linear branch's feature map (upstream of
+ * vdn_attn_fwd's linear-branch inputs).
+ *
+ * Paper, method (the two branches): the linear branch applies a separable
+ * short convolution to K and V -- a depthwise spatial filter and a five-tap
+ * temporal filter -- then SiLU, and L2-normalises Q and K; system section
+ * (fused VDA kernels): VDA-Prep fuses the temporal convolution, SiLU, L2
+ * normalisation and the conversion to the frame-major layout.
+ *   conv(x)[f,y,x,c] = sum_tau w_temporal[h,c,tau] sum_{dy,dx} w_spatial[h,c,dy,dx]
+ *                      * x[f+tau-t0, y+dy-(kernel_h-1)/2, x+dx-(kernel_w-1)/2, c]
+ *     with zeros outside the clip and the grid; t0 = (taps-1)/2 (centred) or
+ *     taps-1 (causal);
+ *   q' = q / sqrt(|q|^2 + l2_eps),  k' = L2(SiLU(conv(k))),  v' = SiLU(conv(v)),
+ *     norms over the d channels of one token of one head.
+ *
+ *  q, k, v             [B,L,H,d] dt   token-major projection outputs; token n
+ *                                     of a frame sits at grid row n / grid_w,
+ *                                     column n % grid_w (N = grid_h * grid_w)
+ *  w_spatial           [H,d,kernel_h,kernel_w] float   depthwise spatial filter
+ *  w_temporal          [H,d,taps]  float   depthwise temporal filter
+ *  q_out, k_out, v_out [B,H,L,d]   dt     frame-major, head-major features
+ * Uses dims B, H, F, N and d_k (== d_v); T and D are ignored; F >= 1.  No
+ * workspace.  Supported: d in {16,32,64,128}; kernel_h, kernel_w odd in [1,7];
+ * taps in [1,5].  Outputs must not alias inputs.
+ */
+typedef struct {
+  int grid_h, grid_w;      /* latent grid of one frame, N = grid_h * grid_w          */
+  int kernel_h, kernel_w;  /* spatial filter size (odd); not printed on the page: 3x3 */
+  int taps;                /* temporal filter taps (5)                               */
+  int causal;              /* 0 = centred taps, 1 = taps end at the output frame     */
+  float l2_eps;            /* epsilon under the L2 norm's square root (1e-6)         */
+} vda_prep_params;
+
+/* Fills *p: the given grid, 3x3 spatial filter, 5 centred taps, eps 1e-6. */
+void vda_prep_default_params(vda_prep_params* p, int grid_h, int grid_w);
+
+vdn_status vda_prep_fwd(const void* q, const void* k, const void* v,
+                        const float* w_spatial, const float* w_temporal,
+                        void* q_out, void* k_out, void* v_out,
+                        const vdn_dims* dims, const vda_prep_params* p, vdn_dtype dt,
+                        void* stream);
+
 /* Workspace bytes that suffice for every entry point above at these sizes;
  * 0 if the arguments are invalid. */
 size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);

@@ -30,7 +30,7 @@ VDN_F32, VDN_BF16 = 0, 1
 EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_window_softmax_fwd", "vdn_workspace_bytes", "vdn_window_plan",
            "vdn_status_string", "vdn_last_error", "vdn_timer_enable", "vdn_timer_read",
-           "vdn_timer_disable")
+           "vdn_timer_disable", "vda_prep_default_params", "vda_prep_fwd")
 
 
 class VdnError(RuntimeError):
@@ -47,6 +47,28 @@ class CParams(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("text_init_scale", ctypes.c_float), ("chunk_frames", ctypes.c_int),
                 ("window_chunks", ctypes.c_int), ("anchors", ctypes.c_int)]
+
+
+class CPrepParams(ctypes.Structure):
+    _fields_ = [("grid_h", ctypes.c_int), ("grid_w", ctypes.c_int), ("kernel_h", ctypes.c_int),
+                ("kernel_w", ctypes.c_int), ("taps", ctypes.c_int), ("causal", ctypes.c_int),
+                ("l2_eps", ctypes.c_float)]
+
+
+@dataclasses.dataclass(frozen=True)
+class PrepParams:
+    """VDA-Prep filter geometry (defaults: 3x3 spatial filter, 5 centred taps, eps 1e-6)."""
+    grid_h: int
+    grid_w: int
+    kernel_h: int = 3
+    kernel_w: int = 3
+    taps: int = 5
+    causal: int = 0
+    l2_eps: float = 1e-6
+
+    def c(self) -> CPrepParams:
+        return CPrepParams(self.grid_h, self.grid_w, self.kernel_h, self.kernel_w, self.taps,
+                           self.causal, self.l2_eps)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -102,6 +124,10 @@ def lib() -> ctypes.CDLL:
     L.vdn_timer_read.restype = I
     L.vdn_timer_disable.argtypes = []
     L.vdn_timer_disable.restype = None
+    L.vda_prep_default_params.argtypes = [ctypes.POINTER(CPrepParams), I, I]
+    L.vda_prep_default_params.restype = None
+    L.vda_prep_fwd.argtypes = [P] * 8 + [dp, ctypes.POINTER(CPrepParams), I, P]
+    L.vda_prep_fwd.restype = I
     _lib = L
     return L
 
@@ -333,3 +359,33 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
         ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
     return out, lse
+
+
+def prep_fwd(q, k, v, w_spatial, w_temporal, F: int, params: PrepParams, q_out=None, k_out=None,
+             v_out=None, stream=None):
+    """VDA-Prep, the linear branch's feature map (vda_prep_fwd).
+
+    q, k, v [B,L,H,d] token-major (bf16 or fp32); w_spatial [H,d,kh,kw] and
+    w_temporal [H,d,taps] fp32.  Returns (q', k', v'), each [B,H,L,d]."""
+    torch = _torch()
+    B, L, H, d = q.shape
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    N = L // F
+    dt = q.dtype
+    code = _dtype_code(q)
+    dev = q.device
+    dims = Dims(B, H, F, N, 0, d, d, H * d)
+    outs = []
+    for o in (q_out, k_out, v_out):
+        outs.append(o if o is not None else torch.empty((B, H, L, d), dtype=dt, device=dev))
+    p = params.c()
+    _check(lib().vda_prep_fwd(
+        _ptr(q, "q", dt, (B, L, H, d), dev), _ptr(k, "k", dt, (B, L, H, d), dev),
+        _ptr(v, "v", dt, (B, L, H, d), dev),
+        _ptr(w_spatial, "w_spatial", torch.float32, (H, d, params.kernel_h, params.kernel_w), dev),
+        _ptr(w_temporal, "w_temporal", torch.float32, (H, d, params.taps), dev),
+        _ptr(outs[0], "q_out", dt, (B, H, L, d), dev), _ptr(outs[1], "k_out", dt, (B, H, L, d), dev),
+        _ptr(outs[2], "v_out", dt, (B, H, L, d), dev),
+        ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return tuple(outs)

@@ -1,0 +1,324 @@
+// VDA-Prep: the linear branch's feature map, fused with the layout change.
+//
+// Paper ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream
+// Video Generation"), method, the two branches: the linear branch applies
+// its own feature map -- a separable short convolution on K and V made of a
+// depthwise spatial filter and a five-tap temporal filter, followed by SiLU,
+// with L2 normalisation on Q and K.  System section, fused VDA kernels:
+// VDA-Prep fuses the temporal convolution, SiLU, L2 normalisation and the
+// conversion to the frame-major layout.
+//
+//   conv(x)[f,y,x,c] = sum_tau wt[c,tau] sum_{dy,dx} ws[c,dy,dx]
+//                      x[f + tau - t0, y + dy - ry, x + dx - rx, c]   (zeros outside)
+//   q' = L2(q),  k' = L2(SiLU(conv(k))),  v' = SiLU(conv(v))
+//
+// Design (HBM-bound: every input element read once from HBM, every output
+// written once):
+//  - Q: one 8-channel chunk per lane; the D/8 lanes of a (token, head) row
+//    reduce the sum of squares with lane shuffles.  Rows are read
+//    token-major [B,L,H,d] (all heads of a token adjacent) and written
+//    head-major [B,H,L,d].
+//  - K, V: one workgroup per (b, h, grid row, tile of XT columns, tensor)
+//    slides over the frames.  For each input frame the kernel_h grid rows
+//    around the row (with a column halo) are staged in LDS as fp32; each lane
+//    task (column, 8 channels) forms the spatial sum for that frame and
+//    shifts it into a per-lane register window of the last kTapsMax frames
+//    (no LDS round trip for the temporal filter).  When the window holds an
+//    output frame's last input frame, the temporal sum, SiLU and (for K) the
+//    L2 norm over the token's D/8 lanes give the output row, written
+//    frame-major.  The next frame's rows are fetched into registers while
+//    the current frame is computed.
+#include "vdn_common.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+constexpr int kPrepThreads = 256;
+
+template <typename T> struct Chunk8;
+template <> struct Chunk8<bf16_t> {   // 8 bf16 = one 16-byte access
+  u32x4 r;
+  __device__ __forceinline__ void load(const bf16_t* p) { r = ld16(p); }
+  __device__ __forceinline__ void zero() { r = u32x4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void to_f32(float* x) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(r[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* x) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    st16(p, o);
+  }
+};
+template <> struct Chunk8<float> {    // 8 float = two 16-byte accesses
+  u32x4 r0, r1;
+  __device__ __forceinline__ void load(const float* p) { r0 = ld16(p); r1 = ld16(p + 4); }
+  __device__ __forceinline__ void zero() { r0 = r1 = u32x4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void to_f32(float* x) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = __uint_as_float(r0[i]);
+      x[4 + i] = __uint_as_float(r1[i]);
+    }
+  }
+  static __device__ __forceinline__ void store(float* p, const float* x) {
+    st16(p, u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+    st16(p + 4, u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+  }
+};
+
+__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+
+// Sum over the `lanes` consecutive lanes (a power of two <= 16) of one row.
+__device__ __forceinline__ float row_sum(float x, int lanes) {
+  for (int off = lanes >> 1; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Q: L2 normalisation + [B,L,H,d] -> [B,H,L,d].
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kPrepThreads) void vda_prep_q_kernel(const T* __restrict__ q,
+                                                                   T* __restrict__ q_out,
+                                                                   long long rows, int H,
+                                                                   long long L, float eps) {
+  constexpr int C8 = D / 8;
+  const long long row = ((long long)blockIdx.x * kPrepThreads + threadIdx.x) / C8;   // (b, l, h)
+  const int c8 = threadIdx.x % C8;
+  const bool ok = row < rows;
+  float x[8] = {};
+  if (ok) {
+    Chunk8<T> c;
+    c.load(q + (size_t)row * D + c8 * 8);
+    c.to_f32(x);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+  ss = row_sum(ss, C8);
+  if (!ok) return;
+  const float r = 1.f / sqrtf(ss + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] *= r;
+  const int h = (int)(row % H);
+  const long long bl = row / H, b = bl / L, l = bl % L;
+  Chunk8<T>::store(q_out + (((size_t)b * H + h) * L + l) * D + c8 * 8, x);
+}
+
+// ---------------------------------------------------------------------------
+// K, V: separable short convolution + SiLU (+ L2 for K) + layout change.
+// ---------------------------------------------------------------------------
+constexpr int kTapsMax = 5;
+constexpr int kPrefetchMax = 8;   // staged 8-channel chunks per thread and frame
+
+struct PrepArgs {
+  const void* src[2];     // k, v   [B,L,H,D]
+  void* dst[2];           // k', v' [B,H,L,D]
+  const float* w_sp;      // [H,D,kh,kw]
+  const float* w_t;       // [H,D,taps]
+  int B, H, F, gh, gw, kh, kw, taps, t0, xt, ntx;
+  long long L;
+  float eps;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
+  constexpr int C8 = D / 8;
+  constexpr int TPT = (32 * C8 + kPrepThreads - 1) / kPrepThreads;   // tasks per thread (xt <= 32)
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  // LDS: staged rows [kh][xt + kw - 1][D] | spatial weights [kh*kw][D] | temporal weights by window slot [kTapsMax][D]
+  const int cols = a.xt + a.kw - 1;
+  float* in_s = sm;
+  float* ws_s = in_s + (size_t)a.kh * cols * D;
+  float* wt_s = ws_s + (size_t)a.kh * a.kw * D;
+
+  int bid = blockIdx.x;
+  const int which = bid & 1; bid >>= 1;             // 0 = K, 1 = V
+  const int xt_i = bid % a.ntx; bid /= a.ntx;
+  const int y = bid % a.gh; bid /= a.gh;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int x0 = xt_i * a.xt;
+  const T* src = static_cast<const T*>(a.src[which]);
+  T* dst = static_cast<T*>(a.dst[which]);
+  const int tid = threadIdx.x;
+  const int N = a.gh * a.gw;
+  const int ry = (a.kh - 1) / 2, rx = (a.kw - 1) / 2;
+
+  // filters of head h: spatial [tap][c]; temporal placed at the window slots
+  // kTapsMax - taps .. kTapsMax - 1 (older slots get zero)
+  for (int e = tid; e < a.kh * a.kw * D; e += kPrepThreads) {
+    const int tap = e / D, c = e % D;
+    ws_s[e] = a.w_sp[((size_t)h * D + c) * a.kh * a.kw + tap];
+  }
+  for (int e = tid; e < kTapsMax * D; e += kPrepThreads) {
+    const int slot = e / D, c = e % D;
+    const int tap = slot - (kTapsMax - a.taps);
+    wt_s[e] = tap >= 0 ? a.w_t[((size_t)h * D + c) * a.taps + tap] : 0.f;
+  }
+
+  // staging: chunk q -> (row r, column cx, c8)
+  const int nchunk = a.kh * cols * C8;
+  Chunk8<T> pf[kPrefetchMax];
+  auto fetch = [&](int fi) {
+#pragma unroll
+    for (int i = 0; i < kPrefetchMax; ++i) {
+      const int qq = tid + kPrepThreads * i;
+      pf[i].zero();
+      if (qq < nchunk) {
+        const int c8 = qq % C8, rc = qq / C8;
+        const int cx = rc % cols, r = rc / cols;
+        const int yy = y + r - ry, xx = x0 + cx - rx;
+        if (fi < a.F && yy >= 0 && yy < a.gh && xx >= 0 && xx < a.gw) {
+          const long long l = (long long)fi * N + (long long)yy * a.gw + xx;
+          pf[i].load(src + (((size_t)b * a.L + l) * a.H + h) * D + c8 * 8);
+        }
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPrefetchMax; ++i) {
+      const int qq = tid + kPrepThreads * i;
+      if (qq < nchunk) {
+        float x[8];
+        pf[i].to_f32(x);
+        float* p = in_s + (size_t)(qq / C8) * D + (qq % C8) * 8;
+        st16(p, u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+        st16(p + 4, u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+      }
+    }
+  };
+
+  float win[TPT][kTapsMax][8];   // spatial sums of the last kTapsMax frames, oldest first
+#pragma unroll
+  for (int j = 0; j < TPT; ++j)
+#pragma unroll
+    for (int s = 0; s < kTapsMax; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) win[j][s][i] = 0.f;
+
+  const int nsteps = a.F + a.taps - 1 - a.t0;
+  fetch(0);
+  for (int fi = 0; fi < nsteps; ++fi) {
+    __syncthreads();     // previous frame's spatial reads done; filters staged
+    stage();
+    __syncthreads();
+    if (fi + 1 < nsteps) fetch(fi + 1);
+    const int fo = fi - (a.taps - 1 - a.t0);
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int t = tid + kPrepThreads * j;
+      const int xl = t / C8, c8 = t % C8;
+      const bool active = xl < a.xt && x0 + xl < a.gw;
+      float s[8] = {};
+      if (active) {
+        for (int dy = 0; dy < a.kh; ++dy)
+          for (int dx = 0; dx < a.kw; ++dx) {
+            const float* xin = in_s + (size_t)(dy * cols + xl + dx) * D + c8 * 8;
+            const float* w = ws_s + (size_t)(dy * a.kw + dx) * D + c8 * 8;
+            const u32x4 x0v = ld16(xin), x1v = ld16(xin + 4), w0v = ld16(w), w1v = ld16(w + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              s[i] = fmaf(__uint_as_float(w0v[i]), __uint_as_float(x0v[i]), s[i]);
+              s[4 + i] = fmaf(__uint_as_float(w1v[i]), __uint_as_float(x1v[i]), s[4 + i]);
+            }
+          }
+      }
+#pragma unroll
+      for (int sl = 0; sl + 1 < kTapsMax; ++sl)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) win[j][sl][i] = win[j][sl + 1][i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) win[j][kTapsMax - 1][i] = s[i];
+      if (fo < 0) continue;
+      float o[8] = {};
+#pragma unroll
+      for (int sl = 0; sl < kTapsMax; ++sl) {
+        const float* w = wt_s + (size_t)sl * D + c8 * 8;
+        const u32x4 w0v = ld16(w), w1v = ld16(w + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] = fmaf(__uint_as_float(w0v[i]), win[j][sl][i], o[i]);
+          o[4 + i] = fmaf(__uint_as_float(w1v[i]), win[j][sl][4 + i], o[4 + i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = silu(o[i]);
+      if (which == 0) {   // K: L2 over the token's D channels (its C8 consecutive lanes)
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(o[i], o[i], ss);
+        ss = row_sum(ss, C8);
+        const float r = 1.f / sqrtf(ss + a.eps);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] *= r;
+      }
+      if (active) {
+        const long long l = (long long)fo * N + (long long)y * a.gw + x0 + xl;
+        Chunk8<T>::store(dst + (((size_t)b * a.H + h) * a.L + l) * D + c8 * 8, o);
+      }
+    }
+  }
+}
+
+// Largest column tile (<= 32) whose LDS footprint stays within 64 KB.
+int prep_tile_cols(int D, int kh, int kw, int gw) {
+  for (int xt = 32; xt >= 1; xt >>= 1) {
+    const size_t bytes = ((size_t)kh * (xt + kw - 1) * D + (size_t)kh * kw * D + (size_t)kTapsMax * D) * 4;
+    const int chunks = kh * (xt + kw - 1) * (D / 8);
+    if (bytes <= 65536 && chunks <= kPrefetchMax * kPrepThreads) return xt < gw ? xt : gw;
+  }
+  return 0;
+}
+
+template <typename T>
+hipError_t launch_vda_prep(const void* q, const void* k, const void* v, const float* w_sp,
+                           const float* w_t, void* q_out, void* k_out, void* v_out, int B, int H,
+                           int F, int gh, int gw, int D, int kh, int kw, int taps, int causal,
+                           float eps, hipStream_t s) {
+  const long long L = (long long)F * gh * gw;
+  const long long rows = (long long)B * L * H;
+  const long long qthreads = rows * (D / 8);
+  const unsigned qgrid = (unsigned)((qthreads + kPrepThreads - 1) / kPrepThreads);
+  PrepArgs a;
+  a.src[0] = k; a.src[1] = v; a.dst[0] = k_out; a.dst[1] = v_out;
+  a.w_sp = w_sp; a.w_t = w_t;
+  a.B = B; a.H = H; a.F = F; a.gh = gh; a.gw = gw; a.kh = kh; a.kw = kw; a.taps = taps;
+  a.t0 = causal ? taps - 1 : (taps - 1) / 2;
+  a.xt = prep_tile_cols(D, kh, kw, gw);
+  if (a.xt <= 0) return hipErrorInvalidValue;
+  a.ntx = (gw + a.xt - 1) / a.xt;
+  a.L = L;
+  a.eps = eps;
+  const unsigned kvgrid = (unsigned)((long long)B * H * gh * a.ntx * 2);
+  const size_t lds = ((size_t)kh * (a.xt + kw - 1) * D + (size_t)kh * kw * D + (size_t)kTapsMax * D) * 4;
+#define VDN_PREP_CASE(DD)                                                                          \
+  case DD:                                                                                         \
+    vda_prep_q_kernel<T, DD><<<qgrid, kPrepThreads, 0, s>>>((const T*)q, (T*)q_out, rows, H, L, eps); \
+    vda_prep_kv_kernel<T, DD><<<kvgrid, kPrepThreads, lds, s>>>(a);                                \
+    break;
+  switch (D) {
+    VDN_PREP_CASE(16)
+    VDN_PREP_CASE(32)
+    VDN_PREP_CASE(64)
+    VDN_PREP_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef VDN_PREP_CASE
+  return hipGetLastError();
+}
+
+template hipError_t launch_vda_prep<bf16_t>(const void*, const void*, const void*, const float*,
+                                            const float*, void*, void*, void*, int, int, int, int,
+                                            int, int, int, int, int, int, float, hipStream_t);
+template hipError_t launch_vda_prep<float>(const void*, const void*, const void*, const float*,
+                                           const float*, void*, void*, void*, int, int, int, int,
+                                           int, int, int, int, int, int, float, hipStream_t);
+
+}  // namespace vdn

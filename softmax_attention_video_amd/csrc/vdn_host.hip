@@ -443,4 +443,56 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   return VDN_OK;
 }
 
+void vda_prep_default_params(vda_prep_params* p, int grid_h, int grid_w) {
+  if (!p) return;
+  p->grid_h = grid_h;
+  p->grid_w = grid_w;
+  p->kernel_h = 3;
+  p->kernel_w = 3;
+  p->taps = 5;
+  p->causal = 0;
+  p->l2_eps = 1e-6f;
+}
+
+vdn_status vda_prep_fwd(const void* q, const void* k, const void* v, const float* w_spatial,
+                        const float* w_temporal, void* q_out, void* k_out, void* v_out,
+                        const vdn_dims* dims, const vda_prep_params* p, vdn_dtype dt,
+                        void* stream) {
+  g_err[0] = 0;
+  if (!dims) return fail(VDN_ERR_INVALID_ARG, "dims is NULL");
+  if (!p) return fail(VDN_ERR_INVALID_ARG, "params is NULL");
+  NEED(q); NEED(k); NEED(v); NEED(w_spatial); NEED(w_temporal);
+  NEED(q_out); NEED(k_out); NEED(v_out);
+  if (dt != VDN_F32 && dt != VDN_BF16) return fail(VDN_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  const vdn_dims& d = *dims;
+  if (d.B < 1 || d.H < 1 || d.F < 1) return fail(VDN_ERR_INVALID_ARG, "B=%d H=%d F=%d must be >= 1", d.B, d.H, d.F);
+  if (p->grid_h < 1 || p->grid_w < 1) return fail(VDN_ERR_INVALID_ARG, "grid %dx%d", p->grid_h, p->grid_w);
+  if ((long long)p->grid_h * p->grid_w != d.N)
+    return fail(VDN_ERR_INVALID_ARG, "N=%d != grid_h*grid_w=%d*%d", d.N, p->grid_h, p->grid_w);
+  if (d.d_k != d.d_v) return fail(VDN_ERR_UNSUPPORTED, "d_k=%d != d_v=%d", d.d_k, d.d_v);
+  if (d.d_k != 16 && d.d_k != 32 && d.d_k != 64 && d.d_k != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "head dim %d not in {16,32,64,128}", d.d_k);
+  if (p->kernel_h < 1 || p->kernel_h > 7 || p->kernel_h % 2 == 0 || p->kernel_w < 1 || p->kernel_w > 7 ||
+      p->kernel_w % 2 == 0)
+    return fail(VDN_ERR_UNSUPPORTED, "spatial filter %dx%d: sides must be odd and <= 7", p->kernel_h, p->kernel_w);
+  if (p->taps < 1 || p->taps > 5) return fail(VDN_ERR_UNSUPPORTED, "taps=%d not in [1,5]", p->taps);
+  if (p->causal != 0 && p->causal != 1) return fail(VDN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", p->causal);
+  if (!(p->l2_eps >= 0.f) || !isfinite(p->l2_eps)) return fail(VDN_ERR_INVALID_ARG, "l2_eps must be finite and >= 0");
+  const long long L = (long long)d.F * d.N;
+  if (L > (1ll << 31) - 1 || (long long)d.B * L * d.H > (1ll << 40))
+    return fail(VDN_ERR_INVALID_ARG, "sequence too long (L=%lld)", L);
+  if (vdn::prep_tile_cols(d.d_k, p->kernel_h, p->kernel_w, p->grid_w) <= 0)
+    return fail(VDN_ERR_UNSUPPORTED, "filter %dx%d does not fit the kernel's LDS tile", p->kernel_h, p->kernel_w);
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == VDN_BF16)
+    VDN_HIP(vdn::launch_vda_prep<uint16_t>(q, k, v, w_spatial, w_temporal, q_out, k_out, v_out, d.B, d.H,
+                                           d.F, p->grid_h, p->grid_w, d.d_k, p->kernel_h, p->kernel_w,
+                                           p->taps, p->causal, p->l2_eps, s));
+  else
+    VDN_HIP(vdn::launch_vda_prep<float>(q, k, v, w_spatial, w_temporal, q_out, k_out, v_out, d.B, d.H,
+                                        d.F, p->grid_h, p->grid_w, d.d_k, p->kernel_h, p->kernel_w,
+                                        p->taps, p->causal, p->l2_eps, s));
+  return VDN_OK;
+}
+
 }  // extern "C"

@@ -77,4 +77,14 @@ hipError_t launch_merge_gemm_simt(const T* a0, const T* a1, const T* w0, const T
 template <typename T>
 hipError_t launch_add(const T* a, const T* b, T* out, long long n, hipStream_t s);
 
+// ---- VDA-Prep (linear-branch feature map) ----
+// q,k,v [B,L,H,D] token-major -> q',k',v' [B,H,L,D]; w_sp [H,D,kh,kw], w_t [H,D,taps].
+template <typename T>
+hipError_t launch_vda_prep(const void* q, const void* k, const void* v, const float* w_sp,
+                           const float* w_t, void* q_out, void* k_out, void* v_out, int B, int H,
+                           int F, int gh, int gw, int D, int kh, int kw, int taps, int causal,
+                           float eps, hipStream_t s);
+// Column tile of the K/V kernel for these sizes (0 = unsupported).
+int prep_tile_cols(int D, int kh, int kw, int gw);
+
 }  // namespace vdn

@@ -161,3 +161,54 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 20, 16)
     with pytest.raises(ValueError):
         vdn.window_softmax_fwd(q, q, q, F=20)
+
+
+def _call_prep(dims, params, null=(), dt=vdn.VDN_BF16):
+    L = vdn.lib()
+    fake = ctypes.c_void_p(0x100000)
+    names = ("q", "k", "v", "w_spatial", "w_temporal", "q_out", "k_out", "v_out")
+    args = [None if n in null else fake for n in names]
+    return L.vda_prep_fwd(*args, ctypes.byref(dims) if dims is not None else None,
+                          ctypes.byref(params) if params is not None else None, dt, None)
+
+
+def test_prep_default_params():
+    p = vdn.CPrepParams()
+    vdn.lib().vda_prep_default_params(ctypes.byref(p), 48, 32)
+    assert (p.grid_h, p.grid_w, p.kernel_h, p.kernel_w, p.taps, p.causal) == (48, 32, 3, 3, 5, 0)
+    assert abs(p.l2_eps - 1e-6) < 1e-12
+    c = vdn.PrepParams(48, 32).c()
+    assert (c.kernel_h, c.kernel_w, c.taps, c.causal) == (3, 3, 5, 0)
+
+
+@pytest.mark.parametrize("dkw,pkw,code", [
+    (dict(), dict(grid_h=4, grid_w=5), vdn.VDN_ERR_INVALID_ARG),             # N != grid_h * grid_w
+    (dict(d_k=48, d_v=48), dict(), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(d_k=64, d_v=32), dict(), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(F=0), dict(), vdn.VDN_ERR_INVALID_ARG),
+    (dict(B=0), dict(), vdn.VDN_ERR_INVALID_ARG),
+    (dict(), dict(kernel_h=2), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(), dict(kernel_w=9), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(), dict(taps=6), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(), dict(taps=0), vdn.VDN_ERR_UNSUPPORTED),
+    (dict(), dict(causal=2), vdn.VDN_ERR_INVALID_ARG),
+    (dict(), dict(l2_eps=-1.0), vdn.VDN_ERR_INVALID_ARG),
+])
+def test_prep_invalid_args(dkw, pkw, code):
+    base = dict(B=1, H=2, F=4, N=16, T=0, d_k=64, d_v=64, D=128)
+    base.update(dkw)
+    d = vdn.Dims(*(base[k] for k in ("B", "H", "F", "N", "T", "d_k", "d_v", "D")))
+    pp = dict(grid_h=4, grid_w=4)
+    pp.update(pkw)
+    assert _call_prep(d, vdn.PrepParams(**pp).c()) == code
+    assert vdn.lib().vdn_last_error() != b""
+
+
+def test_prep_null_pointers_and_dtype():
+    d = vdn.Dims(1, 2, 4, 16, 0, 64, 64, 128)
+    p = vdn.PrepParams(4, 4).c()
+    assert _call_prep(None, p) == vdn.VDN_ERR_INVALID_ARG
+    assert _call_prep(d, None) == vdn.VDN_ERR_INVALID_ARG
+    for n in ("q", "k", "v", "w_spatial", "w_temporal", "q_out", "k_out", "v_out"):
+        assert _call_prep(d, p, null=(n,)) == vdn.VDN_ERR_INVALID_ARG, n
+    assert _call_prep(d, p, dt=7) == vdn.VDN_ERR_UNSUPPORTED

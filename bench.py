@@ -150,6 +150,62 @@ def softmax_source_digest() -> str:
     return h.hexdigest()
 
 
+def measure_prep(cfg, t, reps: int = 10, cpu: bool = True) -> dict:
+    """VDA-Prep (vda_prep_fwd, the linear branch's feature map, upstream of the
+    timed layer) on the layer's q, k, v laid out token-major: HIP-event time of
+    one call, HBM-roofline figures, and the oracle on one head scaled to all."""
+    import numpy as np
+    import torch
+
+    import softmax_attention_video_amd as vdn
+    from vdn_inputs import GRIDS, prep_filters
+
+    gh, gw = GRIDS[cfg.name]
+    params = vdn.PrepParams(gh, gw)
+    ws_np, wt_np = prep_filters(cfg)
+    dev = t["q"].device
+    src = [t[x].permute(0, 2, 1, 3).contiguous() for x in ("q", "k", "v")]
+    wsd, wtd = torch.from_numpy(ws_np).to(dev), torch.from_numpy(wt_np).to(dev)
+    outs = [torch.empty_like(t["q"]) for _ in range(3)]
+
+    def run():
+        vdn.prep_fwd(*src, wsd, wtd, cfg.F, params, *outs)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    B, H, L, d = t["q"].shape
+    nbytes = 6 * B * L * H * d * t["q"].element_size() + ws_np.nbytes + wt_np.nbytes
+    gbps = nbytes / (ms / 1e3) / 1e9
+    res = {"entry": "vda_prep_fwd", "workload": f"{cfg.name}: B={B} H={H} d={d} F={cfg.F} grid={gh}x{gw}, "
+                                                 "3x3 spatial x 5 centred temporal taps",
+           "ms": ms, "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": gbps / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
+    del src, outs
+    if cpu:
+        import threadpoolctl
+        from oracle import vda_prep as OP
+        from vdn_inputs import prep_head_inputs
+        h = prep_head_inputs(cfg, 0, 0)
+        op = OP.PrepParams(gh, gw)
+        t0 = time.perf_counter()
+        OP.prep_head(h["q"].astype(np.float64), h["k"].astype(np.float64), h["v"].astype(np.float64),
+                     ws_np[0].astype(np.float64), wt_np[0].astype(np.float64), op)
+        t_head = time.perf_counter() - t0
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        res["cpu_baseline"] = {"value": B * L / (t_head * B * H), "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle", "sample": f"head (b=0,h=0) in full ({t_head:.2f} s), scaled to "
+                                                           f"{B * H} heads"}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +213,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="h3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prep", action="store_true",
+                    help="skip the separate VDA-Prep (vda_prep_fwd) measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one elementwise copy of this many MiB before timing "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -282,6 +340,12 @@ def main() -> int:
             "kernel_ms": float(k_ms.mean()),
         },
     }
+    if not args.no_prep:
+        from vdn_inputs import GRIDS
+        if cfg.name in GRIDS:
+            res["vda_prep"] = measure_prep(cfg, t, cpu=not args.no_cpu_baseline)
+            print(f"[bench] vda_prep_fwd: {res['vda_prep']['ms']:.3f} ms, "
+                  f"{res['vda_prep']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(res), flush=True)

@@ -22,14 +22,16 @@
 //    slides over the frames.  For each input frame the kernel_h grid rows
 //    around the row (with a column halo) are staged in LDS as fp32; each lane
 //    task (column, 8 channels) forms the spatial sum for that frame and
-//    shifts it into a per-lane register window of the last kTapsMax frames
-//    (no LDS round trip for the temporal filter).  When the window holds an
+//    keeps it in a per-lane circular register window of the last kTapsMax
+//    frames (no LDS round trip for the temporal filter).  When the window holds an
 //    output frame's last input frame, the temporal sum, SiLU and (for K) the
 //    L2 norm over the token's D/8 lanes give the output row, written
 //    frame-major.  The next frame's rows are fetched into registers while
 //    the current frame is computed.
 #include "vdn_common.h"
 #include "vdn_internal.h"
+
+#include <type_traits>
 
 namespace vdn {
 
@@ -71,7 +73,8 @@ template <> struct Chunk8<float> {    // 8 float = two 16-byte accesses
   }
 };
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+// SiLU with a hardware reciprocal (about 1 ulp): x -> -inf gives -0.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // Sum over the `lanes` consecutive lanes (a power of two <= 16) of one row.
 __device__ __forceinline__ float row_sum(float x, int lanes) {
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_q_kernel(const T* __res
   for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
   ss = row_sum(ss, C8);
   if (!ok) return;
-  const float r = 1.f / sqrtf(ss + eps);
+  const float r = rsqrtf(ss + eps);
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] *= r;
   const int h = (int)(row % H);
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_q_kernel(const T* __res
 // K, V: separable short convolution + SiLU (+ L2 for K) + layout change.
 // ---------------------------------------------------------------------------
 constexpr int kTapsMax = 5;
+constexpr int kRing = 5;          // register window slots
 constexpr int kPrefetchMax = 8;   // staged 8-channel chunks per thread and frame
 
 struct PrepArgs {
@@ -126,16 +130,19 @@ struct PrepArgs {
   float eps;
 };
 
-template <typename T, int D>
+// KH, KW > 0 fix the spatial filter size at compile time (fully unrolled
+// taps); 0 reads it from the arguments.
+template <typename T, int D, int KH, int KW>
 __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
   constexpr int C8 = D / 8;
-  constexpr int TPT = (32 * C8 + kPrepThreads - 1) / kPrepThreads;   // tasks per thread (xt <= 32)
+  const int kh = KH > 0 ? KH : a.kh, kw = KW > 0 ? KW : a.kw;
+  constexpr int TPT = (16 * C8 + kPrepThreads - 1) / kPrepThreads;   // column-pair tasks per thread (xt <= 32)
   extern __shared__ __attribute__((aligned(16))) float sm[];
   // LDS: staged rows [kh][xt + kw - 1][D] | spatial weights [kh*kw][D] | temporal weights by window slot [kTapsMax][D]
-  const int cols = a.xt + a.kw - 1;
+  const int cols = a.xt + kw - 1;
   float* in_s = sm;
-  float* ws_s = in_s + (size_t)a.kh * cols * D;
-  float* wt_s = ws_s + (size_t)a.kh * a.kw * D;
+  float* ws_s = in_s + (size_t)kh * cols * D;
+  float* wt_s = ws_s + (size_t)kh * kw * D;
 
   int bid = blockIdx.x;
   const int which = bid & 1; bid >>= 1;             // 0 = K, 1 = V
@@ -148,13 +155,13 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
   T* dst = static_cast<T*>(a.dst[which]);
   const int tid = threadIdx.x;
   const int N = a.gh * a.gw;
-  const int ry = (a.kh - 1) / 2, rx = (a.kw - 1) / 2;
+  const int ry = (kh - 1) / 2, rx = (kw - 1) / 2;
 
   // filters of head h: spatial [tap][c]; temporal placed at the window slots
   // kTapsMax - taps .. kTapsMax - 1 (older slots get zero)
-  for (int e = tid; e < a.kh * a.kw * D; e += kPrepThreads) {
+  for (int e = tid; e < kh * kw * D; e += kPrepThreads) {
     const int tap = e / D, c = e % D;
-    ws_s[e] = a.w_sp[((size_t)h * D + c) * a.kh * a.kw + tap];
+    ws_s[e] = a.w_sp[((size_t)h * D + c) * kh * kw + tap];
   }
   for (int e = tid; e < kTapsMax * D; e += kPrepThreads) {
     const int slot = e / D, c = e % D;
@@ -163,9 +170,9 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
   }
 
   // staging: chunk q -> (row r, column cx, c8)
-  const int nchunk = a.kh * cols * C8;
-  Chunk8<T> pf[kPrefetchMax];
-  auto fetch = [&](int fi) {
+  const int nchunk = kh * cols * C8;
+  Chunk8<T> pf[kPrefetchMax];   // next frame's rows, fetched one frame ahead
+  auto fetch = [&](Chunk8<T>* pf, int fi) {
 #pragma unroll
     for (int i = 0; i < kPrefetchMax; ++i) {
       const int qq = tid + kPrepThreads * i;
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
       }
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](const Chunk8<T>* pf) {
 #pragma unroll
     for (int i = 0; i < kPrefetchMax; ++i) {
       const int qq = tid + kPrepThreads * i;
@@ -195,84 +202,126 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
     }
   };
 
-  float win[TPT][kTapsMax][8];   // spatial sums of the last kTapsMax frames, oldest first
+  // spatial sums of recent frames in a circular window: frame fi lives in
+  // slot fi % kRing, so the frame loop is unrolled kRing times and every slot
+  // index is static (no register shuffling).  A lane task covers two
+  // adjacent columns, which share kw of their kw + 1 input columns.
+  float win[TPT][kRing][2][8];
 #pragma unroll
   for (int j = 0; j < TPT; ++j)
 #pragma unroll
-    for (int s = 0; s < kTapsMax; ++s)
+    for (int sl = 0; sl < kRing; ++sl)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) win[j][s][i] = 0.f;
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) win[j][sl][e][i] = 0.f;
 
+  constexpr int KWM = KW > 0 ? KW : 7, KHM = KH > 0 ? KH : 7;
   const int nsteps = a.F + a.taps - 1 - a.t0;
-  fetch(0);
-  for (int fi = 0; fi < nsteps; ++fi) {
+  auto step = [&](int fi, auto uc) {
+    constexpr int u = decltype(uc)::value;   // = fi % kRing
     __syncthreads();     // previous frame's spatial reads done; filters staged
-    stage();
+    stage(pf);
     __syncthreads();
-    if (fi + 1 < nsteps) fetch(fi + 1);
+    if (fi + 1 < nsteps) fetch(pf, fi + 1);
     const int fo = fi - (a.taps - 1 - a.t0);
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
       const int t = tid + kPrepThreads * j;
-      const int xl = t / C8, c8 = t % C8;
-      const bool active = xl < a.xt && x0 + xl < a.gw;
-      float s[8] = {};
-      if (active) {
-        for (int dy = 0; dy < a.kh; ++dy)
-          for (int dx = 0; dx < a.kw; ++dx) {
-            const float* xin = in_s + (size_t)(dy * cols + xl + dx) * D + c8 * 8;
-            const float* w = ws_s + (size_t)(dy * a.kw + dx) * D + c8 * 8;
-            const u32x4 x0v = ld16(xin), x1v = ld16(xin + 4), w0v = ld16(w), w1v = ld16(w + 4);
+      const int xl = 2 * (t / C8), c8 = t % C8;
+      const bool act[2] = {xl < a.xt && x0 + xl < a.gw, xl + 1 < a.xt && x0 + xl + 1 < a.gw};
+      float s[2][8] = {};
+      if (act[0]) {
+#pragma unroll
+        for (int dy = 0; dy < KHM; ++dy) {
+          if (KH == 0 && dy >= kh) continue;
+          float xc[KWM + 1][8];
+#pragma unroll
+          for (int cx = 0; cx <= KWM; ++cx) {
+            if (KW == 0 && cx > kw) continue;
+            const float* xin = in_s + (size_t)(dy * cols + xl + cx) * D + c8 * 8;
+            const u32x4 v0 = ld16(xin), v1 = ld16(xin + 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              s[i] = fmaf(__uint_as_float(w0v[i]), __uint_as_float(x0v[i]), s[i]);
-              s[4 + i] = fmaf(__uint_as_float(w1v[i]), __uint_as_float(x1v[i]), s[4 + i]);
+              xc[cx][i] = __uint_as_float(v0[i]);
+              xc[cx][4 + i] = __uint_as_float(v1[i]);
             }
           }
-      }
 #pragma unroll
-      for (int sl = 0; sl + 1 < kTapsMax; ++sl)
+          for (int dx = 0; dx < KWM; ++dx) {
+            if (KW == 0 && dx >= kw) continue;
+            const float* w = ws_s + (size_t)(dy * kw + dx) * D + c8 * 8;
+            const u32x4 w0v = ld16(w), w1v = ld16(w + 4);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) win[j][sl][i] = win[j][sl + 1][i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) win[j][kTapsMax - 1][i] = s[i];
-      if (fo < 0) continue;
-      float o[8] = {};
-#pragma unroll
-      for (int sl = 0; sl < kTapsMax; ++sl) {
-        const float* w = wt_s + (size_t)sl * D + c8 * 8;
-        const u32x4 w0v = ld16(w), w1v = ld16(w + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[i] = fmaf(__uint_as_float(w0v[i]), win[j][sl][i], o[i]);
-          o[4 + i] = fmaf(__uint_as_float(w1v[i]), win[j][sl][4 + i], o[4 + i]);
+            for (int i = 0; i < 4; ++i) {
+              const float wa = __uint_as_float(w0v[i]), wb = __uint_as_float(w1v[i]);
+              s[0][i] = fmaf(wa, xc[dx][i], s[0][i]);
+              s[0][4 + i] = fmaf(wb, xc[dx][4 + i], s[0][4 + i]);
+              s[1][i] = fmaf(wa, xc[dx + 1][i], s[1][i]);
+              s[1][4 + i] = fmaf(wb, xc[dx + 1][4 + i], s[1][4 + i]);
+            }
+          }
         }
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = silu(o[i]);
-      if (which == 0) {   // K: L2 over the token's D channels (its C8 consecutive lanes)
-        float ss = 0.f;
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss = fmaf(o[i], o[i], ss);
-        ss = row_sum(ss, C8);
-        const float r = 1.f / sqrtf(ss + a.eps);
+        for (int i = 0; i < 8; ++i) win[j][u][e][i] = s[e][i];
+      if (fo < 0) continue;
+      // frame fi - k (slot (u - k) mod kRing) meets temporal weight slot kTapsMax - 1 - k
+      float o[2][8] = {};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] *= r;
+      for (int k = 0; k < kTapsMax; ++k) {
+        const int sl = (u - k + kRing) % kRing;
+        const float* w = wt_s + (size_t)(kTapsMax - 1 - k) * D + c8 * 8;
+        const u32x4 w0v = ld16(w), w1v = ld16(w + 4);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[e][i] = fmaf(__uint_as_float(w0v[i]), win[j][sl][e][i], o[e][i]);
+            o[e][4 + i] = fmaf(__uint_as_float(w1v[i]), win[j][sl][e][4 + i], o[e][4 + i]);
+          }
       }
-      if (active) {
-        const long long l = (long long)fo * N + (long long)y * a.gw + x0 + xl;
-        Chunk8<T>::store(dst + (((size_t)b * a.H + h) * a.L + l) * D + c8 * 8, o);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[e][i] = silu(o[e][i]);
+        if (which == 0) {   // K: L2 over the token's D channels (its C8 consecutive lanes)
+          float ss = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ss = fmaf(o[e][i], o[e][i], ss);
+          ss = row_sum(ss, C8);
+          const float r = rsqrtf(ss + a.eps);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[e][i] *= r;
+        }
+        if (act[e]) {
+          const long long l = (long long)fo * N + (long long)y * a.gw + x0 + xl + e;
+          Chunk8<T>::store(dst + (((size_t)b * a.H + h) * a.L + l) * D + c8 * 8, o[e]);
+        }
       }
     }
+  };
+  fetch(pf, 0);
+  for (int fb = 0; fb < nsteps; fb += kRing) {
+    step(fb, std::integral_constant<int, 0>{});
+    if (fb + 1 < nsteps) step(fb + 1, std::integral_constant<int, 1>{});
+    if (fb + 2 < nsteps) step(fb + 2, std::integral_constant<int, 2>{});
+    if (fb + 3 < nsteps) step(fb + 3, std::integral_constant<int, 3>{});
+    if (fb + 4 < nsteps) step(fb + 4, std::integral_constant<int, 4>{});
   }
+  static_assert(kRing == 5 && kRing >= kTapsMax, "the frame loop is unrolled kRing times");
 }
 
-// Largest column tile (<= 32) whose LDS footprint stays within 64 KB.
+// Largest even column tile (<= 32) whose LDS footprint stays within 64 KB;
+// a grid narrower than the tile rounds up to even (the extra column is
+// outside the grid and reads as zeros).
 int prep_tile_cols(int D, int kh, int kw, int gw) {
-  for (int xt = 32; xt >= 1; xt >>= 1) {
+  for (int xt = 32; xt >= 2; xt >>= 1) {
     const size_t bytes = ((size_t)kh * (xt + kw - 1) * D + (size_t)kh * kw * D + (size_t)kTapsMax * D) * 4;
     const int chunks = kh * (xt + kw - 1) * (D / 8);
-    if (bytes <= 65536 && chunks <= kPrefetchMax * kPrepThreads) return xt < gw ? xt : gw;
+    if (bytes <= 65536 && chunks <= kPrefetchMax * kPrepThreads) return xt < gw ? xt : (gw + 1) / 2 * 2;
   }
   return 0;
 }
@@ -301,7 +350,10 @@ hipError_t launch_vda_prep(const void* q, const void* k, const void* v, const fl
 #define VDN_PREP_CASE(DD)                                                                          \
   case DD:                                                                                         \
     vda_prep_q_kernel<T, DD><<<qgrid, kPrepThreads, 0, s>>>((const T*)q, (T*)q_out, rows, H, L, eps); \
-    vda_prep_kv_kernel<T, DD><<<kvgrid, kPrepThreads, lds, s>>>(a);                                \
+    if (kh == 3 && kw == 3)                                                                        \
+      vda_prep_kv_kernel<T, DD, 3, 3><<<kvgrid, kPrepThreads, lds, s>>>(a);                        \
+    else                                                                                           \
+      vda_prep_kv_kernel<T, DD, 0, 0><<<kvgrid, kPrepThreads, lds, s>>>(a);                        \
     break;
   switch (D) {
     VDN_PREP_CASE(16)

@@ -144,10 +144,17 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
   float* ws_s = in_s + (size_t)kh * cols * D;
   float* wt_s = ws_s + (size_t)kh * kw * D;
 
-  int bid = blockIdx.x;
-  const int which = bid & 1; bid >>= 1;             // 0 = K, 1 = V
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so XCD
+  // x = blockIdx % 8 takes a contiguous run of the logical order (b, h,
+  // tensor, grid row, column tile); workgroups of neighbouring grid rows,
+  // which stage the same input rows, then share that XCD's L2.
+  const int total = a.B * a.H * 2 * a.gh * a.ntx;
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  int bid = (int)(blockIdx.x % kNumXcd) * per + (int)(blockIdx.x / kNumXcd);
+  if (bid >= total) return;
   const int xt_i = bid % a.ntx; bid /= a.ntx;
   const int y = bid % a.gh; bid /= a.gh;
+  const int which = bid & 1; bid >>= 1;             // 0 = K, 1 = V
   const int h = bid % a.H;
   const int b = bid / a.H;
   const int x0 = xt_i * a.xt;
@@ -345,7 +352,8 @@ hipError_t launch_vda_prep(const void* q, const void* k, const void* v, const fl
   a.ntx = (gw + a.xt - 1) / a.xt;
   a.L = L;
   a.eps = eps;
-  const unsigned kvgrid = (unsigned)((long long)B * H * gh * a.ntx * 2);
+  const long long kvtotal = (long long)B * H * gh * a.ntx * 2;
+  const unsigned kvgrid = (unsigned)((kvtotal + kNumXcd - 1) / kNumXcd * kNumXcd);
   const size_t lds = ((size_t)kh * (a.xt + kw - 1) * D + (size_t)kh * kw * D + (size_t)kTapsMax * D) * 4;
 #define VDN_PREP_CASE(DD)                                                                          \
   case DD:                                                                                         \

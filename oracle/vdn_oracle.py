@@ -45,6 +45,14 @@ class Params:
     text_init_scale: each directional scan starts from this multiple of the
       text state.  The page says the two readouts together count the prompt
       exactly once, which fixes the reading 1/2.
+    text_softmax: False (the default) is the video-to-video operator: the
+      Softmax branch sees video keys only.  True adds the T text tokens to
+      the key set of every video query, always visible, in the same
+      normalisation (method, bidirectional linear attention: the text stays
+      directly visible to the Softmax branch while the linear memory also
+      starts from its summary).  Reading: the text keys join the one softmax
+      of each query (not a separate, separately normalised attention), and
+      anchor frames see them as well.
     """
     chunk_frames: int = 5
     window_chunks: int = 1
@@ -52,6 +60,7 @@ class Params:
     softmax_scale: float | None = None     # None -> 1/sqrt(dk)
     rms_eps: float = 1e-6
     text_init_scale: float = 0.5
+    text_softmax: bool = False
 
 
 DEFAULT = Params()
@@ -356,20 +365,27 @@ def linear_branch(Q, M_fwd, M_rev, g_l, gamma, p: Params = DEFAULT):
 # --------------------------------------------------------------------------
 # Softmax branch
 # --------------------------------------------------------------------------
-def softmax_rows(Qrows, t, Kf, Vf, p: Params = DEFAULT):
+def softmax_rows(Qrows, t, Kf, Vf, p: Params = DEFAULT, K_text=None, V_text=None):
     """Softmax attention of query rows of frame t over Vis(t).
 
     Method, local Softmax window: exact Softmax attention over the tokens of
-    every visible key frame (each frame once).  Scale 1/sqrt(dk) unless
-    given.  Returns (O [n, dv], lse [n]) with lse the natural-log
-    normaliser of the scaled logits.
+    every visible key frame (each frame once).  With p.text_softmax the T
+    text tokens (K_text [T, dk], V_text [T, dv]) are further keys of the
+    same softmax, visible to every query.  Scale 1/sqrt(dk) unless given.
+    Returns (O [n, dv], lse [n]) with lse the natural-log normaliser of the
+    scaled logits.
     """
     F = Kf.shape[0]
     dk = Kf.shape[2]
     scale = (1.0 / math.sqrt(dk)) if p.softmax_scale is None else p.softmax_scale
     fr = sorted(visible_frames(t, F, p))
-    Kv = np.concatenate([np.asarray(Kf[f], np.float64) for f in fr])
-    Vv = np.concatenate([np.asarray(Vf[f], np.float64) for f in fr])
+    blocks_k = [np.asarray(Kf[f], np.float64) for f in fr]
+    blocks_v = [np.asarray(Vf[f], np.float64) for f in fr]
+    if p.text_softmax and K_text is not None and len(K_text):
+        blocks_k.append(np.asarray(K_text, np.float64))
+        blocks_v.append(np.asarray(V_text, np.float64))
+    Kv = np.concatenate(blocks_k)
+    Vv = np.concatenate(blocks_v)
     s = (np.asarray(Qrows, np.float64) @ Kv.T) * scale
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -379,19 +395,20 @@ def softmax_rows(Qrows, t, Kf, Vf, p: Params = DEFAULT):
     return O, lse
 
 
-def softmax_branch(Qf, Kf, Vf, g_s, p: Params = DEFAULT):
+def softmax_branch(Qf, Kf, Vf, g_s, p: Params = DEFAULT, K_text=None, V_text=None):
     """O_s and Ohat_s = g_s * O_s for every token of one head.
 
     Method, branch calibration: a content-dependent sigmoid gate scales the
     Softmax readout (the gate values are inputs here).
-    Qf, Kf, Vf: [F, N, d]; g_s: [F, N].  Returns (O_s, Ohat_s, lse).
+    Qf, Kf, Vf: [F, N, d]; g_s: [F, N]; K_text, V_text: [T, d] (used only
+    with p.text_softmax).  Returns (O_s, Ohat_s, lse).
     """
     F, N = Qf.shape[:2]
     dv = Vf.shape[2]
     O = np.zeros((F, N, dv))
     lse = np.zeros((F, N))
     for t in range(F):
-        O[t], lse[t] = softmax_rows(Qf[t], t, Kf, Vf, p)
+        O[t], lse[t] = softmax_rows(Qf[t], t, Kf, Vf, p, K_text, V_text)
     return O, np.asarray(g_s, np.float64)[..., None] * O, lse
 
 
@@ -452,7 +469,7 @@ def vdn_head(q, k, v, beta, alpha, k_text, v_text, beta_text, g_s, g_l,
     O_l, Ohat_l = linear_branch(Qf, M_fwd, M_rev, np.reshape(g_l, (F, N)), gamma, p)
     out["O_l"], out["Ohat_l"] = O_l.reshape(L, dv), Ohat_l.reshape(L, dv)
     if want_softmax:
-        O_s, Ohat_s, lse = softmax_branch(Qf, Kf, Vf, np.reshape(g_s, (F, N)), p)
+        O_s, Ohat_s, lse = softmax_branch(Qf, Kf, Vf, np.reshape(g_s, (F, N)), p, k_text, v_text)
         out["O_s"], out["Ohat_s"], out["lse"] = (O_s.reshape(L, dv),
                                                  Ohat_s.reshape(L, dv), lse.reshape(L))
     return out
@@ -522,7 +539,7 @@ def head_rows(q, k, v, beta, alpha, k_text, v_text, beta_text, g_s, g_l, rows,
                                   np.asarray(g_l, np.float64)[rows[sel]][None], gamma, p)
         out["O_l"][sel], out["Ohat_l"][sel] = O_l[0], Oh_l[0]
         if want_softmax:
-            O_s, lse = softmax_rows(qr, int(t), Kf, Vf, p)
+            O_s, lse = softmax_rows(qr, int(t), Kf, Vf, p, k_text, v_text)
             out["O_s"][sel] = O_s
             out["Ohat_s"][sel] = np.asarray(g_s, np.float64)[rows[sel]][:, None] * O_s
             out["lse"][sel] = lse

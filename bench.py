@@ -206,6 +206,53 @@ def measure_prep(cfg, t, reps: int = 10, cpu: bool = True) -> dict:
     return res
 
 
+def measure_text(cfg, t, reps: int = 5) -> dict:
+    """The same layer with the text keys inside the Softmax branch
+    (params.text_softmax = 1: every video query also sees the T text keys):
+    ms per vdn_attn_fwd call and the Softmax kernel's MFMA roofline figures,
+    counting the extra F*N*T (query, text key) pairs."""
+    import torch
+
+    import softmax_attention_video_amd as vdn
+
+    params = vdn.Params(text_softmax=1)
+    B, H, L, d = t["q"].shape
+    dev = t["q"].device
+    dims = vdn.Dims(B, H, cfg.F, cfg.N, cfg.T, d, d, cfg.D)
+    code = vdn.VDN_BF16 if t["q"].dtype == torch.bfloat16 else vdn.VDN_F32
+    ws = torch.empty(vdn.workspace_bytes(dims, params, code), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, L, cfg.D), dtype=t["q"].dtype, device=dev)
+
+    def run():
+        vdn.attn_fwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["k_text"], t["v_text"],
+                     t["beta_text"], t["g_s"], t["g_l"], gamma=t["gamma"], W_s=t["W_s"],
+                     W_l=t["W_l"], out=out, workspace=ws, params=params)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    timer = vdn.KernelTimer(reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    k_ms = timer.read()
+    timer.close()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = int(vdn.window_plan(cfg.F)[0].sum())
+    sm_flops = 4.0 * d * (pairs * cfg.N * cfg.N + cfg.F * cfg.N * cfg.T) * H * B
+    ach = sm_flops / (float(k_ms.mean()) / 1e3) / 1e12
+    del ws, out
+    return {"entry": "vdn_attn_fwd with text_softmax = 1",
+            "workload": f"{cfg.name} with its T={cfg.T} text keys visible to every video query",
+            "ms_per_step": ms, "tokens_per_s": B * L / (ms / 1e3),
+            "kernel": "window_softmax_mfma_kernel<128, text>", "kernel_ms": float(k_ms.mean()),
+            "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "softmax_flops": sm_flops}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +262,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prep", action="store_true",
                     help="skip the separate VDA-Prep (vda_prep_fwd) measurement")
+    ap.add_argument("--no-text", action="store_true",
+                    help="skip the separate text-keys-in-Softmax measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one elementwise copy of this many MiB before timing "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -346,6 +395,10 @@ def main() -> int:
             res["vda_prep"] = measure_prep(cfg, t, cpu=not args.no_cpu_baseline)
             print(f"[bench] vda_prep_fwd: {res['vda_prep']['ms']:.3f} ms, "
                   f"{res['vda_prep']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
+    if not args.no_text and cfg.T > 0 and cfg.dtype == "bf16":
+        res["text_softmax"] = measure_text(cfg, t)
+        print(f"[bench] text keys in the Softmax: {res['text_softmax']['ms_per_step']:.3f} ms/step, "
+              f"Softmax kernel {res['text_softmax']['kernel_ms']:.3f} ms", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(res), flush=True)

@@ -70,7 +70,13 @@ typedef struct {
  *  chunk_frames    : latent frames per VAE temporal chunk (5).
  *  window_chunks   : a query chunk sees this many chunks on each side (1).
  *  anchors         : 1 = frames 0 and F-1 are boundary anchors with
- *                    four-way connectivity, 0 = no anchors.            */
+ *                    four-way connectivity, 0 = no anchors.
+ *  text_softmax    : 0 = the Softmax branch sees video keys only (the
+ *                    video-to-video operator, default); 1 = the T text
+ *                    tokens are keys of every video query too, always
+ *                    visible, inside the same softmax (method, bidirectional
+ *                    linear attention: the prompt stays directly visible to
+ *                    the Softmax branch).  The linear branch is unchanged. */
 typedef struct {
   float softmax_scale;
   float rms_eps;
@@ -78,6 +84,7 @@ typedef struct {
   int chunk_frames;
   int window_chunks;
   int anchors;
+  int text_softmax;
 } vdn_params;
 
 /* Fills *p with the defaults listed above. */
@@ -89,6 +96,7 @@ void vdn_default_params(vdn_params* p);
  * Method, hybrid attention (paper: local Softmax window and boundary
  * anchors; bidirectional linear attention; branch calibration):
  *   Ohat_s = g_s * Softmax-window/anchor attention(q, k, v)
+ *            (plus the text keys when p->text_softmax = 1)
  *   Ohat_l = g_l * gamma * O_l / sqrt(mean_dv(O_l^2) + rms_eps),
  *            O_l = q^T (M_fwd + M_rev), the two VDA directional memories
  *   out    = Ohat_s W_s + Ohat_l W_l      (heads concatenated, h*d_v + j)
@@ -160,11 +168,15 @@ vdn_status vda_scan_rev(const void* k, const void* v, const float* beta, const f
  * token of the frames whose chunk is within window_chunks of c, plus (with
  * anchors) frames 0 and F-1; frames 0 and F-1 see every frame; each frame is
  * counted once.  out = g_s * softmax(scale * q k^T) v over those keys.
+ * With p->text_softmax = 1 the dims->T text tokens join every query's keys.
  *
  *  q, k, v [B,H,L,d] dt;  g_s [B,H,L] float, NULL = 1
+ *  k_text, v_text [B,H,T,d] dt   read only when p->text_softmax = 1 and
+ *                                T > 0 (then non-NULL), else may be NULL
  *  out [B,L,H,d_v] dt;  lse [B,H,L] float natural-log normaliser, nullable
  */
-vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v, const float* g_s,
+vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v,
+                                  const void* k_text, const void* v_text, const float* g_s,
                                   void* out, float* lse,
                                   void* workspace, size_t workspace_bytes,
                                   const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,

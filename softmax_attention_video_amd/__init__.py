@@ -46,7 +46,8 @@ class Dims(ctypes.Structure):
 class CParams(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("text_init_scale", ctypes.c_float), ("chunk_frames", ctypes.c_int),
-                ("window_chunks", ctypes.c_int), ("anchors", ctypes.c_int)]
+                ("window_chunks", ctypes.c_int), ("anchors", ctypes.c_int),
+                ("text_softmax", ctypes.c_int)]
 
 
 class CPrepParams(ctypes.Structure):
@@ -74,17 +75,19 @@ class PrepParams:
 @dataclasses.dataclass(frozen=True)
 class Params:
     """Operator hyper-parameters (defaults: 5-frame chunks, +-1 chunk window,
-    anchors on, scale 1/sqrt(d_k) (0 = default), eps 1e-6, text split 1/2)."""
+    anchors on, scale 1/sqrt(d_k) (0 = default), eps 1e-6, text split 1/2,
+    text keys outside the Softmax branch)."""
     softmax_scale: float = 0.0
     rms_eps: float = 1e-6
     text_init_scale: float = 0.5
     chunk_frames: int = 5
     window_chunks: int = 1
     anchors: int = 1
+    text_softmax: int = 0
 
     def c(self) -> CParams:
         return CParams(self.softmax_scale, self.rms_eps, self.text_init_scale,
-                       self.chunk_frames, self.window_chunks, self.anchors)
+                       self.chunk_frames, self.window_chunks, self.anchors, self.text_softmax)
 
 
 _lib = None
@@ -108,7 +111,7 @@ def lib() -> ctypes.CDLL:
     for n in ("vda_scan_fwd", "vda_scan_rev"):
         getattr(L, n).argtypes = [P] * 10 + [S, dp, pp, I, P]
         getattr(L, n).restype = I
-    L.vdn_window_softmax_fwd.argtypes = [P] * 7 + [S, dp, pp, I, P]
+    L.vdn_window_softmax_fwd.argtypes = [P] * 9 + [S, dp, pp, I, P]
     L.vdn_window_softmax_fwd.restype = I
     L.vdn_workspace_bytes.argtypes = [dp, pp, I]
     L.vdn_workspace_bytes.restype = S
@@ -143,7 +146,7 @@ def default_params() -> Params:
     c = CParams()
     lib().vdn_default_params(ctypes.byref(c))
     return Params(c.softmax_scale, c.rms_eps, c.text_init_scale, c.chunk_frames,
-                  c.window_chunks, c.anchors)
+                  c.window_chunks, c.anchors, c.text_softmax)
 
 
 def window_plan(F: int, params: Params | None = None):
@@ -332,9 +335,11 @@ def scan_rev(k, v, beta, alpha, k_text, v_text, beta_text, params=None, workspac
 
 
 def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=None,
-                       params: Params | None = None, workspace=None, stream=None):
-    """Window/anchor Softmax branch (vdn_window_softmax_fwd).
-    Returns (out [B,L,H,d], lse [B,H,L] or None)."""
+                       params: Params | None = None, workspace=None, stream=None,
+                       k_text=None, v_text=None):
+    """Window/anchor Softmax branch (vdn_window_softmax_fwd).  With
+    params.text_softmax the text keys k_text, v_text [B,H,T,d] join every
+    query's keys.  Returns (out [B,L,H,d], lse [B,H,L] or None)."""
     torch = _torch()
     params = params or Params()
     B, H, L, d = q.shape
@@ -344,7 +349,8 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
     dt = q.dtype
     code = _dtype_code(q)
     dev = q.device
-    dims = Dims(B, H, F, N, 0, d, d, H * d)
+    T = k_text.shape[2] if k_text is not None else 0
+    dims = Dims(B, H, F, N, T, d, d, H * d)
     if out is None:
         out = torch.empty((B, L, H, d), dtype=dt, device=dev)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=dev) if want_lse else None
@@ -353,6 +359,8 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
     _check(lib().vdn_window_softmax_fwd(
         _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
         _ptr(v, "v", dt, (B, H, L, d), dev),
+        _ptr(k_text, "k_text", dt, (B, H, T, d), dev, allow_none=True),
+        _ptr(v_text, "v_text", dt, (B, H, T, d), dev, allow_none=T == 0),
         _ptr(g_s, "g_s", torch.float32, (B, H, L), dev, allow_none=True),
         _ptr(out, "out", dt, (B, L, H, d), dev),
         _ptr(lse, "lse", torch.float32, (B, H, L), dev, allow_none=True),

@@ -6,13 +6,18 @@
 // side; with anchors every frame also sees frames 0 and F-1 and those two
 // frames see every frame; each key frame counts once.
 //
+// Optionally (method, bidirectional linear attention: the prompt stays
+// directly visible to the Softmax branch) the Ts text tokens are keys of
+// every video query as well, in the same softmax.
+//
 // Work decomposition.  All non-anchor query frames of one chunk share one
 // key set, so a "chunk group" is the contiguous query range of a chunk minus
 // its anchor frames, and its keys are at most three contiguous token spans
 // (anchor 0, the window, anchor F-1).  An "anchor group" is one anchor frame,
-// whose keys are the whole sequence.  Groups are cut into query tiles; one
-// workgroup owns one tile and streams the key spans through LDS with an
-// online softmax (no mask tensor, no gathered copies).
+// whose keys are the whole sequence.  The text keys are one more span, after
+// the video ones, numbered L .. L+Ts-1 in the walk.  Groups are cut into
+// query tiles; one workgroup owns one tile and streams the key spans through
+// LDS with an online softmax (no mask tensor, no gathered copies).
 //
 // XCD-aware order: MI355X deals workgroups round-robin to its 8 XCDs, so
 // blockIdx b runs on XCD b % 8.  Each XCD gets a contiguous slice of groups
@@ -22,6 +27,8 @@
 #include "vdn_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace vdn {
 
@@ -50,40 +57,60 @@ struct Item {
   int bh;            // b * H + h
   int q_begin, q_end;
   int nspan;
-  int kb0, ke0, kb1, ke1, kb2, ke2;   // up to three key spans [kb, ke) in tokens
+  int kb0, ke0, kb1, ke1, kb2, ke2, kb3, ke3;   // up to four key spans [kb, ke)
 };
 
-// Key tiles of BK over the (up to three) spans, flattened: tile j of the
+// Key tiles of BK over the (up to NS <= 4) spans, flattened: tile j of the
 // walk starts at key ks and holds nk valid keys.  The lookup is plain
 // arithmetic on the span index (no selects of struct members), which keeps
 // the walk in scalar registers instead of private memory.
-template <int BK>
+template <int BK, int NS>
 struct SpanWalk {
-  int n0, n01, n;      // cumulative tile counts
-  int o0, o1, o2;      // key start of tile j in span i is j * BK + o_i
-  int e0, e1, e2;      // span ends
+  int n0, n01, n012, n;   // cumulative tile counts
+  int o0, o1, o2, o3;     // key start of tile j in span i is j * BK + o_i
+  int e0, e1, e2, e3;     // span ends
   __device__ __forceinline__ SpanWalk(const Item& it) {
     const int kb1 = it.nspan > 1 ? it.kb1 : 0, ke1 = it.nspan > 1 ? it.ke1 : 0;
     const int kb2 = it.nspan > 2 ? it.kb2 : 0, ke2 = it.nspan > 2 ? it.ke2 : 0;
+    const int kb3 = NS > 3 && it.nspan > 3 ? it.kb3 : 0, ke3 = NS > 3 && it.nspan > 3 ? it.ke3 : 0;
     n0 = (it.ke0 - it.kb0 + BK - 1) / BK;
     n01 = n0 + (ke1 - kb1 + BK - 1) / BK;
-    n = n01 + (ke2 - kb2 + BK - 1) / BK;
+    n012 = n01 + (ke2 - kb2 + BK - 1) / BK;
+    n = n012 + (ke3 - kb3 + BK - 1) / BK;
     o0 = it.kb0;
     o1 = kb1 - n0 * BK;
     o2 = kb2 - n01 * BK;
-    e0 = it.ke0; e1 = ke1; e2 = ke2;
+    o3 = kb3 - n012 * BK;
+    e0 = it.ke0; e1 = ke1; e2 = ke2; e3 = ke3;
   }
   __device__ __forceinline__ void tile(int j, int& ks, int& nk) const {
-    const int s1 = j >= n0, s2 = j >= n01;
-    ks = j * BK + o0 + (o1 - o0) * s1 + (o2 - o1) * s2;
-    const int e = e0 + (e1 - e0) * s1 + (e2 - e1) * s2;
+    const int s1 = j >= n0, s2 = j >= n01, s3 = NS > 3 && j >= n012;
+    ks = j * BK + o0 + (o1 - o0) * s1 + (o2 - o1) * s2 + (o3 - o2) * s3;
+    const int e = e0 + (e1 - e0) * s1 + (e2 - e1) * s2 + (e3 - e2) * s3;
     nk = min(BK, e - ks);
   }
 };
 
+// Appends the text span [L, L + nt) after the item's video spans.
+__device__ __forceinline__ void add_text_span(const Geometry& g, int nt, Item& it) {
+  it.kb3 = it.ke3 = 0;
+  if (nt <= 0) return;
+  const int tb = (int)g.L, te = (int)(g.L + nt);
+  if (it.nspan == 1) {
+    it.kb1 = tb; it.ke1 = te;
+  } else if (it.nspan == 2) {
+    it.kb2 = tb; it.ke2 = te;
+  } else {
+    it.kb3 = tb; it.ke3 = te;
+  }
+  ++it.nspan;
+}
+
 // Decode workgroup id -> (query range, key spans).  Returns false if idle.
+// TEXT: append a span of the first nt text keys (none if nt == 0).
+template <bool TEXT>
 __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork& w, int bq,
-                                            int bid, Item& it, int& q0) {
+                                            int bid, int nt, Item& it, int& q0) {
   const int x = bid % kNumXcd;
   int k = bid / kNumXcd;
   const int a0 = x * w.pa;
@@ -100,7 +127,8 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
     it.nspan = 1;
     it.kb0 = 0;
     it.ke0 = (int)g.L;
-    it.kb1 = it.ke1 = it.kb2 = it.ke2 = 0;
+    it.kb1 = it.ke1 = it.kb2 = it.ke2 = it.kb3 = it.ke3 = 0;
+    if (TEXT) add_text_span(g, nt, it);
     q0 = it.q_begin + tile * bq;
     return true;
   }
@@ -133,6 +161,8 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
   it.kb2 = (g.F - 1) * nN;
   it.ke2 = g.F * nN;
   it.nspan = 1 + (a_lo ? 1 : 0) + (a_hi ? 1 : 0);
+  it.kb3 = it.ke3 = 0;
+  if (TEXT) add_text_span(g, nt, it);
   q0 = it.q_begin + tile * bq;
   return q0 < it.q_end;
 }
@@ -167,7 +197,9 @@ struct WinArgs {
   SoftmaxWork w;
   const bf16_t* q;
   const bf16_t* k;
-  const bf16_t* vt;
+  const bf16_t* kt;      // text keys [B,H,Ts,D]
+  const bf16_t* vt;      // V^T [B,H,D,Lp]: video keys, then text keys
+  long long vt_pitch;    // Lp
   const float* g_s;
   bf16_t* out;
   float* lse;
@@ -180,7 +212,7 @@ constexpr float kLazySum = 256.f;
 
 __device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
-template <int D>
+template <int D, bool TEXT>
 __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArgs a) {
   // 96-key tiles at D = 128 keep two K and three V buffers within LDS.
   constexpr int BQ = kWinBQ, BK = D == 128 ? 96 : 128, NT = kWinNW * 64;
@@ -198,14 +230,19 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   const Geometry& g = a.g;
   Item it;
   int q0;
-  if (!decode_item(g, a.w, BQ, blockIdx.x, it, q0)) return;
+  // The walk holds the text keys in whole 16-key groups; the last Ts % 16
+  // are one masked block after it.
+  const int t16 = TEXT ? g.Ts & ~15 : 0;
+  if (!decode_item<TEXT>(g, a.w, BQ, blockIdx.x, t16, it, q0)) return;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
   const long long L = g.L;
+  const long long Lp = a.vt_pitch;
   const bf16_t* Q = a.q + (size_t)it.bh * L * D;
   const bf16_t* K = a.k + (size_t)it.bh * L * D;
-  const bf16_t* Vt = a.vt + (size_t)it.bh * L * D;
+  const bf16_t* Kt = a.kt + (size_t)it.bh * g.Ts * D;
+  const bf16_t* Vt = a.vt + (size_t)it.bh * Lp * D;
   const float sl2 = a.scale_log2;
 
   bf16x8 qf[NKK];
@@ -223,7 +260,7 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   for (int b = 0; b < NDB; ++b) o[b] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const int krow_perm = key_perm(l32);
-  const SpanWalk<BK> walk(it);
+  const SpanWalk<BK, TEXT ? 4 : 3> walk(it);
 
   // Tile staging.  A tile is KCH K chunks and VCH V^T chunks of 16 bytes
   // per thread, cut into NB pieces; one piece is stored to LDS and the same
@@ -233,15 +270,15 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   // are loop invariant, the tile position goes into the descriptor base; K
   // rows past the tile's valid keys fall outside the descriptor and read as
   // zero, V^T columns past them are steered out of range the same way.
+  // Text tiles (keys L and up) take their K rows from the text keys.
   constexpr int CH = KCH + VCH, CPP = CH / NB;
   static_assert(CPP * NB == CH, "pieces");
   u32x4 cA[CH], cB[CH];   // staging registers of even / odd tiles
-  const uint32_t vt_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
-  auto load_piece = [&](u32x4* creg, int p, int j) {   // tiles past the walk read as zeros
-    int ks, nk;
-    walk.tile(j, ks, nk);
-    if (j >= walk.n) ks = 0, nk = 0;
-    const rsrc_t krs = make_rsrc(K + (size_t)ks * D, (uint32_t)nk * D * 2);
+  const uint32_t vt_bytes = (uint32_t)min((long long)D * Lp * 2, 0x7FFFFFF0ll);
+  const int Li = (int)L;
+  auto load_keys = [&](u32x4* creg, int p, int ks, int nk) {
+    const bf16_t* kbase = !TEXT || ks < Li ? K + (size_t)ks * D : Kt + (size_t)(ks - Li) * D;
+    const rsrc_t krs = make_rsrc(kbase, (uint32_t)nk * D * 2);
     const rsrc_t vrs = make_rsrc(Vt + ks, vt_bytes - (uint32_t)ks * 2);
 #pragma unroll
     for (int q = p * CPP; q < (p + 1) * CPP; ++q) {
@@ -251,10 +288,16 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
       } else {
         const int c = tid + NT * (q - KCH);
         const int r = c / (BK / 8), c8 = c % (BK / 8);
-        const uint32_t off = (uint32_t)(r * L + c8 * 8) * 2;
+        const uint32_t off = (uint32_t)(r * Lp + c8 * 8) * 2;
         creg[q] = buf_ld16(vrs, c8 * 8 < nk ? off : 0x80000000u);
       }
     }
+  };
+  auto load_piece = [&](u32x4* creg, int p, int j) {   // tiles past the walk read as zeros
+    int ks, nk;
+    walk.tile(j, ks, nk);
+    if (j >= walk.n) ks = 0, nk = 0;
+    load_keys(creg, p, ks, nk);
   };
   auto store_piece = [&](const u32x4* creg, int p, int j) {
 #pragma unroll
@@ -280,14 +323,23 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   // partial row sum bounds every p it holds, so while it stays <= 2^8 no p
   // can overflow and the reference may stay.  Otherwise (also on the first
   // block, where m_run = -inf makes every p infinite) the block max moves the
-  // reference, O and l are rescaled, and P is recomputed.
-  auto probs = [&](const f32x16& s, bool valid, bf16x8* pb) {
+  // reference, O and l are rescaled, and P is recomputed.  nv is the number
+  // of valid keys in the block (0..32, workgroup-uniform); a lane half with
+  // none is masked through nm.  With MASK (only the block of the last
+  // Ts % 16 text keys) a half may hold some: its missing keys get offset
+  // -inf.
+  auto probs = [&](auto mask, const f32x16& s, int nv, bf16x8* pb) {
+    constexpr bool MASK = decltype(mask)::value;
+    const int nvh = nv - hg * 16;
+    const bool valid = nvh > 0;
+    // offset of key i: nm on valid keys, -inf on masked ones
+    auto key_nm = [&](int i, float nm) { return !MASK || i < nvh ? nm : -INFINITY; };
     float ls = 0.f;
     {
       const float nm = valid ? -m_run : -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[i], sl2, nm));
+        const float p = fast_exp2(fmaf(s[i], sl2, key_nm(i, nm)));
         ls += p;
         pb[i >> 3][i & 7] = static_cast<__bf16>(p);
       }
@@ -295,7 +347,7 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
     if (__any(!(ls <= kLazySum))) {
       float m = s[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) m = fmaxf(m, s[i]);
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, !MASK || i < nvh ? s[i] : -INFINITY);
       m = valid ? m : -INFINITY;
       const float m_new = fmaxf(m_run, half_max(m) * sl2);
       const float corr = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
@@ -307,7 +359,7 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
       ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[i], sl2, nm));
+        const float p = fast_exp2(fmaf(s[i], sl2, key_nm(i, nm)));
         ls += p;
         pb[i >> 3][i & 7] = static_cast<__bf16>(p);
       }
@@ -329,9 +381,10 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   int ks, nk;
   walk.tile(0, ks, nk);
   f32x16 s_cur = qk(Ks[0], 0);
-  bool v_cur = hg * 16 < nk;
+  int nv_cur = min(nk, 32);
   // Pieces are requested two tiles ahead of their LDS store, in the register
   // set of the tile's parity.
+  constexpr std::integral_constant<bool, false> kNoMask{};
   auto tile_body = [&](int j, u32x4* c_near, u32x4* c_far) {
     const bf16_t* Kb = Ks[j & 1];
     const bf16_t* Vb = Vs[j % 3];
@@ -342,9 +395,9 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
     for (int kb2 = 0; kb2 < NB; ++kb2) {
       // (1) S of the next block on the matrix core, P of this block on the VALU
       const f32x16 s_next = kb2 + 1 < NB ? qk(Kb, kb2 + 1) : qk(Kn, 0);
-      const bool v_next = kb2 + 1 < NB ? (kb2 + 1) * 32 + hg * 16 < nk : hg * 16 < nk1;
+      const int nv_next = kb2 + 1 < NB ? max(0, min(nk - (kb2 + 1) * 32, 32)) : min(nk1, 32);
       bf16x8 pb[2];
-      probs(s_cur, v_cur, pb);
+      probs(kNoMask, s_cur, nv_cur, pb);
       // (2) O += V P of this block
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
@@ -354,7 +407,7 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
           o[b] = mfma32x32x16(vf, pb[h2], o[b]);
         }
       s_cur = s_next;
-      v_cur = v_next;
+      nv_cur = nv_next;
       // Stage piece p of the next tile (of the one after, on the last
       // block); one barrier per tile, once the next tile is complete.  K
       // tiles are read one block ahead of V tiles, so K needs two buffers
@@ -375,6 +428,27 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
   for (int j = 0; j < walk.n; j += 2) {
     tile_body(j, cB, cA);
     if (j + 1 < walk.n) tile_body(j + 1, cA, cB);
+  }
+  if constexpr (TEXT) {
+    // the last Ts % 16 text keys: one 32-key block with a per-key mask
+    const int rem = g.Ts - t16;
+    if (rem > 0) {
+      __syncthreads();   // every wave is done with the walk's LDS tiles
+#pragma unroll
+      for (int p = 0; p < NB; ++p) load_keys(cA, p, Li + t16, rem);
+#pragma unroll
+      for (int p = 0; p < NB; ++p) store_piece(cA, p, 0);
+      __syncthreads();
+      bf16x8 pb[2];
+      probs(std::integral_constant<bool, true>{}, qk(Ks[0], 0), rem, pb);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const bf16x8 vf = as_bf16x8(ld16(Vs[0] + (b * 32 + l32) * VP + hg * 16 + h2 * 8));
+          o[b] = mfma32x32x16(vf, pb[h2], o[b]);
+        }
+    }
   }
 
   const int bidx = it.bh / g.H, h = it.bh % g.H;
@@ -399,66 +473,83 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
 }
 
 bool window_softmax_mfma_ok(const Geometry& g) {
-  // 16-key granularity of the masks; V^T of one head addressed by a single
-  // 32-bit buffer descriptor
-  return (g.D == 64 || g.D == 128) && (g.N % 16 == 0) && (long long)g.D * g.L * 2 <= 0x7FFFFFF0ll;
+  // whole 16-key groups in every video span; V^T of one head addressed by a
+  // single 32-bit buffer descriptor
+  return (g.D == 64 || g.D == 128) && (g.N % 16 == 0) &&
+         (long long)g.D * softmax_vt_pitch(g) * 2 <= 0x7FFFFFF0ll;
 }
 
 hipError_t launch_window_softmax_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
-                                      const uint16_t* vt, const float* g_s, uint16_t* out,
-                                      float* lse, float scale, hipStream_t s) {
+                                      const uint16_t* k_text, const uint16_t* vt,
+                                      const float* g_s, uint16_t* out, float* lse, float scale,
+                                      hipStream_t s) {
+  if (g.Ts > 0 && !k_text) return hipErrorInvalidValue;
   WinArgs a;
   a.g = g;
   a.w = window_work(g, kWinBQ);
-  a.q = q; a.k = k; a.vt = vt; a.g_s = g_s; a.out = out; a.lse = lse;
+  a.q = q; a.k = k; a.kt = k_text; a.vt = vt; a.g_s = g_s; a.out = out; a.lse = lse;
+  a.vt_pitch = softmax_vt_pitch(g);
   a.scale_log2 = scale * kLog2e;
   if (a.w.grid == 0) return hipSuccess;
-  if (g.D == 128)
-    window_softmax_mfma_kernel<128><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
+  if (g.D == 128 && g.Ts > 0)
+    window_softmax_mfma_kernel<128, true><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
+  else if (g.D == 128)
+    window_softmax_mfma_kernel<128, false><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
+  else if (g.Ts > 0)
+    window_softmax_mfma_kernel<64, true><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
   else
-    window_softmax_mfma_kernel<64><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
+    window_softmax_mfma_kernel<64, false><<<a.w.grid, kWinNW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // -------------------------------------------------------------------------
 // [rows, cols] -> [cols, rows] per batch, bf16, through a 64x64 LDS tile.
-// Used to lay V out key-contiguous for the PV product.
+// Used to lay V (and the text values) out key-contiguous for the PV product
+// and the output projections out K-contiguous for the merge.  Source rows
+// src_rows .. rows-1 read as zeros (the padding of the text columns).
 // -------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src,
-                                                             bf16_t* __restrict__ dst,
-                                                             long long rows, int cols) {
+struct TransposeArgs {
+  const bf16_t* src;
+  bf16_t* dst;
+  long long rows, src_rows;
+  int cols;
+  long long ldd, dst_bstride;
+};
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeArgs a) {
   __shared__ bf16_t t[64][65];
   const long long r0 = (long long)blockIdx.x * 64;
   const int c0 = blockIdx.y * 64;
-  const size_t boff = (size_t)blockIdx.z * rows * cols;
+  const bf16_t* src = a.src + (size_t)blockIdx.z * a.src_rows * a.cols;
+  bf16_t* dst = a.dst + (size_t)blockIdx.z * a.dst_bstride;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int r = ty; r < 64; r += 4) {
     const long long gr = r0 + r;
     const int gc = c0 + tx;
-    t[r][tx] = (gr < rows && gc < cols) ? src[boff + gr * cols + gc] : (bf16_t)0;
+    t[r][tx] = (gr < a.src_rows && gc < a.cols) ? src[gr * a.cols + gc] : (bf16_t)0;
   }
   __syncthreads();
   for (int c = ty; c < 64; c += 4) {
     const int gc = c0 + c;
     const long long gr = r0 + tx;
-    if (gc < cols && gr < rows) dst[boff + (size_t)gc * rows + gr] = t[tx][c];
+    if (gc < a.cols && gr < a.rows) dst[(size_t)gc * a.ldd + gr] = t[tx][c];
   }
 }
 
-// Same transpose with 16-byte global accesses (rows % 8 == 0, cols % 8 == 0).
-__global__ __launch_bounds__(256) void transpose16_bf16_kernel(const bf16_t* __restrict__ src,
-                                                               bf16_t* __restrict__ dst,
-                                                               long long rows, int cols) {
+// Same transpose with 16-byte global accesses (rows, cols, ldd multiples of
+// 8 and a 16-byte aligned destination).
+__global__ __launch_bounds__(256) void transpose16_bf16_kernel(TransposeArgs a) {
   __shared__ bf16_t t[64][66];
   const long long r0 = (long long)blockIdx.x * 64;
   const int c0 = blockIdx.y * 64;
-  const size_t boff = (size_t)blockIdx.z * rows * cols;
+  const bf16_t* src = a.src + (size_t)blockIdx.z * a.src_rows * a.cols;
+  bf16_t* dst = a.dst + (size_t)blockIdx.z * a.dst_bstride;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int ch = threadIdx.x + 256 * i;
     const int r = ch >> 3, c8 = (ch & 7) * 8;
     u32x4 v = {0, 0, 0, 0};
-    if (r0 + r < rows && c0 + c8 < cols) v = ld16(src + boff + (size_t)(r0 + r) * cols + c0 + c8);
+    if (r0 + r < a.src_rows && c0 + c8 < a.cols) v = ld16(src + (size_t)(r0 + r) * a.cols + c0 + c8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       t[r][c8 + 2 * j] = (bf16_t)(v[j] & 0xFFFFu);
@@ -470,23 +561,28 @@ __global__ __launch_bounds__(256) void transpose16_bf16_kernel(const bf16_t* __r
   for (int i = 0; i < 2; ++i) {
     const int ch = threadIdx.x + 256 * i;
     const int c = ch >> 3, r8 = (ch & 7) * 8;
-    if (c0 + c >= cols || r0 + r8 >= rows) continue;
+    if (c0 + c >= a.cols || r0 + r8 >= a.rows) continue;
     u32x4 v;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       v[j] = (uint32_t)t[r8 + 2 * j][c] | ((uint32_t)t[r8 + 2 * j + 1][c] << 16);
-    st16(dst + boff + (size_t)(c0 + c) * rows + r0 + r8, v);
+    st16(dst + (size_t)(c0 + c) * a.ldd + r0 + r8, v);
   }
 }
 
-hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, long long rows, int cols,
-                                 long long batch, hipStream_t s) {
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, long long rows,
+                                 long long src_rows, int cols, long long ldd,
+                                 long long dst_bstride, long long batch, hipStream_t s) {
   if (rows == 0 || cols == 0 || batch == 0) return hipSuccess;
+  if (src_rows > rows || ldd < rows) return hipErrorInvalidValue;
+  if (src_rows > 0 && !src) return hipErrorInvalidValue;
+  const TransposeArgs a{src, dst, rows, src_rows, cols, ldd, dst_bstride};
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols + 63) / 64), (unsigned)batch);
-  if (rows % 8 == 0 && cols % 8 == 0)
-    transpose16_bf16_kernel<<<grid, 256, 0, s>>>(src, dst, rows, cols);
+  if (rows % 8 == 0 && cols % 8 == 0 && ldd % 8 == 0 && dst_bstride % 8 == 0 &&
+      ((uintptr_t)dst & 15) == 0 && ((uintptr_t)src & 15) == 0)
+    transpose16_bf16_kernel<<<grid, 256, 0, s>>>(a);
   else
-    transpose_bf16_kernel<<<grid, 256, 0, s>>>(src, dst, rows, cols);
+    transpose_bf16_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -499,6 +595,8 @@ __global__ __launch_bounds__(128) void window_softmax_simt_kernel(Geometry g, So
                                                                   const T* __restrict__ qp,
                                                                   const T* __restrict__ kp,
                                                                   const T* __restrict__ vp,
+                                                                  const T* __restrict__ ktp,
+                                                                  const T* __restrict__ vtp,
                                                                   const float* __restrict__ g_s,
                                                                   T* __restrict__ out,
                                                                   float* __restrict__ lse,
@@ -508,12 +606,13 @@ __global__ __launch_bounds__(128) void window_softmax_simt_kernel(Geometry g, So
   __shared__ float Vs[BK][DMAX + 1];
   Item it;
   int q0;
-  if (!decode_item(g, w, BQ, blockIdx.x, it, q0)) return;
+  if (!decode_item<true>(g, w, BQ, blockIdx.x, g.Ts, it, q0)) return;
   const int D = g.D;
   const long long L = g.L;
   const int qrow = q0 + threadIdx.x;
   const bool qvalid = qrow < it.q_end;
   const size_t base = (size_t)it.bh * L * D;
+  const size_t tbase = (size_t)it.bh * g.Ts * D;
   float qv[DMAX], ov[DMAX];
 #pragma unroll
   for (int j = 0; j < DMAX; ++j) {
@@ -521,16 +620,20 @@ __global__ __launch_bounds__(128) void window_softmax_simt_kernel(Geometry g, So
     ov[j] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
-  const SpanWalk<BK> walk(it);
+  const SpanWalk<BK, 4> walk(it);
   for (int jt = 0; jt < walk.n; ++jt) {
     {
       int ks, nk;
       walk.tile(jt, ks, nk);
+      // a tile lies in one span: video keys, or text keys (ks >= L)
+      const bool text = ks >= L;
+      const T* kb = text ? ktp + tbase + (size_t)(ks - L) * D : kp + base + (size_t)ks * D;
+      const T* vb = text ? vtp + tbase + (size_t)(ks - L) * D : vp + base + (size_t)ks * D;
       __syncthreads();
       for (int e = threadIdx.x; e < BK * D; e += blockDim.x) {
         const int r = e / D, c = e % D;
-        Ks[r][c] = r < nk ? Elem<T>::load(kp, base + (size_t)(ks + r) * D + c) : 0.f;
-        Vs[r][c] = r < nk ? Elem<T>::load(vp, base + (size_t)(ks + r) * D + c) : 0.f;
+        Ks[r][c] = r < nk ? Elem<T>::load(kb, (size_t)r * D + c) : 0.f;
+        Vs[r][c] = r < nk ? Elem<T>::load(vb, (size_t)r * D + c) : 0.f;
       }
       __syncthreads();
       for (int r = 0; r < nk; ++r) {
@@ -563,27 +666,30 @@ __global__ __launch_bounds__(128) void window_softmax_simt_kernel(Geometry g, So
 
 template <typename T>
 hipError_t launch_window_softmax_simt(const Geometry& g, const T* q, const T* k, const T* v,
-                                      const float* g_s, T* out, float* lse, float scale,
-                                      hipStream_t s) {
+                                      const T* k_text, const T* v_text, const float* g_s, T* out,
+                                      float* lse, float scale, hipStream_t s) {
+  if (g.Ts > 0 && (!k_text || !v_text)) return hipErrorInvalidValue;
   const SoftmaxWork w = window_work(g, 128);
   if (w.grid == 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (g.D <= 16)
-    window_softmax_simt_kernel<T, 16><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+    window_softmax_simt_kernel<T, 16><<<w.grid, 128, 0, s>>>(g, w, q, k, v, k_text, v_text, g_s, out, lse, sl2);
   else if (g.D <= 32)
-    window_softmax_simt_kernel<T, 32><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+    window_softmax_simt_kernel<T, 32><<<w.grid, 128, 0, s>>>(g, w, q, k, v, k_text, v_text, g_s, out, lse, sl2);
   else if (g.D <= 64)
-    window_softmax_simt_kernel<T, 64><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+    window_softmax_simt_kernel<T, 64><<<w.grid, 128, 0, s>>>(g, w, q, k, v, k_text, v_text, g_s, out, lse, sl2);
   else
-    window_softmax_simt_kernel<T, 128><<<w.grid, 128, 0, s>>>(g, w, q, k, v, g_s, out, lse, sl2);
+    window_softmax_simt_kernel<T, 128><<<w.grid, 128, 0, s>>>(g, w, q, k, v, k_text, v_text, g_s, out, lse, sl2);
   return hipGetLastError();
 }
 
 template hipError_t launch_window_softmax_simt<float>(const Geometry&, const float*, const float*,
-                                                      const float*, const float*, float*, float*,
-                                                      float, hipStream_t);
+                                                      const float*, const float*, const float*,
+                                                      const float*, float*, float*, float,
+                                                      hipStream_t);
 template hipError_t launch_window_softmax_simt<bf16_t>(const Geometry&, const bf16_t*,
-                                                       const bf16_t*, const bf16_t*, const float*,
-                                                       bf16_t*, float*, float, hipStream_t);
+                                                       const bf16_t*, const bf16_t*, const bf16_t*,
+                                                       const bf16_t*, const float*, bf16_t*, float*,
+                                                       float, hipStream_t);
 
 }  // namespace vdn

@@ -82,7 +82,7 @@ Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt) {
   Layout l{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
-  l.vt = take(dt == VDN_BF16 ? BH * g.L * g.D * es : 0);
+  l.vt = take(dt == VDN_BF16 ? BH * (size_t)vdn::softmax_vt_pitch(g) * g.D * es : 0);
   l.wt0 = take(dt == VDN_BF16 ? (size_t)g.H * g.D * Dm * es : 0);
   l.wt1 = take(dt == VDN_BF16 ? (size_t)g.H * g.D * Dm * es : 0);
   l.Tf = take(BH * g.F * DD * 4);
@@ -106,6 +106,7 @@ vdn_params defaults() {
   p.chunk_frames = 5;
   p.window_chunks = 1;
   p.anchors = 1;
+  p.text_softmax = 0;
   return p;
 }
 
@@ -121,6 +122,8 @@ vdn_status check_geometry(const vdn_dims* d, const vdn_params* p, vdn_dtype dt, 
   if (p->chunk_frames < 1) return fail(VDN_ERR_INVALID_ARG, "chunk_frames=%d must be >= 1", p->chunk_frames);
   if (p->window_chunks < 0) return fail(VDN_ERR_INVALID_ARG, "window_chunks=%d must be >= 0", p->window_chunks);
   if (p->anchors != 0 && p->anchors != 1) return fail(VDN_ERR_INVALID_ARG, "anchors=%d must be 0 or 1", p->anchors);
+  if (p->text_softmax != 0 && p->text_softmax != 1)
+    return fail(VDN_ERR_INVALID_ARG, "text_softmax=%d must be 0 or 1", p->text_softmax);
   if (d->F % p->chunk_frames != 0)
     return fail(VDN_ERR_INVALID_ARG, "F=%d is not a multiple of chunk_frames=%d", d->F, p->chunk_frames);
   if (!(p->rms_eps >= 0.f) || !isfinite(p->text_init_scale) || !isfinite(p->softmax_scale))
@@ -130,13 +133,14 @@ vdn_status check_geometry(const vdn_dims* d, const vdn_params* p, vdn_dtype dt, 
     return fail(VDN_ERR_UNSUPPORTED, "head dim %d not in {16,32,64,128}", d->d_k);
   const long long L = (long long)d->F * d->N;
   const long long rows = (long long)d->B * d->H * L;
-  if (L > (1ll << 31) - 1 || rows > (1ll << 40))
+  if (L + d->T + 16 > (1ll << 31) - 1 || rows > (1ll << 40))
     return fail(VDN_ERR_INVALID_ARG, "sequence too long (L=%lld)", L);
   if (d->N > (1 << 26)) return fail(VDN_ERR_INVALID_ARG, "N=%d too large", d->N);
   g->B = d->B; g->H = d->H; g->F = d->F; g->N = d->N; g->T = d->T; g->D = d->d_k;
   g->cf = p->chunk_frames; g->wc = p->window_chunks; g->anchors = p->anchors;
   g->C = d->F / p->chunk_frames;
   g->L = L;
+  g->Ts = p->text_softmax ? d->T : 0;
   return VDN_OK;
 }
 
@@ -171,27 +175,40 @@ vdn_status run_scan(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, c
   return VDN_OK;
 }
 
+// The Softmax branch (a7).  With g.Ts > 0 the text keys k_text / v_text
+// [B,H,Ts,d] are keys of every query as well.
 vdn_status run_softmax(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, const void* q,
-                       const void* k, const void* v, const float* g_s, void* out, float* lse,
-                       char* ws, const Layout& lay, hipStream_t s) {
+                       const void* k, const void* v, const void* k_text, const void* v_text,
+                       const float* g_s, void* out, float* lse, char* ws, const Layout& lay,
+                       hipStream_t s) {
   const float sc = softmax_scale(p, g.D);
+  const long long BH = (long long)g.B * g.H;
   if (dt == VDN_BF16 && vdn::window_softmax_mfma_ok(g)) {
+    // V^T [B,H,D,Lp]: columns 0..L-1 the video values, then the text values
+    // and zero padding up to Lp
     uint16_t* vt = (uint16_t*)(ws + lay.vt);
-    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)v, vt, g.L, g.D, (long long)g.B * g.H, s));
+    const long long Lp = vdn::softmax_vt_pitch(g);
+    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)v, vt, g.L, g.L, g.D, Lp, Lp * g.D, BH, s));
+    if (g.Ts > 0)
+      VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)v_text, vt + g.L, Lp - g.L, g.Ts, g.D, Lp,
+                                         Lp * g.D, BH, s));
     VDN_HIP(timer_mark(s, true));
-    VDN_HIP(vdn::launch_window_softmax_mfma(g, (const uint16_t*)q, (const uint16_t*)k, vt, g_s,
-                                            (uint16_t*)out, lse, sc, s));
+    VDN_HIP(vdn::launch_window_softmax_mfma(g, (const uint16_t*)q, (const uint16_t*)k,
+                                            (const uint16_t*)k_text, vt, g_s, (uint16_t*)out, lse,
+                                            sc, s));
     VDN_HIP(timer_mark(s, false));
   } else if (dt == VDN_BF16) {
     VDN_HIP(timer_mark(s, true));
-    VDN_HIP(vdn::launch_window_softmax_simt<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k,
-                                                      (const uint16_t*)v, g_s, (uint16_t*)out, lse,
-                                                      sc, s));
+    VDN_HIP(vdn::launch_window_softmax_simt<uint16_t>(
+        g, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)k_text,
+        (const uint16_t*)v_text, g_s, (uint16_t*)out, lse, sc, s));
     VDN_HIP(timer_mark(s, false));
   } else {
     VDN_HIP(timer_mark(s, true));
     VDN_HIP(vdn::launch_window_softmax_simt<float>(g, (const float*)q, (const float*)k,
-                                                   (const float*)v, g_s, (float*)out, lse, sc, s));
+                                                   (const float*)v, (const float*)k_text,
+                                                   (const float*)v_text, g_s, (float*)out, lse,
+                                                   sc, s));
     VDN_HIP(timer_mark(s, false));
   }
   return VDN_OK;
@@ -347,7 +364,8 @@ vdn_status vda_scan_rev(const void* k, const void* v, const float* beta, const f
                     workspace, workspace_bytes, dims, p, dt, stream);
 }
 
-vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v, const float* g_s,
+vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v,
+                                  const void* k_text, const void* v_text, const float* g_s,
                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
                                   const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
                                   void* stream) {
@@ -356,10 +374,12 @@ vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v, c
   vdn_status st = check_geometry(dims, p, dt, &g);
   if (st != VDN_OK) return st;
   NEED(q); NEED(k); NEED(v); NEED(out);
+  if (g.Ts > 0) { NEED(k_text); NEED(v_text); }
   const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt);
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
-  return run_softmax(g, p, dt, q, k, v, g_s, out, lse, (char*)workspace, lay, (hipStream_t)stream);
+  return run_softmax(g, p, dt, q, k, v, k_text, v_text, g_s, out, lse, (char*)workspace, lay,
+                     (hipStream_t)stream);
 }
 
 vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float* beta,
@@ -411,7 +431,8 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   // join is recorded even after a failure, so the caller's stream never
   // runs ahead of work already queued on the side stream
   const hipError_t ej = hipEventRecord(ss->join, ss->stream);
-  if (st == VDN_OK) st = run_softmax(g, p, dt, q, k, v, g_s, ohs, nullptr, ws, lay, s);
+  if (st == VDN_OK)
+    st = run_softmax(g, p, dt, q, k, v, k_text, v_text, g_s, ohs, nullptr, ws, lay, s);
   const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, ss->join, 0) : ej;
   if (st != VDN_OK) return st;
   if (ew != hipSuccess) return fail(VDN_ERR_HIP, "side-stream join failed: %s", hipGetErrorString(ew));
@@ -427,8 +448,8 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   } else if (dt == VDN_BF16 && Dm % 8 == 0 && K % 64 == 0) {
     uint16_t* w0t = (uint16_t*)(ws + lay.wt0);
     uint16_t* w1t = (uint16_t*)(ws + lay.wt1);
-    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_s, w0t, K, Dm, 1, s));
-    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_l, w1t, K, Dm, 1, s));
+    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_s, w0t, K, K, Dm, K, (long long)K * Dm, 1, s));
+    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_l, w1t, K, K, Dm, K, (long long)K * Dm, 1, s));
     VDN_HIP(vdn::launch_merge_gemm_bf16((const uint16_t*)ohs, (const uint16_t*)ohl, w0t, w1t,
                                         (uint16_t*)out, M, K, Dm, s));
   } else if (dt == VDN_BF16) {

@@ -15,7 +15,15 @@ struct Geometry {
   int anchors;   // 0 / 1
   int C;         // F / cf
   long long L;   // F * N
+  int Ts;        // text keys inside the Softmax branch (0 = video keys only)
 };
+
+// Column pitch of the transposed values V^T [D, Lp] of one head on the MFMA
+// Softmax path: the L video keys, then the Ts text keys, zero-padded to a
+// multiple of 16 columns.
+inline long long softmax_vt_pitch(const Geometry& g) {
+  return g.L + (g.Ts > 0 ? ((long long)g.Ts + 15) / 16 * 16 : 0);
+}
 
 // Work split of the window Softmax over query groups (see window_work()).
 struct SoftmaxWork {
@@ -30,16 +38,23 @@ constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dealt round-robin
 SoftmaxWork window_work(const Geometry& g, int bq);
 
 // ---- window Softmax (Softmax branch) ----
-// q,k [B,H,L,D]; vt [B,H,D,L] (bf16 path only); out [B,L,H,D]; lse [B,H,L].
-hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, long long rows, int cols,
-                                 long long batch, hipStream_t s);
+// q,k [B,H,L,D]; k_text [B,H,Ts,D] (read only when Ts > 0); vt [B,H,D,Lp]
+// (bf16 path only, Lp = softmax_vt_pitch); out [B,L,H,D]; lse [B,H,L].
+//
+// Batched transpose: src [batch][src_rows][cols] -> dst [batch][cols][rows]
+// with dst row pitch ldd and batch stride dst_bstride (elements); source rows
+// src_rows .. rows-1 are written as zeros.
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, long long rows,
+                                 long long src_rows, int cols, long long ldd,
+                                 long long dst_bstride, long long batch, hipStream_t s);
 hipError_t launch_window_softmax_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
-                                      const uint16_t* vt, const float* g_s, uint16_t* out,
-                                      float* lse, float scale, hipStream_t s);
+                                      const uint16_t* k_text, const uint16_t* vt,
+                                      const float* g_s, uint16_t* out, float* lse, float scale,
+                                      hipStream_t s);
 template <typename T>
 hipError_t launch_window_softmax_simt(const Geometry& g, const T* q, const T* k, const T* v,
-                                      const float* g_s, T* out, float* lse, float scale,
-                                      hipStream_t s);
+                                      const T* k_text, const T* v_text, const float* g_s, T* out,
+                                      float* lse, float scale, hipStream_t s);
 bool window_softmax_mfma_ok(const Geometry& g);
 
 // ---- VDA frame statistics + solve (per frame and the text frame) ----

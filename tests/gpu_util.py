@@ -69,7 +69,8 @@ def run_library(cfg, t, params=None, with_parts=True):
         res["P_fwd"], res["S_text"] = vdn.scan_fwd(*sargs, params=params)
         res["P_rev"], _ = vdn.scan_rev(*sargs, params=params)
         res["sm"], res["lse"] = vdn.window_softmax_fwd(t["q"], t["k"], t["v"], F, g_s=t["g_s"],
-                                                       want_lse=True, params=params)
+                                                       want_lse=True, params=params,
+                                                       k_text=t["k_text"], v_text=t["v_text"])
     torch.cuda.synchronize()
     return {k: to_np(v) for k, v in res.items()}
 
@@ -81,4 +82,43 @@ def oracle_params(params):
     return O.Params(chunk_frames=params.chunk_frames, window_chunks=params.window_chunks,
                     anchors=bool(params.anchors),
                     softmax_scale=params.softmax_scale if params.softmax_scale > 0 else None,
-                    rms_eps=params.rms_eps, text_init_scale=params.text_init_scale)
+                    rms_eps=params.rms_eps, text_init_scale=params.text_init_scale,
+                    text_softmax=bool(params.text_softmax))
+
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+TOL_STATE = 1e-4
+
+
+def check_full(cfg, params=None, tol=None):
+    """Every entry point on the full inputs of cfg against the oracle
+    (vdn_attn over all heads); asserts the tolerances and returns the
+    rel-L2 errors."""
+    from oracle import vdn_oracle as O
+    from vdn_inputs import full_inputs
+    import softmax_attention_video_amd as vdn  # noqa: F401  (fails loudly if unbuilt)
+    log(f"[parity] {cfg}")
+    inp = full_inputs(cfg)
+    t = gpu_tensors(cfg, inp)
+    got = run_library(cfg, t, params)
+    op = oracle_params(params)
+    ref = O.vdn_attn(inp, op)
+    tol = tol or TOL[cfg.dtype]
+    B, H, L, d = inp["q"].shape
+    errs = {
+        "P_fwd": rel_l2(got["P_fwd"], ref["P_fwd"]),
+        "P_rev": rel_l2(got["P_rev"], ref["P_rev"]),
+        "S_text": rel_l2(got["S_text"], ref["S_text"]) if cfg.T else float(np.abs(got["S_text"]).max()),
+        "Ohat_s": rel_l2(got["Ohat_s"], ref["Ohat_s"].transpose(0, 2, 1, 3)),
+        "Ohat_l": rel_l2(got["Ohat_l"], ref["Ohat_l"].transpose(0, 2, 1, 3)),
+        "sm": rel_l2(got["sm"], ref["Ohat_s"].transpose(0, 2, 1, 3)),
+        "lse": rel_l2(got["lse"], ref["lse"]),
+        "out": rel_l2(got["out"].reshape(ref["out"].shape), ref["out"]),
+    }
+    log(f"[parity] rel-L2 {errs}")
+    for key in ("P_fwd", "P_rev", "S_text"):
+        assert errs[key] <= TOL_STATE, (key, errs)
+    for key in ("Ohat_s", "Ohat_l", "sm", "out"):
+        assert errs[key] <= tol, (key, errs)
+    assert errs["lse"] <= 1e-5, errs
+    return errs

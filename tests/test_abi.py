@@ -31,7 +31,7 @@ def test_library_exports_every_header_symbol():
 def test_default_params():
     p = vdn.default_params()
     assert (p.chunk_frames, p.window_chunks, p.anchors) == (5, 1, 1)
-    assert p.text_init_scale == 0.5 and p.softmax_scale == 0.0
+    assert p.text_init_scale == 0.5 and p.softmax_scale == 0.0 and p.text_softmax == 0
     assert abs(p.rms_eps - 1e-6) < 1e-12
 
 
@@ -148,12 +148,33 @@ def test_scan_and_softmax_validation():
         # workspace too small
         assert fn(*[fake] * 9, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p),
                   vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
-    assert L.vdn_window_softmax_fwd(None, fake, fake, None, fake, None, fake,
-                                    ctypes.c_size_t(1 << 40), ctypes.byref(d), ctypes.byref(p),
-                                    vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
-    assert L.vdn_window_softmax_fwd(fake, fake, fake, None, fake, None, fake,
-                                    ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p),
-                                    vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+    sm = L.vdn_window_softmax_fwd
+    assert sm(None, fake, fake, None, None, None, fake, None, fake, ctypes.c_size_t(1 << 40),
+              ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    assert sm(fake, fake, fake, None, None, None, fake, None, fake, ctypes.c_size_t(16),
+              ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+    # text keys inside the Softmax: both text pointers are required when T > 0
+    pt = vdn.Params(text_softmax=1).c()
+    for kt, vt in ((None, fake), (fake, None)):
+        assert sm(fake, fake, fake, kt, vt, None, fake, None, fake, ctypes.c_size_t(1 << 40),
+                  ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    # ... and not read without the option (T > 0, NULL text, workspace check reached)
+    assert sm(fake, fake, fake, None, None, None, fake, None, fake, ctypes.c_size_t(16),
+              ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+    assert d.T > 0
+    # text_softmax must be 0 or 1
+    assert _call_attn(_dims(), params=vdn.Params(text_softmax=2)) == vdn.VDN_ERR_INVALID_ARG
+
+
+def test_text_softmax_workspace_holds_padded_text_columns():
+    # bf16 MFMA path: V^T of a head spans L video + T text columns rounded up to 16
+    d = _dims(B=1, H=2, F=20, N=16, T=5, d_k=64, d_v=64, D=128)
+    base = vdn.workspace_bytes(d, vdn.Params())
+    text = vdn.workspace_bytes(d, vdn.Params(text_softmax=1))
+    assert text >= base + 2 * 64 * 16 * 2 - 256
+    assert text <= base + 2 * 64 * 16 * 2 + 256
+    d0 = _dims(B=1, H=2, F=20, N=16, T=0, d_k=64, d_v=64, D=128)
+    assert vdn.workspace_bytes(d0, vdn.Params(text_softmax=1)) == vdn.workspace_bytes(d0)
 
 
 def test_binding_rejects_host_tensors():

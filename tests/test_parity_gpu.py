@@ -5,43 +5,11 @@ storage 1e-2 on every branch output; fp32 states (P_fwd, P_rev, S_text)
 import numpy as np
 import pytest
 
-from gpu_util import gpu_tensors, log, oracle_params, rel_l2, run_library
-from oracle import vdn_oracle as O
+from gpu_util import check_full as _check_full
+from gpu_util import gpu_tensors, run_library
 from vdn_inputs import CONFIGS, full_inputs
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-4, "bf16": 1e-2}
-TOL_STATE = 1e-4
-
-
-def _check_full(cfg, params=None, tol=None):
-    import softmax_attention_video_amd as vdn  # noqa: F401  (fails loudly if unbuilt)
-    log(f"[parity] {cfg}")
-    inp = full_inputs(cfg)
-    t = gpu_tensors(cfg, inp)
-    got = run_library(cfg, t, params)
-    op = oracle_params(params)
-    ref = O.vdn_attn(inp, op)
-    tol = tol or TOL[cfg.dtype]
-    B, H, L, d = inp["q"].shape
-    errs = {
-        "P_fwd": rel_l2(got["P_fwd"], ref["P_fwd"]),
-        "P_rev": rel_l2(got["P_rev"], ref["P_rev"]),
-        "S_text": rel_l2(got["S_text"], ref["S_text"]) if cfg.T else float(np.abs(got["S_text"]).max()),
-        "Ohat_s": rel_l2(got["Ohat_s"], ref["Ohat_s"].transpose(0, 2, 1, 3)),
-        "Ohat_l": rel_l2(got["Ohat_l"], ref["Ohat_l"].transpose(0, 2, 1, 3)),
-        "sm": rel_l2(got["sm"], ref["Ohat_s"].transpose(0, 2, 1, 3)),
-        "lse": rel_l2(got["lse"], ref["lse"]),
-        "out": rel_l2(got["out"].reshape(ref["out"].shape), ref["out"]),
-    }
-    log(f"[parity] rel-L2 {errs}")
-    for key in ("P_fwd", "P_rev", "S_text"):
-        assert errs[key] <= TOL_STATE, (key, errs)
-    for key in ("Ohat_s", "Ohat_l", "sm", "out"):
-        assert errs[key] <= tol, (key, errs)
-    assert errs["lse"] <= 1e-5, errs
-    return errs
 
 
 # ---- the two small named configurations, in full ----

@@ -100,7 +100,7 @@ def cpu_baseline(cfg, target_s: float = 30.0) -> dict:
 
 
 COPY_KERNEL_TAG = "MulFunctor"      # torch.mul(x, 1, out=y): reads and writes its size once
-SOFTMAX_KERNEL_TAG = "window_softmax_mfma_kernel"
+SOFTMAX_KERNEL_TAG = "window_softmax_mfma_kernel<"   # the video-keys-only variant (", false>")
 
 
 def traffic_from_counters(fetch_csv: str, write_csv: str, config: str, calib_bytes: int) -> dict:
@@ -127,7 +127,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, config: str, calib_byt
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         v = per_dispatch(path, counter)
         copies = [b for (k, _), b in v.items() if COPY_KERNEL_TAG in k]
-        sm = [b for (k, _), b in v.items() if SOFTMAX_KERNEL_TAG in k]
+        sm = [b for (k, _), b in v.items() if SOFTMAX_KERNEL_TAG in k and ", false>" in k]
         if not copies or not sm:
             raise SystemExit(f"{path}: calibration copy or softmax dispatches missing")
         factor = calib_bytes / statistics.median(copies)
@@ -248,7 +248,7 @@ def measure_text(cfg, t, reps: int = 5) -> dict:
     return {"entry": "vdn_attn_fwd with text_softmax = 1",
             "workload": f"{cfg.name} with its T={cfg.T} text keys visible to every video query",
             "ms_per_step": ms, "tokens_per_s": B * L / (ms / 1e3),
-            "kernel": "window_softmax_mfma_kernel<128, text>", "kernel_ms": float(k_ms.mean()),
+            "kernel": f"window_softmax_mfma_kernel<{d}, true>", "kernel_ms": float(k_ms.mean()),
             "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": ach / PEAK_BF16_TFLOPS, "softmax_flops": sm_flops}
 
@@ -379,7 +379,7 @@ def main() -> int:
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "flops_per_step": fl,
         "roofline": {
-            "kernel": "window_softmax_mfma_kernel<128>",
+            "kernel": f"window_softmax_mfma_kernel<{d}, false>",
             "bound": "mfma",
             "achieved": k_tflops,
             "peak": PEAK_BF16_TFLOPS,

@@ -253,6 +253,64 @@ def measure_text(cfg, t, reps: int = 5) -> dict:
             "frac": ach / PEAK_BF16_TFLOPS, "softmax_flops": sm_flops}
 
 
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 / MX-FP8 MFMA (2 x the bf16 peak)
+
+
+def measure_mx(cfg, t, reps: int = 10) -> dict:
+    """The merge (vdn_merge_fwd) on the layer's branch outputs, bf16 against
+    MX-FP8 (params.merge_mxfp8 = 1: quantization of both operands included),
+    and the layer step with the MX-FP8 merge.  HIP-event times on the stream."""
+    import torch
+
+    import softmax_attention_video_amd as vdn
+
+    B, H, L, d = t["q"].shape
+    dev = t["q"].device
+    if t["W_s"] is None or t["q"].dtype != torch.bfloat16:
+        return {}
+    ohs = torch.empty((B, L, H, d), dtype=t["q"].dtype, device=dev)
+    ohl = torch.empty_like(ohs)
+    mx = vdn.Params(merge_mxfp8=1)
+    dims = vdn.Dims(B, H, cfg.F, cfg.N, cfg.T, d, d, cfg.D)
+    ws = torch.empty(vdn.workspace_bytes(dims, mx, vdn.VDN_BF16), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, L, cfg.D), dtype=t["q"].dtype, device=dev)
+
+    def layer(params):
+        vdn.attn_fwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["k_text"], t["v_text"],
+                     t["beta_text"], t["g_s"], t["g_l"], gamma=t["gamma"], W_s=t["W_s"],
+                     W_l=t["W_l"], out=out, ohat_s=ohs, ohat_l=ohl, workspace=ws, params=params)
+
+    def merge(params):
+        vdn.merge_fwd(ohs, ohl, t["W_s"], t["W_l"], cfg.F, params=params, out=out, workspace=ws)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_layer = timed(lambda: layer(mx), 5)
+    ms_bf16 = timed(lambda: merge(None), reps)
+    ms_mx = timed(lambda: merge(mx), reps)
+    flops = 4.0 * B * L * (H * d) * cfg.D
+    del ws, out, ohs, ohl
+    return {"entry": "vdn_merge_fwd (bf16 vs merge_mxfp8 = 1); vdn_attn_fwd with merge_mxfp8 = 1",
+            "workload": f"{cfg.name} merge: M={B * L} tokens, K=2x{H * d}, D={cfg.D}",
+            "merge_bf16_ms": ms_bf16, "merge_mx_ms": ms_mx,
+            "bound": "mfma", "achieved": flops / (ms_mx / 1e3) / 1e12, "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": flops / (ms_mx / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
+            "bf16_achieved": flops / (ms_bf16 / 1e3) / 1e12, "bf16_frac":
+            flops / (ms_bf16 / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "layer_ms_per_step": ms_layer, "layer_tokens_per_s": B * L / (ms_layer / 1e3),
+            "note": "reduced precision (MX-FP8 operands); not the headline"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +322,8 @@ def main() -> int:
                     help="skip the separate VDA-Prep (vda_prep_fwd) measurement")
     ap.add_argument("--no-text", action="store_true",
                     help="skip the separate text-keys-in-Softmax measurement")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the separate MX-FP8 merge measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one elementwise copy of this many MiB before timing "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -399,6 +459,11 @@ def main() -> int:
         res["text_softmax"] = measure_text(cfg, t)
         print(f"[bench] text keys in the Softmax: {res['text_softmax']['ms_per_step']:.3f} ms/step, "
               f"Softmax kernel {res['text_softmax']['kernel_ms']:.3f} ms", file=sys.stderr, flush=True)
+    if not args.no_mx and cfg.proj and cfg.dtype == "bf16":
+        res["merge_mxfp8"] = measure_mx(cfg, t)
+        r = res["merge_mxfp8"]
+        print(f"[bench] merge: bf16 {r['merge_bf16_ms']:.3f} ms, MX-FP8 {r['merge_mx_ms']:.3f} ms; "
+              f"layer with the MX-FP8 merge {r['layer_ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(res), flush=True)

@@ -76,7 +76,16 @@ typedef struct {
  *                    tokens are keys of every video query too, always
  *                    visible, inside the same softmax (method, bidirectional
  *                    linear attention: the prompt stays directly visible to
- *                    the Softmax branch).  The linear branch is unchanged. */
+ *                    the Softmax branch).  The linear branch is unchanged.
+ *  merge_mxfp8     : 0 = the merge GEMM in bf16 with fp32 accumulation
+ *                    (default); 1 = both merge operands in MX-FP8 (system
+ *                    section: MXFP8 for the wide output GEMMs, states in
+ *                    FP32): OCP MX blocks of 32 along the contraction index,
+ *                    E8M0 scale 2^(floor(log2 amax) - 8), E4M3 elements
+ *                    rounded to nearest even and saturated at 448, fp32
+ *                    accumulation.  A reduced-precision mode: bf16 storage
+ *                    and the projections W_s, W_l only, H*d_v % 64 == 0,
+ *                    D % 8 == 0 (else VDN_ERR_UNSUPPORTED). */
 typedef struct {
   float softmax_scale;
   float rms_eps;
@@ -85,6 +94,7 @@ typedef struct {
   int window_chunks;
   int anchors;
   int text_softmax;
+  int merge_mxfp8;
 } vdn_params;
 
 /* Fills *p with the defaults listed above. */
@@ -181,6 +191,39 @@ vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v,
                                   void* workspace, size_t workspace_bytes,
                                   const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
                                   void* stream);
+
+/*
+ * vdn_merge_fwd -- the merge alone (step a8 of vdn_attn_fwd).
+ *
+ * Paper, method, branch calibration: each branch has its own output
+ * projection and the projected outputs are added:
+ *   out = Ohat_s W_s + Ohat_l W_l       (heads concatenated, h*d_v + j)
+ * in bf16 with fp32 accumulation, or in MX-FP8 with p->merge_mxfp8 = 1
+ * (system section, other optimizations).  Only dims->B, H, F, N, d_k, d_v
+ * and D are used (L = F*N tokens); the other fields must still be valid.
+ *
+ *  ohat_s, ohat_l [B,L,H,d_v] dt;  W_s, W_l [H*d_v, D] dt, both NULL = identity
+ *  out [B,L,D] dt;  workspace of vdn_workspace_bytes(dims, p, dt) bytes
+ */
+vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s, const void* W_l,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream);
+
+/*
+ * vdn_mx_quantize -- MX-FP8 quantization of bf16 rows (the operand format of
+ * the MX-FP8 merge; e.g. to inspect it or to quantize weights ahead of time).
+ *
+ * OCP Microscaling (MX) v1.0 with E4M3 elements: each block of 32
+ * consecutive elements of a row gets scale byte s + 127 with
+ * s = floor(log2(max |x|)) - 8 clamped to [-127, 127] (s = -127 for a zero
+ * block), and codes[i] = E4M3(x[i] / 2^s), rounded to nearest even, with
+ * magnitudes >= 448 saturated to 448 and the sign of x kept.
+ *
+ *  src    [rows, cols] bf16 (device);  cols % 32 == 0
+ *  codes  [rows, cols] uint8 (device);  scales [rows, cols/32] uint8 (device)
+ */
+vdn_status vdn_mx_quantize(const void* src, void* codes, void* scales, long long rows, int cols,
+                           void* stream);
 
 /*
  * vda_prep_fwd -- VDA-Prep, the linear branch's feature map (upstream of

@@ -10,6 +10,9 @@ Entry points (same names as the C-ABI):
   attn_fwd(...)               -> out            (vdn_attn_fwd)
   scan_fwd(...), scan_rev(...) -> P, S_text     (vda_scan_fwd / vda_scan_rev)
   window_softmax_fwd(...)     -> out, lse       (vdn_window_softmax_fwd)
+  merge_fwd(...)              -> out            (vdn_merge_fwd)
+  mx_quantize(x)              -> codes, scales  (vdn_mx_quantize)
+  prep_fwd(...)               -> q', k', v'     (vda_prep_fwd)
   window_plan(F, params)      -> host tables    (vdn_window_plan)
   workspace_bytes(...)
 """
@@ -30,7 +33,8 @@ VDN_F32, VDN_BF16 = 0, 1
 EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_window_softmax_fwd", "vdn_workspace_bytes", "vdn_window_plan",
            "vdn_status_string", "vdn_last_error", "vdn_timer_enable", "vdn_timer_read",
-           "vdn_timer_disable", "vda_prep_default_params", "vda_prep_fwd")
+           "vdn_timer_disable", "vda_prep_default_params", "vda_prep_fwd", "vdn_merge_fwd",
+           "vdn_mx_quantize")
 
 
 class VdnError(RuntimeError):
@@ -47,7 +51,7 @@ class CParams(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("text_init_scale", ctypes.c_float), ("chunk_frames", ctypes.c_int),
                 ("window_chunks", ctypes.c_int), ("anchors", ctypes.c_int),
-                ("text_softmax", ctypes.c_int)]
+                ("text_softmax", ctypes.c_int), ("merge_mxfp8", ctypes.c_int)]
 
 
 class CPrepParams(ctypes.Structure):
@@ -76,7 +80,7 @@ class PrepParams:
 class Params:
     """Operator hyper-parameters (defaults: 5-frame chunks, +-1 chunk window,
     anchors on, scale 1/sqrt(d_k) (0 = default), eps 1e-6, text split 1/2,
-    text keys outside the Softmax branch)."""
+    text keys outside the Softmax branch, bf16 merge)."""
     softmax_scale: float = 0.0
     rms_eps: float = 1e-6
     text_init_scale: float = 0.5
@@ -84,10 +88,12 @@ class Params:
     window_chunks: int = 1
     anchors: int = 1
     text_softmax: int = 0
+    merge_mxfp8: int = 0
 
     def c(self) -> CParams:
         return CParams(self.softmax_scale, self.rms_eps, self.text_init_scale,
-                       self.chunk_frames, self.window_chunks, self.anchors, self.text_softmax)
+                       self.chunk_frames, self.window_chunks, self.anchors, self.text_softmax,
+                       self.merge_mxfp8)
 
 
 _lib = None
@@ -131,6 +137,10 @@ def lib() -> ctypes.CDLL:
     L.vda_prep_default_params.restype = None
     L.vda_prep_fwd.argtypes = [P] * 8 + [dp, ctypes.POINTER(CPrepParams), I, P]
     L.vda_prep_fwd.restype = I
+    L.vdn_merge_fwd.argtypes = [P] * 6 + [S, dp, pp, I, P]
+    L.vdn_merge_fwd.restype = I
+    L.vdn_mx_quantize.argtypes = [P, P, P, ctypes.c_longlong, I, P]
+    L.vdn_mx_quantize.restype = I
     _lib = L
     return L
 
@@ -146,7 +156,7 @@ def default_params() -> Params:
     c = CParams()
     lib().vdn_default_params(ctypes.byref(c))
     return Params(c.softmax_scale, c.rms_eps, c.text_init_scale, c.chunk_frames,
-                  c.window_chunks, c.anchors, c.text_softmax)
+                  c.window_chunks, c.anchors, c.text_softmax, c.merge_mxfp8)
 
 
 def window_plan(F: int, params: Params | None = None):
@@ -367,6 +377,55 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
         ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
     return out, lse
+
+
+def merge_fwd(ohat_s, ohat_l, W_s, W_l, F: int, params: Params | None = None, out=None,
+              workspace=None, stream=None):
+    """The merge alone (vdn_merge_fwd): out [B,L,D] = Ohat_s W_s + Ohat_l W_l
+    (bf16, or MX-FP8 with params.merge_mxfp8).  ohat_* [B,L,H,d]; W_* [H*d, D]
+    or both None (identity, D = H*d)."""
+    torch = _torch()
+    params = params or Params()
+    B, L, H, d = ohat_s.shape
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    dt = ohat_s.dtype
+    code = _dtype_code(ohat_s)
+    dev = ohat_s.device
+    Dm = W_s.shape[1] if W_s is not None else H * d
+    dims = Dims(B, H, F, L // F, 0, d, d, Dm)
+    if out is None:
+        out = torch.empty((B, L, Dm), dtype=dt, device=dev)
+    ws = _workspace(dims, params, code, dev, workspace)
+    p = params.c()
+    _check(lib().vdn_merge_fwd(
+        _ptr(ohat_s, "ohat_s", dt, (B, L, H, d), dev), _ptr(ohat_l, "ohat_l", dt, (B, L, H, d), dev),
+        _ptr(W_s, "W_s", dt, (H * d, Dm), dev, allow_none=True),
+        _ptr(W_l, "W_l", dt, (H * d, Dm), dev, allow_none=True),
+        _ptr(out, "out", dt, (B, L, Dm), dev),
+        ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+        ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return out
+
+
+def mx_quantize(x, stream=None):
+    """MX-FP8 of a bf16 matrix [rows, cols] along its rows (vdn_mx_quantize).
+    Returns (codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    dev = x.device
+    if cols % 32:
+        raise ValueError(f"cols={cols} is not a multiple of 32")
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    if rows == 0 or cols == 0:
+        return codes, scales
+    _check(lib().vdn_mx_quantize(_ptr(x, "x", torch.bfloat16, (rows, cols), dev),
+                                 _ptr(codes, "codes"), _ptr(scales, "scales"),
+                                 ctypes.c_longlong(rows), ctypes.c_int(cols), _stream(stream, dev)))
+    return codes, scales
 
 
 def prep_fwd(q, k, v, w_spatial, w_temporal, F: int, params: PrepParams, q_out=None, k_out=None,

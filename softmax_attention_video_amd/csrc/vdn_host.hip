@@ -73,12 +73,16 @@ hipError_t side_stream(SideStream** out) {
 
 // Workspace carve-up (offsets in bytes, each 256-aligned).
 struct Layout {
-  size_t vt, wt0, wt1, Tf, Uf, St, Tc, Uc, Pf, Pr, ohs, ohl, total;
+  size_t vt, wt0, wt1, Tf, Uf, St, Tc, Uc, Pf, Pr, ohs, ohl;
+  size_t mxa, mxas, mxw, mxws;   // MX-FP8 merge operands: codes and scales of A and W^T
+  size_t total;
 };
 
-Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt) {
+// mx: the merge runs in MX-FP8 (vdn_params.merge_mxfp8 on the bf16 path).
+Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt, bool mx) {
   const size_t es = dt == VDN_BF16 ? 2 : 4;
   const size_t BH = (size_t)g.B * g.H, DD = (size_t)g.D * g.D;
+  const size_t M = (size_t)g.B * g.L, K2 = 2 * (size_t)g.H * g.D;
   Layout l{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
@@ -94,9 +98,15 @@ Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt) {
   l.Pr = take(BH * (g.C + 1) * DD * 4);
   l.ohs = take(BH * g.L * g.D * es);
   l.ohl = take(BH * g.L * g.D * es);
+  l.mxa = take(mx ? M * K2 : 0);
+  l.mxas = take(mx ? M * K2 / 32 : 0);
+  l.mxw = take(mx ? (size_t)Dm * K2 : 0);
+  l.mxws = take(mx ? (size_t)Dm * K2 / 32 : 0);
   l.total = o;
   return l;
 }
+
+bool use_mx(const vdn_params* p, vdn_dtype dt) { return p->merge_mxfp8 == 1 && dt == VDN_BF16; }
 
 vdn_params defaults() {
   vdn_params p;
@@ -107,6 +117,7 @@ vdn_params defaults() {
   p.window_chunks = 1;
   p.anchors = 1;
   p.text_softmax = 0;
+  p.merge_mxfp8 = 0;
   return p;
 }
 
@@ -124,6 +135,8 @@ vdn_status check_geometry(const vdn_dims* d, const vdn_params* p, vdn_dtype dt, 
   if (p->anchors != 0 && p->anchors != 1) return fail(VDN_ERR_INVALID_ARG, "anchors=%d must be 0 or 1", p->anchors);
   if (p->text_softmax != 0 && p->text_softmax != 1)
     return fail(VDN_ERR_INVALID_ARG, "text_softmax=%d must be 0 or 1", p->text_softmax);
+  if (p->merge_mxfp8 != 0 && p->merge_mxfp8 != 1)
+    return fail(VDN_ERR_INVALID_ARG, "merge_mxfp8=%d must be 0 or 1", p->merge_mxfp8);
   if (d->F % p->chunk_frames != 0)
     return fail(VDN_ERR_INVALID_ARG, "F=%d is not a multiple of chunk_frames=%d", d->F, p->chunk_frames);
   if (!(p->rms_eps >= 0.f) || !isfinite(p->text_init_scale) || !isfinite(p->softmax_scale))
@@ -214,6 +227,85 @@ vdn_status run_softmax(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt
   return VDN_OK;
 }
 
+// Checks of the merge (a8) arguments shared by vdn_attn_fwd and vdn_merge_fwd.
+vdn_status check_merge(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, const void* W_s,
+                       const void* W_l, int Dm) {
+  if ((W_s == nullptr) != (W_l == nullptr))
+    return fail(VDN_ERR_INVALID_ARG, "W_s and W_l must both be given or both be NULL");
+  if (Dm < 1) return fail(VDN_ERR_INVALID_ARG, "D=%d must be >= 1", Dm);
+  if (!W_s && Dm != g.H * g.D)
+    return fail(VDN_ERR_INVALID_ARG, "without projections D=%d must equal H*d_v=%d", Dm, g.H * g.D);
+  if (p->merge_mxfp8) {
+    if (dt != VDN_BF16) return fail(VDN_ERR_UNSUPPORTED, "the MX-FP8 merge needs bf16 storage");
+    if (!W_s) return fail(VDN_ERR_INVALID_ARG, "the MX-FP8 merge needs the projections W_s, W_l");
+    if ((g.H * g.D) % 64 != 0 || Dm % 8 != 0)
+      return fail(VDN_ERR_UNSUPPORTED, "the MX-FP8 merge needs H*d_v %% 64 == 0 and D %% 8 == 0");
+  }
+  return VDN_OK;
+}
+
+// Merge, part 1 (may run on the linear branch's stream once Ohat_l exists):
+// transposed projections, and with MX-FP8 the W^T and Ohat_l operands.
+vdn_status merge_prepare(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, const void* W_s,
+                         const void* W_l, const void* ohl, int Dm, char* ws, const Layout& lay,
+                         hipStream_t s) {
+  const long long M = (long long)g.B * g.L;
+  const int K = g.H * g.D;
+  if (!W_s || dt != VDN_BF16) return VDN_OK;
+  const bool mx = use_mx(p, dt);
+  if (!mx && !(Dm % 8 == 0 && K % 64 == 0)) return VDN_OK;   // the SIMT GEMM reads W directly
+  uint16_t* w0t = (uint16_t*)(ws + lay.wt0);
+  uint16_t* w1t = (uint16_t*)(ws + lay.wt1);
+  VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_s, w0t, K, K, Dm, K, (long long)K * Dm, 1, s));
+  VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_l, w1t, K, K, Dm, K, (long long)K * Dm, 1, s));
+  if (mx) {
+    uint8_t* wc = (uint8_t*)(ws + lay.mxw);
+    uint8_t* wsc = (uint8_t*)(ws + lay.mxws);
+    VDN_HIP(vdn::launch_mx_quant_rows(w0t, Dm, K, wc, wsc, 2LL * K, 0, s));
+    VDN_HIP(vdn::launch_mx_quant_rows(w1t, Dm, K, wc, wsc, 2LL * K, K, s));
+    VDN_HIP(vdn::launch_mx_quant_rows((const uint16_t*)ohl, M, K, (uint8_t*)(ws + lay.mxa),
+                                      (uint8_t*)(ws + lay.mxas), 2LL * K, K, s));
+  }
+  return VDN_OK;
+}
+
+// Merge, part 2, on the caller's stream after both branches: out = [Ohat_s |
+// Ohat_l] [W_s ; W_l] (or Ohat_s + Ohat_l without projections).
+vdn_status merge_finish(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, const void* W_s,
+                        const void* W_l, const void* ohs, const void* ohl, void* out, int Dm,
+                        char* ws, const Layout& lay, hipStream_t s) {
+  const long long M = (long long)g.B * g.L;
+  const int K = g.H * g.D;
+  if (!W_s) {
+    if (dt == VDN_BF16)
+      VDN_HIP(vdn::launch_add<uint16_t>((const uint16_t*)ohs, (const uint16_t*)ohl, (uint16_t*)out,
+                                        M * K, s));
+    else
+      VDN_HIP(vdn::launch_add<float>((const float*)ohs, (const float*)ohl, (float*)out, M * K, s));
+  } else if (use_mx(p, dt)) {
+    uint8_t* ac = (uint8_t*)(ws + lay.mxa);
+    uint8_t* asc = (uint8_t*)(ws + lay.mxas);
+    VDN_HIP(vdn::launch_mx_quant_rows((const uint16_t*)ohs, M, K, ac, asc, 2LL * K, 0, s));
+    VDN_HIP(vdn::launch_merge_gemm_mx(ac, asc, (const uint8_t*)(ws + lay.mxw),
+                                      (const uint8_t*)(ws + lay.mxws), (uint16_t*)out, M, 2 * K,
+                                      Dm, s));
+  } else if (dt == VDN_BF16 && Dm % 8 == 0 && K % 64 == 0) {
+    VDN_HIP(vdn::launch_merge_gemm_bf16((const uint16_t*)ohs, (const uint16_t*)ohl,
+                                        (const uint16_t*)(ws + lay.wt0),
+                                        (const uint16_t*)(ws + lay.wt1), (uint16_t*)out, M, K, Dm,
+                                        s));
+  } else if (dt == VDN_BF16) {
+    VDN_HIP(vdn::launch_merge_gemm_simt<uint16_t>((const uint16_t*)ohs, (const uint16_t*)ohl,
+                                                  (const uint16_t*)W_s, (const uint16_t*)W_l,
+                                                  (uint16_t*)out, M, K, Dm, s));
+  } else {
+    VDN_HIP(vdn::launch_merge_gemm_simt<float>((const float*)ohs, (const float*)ohl,
+                                               (const float*)W_s, (const float*)W_l, (float*)out,
+                                               M, K, Dm, s));
+  }
+  return VDN_OK;
+}
+
 vdn_status check_workspace(void* ws, size_t bytes, size_t need) {
   if (bytes < need)
     return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", bytes, need);
@@ -233,7 +325,7 @@ vdn_status scan_entry(const void* k, const void* v, const float* beta, const flo
   NEED(k); NEED(v); NEED(beta); NEED(alpha);
   if (g.T > 0) { NEED(k_text); NEED(v_text); NEED(beta_text); }
   if (!P_fwd && !P_rev) return fail(VDN_ERR_INVALID_ARG, "output state pointer is NULL");
-  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt);
+  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt, use_mx(p, dt));
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -312,7 +404,7 @@ size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype 
   vdn::Geometry g;
   if (check_geometry(dims, p, dt, &g) != VDN_OK) return 0;
   const int Dm = dims->D > 0 ? dims->D : g.H * g.D;
-  return make_layout(g, Dm, dt).total;
+  return make_layout(g, Dm, dt, use_mx(p, dt)).total;
 }
 
 vdn_status vdn_window_plan(int F, const vdn_params* p, uint8_t* vis, int32_t* i_fwd, int32_t* ws,
@@ -375,7 +467,7 @@ vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v,
   if (st != VDN_OK) return st;
   NEED(q); NEED(k); NEED(v); NEED(out);
   if (g.Ts > 0) { NEED(k_text); NEED(v_text); }
-  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt);
+  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt, use_mx(p, dt));
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
   return run_softmax(g, p, dt, q, k, v, k_text, v_text, g_s, out, lse, (char*)workspace, lay,
@@ -394,14 +486,10 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   if (st != VDN_OK) return st;
   NEED(q); NEED(k); NEED(v); NEED(beta); NEED(alpha); NEED(g_s); NEED(g_l); NEED(out);
   if (g.T > 0) { NEED(k_text); NEED(v_text); NEED(beta_text); }
-  if ((W_s == nullptr) != (W_l == nullptr))
-    return fail(VDN_ERR_INVALID_ARG, "W_s and W_l must both be given or both be NULL");
-  const bool proj = W_s != nullptr;
   const int Dm = dims->D;
-  if (Dm < 1) return fail(VDN_ERR_INVALID_ARG, "D=%d must be >= 1", Dm);
-  if (!proj && Dm != g.H * g.D)
-    return fail(VDN_ERR_INVALID_ARG, "without projections D=%d must equal H*d_v=%d", Dm, g.H * g.D);
-  const Layout lay = make_layout(g, Dm, dt);
+  st = check_merge(g, p, dt, W_s, W_l, Dm);
+  if (st != VDN_OK) return st;
+  const Layout lay = make_layout(g, Dm, dt, use_mx(p, dt));
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
 
@@ -428,6 +516,9 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
                                          p->rms_eps, (float*)ohl, ss->stream);
     if (e != hipSuccess) st = fail(VDN_ERR_HIP, "readout launch failed: %s", hipGetErrorString(e));
   }
+  // the merge's projection transposes (and MX-FP8 operands of W and Ohat_l)
+  // also run on the side stream, off the Softmax's path
+  if (st == VDN_OK) st = merge_prepare(g, p, dt, W_s, W_l, ohl, Dm, ws, lay, ss->stream);
   // join is recorded even after a failure, so the caller's stream never
   // runs ahead of work already queued on the side stream
   const hipError_t ej = hipEventRecord(ss->join, ss->stream);
@@ -437,30 +528,39 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   if (st != VDN_OK) return st;
   if (ew != hipSuccess) return fail(VDN_ERR_HIP, "side-stream join failed: %s", hipGetErrorString(ew));
   // Merge (a8)
-  const long long M = (long long)g.B * g.L;
-  const int K = g.H * g.D;
-  if (!proj) {
-    if (dt == VDN_BF16)
-      VDN_HIP(vdn::launch_add<uint16_t>((const uint16_t*)ohs, (const uint16_t*)ohl,
-                                        (uint16_t*)out, M * K, s));
-    else
-      VDN_HIP(vdn::launch_add<float>((const float*)ohs, (const float*)ohl, (float*)out, M * K, s));
-  } else if (dt == VDN_BF16 && Dm % 8 == 0 && K % 64 == 0) {
-    uint16_t* w0t = (uint16_t*)(ws + lay.wt0);
-    uint16_t* w1t = (uint16_t*)(ws + lay.wt1);
-    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_s, w0t, K, K, Dm, K, (long long)K * Dm, 1, s));
-    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)W_l, w1t, K, K, Dm, K, (long long)K * Dm, 1, s));
-    VDN_HIP(vdn::launch_merge_gemm_bf16((const uint16_t*)ohs, (const uint16_t*)ohl, w0t, w1t,
-                                        (uint16_t*)out, M, K, Dm, s));
-  } else if (dt == VDN_BF16) {
-    VDN_HIP(vdn::launch_merge_gemm_simt<uint16_t>((const uint16_t*)ohs, (const uint16_t*)ohl,
-                                                  (const uint16_t*)W_s, (const uint16_t*)W_l,
-                                                  (uint16_t*)out, M, K, Dm, s));
-  } else {
-    VDN_HIP(vdn::launch_merge_gemm_simt<float>((const float*)ohs, (const float*)ohl,
-                                               (const float*)W_s, (const float*)W_l, (float*)out,
-                                               M, K, Dm, s));
-  }
+  return merge_finish(g, p, dt, W_s, W_l, ohs, ohl, out, Dm, ws, lay, s);
+}
+
+vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s, const void* W_l,
+                         void* out, void* workspace, size_t workspace_bytes, const vdn_dims* dims,
+                         const vdn_params* p, vdn_dtype dt, void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(ohat_s); NEED(ohat_l); NEED(out);
+  const int Dm = dims->D;
+  st = check_merge(g, p, dt, W_s, W_l, Dm);
+  if (st != VDN_OK) return st;
+  const Layout lay = make_layout(g, Dm, dt, use_mx(p, dt));
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != VDN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  st = merge_prepare(g, p, dt, W_s, W_l, ohat_l, Dm, ws, lay, s);
+  if (st != VDN_OK) return st;
+  return merge_finish(g, p, dt, W_s, W_l, ohat_s, ohat_l, out, Dm, ws, lay, s);
+}
+
+vdn_status vdn_mx_quantize(const void* src, void* codes, void* scales, long long rows, int cols,
+                           void* stream) {
+  g_err[0] = 0;
+  NEED(src); NEED(codes); NEED(scales);
+  if (rows < 0 || cols < 0) return fail(VDN_ERR_INVALID_ARG, "rows=%lld cols=%d", rows, cols);
+  if (cols % 32) return fail(VDN_ERR_INVALID_ARG, "cols=%d is not a multiple of 32", cols);
+  if (rows * (long long)(cols / 32) > (1ll << 40)) return fail(VDN_ERR_INVALID_ARG, "too many blocks");
+  VDN_HIP(vdn::launch_mx_quant_rows((const uint16_t*)src, rows, cols, (uint8_t*)codes,
+                                    (uint8_t*)scales, cols, 0, (hipStream_t)stream));
   return VDN_OK;
 }
 

@@ -92,6 +92,15 @@ hipError_t launch_merge_gemm_simt(const T* a0, const T* a1, const T* w0, const T
 template <typename T>
 hipError_t launch_add(const T* a, const T* b, T* out, long long n, hipStream_t s);
 
+// ---- MX-FP8 merge (OCP MX: blocks of 32 along rows, E8M0 scales, E4M3) ----
+// src bf16 [rows, cols] -> codes[r * dst_ld + dst_col0 + c], scales[r * dst_ld/32 + (dst_col0 + c)/32].
+hipError_t launch_mx_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* codes,
+                                uint8_t* scales, long long dst_ld, int dst_col0, hipStream_t s);
+// out[M, Dm] (bf16) = A[M, K2] B^T with A, B^T [Dm, K2] as codes + scales (K2 % 128 == 0).
+hipError_t launch_merge_gemm_mx(const uint8_t* a, const uint8_t* a_sc, const uint8_t* bt,
+                                const uint8_t* b_sc, uint16_t* out, long long M, int K2, int Dm,
+                                hipStream_t s);
+
 // ---- VDA-Prep (linear-branch feature map) ----
 // q,k,v [B,L,H,D] token-major -> q',k',v' [B,H,L,D]; w_sp [H,D,kh,kw], w_t [H,D,taps].
 template <typename T>

@@ -233,3 +233,49 @@ def test_prep_null_pointers_and_dtype():
     for n in ("q", "k", "v", "w_spatial", "w_temporal", "q_out", "k_out", "v_out"):
         assert _call_prep(d, p, null=(n,)) == vdn.VDN_ERR_INVALID_ARG, n
     assert _call_prep(d, p, dt=7) == vdn.VDN_ERR_UNSUPPORTED
+
+
+def test_mx_merge_validation():
+    d = _dims()
+    assert _call_attn(d, params=vdn.Params(merge_mxfp8=2)) == vdn.VDN_ERR_INVALID_ARG
+    assert _call_attn(d, params=vdn.Params(merge_mxfp8=1), dt=vdn.VDN_F32) == vdn.VDN_ERR_UNSUPPORTED
+    assert _call_attn(d, params=vdn.Params(merge_mxfp8=1), W=False) == vdn.VDN_ERR_INVALID_ARG
+    # H * d_v must be a multiple of 64 (128-deep K steps over the concatenated K)
+    assert _call_attn(_dims(H=1, d_k=32, d_v=32, D=32),
+                      params=vdn.Params(merge_mxfp8=1)) == vdn.VDN_ERR_UNSUPPORTED
+    assert _call_attn(_dims(D=130), params=vdn.Params(merge_mxfp8=1)) == vdn.VDN_ERR_UNSUPPORTED
+
+
+def test_mx_workspace_holds_codes_and_scales():
+    d = _dims(B=1, H=2, F=20, N=16, T=4, d_k=64, d_v=64, D=96)
+    base = vdn.workspace_bytes(d, vdn.Params())
+    mx = vdn.workspace_bytes(d, vdn.Params(merge_mxfp8=1))
+    M, K2, Dm = 20 * 16, 2 * 128, 96
+    extra = M * K2 + M * K2 // 32 + Dm * K2 + Dm * K2 // 32
+    assert extra <= mx - base <= extra + 4 * 256
+    # fp32 storage never uses the MX operands
+    assert vdn.workspace_bytes(d, vdn.Params(merge_mxfp8=1), vdn.VDN_F32) == \
+        vdn.workspace_bytes(d, vdn.Params(), vdn.VDN_F32)
+
+
+def test_merge_fwd_and_quantize_validation():
+    L = vdn.lib()
+    fake = ctypes.c_void_p(0x100000)
+    d = _dims()
+    p = vdn.Params().c()
+    pm = vdn.Params(merge_mxfp8=1).c()
+    big = ctypes.c_size_t(1 << 40)
+    assert L.vdn_merge_fwd(None, fake, fake, fake, fake, fake, big, ctypes.byref(d), ctypes.byref(p),
+                           vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    assert L.vdn_merge_fwd(fake, fake, fake, None, fake, fake, big, ctypes.byref(d), ctypes.byref(p),
+                           vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    assert L.vdn_merge_fwd(fake, fake, fake, fake, fake, fake, ctypes.c_size_t(16), ctypes.byref(d),
+                           ctypes.byref(pm), vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+    assert L.vdn_merge_fwd(fake, fake, None, None, fake, fake, big, ctypes.byref(d), ctypes.byref(pm),
+                           vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    q = L.vdn_mx_quantize
+    assert q(None, fake, fake, 4, 64, None) == vdn.VDN_ERR_INVALID_ARG
+    assert q(fake, fake, None, 4, 64, None) == vdn.VDN_ERR_INVALID_ARG
+    assert q(fake, fake, fake, 4, 48, None) == vdn.VDN_ERR_INVALID_ARG
+    assert b"multiple of 32" in L.vdn_last_error()
+    assert q(fake, fake, fake, -1, 64, None) == vdn.VDN_ERR_INVALID_ARG

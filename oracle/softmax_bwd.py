@@ -1,0 +1,71 @@
+"""Backward pass of the window + anchor Softmax branch -- CPU fp64 oracle.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke entry point and the
+benchmark's CPU-baseline leg may import this module; the product path never
+calls it and shares no code with it.
+
+Source: "Video DeltaNet: A Video-Native Hybrid Attention for Livestream Video
+Generation" (arXiv 2609.20744).  Method, local Softmax window and branch
+calibration, defines the forward: for query frame t,
+  O_s[t] = softmax(scale * Q_t K_vis^T) V_vis,   Ohat_s = g_s * O_s,
+with K_vis, V_vis the tokens of the visible key frames Vis(t), each frame
+once.  The experiments section trains the model through this operator (the
+staged adaptation), which needs its gradients; the page prints none, so they
+are the chain rule applied to that definition, written out per query frame:
+  dO  = g_s * dOhat                     (gradient of the ungated output)
+  dg  = rowsum(dOhat * O_s)
+  P   = softmax(scale * Q_t K_vis^T)
+  dV_vis += P^T dO
+  dP  = dO V_vis^T
+  dS  = P * (dP - rowsum(dO * O_s))
+  dQ_t = scale * dS K_vis,   dK_vis += scale * dS^T Q_t
+Contributions to the keys and values of a frame are summed over every query
+frame that sees it.  Everything in float64.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import vdn_oracle as O
+
+
+def softmax_branch_bwd(Qf, Kf, Vf, g_s, dOhat, p: O.Params = O.DEFAULT):
+    """Gradients of the gated Softmax branch for one head.
+
+    Qf, Kf, Vf: [F, N, d]; g_s: [F, N] (post-sigmoid gate values, an input);
+    dOhat: [F, N, dv] the gradient of Ohat_s.  Video keys only (the
+    text-keys option is not covered).  Returns (dQ, dK, dV, dg) with the
+    shapes of Qf, Kf, Vf and g_s.
+    """
+    Qf = np.asarray(Qf, np.float64)
+    Kf = np.asarray(Kf, np.float64)
+    Vf = np.asarray(Vf, np.float64)
+    g = np.asarray(g_s, np.float64)
+    dOh = np.asarray(dOhat, np.float64)
+    F, N, dk = Qf.shape
+    scale = (1.0 / math.sqrt(dk)) if p.softmax_scale is None else p.softmax_scale
+    dQ = np.zeros_like(Qf)
+    dK = np.zeros_like(Kf)
+    dV = np.zeros_like(Vf)
+    dg = np.zeros((F, N))
+    for t in range(F):
+        fr = sorted(O.visible_frames(t, F, p))
+        Kv = np.concatenate([Kf[f] for f in fr])
+        Vv = np.concatenate([Vf[f] for f in fr])
+        s = scale * (Qf[t] @ Kv.T)
+        P = np.exp(s - s.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        Os = P @ Vv
+        dO = g[t][:, None] * dOh[t]
+        dg[t] = np.sum(dOh[t] * Os, axis=1)
+        dVv = P.T @ dO
+        dP = dO @ Vv.T
+        dS = P * (dP - np.sum(dO * Os, axis=1, keepdims=True))
+        dQ[t] = scale * (dS @ Kv)
+        dKv = scale * (dS.T @ Qf[t])
+        for i, f in enumerate(fr):
+            dK[f] += dKv[i * N:(i + 1) * N]
+            dV[f] += dVv[i * N:(i + 1) * N]
+    return dQ, dK, dV, dg

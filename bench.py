@@ -144,7 +144,7 @@ def softmax_source_digest() -> str:
     stored traffic figure is only reported while it matches."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("k_window_softmax.hip", "vdn_common.h", "vdn_internal.h"):
+    for f in ("k_window_softmax.hip", "window_items.h", "vdn_common.h", "vdn_internal.h"):
         with open(os.path.join(ROOT, "softmax_attention_video_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

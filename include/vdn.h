@@ -210,6 +210,36 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
                          const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream);
 
 /*
+ * vdn_window_softmax_bwd -- gradients of the Softmax branch (a7), video keys
+ * only (p->text_softmax = 0).
+ *
+ * Paper, method (local Softmax window; branch calibration) defines the
+ * forward Ohat_s = g_s * softmax(scale q k^T) v over the visible keys; the
+ * experiments train through it.  The gradients are its chain rule:
+ *   dO = g_s * d_out,  Dq = rowsum(dO * o),  P = exp(scale q.k - lse),
+ *   dS = P * (dO.v - Dq),  dq = scale * sum_k dS k,  dk = scale * sum_q dS q,
+ *   dv = sum_q P dO,  dg_s = rowsum(d_out * o).
+ *
+ *  q, k, v     [B,H,L,d] dt     the forward's inputs
+ *  o           [B,L,H,d] dt     the ungated Softmax output O_s
+ *                               (vdn_window_softmax_fwd with g_s = NULL)
+ *  lse         [B,H,L]   float  the forward's log-sum-exp (same call)
+ *  g_s         [B,H,L]   float  the gate, NULL = 1
+ *  d_out       [B,L,H,d] dt     gradient of the gated output Ohat_s
+ *  dq, dk, dv  [B,H,L,d] dt     outputs (fully written)
+ *  dg_s        [B,H,L]   float  output gradient of g_s, nullable
+ *  workspace   vdn_softmax_bwd_workspace_bytes(dims, p, dt) bytes
+ */
+vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const float* g_s, const void* d_out, void* dq,
+                                  void* dk, void* dv, float* dg_s, void* workspace,
+                                  size_t workspace_bytes, const vdn_dims* dims, const vdn_params* p,
+                                  vdn_dtype dt, void* stream);
+
+/* Workspace bytes of vdn_window_softmax_bwd (0 if the arguments are invalid). */
+size_t vdn_softmax_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
+
+/*
  * vdn_mx_quantize -- MX-FP8 quantization of bf16 rows (the operand format of
  * the MX-FP8 merge; e.g. to inspect it or to quantize weights ahead of time).
  *

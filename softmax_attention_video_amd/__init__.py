@@ -10,6 +10,7 @@ Entry points (same names as the C-ABI):
   attn_fwd(...)               -> out            (vdn_attn_fwd)
   scan_fwd(...), scan_rev(...) -> P, S_text     (vda_scan_fwd / vda_scan_rev)
   window_softmax_fwd(...)     -> out, lse       (vdn_window_softmax_fwd)
+  window_softmax_bwd(...)     -> dq, dk, dv, dg (vdn_window_softmax_bwd)
   merge_fwd(...)              -> out            (vdn_merge_fwd)
   mx_quantize(x)              -> codes, scales  (vdn_mx_quantize)
   prep_fwd(...)               -> q', k', v'     (vda_prep_fwd)
@@ -34,7 +35,7 @@ EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_window_softmax_fwd", "vdn_workspace_bytes", "vdn_window_plan",
            "vdn_status_string", "vdn_last_error", "vdn_timer_enable", "vdn_timer_read",
            "vdn_timer_disable", "vda_prep_default_params", "vda_prep_fwd", "vdn_merge_fwd",
-           "vdn_mx_quantize")
+           "vdn_mx_quantize", "vdn_window_softmax_bwd", "vdn_softmax_bwd_workspace_bytes")
 
 
 class VdnError(RuntimeError):
@@ -141,6 +142,10 @@ def lib() -> ctypes.CDLL:
     L.vdn_merge_fwd.restype = I
     L.vdn_mx_quantize.argtypes = [P, P, P, ctypes.c_longlong, I, P]
     L.vdn_mx_quantize.restype = I
+    L.vdn_window_softmax_bwd.argtypes = [P] * 12 + [S, dp, pp, I, P]
+    L.vdn_window_softmax_bwd.restype = I
+    L.vdn_softmax_bwd_workspace_bytes.argtypes = [dp, pp, I]
+    L.vdn_softmax_bwd_workspace_bytes.restype = S
     _lib = L
     return L
 
@@ -377,6 +382,43 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
         ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
     return out, lse
+
+
+def window_softmax_bwd(q, k, v, o, lse, d_out, F: int, g_s=None, want_dg: bool = False,
+                       params: Params | None = None, workspace=None, stream=None):
+    """Gradients of the Softmax branch (vdn_window_softmax_bwd), video keys only.
+
+    q, k, v [B,H,L,d]; o [B,L,H,d] the ungated output and lse [B,H,L] of
+    window_softmax_fwd(..., g_s=None, want_lse=True); d_out [B,L,H,d] the
+    gradient of the gated output; g_s [B,H,L] or None.
+    Returns (dq, dk, dv [B,H,L,d], dg [B,H,L] or None)."""
+    torch = _torch()
+    params = params or Params()
+    B, H, L, d = q.shape
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    dt = q.dtype
+    code = _dtype_code(q)
+    dev = q.device
+    f32 = torch.float32
+    dims = Dims(B, H, F, L // F, 0, d, d, H * d)
+    p = params.c()
+    need = int(lib().vdn_softmax_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p), code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace of {workspace.numel()} bytes < {need}")
+    dq, dk, dv = (torch.empty((B, H, L, d), dtype=dt, device=dev) for _ in range(3))
+    dg = torch.empty((B, H, L), dtype=f32, device=dev) if want_dg else None
+    _check(lib().vdn_window_softmax_bwd(
+        _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
+        _ptr(v, "v", dt, (B, H, L, d), dev), _ptr(o, "o", dt, (B, L, H, d), dev),
+        _ptr(lse, "lse", f32, (B, H, L), dev), _ptr(g_s, "g_s", f32, (B, H, L), dev, allow_none=True),
+        _ptr(d_out, "d_out", dt, (B, L, H, d), dev), _ptr(dq, "dq"), _ptr(dk, "dk"), _ptr(dv, "dv"),
+        _ptr(dg, "dg", allow_none=True),
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+        ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return dq, dk, dv, dg
 
 
 def merge_fwd(ohat_s, ohat_l, W_s, W_l, F: int, params: Params | None = None, out=None,

@@ -25,6 +25,7 @@
 // that XCD's L2), anchor groups (7x longer at 120 frames) first.
 #include "vdn_common.h"
 #include "vdn_internal.h"
+#include "window_items.h"
 
 #include <math.h>
 
@@ -53,119 +54,6 @@ SoftmaxWork window_work(const Geometry& g, int bq) {
   return w;
 }
 
-struct Item {
-  int bh;            // b * H + h
-  int q_begin, q_end;
-  int nspan;
-  int kb0, ke0, kb1, ke1, kb2, ke2, kb3, ke3;   // up to four key spans [kb, ke)
-};
-
-// Key tiles of BK over the (up to NS <= 4) spans, flattened: tile j of the
-// walk starts at key ks and holds nk valid keys.  The lookup is plain
-// arithmetic on the span index (no selects of struct members), which keeps
-// the walk in scalar registers instead of private memory.
-template <int BK, int NS>
-struct SpanWalk {
-  int n0, n01, n012, n;   // cumulative tile counts
-  int o0, o1, o2, o3;     // key start of tile j in span i is j * BK + o_i
-  int e0, e1, e2, e3;     // span ends
-  __device__ __forceinline__ SpanWalk(const Item& it) {
-    const int kb1 = it.nspan > 1 ? it.kb1 : 0, ke1 = it.nspan > 1 ? it.ke1 : 0;
-    const int kb2 = it.nspan > 2 ? it.kb2 : 0, ke2 = it.nspan > 2 ? it.ke2 : 0;
-    const int kb3 = NS > 3 && it.nspan > 3 ? it.kb3 : 0, ke3 = NS > 3 && it.nspan > 3 ? it.ke3 : 0;
-    n0 = (it.ke0 - it.kb0 + BK - 1) / BK;
-    n01 = n0 + (ke1 - kb1 + BK - 1) / BK;
-    n012 = n01 + (ke2 - kb2 + BK - 1) / BK;
-    n = n012 + (ke3 - kb3 + BK - 1) / BK;
-    o0 = it.kb0;
-    o1 = kb1 - n0 * BK;
-    o2 = kb2 - n01 * BK;
-    o3 = kb3 - n012 * BK;
-    e0 = it.ke0; e1 = ke1; e2 = ke2; e3 = ke3;
-  }
-  __device__ __forceinline__ void tile(int j, int& ks, int& nk) const {
-    const int s1 = j >= n0, s2 = j >= n01, s3 = NS > 3 && j >= n012;
-    ks = j * BK + o0 + (o1 - o0) * s1 + (o2 - o1) * s2 + (o3 - o2) * s3;
-    const int e = e0 + (e1 - e0) * s1 + (e2 - e1) * s2 + (e3 - e2) * s3;
-    nk = min(BK, e - ks);
-  }
-};
-
-// Appends the text span [L, L + nt) after the item's video spans.
-__device__ __forceinline__ void add_text_span(const Geometry& g, int nt, Item& it) {
-  it.kb3 = it.ke3 = 0;
-  if (nt <= 0) return;
-  const int tb = (int)g.L, te = (int)(g.L + nt);
-  if (it.nspan == 1) {
-    it.kb1 = tb; it.ke1 = te;
-  } else if (it.nspan == 2) {
-    it.kb2 = tb; it.ke2 = te;
-  } else {
-    it.kb3 = tb; it.ke3 = te;
-  }
-  ++it.nspan;
-}
-
-// Decode workgroup id -> (query range, key spans).  Returns false if idle.
-// TEXT: append a span of the first nt text keys (none if nt == 0).
-template <bool TEXT>
-__device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork& w, int bq,
-                                            int bid, int nt, Item& it, int& q0) {
-  const int x = bid % kNumXcd;
-  int k = bid / kNumXcd;
-  const int a0 = x * w.pa;
-  int na = w.GA - a0;
-  na = na < 0 ? 0 : (na > w.pa ? w.pa : na);
-  const long long N = g.N;
-  if (k < na * w.tA) {
-    const int ga = a0 + k / w.tA;
-    const int tile = k % w.tA;
-    it.bh = ga >> 1;
-    const int f = (ga & 1) ? g.F - 1 : 0;
-    it.q_begin = (int)(f * N);
-    it.q_end = (int)((f + 1) * N);
-    it.nspan = 1;
-    it.kb0 = 0;
-    it.ke0 = (int)g.L;
-    it.kb1 = it.ke1 = it.kb2 = it.ke2 = it.kb3 = it.ke3 = 0;
-    if (TEXT) add_text_span(g, nt, it);
-    q0 = it.q_begin + tile * bq;
-    return true;
-  }
-  k -= na * w.tA;
-  const int gc = x * w.pc + k / w.tC;
-  const int tile = k % w.tC;
-  if (gc >= w.GC || gc >= (x + 1) * w.pc) return false;
-  it.bh = gc / g.C;
-  const int c = gc % g.C;
-  int f0 = c * g.cf, f1 = (c + 1) * g.cf;
-  if (f1 > g.F) f1 = g.F;
-  if (g.anchors) {
-    if (f0 == 0) f0 = 1;
-    if (f1 == g.F) f1 = g.F - 1;
-  }
-  if (f1 <= f0) return false;
-  it.q_begin = (int)(f0 * N);
-  it.q_end = (int)(f1 * N);
-  int lo = c - g.wc;
-  lo = (lo < 0 ? 0 : lo) * g.cf;
-  int hi = (c + g.wc + 1) * g.cf;
-  hi = hi > g.F ? g.F : hi;
-  // spans in ascending key order: [anchor 0] window [anchor F-1]
-  const int nN = (int)N;
-  const bool a_lo = g.anchors && lo > 0, a_hi = g.anchors && hi < g.F;
-  it.kb0 = a_lo ? 0 : lo * nN;
-  it.ke0 = a_lo ? nN : hi * nN;
-  it.kb1 = a_lo ? lo * nN : (g.F - 1) * nN;
-  it.ke1 = a_lo ? hi * nN : g.F * nN;
-  it.kb2 = (g.F - 1) * nN;
-  it.ke2 = g.F * nN;
-  it.nspan = 1 + (a_lo ? 1 : 0) + (a_hi ? 1 : 0);
-  it.kb3 = it.ke3 = 0;
-  if (TEXT) add_text_span(g, nt, it);
-  q0 = it.q_begin + tile * bq;
-  return q0 < it.q_end;
-}
 
 // -------------------------------------------------------------------------
 // bf16 MFMA flash kernel.  512 threads = 8 waves of 32 queries each (256

@@ -106,6 +106,23 @@ Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt, bool mx) {
   return l;
 }
 
+// Workspace of the Softmax backward: g_s * dOhat in head-major order, and Dq.
+struct BwdLayout {
+  size_t dohm, Dq, total;
+};
+
+BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
+  const size_t es = dt == VDN_BF16 ? 2 : 4;
+  const size_t rows = (size_t)g.B * g.H * g.L;
+  BwdLayout l{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+  l.dohm = take(rows * g.D * es);
+  l.Dq = take(rows * 4);
+  l.total = o;
+  return l;
+}
+
 bool use_mx(const vdn_params* p, vdn_dtype dt) { return p->merge_mxfp8 == 1 && dt == VDN_BF16; }
 
 vdn_params defaults() {
@@ -550,6 +567,48 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
   st = merge_prepare(g, p, dt, W_s, W_l, ohat_l, Dm, ws, lay, s);
   if (st != VDN_OK) return st;
   return merge_finish(g, p, dt, W_s, W_l, ohat_s, ohat_l, out, Dm, ws, lay, s);
+}
+
+size_t vdn_softmax_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
+  vdn::Geometry g;
+  if (check_geometry(dims, p, dt, &g) != VDN_OK) return 0;
+  return bwd_layout(g, dt).total;
+}
+
+vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const float* g_s, const void* d_out, void* dq,
+                                  void* dk, void* dv, float* dg_s, void* workspace,
+                                  size_t workspace_bytes, const vdn_dims* dims, const vdn_params* p,
+                                  vdn_dtype dt, void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(q); NEED(k); NEED(v); NEED(o); NEED(lse); NEED(d_out); NEED(dq); NEED(dk); NEED(dv);
+  if (g.Ts > 0) return fail(VDN_ERR_UNSUPPORTED, "the Softmax backward covers video keys only (text_softmax = 0)");
+  const BwdLayout lay = bwd_layout(g, dt);
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != VDN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* Dq = (float*)(ws + lay.Dq);
+  const float sc = softmax_scale(p, g.D);
+  if (dt == VDN_BF16) {
+    uint16_t* dohm = (uint16_t*)(ws + lay.dohm);
+    VDN_HIP(vdn::launch_softmax_bwd_prep<uint16_t>(g, (const uint16_t*)o, (const uint16_t*)d_out, g_s,
+                                                   dohm, Dq, dg_s, s));
+    VDN_HIP(vdn::launch_softmax_bwd_simt<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k,
+                                                   (const uint16_t*)v, dohm, lse, Dq, (uint16_t*)dq,
+                                                   (uint16_t*)dk, (uint16_t*)dv, sc, s));
+  } else {
+    float* dohm = (float*)(ws + lay.dohm);
+    VDN_HIP(vdn::launch_softmax_bwd_prep<float>(g, (const float*)o, (const float*)d_out, g_s, dohm,
+                                                Dq, dg_s, s));
+    VDN_HIP(vdn::launch_softmax_bwd_simt<float>(g, (const float*)q, (const float*)k, (const float*)v,
+                                                dohm, lse, Dq, (float*)dq, (float*)dk, (float*)dv,
+                                                sc, s));
+  }
+  return VDN_OK;
 }
 
 vdn_status vdn_mx_quantize(const void* src, void* codes, void* scales, long long rows, int cols,

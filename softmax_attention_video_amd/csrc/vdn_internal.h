@@ -92,6 +92,18 @@ hipError_t launch_merge_gemm_simt(const T* a0, const T* a1, const T* w0, const T
 template <typename T>
 hipError_t launch_add(const T* a, const T* b, T* out, long long n, hipStream_t s);
 
+// ---- window Softmax backward ----
+// o, dout [B,L,H,D] (ungated output and the gradient of the gated output);
+// do_hm [B,H,L,D] = g_s * dout; Dq [B,H,L] = g_s * rowsum(dout * o); dg nullable.
+template <typename T>
+hipError_t launch_softmax_bwd_prep(const Geometry& g, const T* o, const T* dout, const float* g_s,
+                                   T* do_hm, float* Dq, float* dg, hipStream_t s);
+// q, k, v, do_hm [B,H,L,D]; lse, Dq [B,H,L]; dq, dk, dv [B,H,L,D].
+template <typename T>
+hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, const T* v,
+                                   const T* do_hm, const float* lse, const float* Dq, T* dq, T* dk,
+                                   T* dv, float scale, hipStream_t s);
+
 // ---- MX-FP8 merge (OCP MX: blocks of 32 along rows, E8M0 scales, E4M3) ----
 // src bf16 [rows, cols] -> codes[r * dst_ld + dst_col0 + c], scales[r * dst_ld/32 + (dst_col0 + c)/32].
 hipError_t launch_mx_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* codes,

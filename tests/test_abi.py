@@ -279,3 +279,23 @@ def test_merge_fwd_and_quantize_validation():
     assert q(fake, fake, fake, 4, 48, None) == vdn.VDN_ERR_INVALID_ARG
     assert b"multiple of 32" in L.vdn_last_error()
     assert q(fake, fake, fake, -1, 64, None) == vdn.VDN_ERR_INVALID_ARG
+
+
+def test_softmax_bwd_validation():
+    L = vdn.lib()
+    fake = ctypes.c_void_p(0x100000)
+    d = _dims()                       # T = 4
+    p = vdn.Params().c()
+    big = ctypes.c_size_t(1 << 40)
+    args = [fake] * 11
+    fn = L.vdn_window_softmax_bwd
+    for i in (0, 3, 4, 6, 7):         # q, o, lse, d_out, dq
+        a = list(args)
+        a[i] = None
+        assert fn(*a, fake, big, ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    assert fn(*args, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16,
+              None) == vdn.VDN_ERR_WORKSPACE
+    pt = vdn.Params(text_softmax=1).c()
+    assert fn(*args, fake, big, ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED
+    need = L.vdn_softmax_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16)
+    assert need >= 2 * 20 * 16 * 64 * 2 + 2 * 20 * 16 * 4

@@ -33,7 +33,7 @@ import numpy as np
 # tensor ids of the seed sequence
 _ID = dict(q=0, k=1, v=2, beta=3, alpha=4, k_text=5, v_text=6, beta_text=7,
            g_s=8, g_l=9, W_s=10, W_l=11, dup=12, prep_q=13, prep_k=14, prep_v=15,
-           prep_ws=16, prep_wt=17)
+           prep_ws=16, prep_wt=17, d_out=18)
 
 # latent grid (rows x columns) of one frame for each configuration, N = rows * columns
 GRIDS = {"tiny": (4, 4), "small": (16, 16), "medium": (24, 16), "h3": (48, 32), "long": (32, 24)}
@@ -245,3 +245,14 @@ def prep_inputs(cfg: Config, threads: int | None = None) -> dict:
     with _cf.ThreadPoolExecutor(max_workers=max(1, n)) as ex:
         list(ex.map(one, [(b, h) for b in range(B) for h in range(H)]))
     return out
+
+
+def grad_output(cfg: Config) -> np.ndarray:
+    """Seeded gradient of the gated Softmax output, dOhat [B, L, H, d] ~ N(0, 1),
+    rounded to cfg.dtype (the output layout of the branch)."""
+    out = np.empty((cfg.B, cfg.L, cfg.H, cfg.d), np.float32)
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            out[b, :, h] = _store(cfg, _normal(cfg, "d_out", b, h, (cfg.L, cfg.d)))
+    return out
+

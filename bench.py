@@ -17,6 +17,7 @@ sample of the same workload and scales it to tokens/s.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -253,6 +254,57 @@ def measure_text(cfg, t, reps: int = 5) -> dict:
             "frac": ach / PEAK_BF16_TFLOPS, "softmax_flops": sm_flops}
 
 
+def measure_bwd(cfg, t, reps: int = 3) -> dict:
+    """Backward of the Softmax branch (vdn_window_softmax_bwd) on the layer's
+    q, k, v and gate, with a seeded random output gradient: the forward
+    (g_s = NULL, with lse) supplies O_s and lse outside the timed region.
+    HIP-event time of the call and of its two MFMA kernels (KernelTimer)."""
+    import torch
+
+    import softmax_attention_video_amd as vdn
+
+    B, H, L, d = t["q"].shape
+    dev = t["q"].device
+    if t["q"].dtype != torch.bfloat16:
+        return {}
+    o, lse = vdn.window_softmax_fwd(t["q"], t["k"], t["v"], cfg.F, want_lse=True)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    dout = torch.randn((B, L, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dims = vdn.Dims(B, H, cfg.F, cfg.N, 0, d, d, H * d)
+    p = vdn.Params().c()
+    ws = torch.empty(vdn.lib().vdn_softmax_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p),
+                                                              vdn.VDN_BF16), dtype=torch.uint8, device=dev)
+
+    def run():
+        return vdn.window_softmax_bwd(t["q"], t["k"], t["v"], o, lse, dout, cfg.F, g_s=t["g_s"],
+                                      want_dg=True, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    timer = vdn.KernelTimer(reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    k_ms = timer.read()
+    timer.close()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = int(vdn.window_plan(cfg.F)[0].sum())
+    flops = 10.0 * d * pairs * cfg.N * cfg.N * H * B      # S, dP, dV, dQ, dK: 5 products of 2 d per pair
+    ach = flops / (float(k_ms.mean()) / 1e3) / 1e12
+    del ws, o, lse, dout
+    return {"entry": "vdn_window_softmax_bwd (dq, dk, dv, dg_s)",
+            "workload": f"{cfg.name}: Softmax branch backward, B={B} H={H} d={d} F={cfg.F} N={cfg.N}",
+            "ms": ms, "kernel": f"softmax_bwd_dq_mfma_kernel<{d}> + softmax_bwd_dkdv_mfma_kernel<{d}>",
+            "kernel_ms": float(k_ms.mean()), "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flops": flops,
+            "executed_mfma_flops": 1.4 * flops,
+            "note": "S and dP are computed in both kernels: 14 d MFMA flops per pair against the 10 d counted"}
+
+
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 / MX-FP8 MFMA (2 x the bf16 peak)
 
 
@@ -324,6 +376,8 @@ def main() -> int:
                     help="skip the separate text-keys-in-Softmax measurement")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the separate MX-FP8 merge measurement")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the separate Softmax-backward measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one elementwise copy of this many MiB before timing "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -464,6 +518,11 @@ def main() -> int:
         r = res["merge_mxfp8"]
         print(f"[bench] merge: bf16 {r['merge_bf16_ms']:.3f} ms, MX-FP8 {r['merge_mx_ms']:.3f} ms; "
               f"layer with the MX-FP8 merge {r['layer_ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    if not args.no_bwd and cfg.dtype == "bf16":
+        res["softmax_bwd"] = measure_bwd(cfg, t)
+        r = res["softmax_bwd"]
+        print(f"[bench] Softmax backward: {r['ms']:.3f} ms, kernels {r['kernel_ms']:.3f} ms, "
+              f"{r['achieved']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(res), flush=True)

@@ -69,3 +69,56 @@ def softmax_branch_bwd(Qf, Kf, Vf, g_s, dOhat, p: O.Params = O.DEFAULT):
             dK[f] += dKv[i * N:(i + 1) * N]
             dV[f] += dVv[i * N:(i + 1) * N]
     return dQ, dK, dV, dg
+
+
+def softmax_bwd_rows(q, k, v, g_s, dOhat, F: int, qrows, kframe: int | None, krows,
+                     p: O.Params = O.DEFAULT):
+    """The same gradients at chosen rows only, for checks at sizes where the
+    whole backward is too slow.  q, k, v, dOhat: [L, d] frame-major rows of
+    one head; g_s: [L].  Returns (dQ at qrows, dK and dV at krows, which must
+    all lie in frame kframe).  dK/dV need every query frame that sees
+    kframe in full (for their normalisers and Dq); by symmetry of the
+    visibility those are visible_frames(kframe)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    g = np.asarray(g_s, np.float64)
+    dOh = np.asarray(dOhat, np.float64)
+    L, dk_ = q.shape
+    N = L // F
+    scale = (1.0 / math.sqrt(dk_)) if p.softmax_scale is None else p.softmax_scale
+    Qf, Kf, Vf = (x.reshape(F, N, -1) for x in (q, k, v))
+
+    def frame_terms(t, rows_in_t):
+        fr = sorted(O.visible_frames(t, F, p))
+        Kv = np.concatenate([Kf[f] for f in fr])
+        Vv = np.concatenate([Vf[f] for f in fr])
+        Q = Qf[t][rows_in_t]
+        s = scale * (Q @ Kv.T)
+        P = np.exp(s - s.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        rows = t * N + np.asarray(rows_in_t)
+        dO = g[rows][:, None] * dOh[rows]
+        Dq = np.sum(dO * (P @ Vv), axis=1, keepdims=True)
+        return fr, Kv, Vv, Q, P, dO, Dq
+
+    qrows = np.asarray(qrows, np.int64)
+    dQ = np.zeros((len(qrows), dk_))
+    for t in np.unique(qrows // N):
+        sel = np.nonzero(qrows // N == t)[0]
+        fr, Kv, Vv, Q, P, dO, Dq = frame_terms(int(t), qrows[sel] % N)
+        dS = P * (dO @ Vv.T - Dq)
+        dQ[sel] = scale * (dS @ Kv)
+    krows = np.asarray(krows, np.int64)
+    dK = np.zeros((len(krows), dk_))
+    dV = np.zeros((len(krows), v.shape[1]))
+    if len(krows):
+        assert np.all(krows // N == kframe)
+        for t in sorted(O.visible_frames(kframe, F, p)):
+            fr, Kv, Vv, Q, P, dO, Dq = frame_terms(t, np.arange(N))
+            col = fr.index(kframe) * N + krows % N      # the sampled keys among t's keys
+            Pc = P[:, col]
+            dS = Pc * (dO @ v[krows].T - Dq)
+            dK += scale * (dS.T @ Q)
+            dV += Pc.T @ dO
+    return dQ, dK, dV

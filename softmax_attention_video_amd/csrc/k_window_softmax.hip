@@ -98,7 +98,6 @@ constexpr int kWinNW = 8;                  // waves per workgroup, 32 queries ea
 constexpr int kWinBQ = kWinNW * 32;        // queries per workgroup
 constexpr float kLazySum = 256.f;
 
-__device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
 template <int D, bool TEXT>
 __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArgs a) {

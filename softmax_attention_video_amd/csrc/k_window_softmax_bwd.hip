@@ -233,6 +233,373 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernels (D = 64, 128; N % 16 == 0), v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulation.  Tiles are staged global -> registers -> LDS one tile
+// ahead with one workgroup barrier per tile; rows past a span's end read as
+// zero through the buffer descriptors.
+//
+// dQ (query-stationary, 8 waves x 32 queries): per 32-key block
+//   S^T  = K Q^T        (A: K rows from LDS, B: the wave's Q fragments)
+//   dP^T = V dO^T       (A: V rows from LDS, B: the wave's dO fragments)
+//   dS^T = P^T (dP^T - Dq),  P^T = exp2(S^T scale log2e - lse log2e)
+//   dQ^T += K^T dS^T    (A: K^T rows from LDS, B: dS^T from registers)
+// K rows are loaded in key_perm order so a lane half holds 16 consecutive
+// keys of the block in register order, which is the B layout of the last
+// product; lse and Dq are per lane (one query per lane).
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  Geometry g;
+  SoftmaxWork w;
+  const bf16_t* q;      // [B,H,L,D]
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* dO;     // g_s * dOhat, [B,H,L,D]
+  const bf16_t* kt;     // K^T  [B,H,D,L]
+  const bf16_t* qt;     // Q^T  [B,H,D,L]
+  const bf16_t* dOt;    // dO^T [B,H,D,L]
+  const float* lse;     // [B,H,L], natural log
+  const float* Dq;      // [B,H,L]
+  bf16_t* dq;
+  bf16_t* dk;
+  bf16_t* dv;
+  float scale, scale_log2;
+};
+
+constexpr int kBwdQW = 8;          // dQ kernel: waves (32 queries each)
+constexpr int kBwdKW = 4;          // dK/dV kernel: waves (32 keys each)
+constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per staged tile (dK/dV)
+
+template <int D>
+__global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArgs a) {
+  constexpr int NT = kBwdQW * 64, BQ = kBwdQW * 32, BK = kBwdBK;
+  constexpr int KP = D + 8, TP = BK + 8;
+  constexpr int NKK = D / 16, NDB = D / 32, NB = BK / 32;
+  constexpr int RCH = BK * D / 8 / NT, TCH = D * BK / 8 / NT;   // 16-byte chunks per thread
+  static_assert(RCH * NT * 8 == BK * D && TCH * NT * 8 == D * BK, "tile split");
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BK * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][BK * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Kts[2][D * TP];
+  const Geometry& g = a.g;
+  Item it;
+  int q0;
+  if (!decode_item<false>(g, a.w, BQ, blockIdx.x, 0, it, q0)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const long long L = g.L;
+  const size_t hb = (size_t)it.bh * L * D;
+  const bf16_t* K = a.k + hb;
+  const bf16_t* V = a.v + hb;
+  const bf16_t* Kt = a.kt + hb;
+  const int qrow = q0 + wave * 32 + l32;
+  const bool qvalid = qrow < it.q_end;
+  bf16x8 qf[NKK], df[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (qvalid) {
+      x = ld16(a.q + hb + (size_t)qrow * D + kk * 16 + hg * 8);
+      y = ld16(a.dO + hb + (size_t)qrow * D + kk * 16 + hg * 8);
+    }
+    qf[kk] = as_bf16x8(x);
+    df[kk] = as_bf16x8(y);
+  }
+  const float lse2 = qvalid ? a.lse[(size_t)it.bh * L + qrow] * kLog2e : 0.f;
+  const float dqv = qvalid ? a.Dq[(size_t)it.bh * L + qrow] : 0.f;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
+  const SpanWalk<BK, 3> walk(it);
+  const uint32_t kt_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
+  u32x4 cr[2 * RCH + TCH];
+  auto load_tile = [&](int j) {
+    int ks, nk;
+    walk.tile(j, ks, nk);
+    const rsrc_t rk = make_rsrc(K + (size_t)ks * D, (uint32_t)nk * D * 2);
+    const rsrc_t rv = make_rsrc(V + (size_t)ks * D, (uint32_t)nk * D * 2);
+    const rsrc_t rt = make_rsrc(Kt + ks, kt_bytes - (uint32_t)ks * 2);
+#pragma unroll
+    for (int i = 0; i < RCH; ++i) {
+      const int c = tid + NT * i;
+      const uint32_t off = (uint32_t)((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
+      cr[i] = buf_ld16(rk, off);
+      cr[RCH + i] = buf_ld16(rv, off);
+    }
+#pragma unroll
+    for (int i = 0; i < TCH; ++i) {
+      const int c = tid + NT * i;
+      const int r = c / (BK / 8), c8 = c % (BK / 8);
+      cr[2 * RCH + i] = buf_ld16(rt, c8 * 8 < nk ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RCH; ++i) {
+      const int c = tid + NT * i;
+      const int off = (c / (D / 8)) * KP + (c % (D / 8)) * 8;
+      st16(&Ks[buf][off], cr[i]);
+      st16(&Vs[buf][off], cr[RCH + i]);
+    }
+#pragma unroll
+    for (int i = 0; i < TCH; ++i) {
+      const int c = tid + NT * i;
+      st16(&Kts[buf][(c / (BK / 8)) * TP + (c % (BK / 8)) * 8], cr[2 * RCH + i]);
+    }
+  };
+  const int rperm = key_perm(l32);
+  if (walk.n > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < walk.n; ++j) {
+    const int buf = j & 1;
+    int ks, nk;
+    walk.tile(j, ks, nk);
+    if (j + 1 < walk.n) load_tile(j + 1);
+    const bf16_t* Kb = Ks[buf];
+    const bf16_t* Vb = Vs[buf];
+    const bf16_t* Tb = Kts[buf];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x16 s = {}, dp = {};
+      const bf16_t* kr = Kb + (blk * 32 + rperm) * KP + hg * 8;
+      const bf16_t* vr = Vb + (blk * 32 + rperm) * KP + hg * 8;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = mfma32x32x16(as_bf16x8(ld16(kr + kk * 16)), qf[kk], s);
+        dp = mfma32x32x16(as_bf16x8(ld16(vr + kk * 16)), df[kk], dp);
+      }
+      const bool valid = blk * 32 + hg * 16 < nk;   // whole 16-key groups
+      bf16x8 pb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = valid ? fast_exp2(fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
+        pb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - dqv));
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const bf16x8 kf = as_bf16x8(ld16(Tb + (b * 32 + l32) * TP + blk * 32 + hg * 16 + h2 * 8));
+          acc[b] = mfma32x32x16(kf, pb[h2], acc[b]);
+        }
+    }
+    if (j + 1 < walk.n) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  if (!qvalid) return;
+  bf16_t* orow = a.dq + hb + (size_t)qrow * D;
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = b * 32 + 8 * i4 + 4 * hg;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[b][i4 * 4 + 0] * a.scale, acc[b][i4 * 4 + 1] * a.scale);
+      pk[1] = pack_bf16x2(acc[b][i4 * 4 + 2] * a.scale, acc[b][i4 * 4 + 3] * a.scale);
+      *reinterpret_cast<u32x2*>(orow + d) = pk;
+    }
+}
+
+// dK, dV (key-stationary, 4 waves x 32 keys; the item's frames are the keys,
+// its spans the queries that see them): per 32-query block
+//   S   = Q K^T         (A: Q rows from LDS in key_perm order, B: K fragments)
+//   dP  = dO V^T        (A: dO rows from LDS, B: V fragments)
+//   P = exp2(S scale log2e - lse log2e), dS = P (dP - Dq), per query register
+//   dV^T += dO^T P      (A: dO^T rows from LDS, B: P from registers)
+//   dK^T += Q^T dS      (A: Q^T rows from LDS, B: dS from registers)
+// A lane holds one key and 16 queries; the block's lse and Dq come from LDS
+// (queries past the span: lse = +inf, so P = 0).
+template <int D>
+__global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
+  constexpr int NT = kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
+  constexpr int KP = D + 8, TP = BQ + 8;
+  constexpr int NKK = D / 16, NDB = D / 32, NB = BQ / 32;
+  constexpr int RCH = BQ * D / 8 / NT, TCH = D * BQ / 8 / NT;
+  static_assert(RCH * NT * 8 == BQ * D && TCH * NT * 8 == D * BQ, "tile split");
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Ds[2][BQ * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Qts[2][D * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Dts[2][D * TP];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Dd[2][BQ];
+  const Geometry& g = a.g;
+  Item it;
+  int k0;
+  if (!decode_item<false>(g, a.w, BKEY, blockIdx.x, 0, it, k0)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const long long L = g.L;
+  const size_t hb = (size_t)it.bh * L * D;
+  const bf16_t* Q = a.q + hb;
+  const bf16_t* dO = a.dO + hb;
+  const bf16_t* Qt = a.qt + hb;
+  const bf16_t* dOt = a.dOt + hb;
+  const float* lse = a.lse + (size_t)it.bh * L;
+  const float* Dq = a.Dq + (size_t)it.bh * L;
+  const int krow = k0 + wave * 32 + l32;
+  const bool kvalid = krow < it.q_end;
+  bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (kvalid) {
+      x = ld16(a.k + hb + (size_t)krow * D + kk * 16 + hg * 8);
+      y = ld16(a.v + hb + (size_t)krow * D + kk * 16 + hg * 8);
+    }
+    kf[kk] = as_bf16x8(x);
+    vf[kk] = as_bf16x8(y);
+  }
+  f32x16 ak[NDB], av[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) {
+    ak[b] = f32x16{};
+    av[b] = f32x16{};
+  }
+  const SpanWalk<BQ, 3> walk(it);
+  const uint32_t t_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
+  u32x4 cr[2 * RCH + 2 * TCH];
+  float cl = 0.f, cd = 0.f;
+  auto load_tile = [&](int j) {
+    int qs, nq;
+    walk.tile(j, qs, nq);
+    const rsrc_t rq = make_rsrc(Q + (size_t)qs * D, (uint32_t)nq * D * 2);
+    const rsrc_t rd = make_rsrc(dO + (size_t)qs * D, (uint32_t)nq * D * 2);
+    const rsrc_t rqt = make_rsrc(Qt + qs, t_bytes - (uint32_t)qs * 2);
+    const rsrc_t rdt = make_rsrc(dOt + qs, t_bytes - (uint32_t)qs * 2);
+#pragma unroll
+    for (int i = 0; i < RCH; ++i) {
+      const int c = tid + NT * i;
+      const uint32_t off = (uint32_t)((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
+      cr[i] = buf_ld16(rq, off);
+      cr[RCH + i] = buf_ld16(rd, off);
+    }
+#pragma unroll
+    for (int i = 0; i < TCH; ++i) {
+      const int c = tid + NT * i;
+      const int r = c / (BQ / 8), c8 = c % (BQ / 8);
+      const uint32_t off = c8 * 8 < nq ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u;
+      cr[2 * RCH + i] = buf_ld16(rqt, off);
+      cr[2 * RCH + TCH + i] = buf_ld16(rdt, off);
+    }
+    if (tid < BQ) {
+      cl = tid < nq ? lse[qs + tid] * kLog2e : INFINITY;
+      cd = tid < nq ? Dq[qs + tid] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RCH; ++i) {
+      const int c = tid + NT * i;
+      const int off = (c / (D / 8)) * KP + (c % (D / 8)) * 8;
+      st16(&Qs[buf][off], cr[i]);
+      st16(&Ds[buf][off], cr[RCH + i]);
+    }
+#pragma unroll
+    for (int i = 0; i < TCH; ++i) {
+      const int c = tid + NT * i;
+      const int off = (c / (BQ / 8)) * TP + (c % (BQ / 8)) * 8;
+      st16(&Qts[buf][off], cr[2 * RCH + i]);
+      st16(&Dts[buf][off], cr[2 * RCH + TCH + i]);
+    }
+    if (tid < BQ) {
+      Ls[buf][tid] = cl;
+      Dd[buf][tid] = cd;
+    }
+  };
+  const int rperm = key_perm(l32);
+  if (walk.n > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < walk.n; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < walk.n) load_tile(j + 1);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x16 s = {}, dp = {};
+      const bf16_t* qr = Qs[buf] + (blk * 32 + rperm) * KP + hg * 8;
+      const bf16_t* dr = Ds[buf] + (blk * 32 + rperm) * KP + hg * 8;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = mfma32x32x16(as_bf16x8(ld16(qr + kk * 16)), kf[kk], s);
+        dp = mfma32x32x16(as_bf16x8(ld16(dr + kk * 16)), vf[kk], dp);
+      }
+      // lse and Dq of the 16 queries this lane half holds
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l4[i] = *reinterpret_cast<const f32x4*>(&Ls[buf][blk * 32 + hg * 16 + 4 * i]);
+        d4[i] = *reinterpret_cast<const f32x4*>(&Dd[buf][blk * 32 + hg * 16 + 4 * i]);
+      }
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[i], a.scale_log2, -l4[i >> 2][i & 3]));
+        pb[i >> 3][i & 7] = static_cast<__bf16>(p);
+        sb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - d4[i >> 2][i & 3]));
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const int col = blk * 32 + hg * 16 + h2 * 8;
+          const bf16x8 dtf = as_bf16x8(ld16(Dts[buf] + (b * 32 + l32) * TP + col));
+          const bf16x8 qtf = as_bf16x8(ld16(Qts[buf] + (b * 32 + l32) * TP + col));
+          av[b] = mfma32x32x16(dtf, pb[h2], av[b]);
+          ak[b] = mfma32x32x16(qtf, sb[h2], ak[b]);
+        }
+    }
+    if (j + 1 < walk.n) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  if (!kvalid) return;
+  bf16_t* krow_k = a.dk + hb + (size_t)krow * D;
+  bf16_t* krow_v = a.dv + hb + (size_t)krow * D;
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = b * 32 + 8 * i4 + 4 * hg;
+      u32x2 pk, pv;
+      pk[0] = pack_bf16x2(ak[b][i4 * 4 + 0] * a.scale, ak[b][i4 * 4 + 1] * a.scale);
+      pk[1] = pack_bf16x2(ak[b][i4 * 4 + 2] * a.scale, ak[b][i4 * 4 + 3] * a.scale);
+      pv[0] = pack_bf16x2(av[b][i4 * 4 + 0], av[b][i4 * 4 + 1]);
+      pv[1] = pack_bf16x2(av[b][i4 * 4 + 2], av[b][i4 * 4 + 3]);
+      *reinterpret_cast<u32x2*>(krow_k + d) = pk;
+      *reinterpret_cast<u32x2*>(krow_v + d) = pv;
+    }
+}
+
+bool softmax_bwd_mfma_ok(const Geometry& g) {
+  return (g.D == 64 || g.D == 128) && g.N % 16 == 0 && (long long)g.D * g.L * 2 <= 0x7FFFFFF0ll;
+}
+
+hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, const uint16_t* do_hm, const uint16_t* kt,
+                                   const uint16_t* qt, const uint16_t* dot, const float* lse,
+                                   const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                                   float scale, hipStream_t s) {
+  BwdArgs a;
+  a.g = g;
+  a.q = q; a.k = k; a.v = v; a.dO = do_hm; a.kt = kt; a.qt = qt; a.dOt = dot;
+  a.lse = lse; a.Dq = Dq; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  BwdArgs b = a;
+  a.w = window_work(g, kBwdQW * 32);
+  b.w = window_work(g, kBwdKW * 32);
+  if (a.w.grid == 0) return hipSuccess;
+  if (g.D == 128) {
+    softmax_bwd_dq_mfma_kernel<128><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
+    softmax_bwd_dkdv_mfma_kernel<128><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+  } else {
+    softmax_bwd_dq_mfma_kernel<64><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
+    softmax_bwd_dkdv_mfma_kernel<64><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+  }
+  return hipGetLastError();
+}
+
 template hipError_t launch_softmax_bwd_prep<float>(const Geometry&, const float*, const float*,
                                                    const float*, float*, float*, float*, hipStream_t);
 template hipError_t launch_softmax_bwd_prep<bf16_t>(const Geometry&, const bf16_t*, const bf16_t*,

@@ -106,9 +106,10 @@ Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt, bool mx) {
   return l;
 }
 
-// Workspace of the Softmax backward: g_s * dOhat in head-major order, and Dq.
+// Workspace of the Softmax backward: g_s * dOhat in head-major order, Dq,
+// and on the MFMA path K^T, Q^T and dO^T.
 struct BwdLayout {
-  size_t dohm, Dq, total;
+  size_t dohm, Dq, kt, qt, dot, total;
 };
 
 BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
@@ -119,6 +120,10 @@ BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
   auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
   l.dohm = take(rows * g.D * es);
   l.Dq = take(rows * 4);
+  const bool mf = dt == VDN_BF16 && vdn::softmax_bwd_mfma_ok(g);
+  l.kt = take(mf ? rows * g.D * es : 0);
+  l.qt = take(mf ? rows * g.D * es : 0);
+  l.dot = take(mf ? rows * g.D * es : 0);
   l.total = o;
   return l;
 }
@@ -597,9 +602,25 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
     uint16_t* dohm = (uint16_t*)(ws + lay.dohm);
     VDN_HIP(vdn::launch_softmax_bwd_prep<uint16_t>(g, (const uint16_t*)o, (const uint16_t*)d_out, g_s,
                                                    dohm, Dq, dg_s, s));
-    VDN_HIP(vdn::launch_softmax_bwd_simt<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k,
-                                                   (const uint16_t*)v, dohm, lse, Dq, (uint16_t*)dq,
-                                                   (uint16_t*)dk, (uint16_t*)dv, sc, s));
+    if (vdn::softmax_bwd_mfma_ok(g)) {
+      const long long BH = (long long)g.B * g.H;
+      uint16_t* kt = (uint16_t*)(ws + lay.kt);
+      uint16_t* qt = (uint16_t*)(ws + lay.qt);
+      uint16_t* dot = (uint16_t*)(ws + lay.dot);
+      VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)k, kt, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
+      VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)q, qt, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
+      VDN_HIP(vdn::launch_transpose_bf16(dohm, dot, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
+      VDN_HIP(timer_mark(s, true));
+      VDN_HIP(vdn::launch_softmax_bwd_mfma(g, (const uint16_t*)q, (const uint16_t*)k,
+                                           (const uint16_t*)v, dohm, kt, qt, dot, lse, Dq,
+                                           (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, sc, s));
+      VDN_HIP(timer_mark(s, false));
+    } else {
+      VDN_HIP(vdn::launch_softmax_bwd_simt<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k,
+                                                     (const uint16_t*)v, dohm, lse, Dq,
+                                                     (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv,
+                                                     sc, s));
+    }
   } else {
     float* dohm = (float*)(ws + lay.dohm);
     VDN_HIP(vdn::launch_softmax_bwd_prep<float>(g, (const float*)o, (const float*)d_out, g_s, dohm,

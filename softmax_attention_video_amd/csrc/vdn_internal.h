@@ -104,6 +104,14 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
                                    const T* do_hm, const float* lse, const float* Dq, T* dq, T* dk,
                                    T* dv, float scale, hipStream_t s);
 
+// bf16 MFMA path (D = 64, 128; N % 16 == 0): kt, qt, dot = K^T, Q^T, dO^T [B,H,D,L].
+bool softmax_bwd_mfma_ok(const Geometry& g);
+hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, const uint16_t* do_hm, const uint16_t* kt,
+                                   const uint16_t* qt, const uint16_t* dot, const float* lse,
+                                   const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                                   float scale, hipStream_t s);
+
 // ---- MX-FP8 merge (OCP MX: blocks of 32 along rows, E8M0 scales, E4M3) ----
 // src bf16 [rows, cols] -> codes[r * dst_ld + dst_col0 + c], scales[r * dst_ld/32 + (dst_col0 + c)/32].
 hipError_t launch_mx_quant_rows(const uint16_t* src, long long rows, int cols, uint8_t* codes,

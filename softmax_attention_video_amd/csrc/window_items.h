@@ -14,6 +14,11 @@
 
 namespace vdn {
 
+// Row order of a 32-row MFMA A operand such that, in the 32 x 32 result,
+// lane half g holds rows 16 g .. 16 g + 15 in register order: loading row
+// key_perm(l % 32) into lane l makes register i of half g row 16 g + i.
+__device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
+
 struct Item {
   int bh;            // b * H + h
   int q_begin, q_end;

@@ -96,3 +96,20 @@ def test_zero_gate_gives_zero_input_gradients():
     assert not dq.any() and not dk.any() and not dv.any()
     _, Oh, _ = O.softmax_branch(q, k, v, np.ones_like(g))
     np.testing.assert_allclose(dg, np.sum(Oh * do, axis=-1), rtol=1e-12)
+
+
+def test_rows_evaluation_matches_full():
+    F, N, d = 25, 3, 4
+    p = O.Params()
+    q, k, v, g, do = _case(F, N, d, 17)
+    dq, dk, dv, _ = SB.softmax_branch_bwd(q, k, v, g, do, p)
+    L = F * N
+    fl = lambda x: x.reshape(L, -1)
+    qrows = np.array([0, 1, 7, 40, 73, 74])
+    for kframe in (0, 7, 24):
+        krows = kframe * N + np.array([0, 2])
+        rq, rk, rv = SB.softmax_bwd_rows(fl(q), fl(k), fl(v), g.reshape(L), fl(do), F, qrows, kframe,
+                                         krows, p)
+        np.testing.assert_allclose(rq, fl(dq)[qrows], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rk, fl(dk)[krows], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rv, fl(dv)[krows], rtol=1e-10, atol=1e-12)

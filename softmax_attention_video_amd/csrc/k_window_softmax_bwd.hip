@@ -267,7 +267,7 @@ struct BwdArgs {
 };
 
 constexpr int kBwdQW = 8;          // dQ kernel: waves (32 queries each)
-constexpr int kBwdKW = 4;          // dK/dV kernel: waves (32 keys each)
+constexpr int kBwdKW = 4;          // dK/dV kernel: key blocks of 32 per workgroup (two waves each)
 constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per staged tile (dK/dV)
 
 template <int D>
@@ -401,18 +401,20 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
     }
 }
 
-// dK, dV (key-stationary, 4 waves x 32 keys; the item's frames are the keys,
-// its spans the queries that see them): per 32-query block
+// dK, dV (key-stationary; the item's frames are the keys, its spans the
+// queries that see them): 8 waves, two per block of 32 keys -- waves 0..3
+// accumulate dV, waves 4..7 dK -- so each wave holds one accumulator set and
+// two waves share each SIMD.  Per 32-query block:
 //   S   = Q K^T         (A: Q rows from LDS in key_perm order, B: K fragments)
-//   dP  = dO V^T        (A: dO rows from LDS, B: V fragments)
-//   P = exp2(S scale log2e - lse log2e), dS = P (dP - Dq), per query register
-//   dV^T += dO^T P      (A: dO^T rows from LDS, B: P from registers)
-//   dK^T += Q^T dS      (A: Q^T rows from LDS, B: dS from registers)
+//   P = exp2(S scale log2e - lse log2e)
+//   dV waves:  dV^T += dO^T P   (A: dO^T rows from LDS, B: P from registers)
+//   dK waves:  dP = dO V^T      (A: dO rows from LDS, B: V fragments)
+//              dS = P (dP - Dq),  dK^T += Q^T dS  (A: Q^T rows, B: dS)
 // A lane holds one key and 16 queries; the block's lse and Dq come from LDS
 // (queries past the span: lse = +inf, so P = 0).
 template <int D>
-__global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
-  constexpr int NT = kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
+__global__ __launch_bounds__(2 * kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
+  constexpr int NT = 2 * kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
   constexpr int KP = D + 8, TP = BQ + 8;
   constexpr int NKK = D / 16, NDB = D / 32, NB = BQ / 32;
   constexpr int RCH = BQ * D / 8 / NT, TCH = D * BQ / 8 / NT;
@@ -436,7 +438,8 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
   const bf16_t* dOt = a.dOt + hb;
   const float* lse = a.lse + (size_t)it.bh * L;
   const float* Dq = a.Dq + (size_t)it.bh * L;
-  const int krow = k0 + wave * 32 + l32;
+  const bool kwave = wave >= kBwdKW;          // this wave accumulates dK (else dV)
+  const int krow = k0 + (wave % kBwdKW) * 32 + l32;
   const bool kvalid = krow < it.q_end;
   bf16x8 kf[NKK], vf[NKK];
 #pragma unroll
@@ -444,17 +447,14 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
     u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (kvalid) {
       x = ld16(a.k + hb + (size_t)krow * D + kk * 16 + hg * 8);
-      y = ld16(a.v + hb + (size_t)krow * D + kk * 16 + hg * 8);
+      if (kwave) y = ld16(a.v + hb + (size_t)krow * D + kk * 16 + hg * 8);
     }
     kf[kk] = as_bf16x8(x);
     vf[kk] = as_bf16x8(y);
   }
-  f32x16 ak[NDB], av[NDB];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) {
-    ak[b] = f32x16{};
-    av[b] = f32x16{};
-  }
+  for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
   const SpanWalk<BQ, 3> walk(it);
   const uint32_t t_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
   u32x4 cr[2 * RCH + 2 * TCH];
@@ -517,57 +517,73 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
     if (j + 1 < walk.n) load_tile(j + 1);
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      f32x16 s = {}, dp = {};
       const bf16_t* qr = Qs[buf] + (blk * 32 + rperm) * KP + hg * 8;
       const bf16_t* dr = Ds[buf] + (blk * 32 + rperm) * KP + hg * 8;
+      const int col = blk * 32 + hg * 16;   // the 16 queries this lane half holds
+      if (!kwave) {
+        f32x16 s = {};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32x32x16(as_bf16x8(ld16(qr + kk * 16)), kf[kk], s);
-        dp = mfma32x32x16(as_bf16x8(ld16(dr + kk * 16)), vf[kk], dp);
-      }
-      // lse and Dq of the 16 queries this lane half holds
-      f32x4 l4[4], d4[4];
+        for (int kk = 0; kk < NKK; ++kk) s = mfma32x32x16(as_bf16x8(ld16(qr + kk * 16)), kf[kk], s);
+        bf16x8 pb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        l4[i] = *reinterpret_cast<const f32x4*>(&Ls[buf][blk * 32 + hg * 16 + 4 * i]);
-        d4[i] = *reinterpret_cast<const f32x4*>(&Dd[buf][blk * 32 + hg * 16 + 4 * i]);
-      }
-      bf16x8 pb[2], sb[2];
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][col + 4 * i4]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[i], a.scale_log2, -l4[i >> 2][i & 3]));
-        pb[i >> 3][i & 7] = static_cast<__bf16>(p);
-        sb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - d4[i >> 2][i & 3]));
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int b = 0; b < NDB; ++b) {
-          const int col = blk * 32 + hg * 16 + h2 * 8;
-          const bf16x8 dtf = as_bf16x8(ld16(Dts[buf] + (b * 32 + l32) * TP + col));
-          const bf16x8 qtf = as_bf16x8(ld16(Qts[buf] + (b * 32 + l32) * TP + col));
-          av[b] = mfma32x32x16(dtf, pb[h2], av[b]);
-          ak[b] = mfma32x32x16(qtf, sb[h2], ak[b]);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            pb[i >> 3][i & 7] = static_cast<__bf16>(fast_exp2(fmaf(s[i], a.scale_log2, -l4[e])));
+          }
         }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int b = 0; b < NDB; ++b) {
+            const bf16x8 dtf = as_bf16x8(ld16(Dts[buf] + (b * 32 + l32) * TP + col + h2 * 8));
+            acc[b] = mfma32x32x16(dtf, pb[h2], acc[b]);
+          }
+      } else {
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          s = mfma32x32x16(as_bf16x8(ld16(qr + kk * 16)), kf[kk], s);
+          dp = mfma32x32x16(as_bf16x8(ld16(dr + kk * 16)), vf[kk], dp);
+        }
+        bf16x8 sb[2];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][col + 4 * i4]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dd[buf][col + 4 * i4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const float p = fast_exp2(fmaf(s[i], a.scale_log2, -l4[e]));
+            sb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - d4[e]));
+          }
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int b = 0; b < NDB; ++b) {
+            const bf16x8 qtf = as_bf16x8(ld16(Qts[buf] + (b * 32 + l32) * TP + col + h2 * 8));
+            acc[b] = mfma32x32x16(qtf, sb[h2], acc[b]);
+          }
+      }
     }
     if (j + 1 < walk.n) store_tile(buf ^ 1);
     __syncthreads();
   }
   if (!kvalid) return;
-  bf16_t* krow_k = a.dk + hb + (size_t)krow * D;
-  bf16_t* krow_v = a.dv + hb + (size_t)krow * D;
+  bf16_t* orow = (kwave ? a.dk : a.dv) + hb + (size_t)krow * D;
+  const float sc = kwave ? a.scale : 1.f;
 #pragma unroll
   for (int b = 0; b < NDB; ++b)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d = b * 32 + 8 * i4 + 4 * hg;
-      u32x2 pk, pv;
-      pk[0] = pack_bf16x2(ak[b][i4 * 4 + 0] * a.scale, ak[b][i4 * 4 + 1] * a.scale);
-      pk[1] = pack_bf16x2(ak[b][i4 * 4 + 2] * a.scale, ak[b][i4 * 4 + 3] * a.scale);
-      pv[0] = pack_bf16x2(av[b][i4 * 4 + 0], av[b][i4 * 4 + 1]);
-      pv[1] = pack_bf16x2(av[b][i4 * 4 + 2], av[b][i4 * 4 + 3]);
-      *reinterpret_cast<u32x2*>(krow_k + d) = pk;
-      *reinterpret_cast<u32x2*>(krow_v + d) = pv;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[b][i4 * 4 + 0] * sc, acc[b][i4 * 4 + 1] * sc);
+      pk[1] = pack_bf16x2(acc[b][i4 * 4 + 2] * sc, acc[b][i4 * 4 + 3] * sc);
+      *reinterpret_cast<u32x2*>(orow + d) = pk;
     }
 }
 
@@ -592,10 +608,10 @@ hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const u
   if (a.w.grid == 0) return hipSuccess;
   if (g.D == 128) {
     softmax_bwd_dq_mfma_kernel<128><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv_mfma_kernel<128><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<128><<<b.w.grid, 2 * kBwdKW * 64, 0, s>>>(b);
   } else {
     softmax_bwd_dq_mfma_kernel<64><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv_mfma_kernel<64><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<64><<<b.w.grid, 2 * kBwdKW * 64, 0, s>>>(b);
   }
   return hipGetLastError();
 }

@@ -231,6 +231,15 @@ __global__ __launch_bounds__(kWinNW * 64) void window_softmax_mfma_kernel(WinArg
         pb[i >> 3][i & 7] = static_cast<__bf16>(p);
       }
     }
+    // Issue order for the scheduler: the next block's K fragment reads, then
+    // its QK^T MFMAs spread one per six VALU instructions of this block's
+    // exponentials, so the matrix core and the VALU of a wave overlap.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 LDS reads
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0); // 6 VALU
+    }
     if (__any(!(ls <= kLazySum))) {
       float m = s[0];
 #pragma unroll

@@ -126,6 +126,19 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
       // stage chunk ks of the next K step, request it for the one after
       store_piece(ks, (kt + 1) & 1);
       load_piece(ks, kt + 2);
+      // issue order: each of the next step's six fragment reads after one
+      // MFMA, then the LDS stores and the global loads between the last two
+      if (ks + 1 < NSUB) {
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);       // 2 LDS writes
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);       // 2 global loads
       __builtin_amdgcn_sched_barrier(0);
     }
     lds_barrier();

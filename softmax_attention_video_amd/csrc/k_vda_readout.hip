@@ -127,6 +127,7 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
   __shared__ __attribute__((aligned(16))) bf16_t mh[D * MP];
   __shared__ __attribute__((aligned(16))) bf16_t ml[D * MP];
   __shared__ float dfs[D], drs[D];
+  __shared__ __attribute__((aligned(16))) float gms[D];
 
   const int t = blockIdx.x % g.F;
   const int bh = blockIdx.x / g.F;
@@ -141,42 +142,53 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
     for (int f = t; f <= we; ++f) dr *= al[(size_t)f * D + k];
     dfs[k] = df;
     drs[k] = dr;
+    gms[k] = gamma ? gamma[k] : 1.f;
   }
   __syncthreads();
   const size_t DD = (size_t)D * D;
   const float* pf = P_fwd + ((size_t)bh * (g.C + 1) + i_f) * DD;
   const float* pr = P_rev + ((size_t)bh * (g.C + 1) + i_r) * DD;
-  for (int e4 = tid; e4 < D * D / 4; e4 += 256) {
-    const int k = e4 / (D / 4), j0 = (e4 % (D / 4)) * 4;
-    const f32x4 a4 = *reinterpret_cast<const f32x4*>(pf + (size_t)k * D + j0);
-    const f32x4 b4 = *reinterpret_cast<const f32x4*>(pr + (size_t)k * D + j0);
+  // M^T as bf16 hi + lo: each thread forms a pair of rows k, k + 1 of M for
+  // four columns and stores them as packed 32-bit pairs of M^T
+  for (int e = tid; e < (D / 2) * (D / 4); e += 256) {
+    const int k = 2 * (e / (D / 4)), j0 = (e % (D / 4)) * 4;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(pf + (size_t)k * D + j0);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(pf + (size_t)(k + 1) * D + j0);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(pr + (size_t)k * D + j0);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(pr + (size_t)(k + 1) * D + j0);
+    const float f0 = dfs[k], f1 = dfs[k + 1], r0 = drs[k], r1 = drs[k + 1];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float mv = dfs[k] * a4[c] + drs[k] * b4[c];
-      const bf16_t hi = f32_to_bf16(mv);
-      mh[(j0 + c) * MP + k] = hi;
-      ml[(j0 + c) * MP + k] = f32_to_bf16(mv - bf16_to_f32(hi));
+      const float m0 = f0 * a0[c] + r0 * b0[c];
+      const float m1 = f1 * a1[c] + r1 * b1[c];
+      const bf16_t h0 = f32_to_bf16(m0), h1 = f32_to_bf16(m1);
+      const bf16_t l0 = f32_to_bf16(m0 - bf16_to_f32(h0)), l1 = f32_to_bf16(m1 - bf16_to_f32(h1));
+      *reinterpret_cast<uint32_t*>(&mh[(j0 + c) * MP + k]) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      *reinterpret_cast<uint32_t*>(&ml[(j0 + c) * MP + k]) = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
   }
   __syncthreads();
 
-  float gm[NDB][16];
-#pragma unroll
-  for (int b = 0; b < NDB; ++b)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) gm[b][i] = gamma ? gamma[b * 32 + mfma32_row(i, hg)] : 1.f;
   const int bidx = bh / g.H, h = bh % g.H;
   const size_t tok0 = (size_t)bh * g.L + (size_t)t * g.N;
-  for (int n0 = wave * 32; n0 < g.N; n0 += 128) {
+  // q fragments of the wave's next 32 tokens are requested while the
+  // current ones are multiplied
+  bf16x8 qf[NKK];
+  auto load_q = [&](int n0, bf16x8* dst) {
     const int n = n0 + l32;
-    const bool valid = n < g.N;
-    bf16x8 qf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
-      if (valid) v = ld16(q + (tok0 + n) * D + kk * 16 + hg * 8);
-      qf[kk] = as_bf16x8(v);
+      if (n < g.N) v = ld16(q + (tok0 + n) * D + kk * 16 + hg * 8);
+      dst[kk] = as_bf16x8(v);
     }
+  };
+  load_q(wave * 32, qf);
+  for (int n0 = wave * 32; n0 < g.N; n0 += 128) {
+    const int n = n0 + l32;
+    const bool valid = n < g.N;
+    bf16x8 qn[NKK];
+    load_q(n0 + 128, qn);
     f32x16 o[NDB];
 #pragma unroll
     for (int b = 0; b < NDB; ++b) {
@@ -194,6 +206,8 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
 #pragma unroll
       for (int i = 0; i < 16; ++i) ss = fmaf(o[b][i], o[b][i], ss);
     ss = half_sum(ss);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = qn[kk];
     if (!valid) continue;
     const size_t l = (size_t)t * g.N + n;
     const float sc = g_l[(size_t)bh * g.L + l] * rsqrtf(ss / (float)D + eps);
@@ -202,9 +216,10 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&gms[b * 32 + 8 * i4 + 4 * hg]);
         u32x2 pk;
-        pk[0] = pack_bf16x2(o[b][i4 * 4 + 0] * sc * gm[b][i4 * 4 + 0], o[b][i4 * 4 + 1] * sc * gm[b][i4 * 4 + 1]);
-        pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc * gm[b][i4 * 4 + 2], o[b][i4 * 4 + 3] * sc * gm[b][i4 * 4 + 3]);
+        pk[0] = pack_bf16x2(o[b][i4 * 4 + 0] * sc * gm[0], o[b][i4 * 4 + 1] * sc * gm[1]);
+        pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc * gm[2], o[b][i4 * 4 + 3] * sc * gm[3]);
         *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * i4 + 4 * hg) = pk;
       }
   }

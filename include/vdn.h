@@ -240,6 +240,50 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
 size_t vdn_softmax_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
 
 /*
+ * vda_bwd -- gradients of the linear (VDA) branch output Ohat_l with respect
+ * to every input of the branch.
+ *
+ * Paper: the Video Delta Attention section (frame statistics A = K^T B K,
+ * W = K^T B V and the frame update S_f = (I + A_f)^{-1}(diag(alpha_f) S_{f-1}
+ * + W_f)), the method's bidirectional linear attention (text-initialised
+ * scans, gather + decay bridge, sum of the two readouts) and branch
+ * calibration (RMSNorm + gate) define the forward of vdn_attn_fwd's linear
+ * branch; the experiments train through it.  These are its chain-rule
+ * gradients.  The call recomputes the forward scans itself (nothing from a
+ * forward call is needed).
+ *
+ *  q, k, v               [B,H,L,d] dt     the forward's inputs
+ *  beta, g_l             [B,H,L]   float
+ *  alpha                 [B,H,F,d] float  decay gates, in (0, 1]
+ *  k_text, v_text        [B,H,T,d] dt     (required when T > 0)
+ *  beta_text             [B,H,T]   float  (required when T > 0)
+ *  gamma                 [d]       float  RMSNorm weight, NULL = 1
+ *  d_out                 [B,L,H,d] dt     gradient of Ohat_l
+ *  dq, dk, dv            [B,H,L,d] dt     outputs, fully written (zero dk,
+ *                                          dv, dbeta on anchor frames, which
+ *                                          the scans do not write)
+ *  dbeta                 [B,H,L]   float  output
+ *  dalpha                [B,H,F,d] float  output
+ *  dk_text, dv_text      [B,H,T,d] dt     outputs (required when T > 0)
+ *  dbeta_text            [B,H,T]   float  output (required when T > 0)
+ *  dg_l                  [B,H,L]   float  output, nullable
+ *  dgamma                [d]       float  output, nullable (summed over
+ *                                          batch, heads and tokens)
+ *  workspace             vda_bwd_workspace_bytes(dims, p, dt) bytes
+ * Errors as for vdn_attn_fwd.  Deterministic (no atomics).
+ */
+vdn_status vda_bwd(const void* q, const void* k, const void* v, const float* beta,
+                   const float* alpha, const void* k_text, const void* v_text,
+                   const float* beta_text, const float* g_l, const float* gamma, const void* d_out,
+                   void* dq, void* dk, void* dv, float* dbeta, float* dalpha, void* dk_text,
+                   void* dv_text, float* dbeta_text, float* dg_l, float* dgamma, void* workspace,
+                   size_t workspace_bytes, const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                   void* stream);
+
+/* Workspace bytes of vda_bwd (0 if the arguments are invalid). */
+size_t vda_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
+
+/*
  * vdn_mx_quantize -- MX-FP8 quantization of bf16 rows (the operand format of
  * the MX-FP8 merge; e.g. to inspect it or to quantize weights ahead of time).
  *

@@ -35,7 +35,8 @@ EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_window_softmax_fwd", "vdn_workspace_bytes", "vdn_window_plan",
            "vdn_status_string", "vdn_last_error", "vdn_timer_enable", "vdn_timer_read",
            "vdn_timer_disable", "vda_prep_default_params", "vda_prep_fwd", "vdn_merge_fwd",
-           "vdn_mx_quantize", "vdn_window_softmax_bwd", "vdn_softmax_bwd_workspace_bytes")
+           "vdn_mx_quantize", "vdn_window_softmax_bwd", "vdn_softmax_bwd_workspace_bytes",
+           "vda_bwd", "vda_bwd_workspace_bytes")
 
 
 class VdnError(RuntimeError):
@@ -146,6 +147,10 @@ def lib() -> ctypes.CDLL:
     L.vdn_window_softmax_bwd.restype = I
     L.vdn_softmax_bwd_workspace_bytes.argtypes = [dp, pp, I]
     L.vdn_softmax_bwd_workspace_bytes.restype = S
+    L.vda_bwd.argtypes = [P] * 22 + [S, dp, pp, I, P]
+    L.vda_bwd.restype = I
+    L.vda_bwd_workspace_bytes.argtypes = [dp, pp, I]
+    L.vda_bwd_workspace_bytes.restype = S
     _lib = L
     return L
 
@@ -419,6 +424,66 @@ def window_softmax_bwd(q, k, v, o, lse, d_out, F: int, g_s=None, want_dg: bool =
         ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
         ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
     return dq, dk, dv, dg
+
+
+def vda_bwd(q, k, v, beta, alpha, k_text, v_text, beta_text, g_l, d_out, gamma=None,
+            want_dg: bool = False, want_dgamma: bool = False, params: Params | None = None,
+            workspace=None, stream=None):
+    """Gradients of the linear (VDA) branch output Ohat_l (vda_bwd).
+
+    Inputs as for attn_fwd (q, k, v [B,H,L,d]; beta, g_l [B,H,L]; alpha
+    [B,H,F,d]; k_text, v_text [B,H,T,d]; beta_text [B,H,T]; gamma [d] or
+    None); d_out [B,L,H,d] the gradient of Ohat_l.  Returns a dict with dq,
+    dk, dv [B,H,L,d]; dbeta [B,H,L]; dalpha [B,H,F,d]; dk_text, dv_text
+    [B,H,T,d]; dbeta_text [B,H,T]; dg_l [B,H,L] and dgamma [d] when asked."""
+    torch = _torch()
+    params = params or Params()
+    B, H, L, d = q.shape
+    F = alpha.shape[2]
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    T = k_text.shape[2]
+    dt = q.dtype
+    code = _dtype_code(q)
+    dev = q.device
+    f32 = torch.float32
+    dims = Dims(B, H, F, L // F, T, d, d, H * d)
+    p = params.c()
+    need = int(lib().vda_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p), code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace of {workspace.numel()} bytes < {need}")
+    out = dict(dq=torch.empty((B, H, L, d), dtype=dt, device=dev),
+               dk=torch.empty((B, H, L, d), dtype=dt, device=dev),
+               dv=torch.empty((B, H, L, d), dtype=dt, device=dev),
+               dbeta=torch.empty((B, H, L), dtype=f32, device=dev),
+               dalpha=torch.empty((B, H, F, d), dtype=f32, device=dev),
+               dk_text=torch.empty((B, H, T, d), dtype=dt, device=dev),
+               dv_text=torch.empty((B, H, T, d), dtype=dt, device=dev),
+               dbeta_text=torch.empty((B, H, T), dtype=f32, device=dev),
+               dg_l=torch.empty((B, H, L), dtype=f32, device=dev) if want_dg else None,
+               dgamma=torch.empty((d,), dtype=f32, device=dev) if want_dgamma else None)
+    tx = T > 0
+    _check(lib().vda_bwd(
+        _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
+        _ptr(v, "v", dt, (B, H, L, d), dev), _ptr(beta, "beta", f32, (B, H, L), dev),
+        _ptr(alpha, "alpha", f32, (B, H, F, d), dev),
+        _ptr(k_text if tx else None, "k_text", dt, (B, H, T, d), dev, allow_none=True),
+        _ptr(v_text if tx else None, "v_text", dt, (B, H, T, d), dev, allow_none=True),
+        _ptr(beta_text if tx else None, "beta_text", f32, (B, H, T), dev, allow_none=True),
+        _ptr(g_l, "g_l", f32, (B, H, L), dev),
+        _ptr(gamma, "gamma", f32, (d,), dev, allow_none=True),
+        _ptr(d_out, "d_out", dt, (B, L, H, d), dev),
+        _ptr(out["dq"], "dq"), _ptr(out["dk"], "dk"), _ptr(out["dv"], "dv"),
+        _ptr(out["dbeta"], "dbeta"), _ptr(out["dalpha"], "dalpha"),
+        _ptr(out["dk_text"] if tx else None, "dk_text", allow_none=True),
+        _ptr(out["dv_text"] if tx else None, "dv_text", allow_none=True),
+        _ptr(out["dbeta_text"] if tx else None, "dbeta_text", allow_none=True),
+        _ptr(out["dg_l"], "dg_l", allow_none=True), _ptr(out["dgamma"], "dgamma", allow_none=True),
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+        ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return out
 
 
 def merge_fwd(ohat_s, ohat_l, W_s, W_l, F: int, params: Params | None = None, out=None,

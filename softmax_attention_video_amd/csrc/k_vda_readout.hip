@@ -20,19 +20,6 @@
 
 namespace vdn {
 
-__device__ __forceinline__ void readout_indices(const Geometry& g, int t, int& i_f, int& ws,
-                                                int& i_r, int& we) {
-  if (g.anchors && (t == 0 || t == g.F - 1)) {
-    i_f = 0; ws = 0; i_r = g.C; we = g.F - 1;
-    return;
-  }
-  const int c = t / g.cf;
-  i_f = c - g.wc < 0 ? 0 : c - g.wc;
-  ws = i_f * g.cf;
-  i_r = c + g.wc + 1 > g.C ? g.C : c + g.wc + 1;
-  we = (i_r * g.cf < g.F ? i_r * g.cf : g.F) - 1;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void vda_readout_simt_kernel(Geometry g, const T* __restrict__ q,
                                                                const float* __restrict__ alpha,

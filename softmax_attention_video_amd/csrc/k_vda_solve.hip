@@ -42,6 +42,7 @@ struct SolveArgs {
   float* Tf;
   float* Uf;
   float* S_text;
+  float* Xf;      // optional: (I + A)^{-1} per frame, text frame last [B,H,F+1,D,D]
 };
 
 struct GJShared {
@@ -120,14 +121,22 @@ __device__ __forceinline__ void gauss_jordan(float (&m)[D / 16][D / 16], float (
   }
 }
 
-// Write T = X diag(alpha), U = X W for a video frame, or S_text = X W.
+// Write T = X diag(alpha), U = X W for a video frame, or S_text = X W; and
+// X itself when Xf is set (the backward pass solves with it).
 template <int D>
 __device__ __forceinline__ void emit_solution(const Geometry& g, const float* alpha, float* Tf,
-                                              float* Uf, float* S_text, int bh, int fr, bool text,
-                                              const float (&m)[D / 16][D / 16],
+                                              float* Uf, float* S_text, float* Xf, int bh, int fr,
+                                              bool text, const float (&m)[D / 16][D / 16],
                                               const float (&w)[D / 16][D / 16], int tr, int tc) {
   constexpr int R = D / 16;
   const size_t DD = (size_t)D * D;
+  if (Xf) {
+    float* X = Xf + ((size_t)bh * (g.F + 1) + fr) * DD;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int j = 0; j < R; ++j) X[(size_t)(tr * R + i) * D + tc * R + j] = m[i][j];
+  }
   if (text) {
     float* S = S_text + (size_t)bh * DD;
 #pragma unroll
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(256) void vda_frame_solve_kernel(SolveArgs<T> a) {
     for (int i = 0; i < R; ++i) m[i][i] += 1.f;
   }
   gauss_jordan<D>(m, w, sh, tr, tc);
-  emit_solution<D>(g, a.alpha, a.Tf, a.Uf, a.S_text, bh, fr, text, m, w, tr, tc);
+  emit_solution<D>(g, a.alpha, a.Tf, a.Uf, a.S_text, a.Xf, bh, fr, text, m, w, tr, tc);
 }
 
 // ---------------------------------------------------------------------------
@@ -386,15 +395,15 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
     for (int i = 0; i < R; ++i) m[i][i] += 1.f;
   }
   gauss_jordan<D>(m, w, sh, tr, tc);
-  emit_solution<D>(g, a.alpha, a.Tf, a.Uf, a.S_text, bh, fr, text, m, w, tr, tc);
+  emit_solution<D>(g, a.alpha, a.Tf, a.Uf, a.S_text, a.Xf, bh, fr, text, m, w, tr, tc);
 }
 
 template <typename T>
 hipError_t launch_vda_frame_solve(const Geometry& g, const T* k, const T* v, const float* beta,
                                   const float* alpha, const T* k_text, const T* v_text,
                                   const float* beta_text, float* Tf, float* Uf, float* S_text,
-                                  hipStream_t s) {
-  SolveArgs<T> a{g, k, v, beta, alpha, k_text, v_text, beta_text, Tf, Uf, S_text};
+                                  hipStream_t s, float* Xf) {
+  SolveArgs<T> a{g, k, v, beta, alpha, k_text, v_text, beta_text, Tf, Uf, S_text, Xf};
   const unsigned grid = (unsigned)(g.B * g.H * (g.F + 1));
   switch (g.D) {
     case 16: vda_frame_solve_kernel<T, 16><<<grid, 256, 0, s>>>(a); break;
@@ -411,8 +420,8 @@ hipError_t launch_vda_frame_solve<bf16_t>(const Geometry& g, const bf16_t* k, co
                                           const float* beta, const float* alpha,
                                           const bf16_t* k_text, const bf16_t* v_text,
                                           const float* beta_text, float* Tf, float* Uf,
-                                          float* S_text, hipStream_t s) {
-  SolveArgs<bf16_t> a{g, k, v, beta, alpha, k_text, v_text, beta_text, Tf, Uf, S_text};
+                                          float* S_text, hipStream_t s, float* Xf) {
+  SolveArgs<bf16_t> a{g, k, v, beta, alpha, k_text, v_text, beta_text, Tf, Uf, S_text, Xf};
   const unsigned grid = (unsigned)(g.B * g.H * (g.F + 1));
   switch (g.D) {
     case 16: vda_frame_solve_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(a); break;
@@ -427,6 +436,6 @@ hipError_t launch_vda_frame_solve<bf16_t>(const Geometry& g, const bf16_t* k, co
 template hipError_t launch_vda_frame_solve<float>(const Geometry&, const float*, const float*,
                                                   const float*, const float*, const float*,
                                                   const float*, const float*, float*, float*,
-                                                  float*, hipStream_t);
+                                                  float*, hipStream_t, float*);
 
 }  // namespace vdn

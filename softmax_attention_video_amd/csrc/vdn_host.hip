@@ -128,6 +128,39 @@ BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
   return l;
 }
 
+// Workspace of the linear-branch backward: the forward recompute (frame maps,
+// inverses, chunk maps, boundary states) and the adjoint buffers (fp32).
+struct VdaBwdLayout {
+  size_t Tf, Uf, Xf, St, Tc, Uc, Pf, Pr, G, Dbr, dDbr, dgp, dP, mu, Sst, Zst, ZT, Rscr, total;
+};
+
+VdaBwdLayout vda_bwd_layout(const vdn::Geometry& g) {
+  const size_t BH = (size_t)g.B * g.H, DD = (size_t)g.D * g.D, F = g.F, C = g.C;
+  VdaBwdLayout l{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+  l.Tf = take(BH * F * DD * 4);
+  l.Uf = take(BH * F * DD * 4);
+  l.Xf = take(BH * (F + 1) * DD * 4);
+  l.St = take(BH * DD * 4);
+  l.Tc = take(BH * 2 * C * DD * 4);
+  l.Uc = take(BH * 2 * C * DD * 4);
+  l.Pf = take(BH * (C + 1) * DD * 4);
+  l.Pr = take(BH * (C + 1) * DD * 4);
+  l.G = take(BH * F * DD * 4);
+  l.Dbr = take(BH * 2 * F * g.D * 4);
+  l.dDbr = take(BH * 2 * F * g.D * 4);
+  l.dgp = take(BH * F * g.D * 4);
+  l.dP = take(BH * 2 * (C + 1) * DD * 4);
+  l.mu = take(BH * 2 * (C + 1) * DD * 4);
+  l.Sst = take(BH * 2 * (F + 1) * DD * 4);
+  l.Zst = take(BH * 2 * F * DD * 4);
+  l.ZT = take(BH * DD * 4);
+  l.Rscr = take(BH * F * g.D * 4);
+  l.total = o;
+  return l;
+}
+
 bool use_mx(const vdn_params* p, vdn_dtype dt) { return p->merge_mxfp8 == 1 && dt == VDN_BF16; }
 
 vdn_params defaults() {
@@ -629,6 +662,70 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
                                                 dohm, lse, Dq, (float*)dq, (float*)dk, (float*)dv,
                                                 sc, s));
   }
+  return VDN_OK;
+}
+
+size_t vda_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
+  vdn::Geometry g;
+  if (check_geometry(dims, p, dt, &g) != VDN_OK) return 0;
+  return vda_bwd_layout(g).total;
+}
+
+vdn_status vda_bwd(const void* q, const void* k, const void* v, const float* beta,
+                   const float* alpha, const void* k_text, const void* v_text,
+                   const float* beta_text, const float* g_l, const float* gamma, const void* d_out,
+                   void* dq, void* dk, void* dv, float* dbeta, float* dalpha, void* dk_text,
+                   void* dv_text, float* dbeta_text, float* dg_l, float* dgamma, void* workspace,
+                   size_t workspace_bytes, const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                   void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(q); NEED(k); NEED(v); NEED(beta); NEED(alpha); NEED(g_l); NEED(d_out);
+  NEED(dq); NEED(dk); NEED(dv); NEED(dbeta); NEED(dalpha);
+  if (g.T > 0) {
+    NEED(k_text); NEED(v_text); NEED(beta_text); NEED(dk_text); NEED(dv_text); NEED(dbeta_text);
+  }
+  const VdaBwdLayout lay = vda_bwd_layout(g);
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != VDN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  auto fp = [&](size_t off) { return (float*)(ws + off); };
+  // forward recompute: frame maps and inverses, chunk maps, boundary states
+  if (dt == VDN_BF16)
+    VDN_HIP(vdn::launch_vda_frame_solve<uint16_t>(g, (const uint16_t*)k, (const uint16_t*)v, beta, alpha,
+                                                  (const uint16_t*)k_text, (const uint16_t*)v_text,
+                                                  beta_text, fp(lay.Tf), fp(lay.Uf), fp(lay.St), s,
+                                                  fp(lay.Xf)));
+  else
+    VDN_HIP(vdn::launch_vda_frame_solve<float>(g, (const float*)k, (const float*)v, beta, alpha,
+                                               (const float*)k_text, (const float*)v_text, beta_text,
+                                               fp(lay.Tf), fp(lay.Uf), fp(lay.St), s, fp(lay.Xf)));
+  VDN_HIP(vdn::launch_vda_chunk_compose(g, fp(lay.Tf), fp(lay.Uf), fp(lay.Tc), fp(lay.Uc), 3, s));
+  VDN_HIP(vdn::launch_vda_chunk_scan(g, fp(lay.Tc), fp(lay.Uc), fp(lay.St), p->text_init_scale,
+                                     fp(lay.Pf), fp(lay.Pr), s));
+  vdn::VdaBwdPtrs bp{beta, alpha, beta_text, g_l, gamma,
+                     fp(lay.Tf), fp(lay.Uf), fp(lay.Pf), fp(lay.Pr), fp(lay.St), fp(lay.Xf), fp(lay.Tc),
+                     fp(lay.G), fp(lay.Dbr), fp(lay.dDbr), fp(lay.dgp), fp(lay.dP), fp(lay.mu),
+                     fp(lay.Sst), fp(lay.Zst), fp(lay.ZT), fp(lay.Rscr),
+                     dbeta, dalpha, dbeta_text, dg_l, dgamma};
+  VDN_HIP(timer_mark(s, true));
+  if (dt == VDN_BF16)
+    VDN_HIP(vdn::launch_vda_bwd<uint16_t>(g, bp, (const uint16_t*)q, (const uint16_t*)k,
+                                          (const uint16_t*)v, (const uint16_t*)k_text,
+                                          (const uint16_t*)v_text, (const uint16_t*)d_out,
+                                          (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv,
+                                          (uint16_t*)dk_text, (uint16_t*)dv_text, p->rms_eps,
+                                          p->text_init_scale, s));
+  else
+    VDN_HIP(vdn::launch_vda_bwd<float>(g, bp, (const float*)q, (const float*)k, (const float*)v,
+                                       (const float*)k_text, (const float*)v_text,
+                                       (const float*)d_out, (float*)dq, (float*)dk, (float*)dv,
+                                       (float*)dk_text, (float*)dv_text, p->rms_eps,
+                                       p->text_init_scale, s));
+  VDN_HIP(timer_mark(s, false));
   return VDN_OK;
 }
 

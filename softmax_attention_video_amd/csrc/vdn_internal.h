@@ -18,6 +18,24 @@ struct Geometry {
   int Ts;        // text keys inside the Softmax branch (0 = video keys only)
 };
 
+// Where query frame t reads the chunk-boundary states and its decay bridge:
+// P_fwd[i_f] decayed over frames ws..t and P_rev[i_r] over t..we.  A
+// non-anchor frame in chunk c reads the states just outside its window
+// (i_f = max(c - wc, 0), i_r = min(c + wc + 1, C)); an anchor frame reads
+// the text-only ends (0 and C) over the whole clip.
+__host__ __device__ inline void readout_indices(const Geometry& g, int t, int& i_f, int& ws,
+                                                int& i_r, int& we) {
+  if (g.anchors && (t == 0 || t == g.F - 1)) {
+    i_f = 0; ws = 0; i_r = g.C; we = g.F - 1;
+    return;
+  }
+  const int c = t / g.cf;
+  i_f = c - g.wc < 0 ? 0 : c - g.wc;
+  ws = i_f * g.cf;
+  i_r = c + g.wc + 1 > g.C ? g.C : c + g.wc + 1;
+  we = (i_r * g.cf < g.F ? i_r * g.cf : g.F) - 1;
+}
+
 // Column pitch of the transposed values V^T [D, Lp] of one head on the MFMA
 // Softmax path: the L video keys, then the Ts text keys, zero-padded to a
 // multiple of 16 columns.
@@ -58,12 +76,14 @@ hipError_t launch_window_softmax_simt(const Geometry& g, const T* q, const T* k,
 bool window_softmax_mfma_ok(const Geometry& g);
 
 // ---- VDA frame statistics + solve (per frame and the text frame) ----
-// Tf [B,H,F,D,D], Uf [B,H,F,D,D], S_text [B,H,D,D] (all fp32).
+// Tf [B,H,F,D,D], Uf [B,H,F,D,D], S_text [B,H,D,D] (all fp32); Xf (nullable)
+// [B,H,F+1,D,D] receives (I + A)^{-1} of every non-anchor frame and of the
+// text frame (index F).
 template <typename T>
 hipError_t launch_vda_frame_solve(const Geometry& g, const T* k, const T* v, const float* beta,
                                   const float* alpha, const T* k_text, const T* v_text,
                                   const float* beta_text, float* Tf, float* Uf, float* S_text,
-                                  hipStream_t s);
+                                  hipStream_t s, float* Xf = nullptr);
 
 // ---- chunk composition and chunk prefix scans ----
 // Tc, Uc [B,H,2,C,D,D] (dir 0 = forward, 1 = reverse)
@@ -80,6 +100,21 @@ template <typename T>
 hipError_t launch_vda_readout(const Geometry& g, const T* q, const float* alpha,
                               const float* P_fwd, const float* P_rev, const float* g_l,
                               const float* gamma, float eps, T* out, hipStream_t s);
+
+// ---- linear-branch backward ----
+// Workspace and fp32 arguments of launch_vda_bwd (device pointers).  The
+// forward recompute (Tf, Uf, Pf, Pr, St, Xf, Tc) must be in place before the
+// launch; the rest is scratch or output.
+struct VdaBwdPtrs {
+  const float *beta, *alpha, *beta_text, *g_l, *gamma;
+  const float *Tf, *Uf, *Pf, *Pr, *St, *Xf, *Tc;
+  float *G, *Dbr, *dDbr, *dgp, *dP, *mu, *Sst, *Zst, *ZT, *Rscr;
+  float *dbeta, *dalpha, *dbeta_text, *dg_l, *dgamma;
+};
+template <typename T>
+hipError_t launch_vda_bwd(const Geometry& g, const VdaBwdPtrs& p, const T* q, const T* k, const T* v,
+                          const T* k_text, const T* v_text, const T* d_out, T* dq, T* dk, T* dv,
+                          T* dk_text, T* dv_text, float eps, float init_scale, hipStream_t s);
 
 // ---- merge ----
 // out[M,Dm] = A0[M,K] W0[K,Dm] + A1[M,K] W1[K,Dm]   (bf16 path via W^T)

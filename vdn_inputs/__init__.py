@@ -33,7 +33,7 @@ import numpy as np
 # tensor ids of the seed sequence
 _ID = dict(q=0, k=1, v=2, beta=3, alpha=4, k_text=5, v_text=6, beta_text=7,
            g_s=8, g_l=9, W_s=10, W_l=11, dup=12, prep_q=13, prep_k=14, prep_v=15,
-           prep_ws=16, prep_wt=17, d_out=18)
+           prep_ws=16, prep_wt=17, d_out=18, d_out_l=19)
 
 # latent grid (rows x columns) of one frame for each configuration, N = rows * columns
 GRIDS = {"tiny": (4, 4), "small": (16, 16), "medium": (24, 16), "h3": (48, 32), "long": (32, 24)}
@@ -247,12 +247,14 @@ def prep_inputs(cfg: Config, threads: int | None = None) -> dict:
     return out
 
 
-def grad_output(cfg: Config) -> np.ndarray:
-    """Seeded gradient of the gated Softmax output, dOhat [B, L, H, d] ~ N(0, 1),
-    rounded to cfg.dtype (the output layout of the branch)."""
+def grad_output(cfg: Config, branch: str = "s") -> np.ndarray:
+    """Seeded gradient of a gated branch output, dOhat [B, L, H, d] ~ N(0, 1),
+    rounded to cfg.dtype (the output layout of the branch); branch "s"
+    (Softmax) or "l" (linear) draws an independent stream."""
+    tid = {"s": "d_out", "l": "d_out_l"}[branch]
     out = np.empty((cfg.B, cfg.L, cfg.H, cfg.d), np.float32)
     for b in range(cfg.B):
         for h in range(cfg.H):
-            out[b, :, h] = _store(cfg, _normal(cfg, "d_out", b, h, (cfg.L, cfg.d)))
+            out[b, :, h] = _store(cfg, _normal(cfg, tid, b, h, (cfg.L, cfg.d)))
     return out
 

@@ -40,6 +40,8 @@
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
+#include <type_traits>
+
 namespace vdn {
 
 namespace {
@@ -251,6 +253,271 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_kernel(VdaBwdArgs<T> a) {
       float s = 0.f;
       for (int r = 0; r < TOK; ++r) s += Qs[r][c];
       a.dgp[((size_t)bh * g.F + t) * D + c] = s;
+    }
+  }
+}
+
+// bf16 kernel (D = 64, 128) on v_mfma_f32_32x32x16_bf16.  Wave w owns the
+// channel block vb = w % (D/32) of a 32-token sub-tile w / (D/32):
+//   O^T  = M^T Q^T   (rows v of its block; M^T rows as bf16 hi + lo fragments,
+//                     kept in registers for the whole frame),
+//   the RMSNorm / gate adjoint (per-token sums exchanged through LDS),
+//   dq^T = M dO^T    (rows k of block vb; M rows as hi + lo fragments; dO of
+//                     every channel block from LDS, hi + lo),
+//   G   += Q^T dO    (its G blocks, contracted over the step's tokens from
+//                     transposed Q and dO tiles in LDS).
+// At the end G goes to memory and the bridge adjoints are row sums of
+// G * P; dgamma partials are reduced through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf16_t> a) {
+  constexpr int NB = D / 32, NKK = D / 16;
+  constexpr int SUBT = 4 / NB, TPS = 32 * SUBT;
+  constexpr int QP = TPS + 8, DP = D + 8;       // pitches (bf16) of the transposed / row tiles
+  constexpr int NGB = NB * NB / 4;              // G blocks per wave
+  struct Tiles {
+    bf16_t qt[D * QP];        // Q^T of the step's tokens
+    bf16_t dth[D * QP];       // dO^T, hi / lo
+    bf16_t dtl[D * QP];
+    bf16_t doh[TPS * DP];     // dO, hi / lo
+    bf16_t dol[TPS * DP];
+  };
+  __shared__ __attribute__((aligned(16))) union {
+    Tiles t;
+    float pd[D * (D + 1)];    // G at the end of the frame
+  } u;
+  __shared__ float gsum[SUBT][D][33];
+  __shared__ float red1[4][32], red2[4][32][2];
+  __shared__ float dfs[D], drs[D];
+  __shared__ __attribute__((aligned(16))) float gms[D];
+
+  const Geometry& g = a.g;
+  const int t = blockIdx.x % g.F;
+  const int bh = blockIdx.x / g.F;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int vb = wave % NB, ts = wave / NB;
+  const size_t DD = (size_t)D * D;
+  int i_f, ws, i_r, we;
+  readout_indices(g, t, i_f, ws, i_r, we);
+  const float* al = a.alpha + (size_t)bh * g.F * D;
+  for (int c = tid; c < D; c += 256) {
+    float df = 1.f, dr = 1.f;
+    for (int f = ws; f <= t; ++f) df *= al[(size_t)f * D + c];
+    for (int f = t; f <= we; ++f) dr *= al[(size_t)f * D + c];
+    dfs[c] = df;
+    drs[c] = dr;
+    gms[c] = a.gamma ? a.gamma[c] : 1.f;
+    a.Dbr[(((size_t)bh * 2 + 0) * g.F + t) * D + c] = df;
+    a.Dbr[(((size_t)bh * 2 + 1) * g.F + t) * D + c] = dr;
+  }
+  __syncthreads();
+  const float* pf = a.Pf + ((size_t)bh * (g.C + 1) + i_f) * DD;
+  const float* pr = a.Pr + ((size_t)bh * (g.C + 1) + i_r) * DD;
+  // M fragments: mt* = rows v = 32 vb + l32 of M^T, m* = rows k = 32 vb + l32 of M
+  bf16x8 mth[NKK], mtl[NKK], mh[NKK], ml[NKK];
+  {
+    const int r = vb * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int k0 = kk * 16 + hg * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = k0 + j;
+        const float xt = dfs[k] * pf[(size_t)k * D + r] + drs[k] * pr[(size_t)k * D + r];   // M[k][r]
+        const float xm = dfs[r] * pf[(size_t)r * D + k] + drs[r] * pr[(size_t)r * D + k];   // M[r][k]
+        const bf16_t ht = f32_to_bf16(xt), hm = f32_to_bf16(xm);
+        mth[kk][j] = __builtin_bit_cast(__bf16, ht);
+        mtl[kk][j] = static_cast<__bf16>(xt - bf16_to_f32(ht));
+        mh[kk][j] = __builtin_bit_cast(__bf16, hm);
+        ml[kk][j] = static_cast<__bf16>(xm - bf16_to_f32(hm));
+      }
+    }
+  }
+  const int bidx = bh / g.H, h = bh % g.H;
+  const size_t tok0 = (size_t)bh * g.L + (size_t)t * g.N;
+  f32x16 G[NGB];
+#pragma unroll
+  for (int b = 0; b < NGB; ++b) G[b] = f32x16{};
+  float gacc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gacc[i] = 0.f;
+
+  bf16x8 qf[NKK];
+  auto load_q = [&](int n, bf16x8* dst) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 x = {0, 0, 0, 0};
+      if (n < g.N) x = ld16(a.q + (tok0 + n) * D + kk * 16 + hg * 8);
+      dst[kk] = as_bf16x8(x);
+    }
+  };
+  const int nl = ts * 32 + l32;                 // token within the step
+  for (int n0 = 0; n0 < g.N; n0 += TPS) {
+    const int n = n0 + nl;
+    const bool valid = n < g.N;
+    load_q(n, qf);
+    // Q^T tile: this wave writes its two k-steps
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      const int kk = vb * 2 + kq;
+      const u32x4 w = __builtin_bit_cast(u32x4, qf[kk]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        u.t.qt[(kk * 16 + hg * 8 + j) * QP + nl] = (bf16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+    }
+    // O^T block
+    f32x16 o = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      o = mfma32x32x16(mth[kk], qf[kk], o);
+      o = mfma32x32x16(mtl[kk], qf[kk], o);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss = fmaf(o[i], o[i], ss);
+    ss = half_sum(ss);
+    if (hg == 0) red1[wave][l32] = ss;
+    lds_barrier();
+    float sst = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sst += red1[ts * NB + b][l32];
+    const float inv = rsqrtf(sst / (float)D + a.eps);
+    const size_t l = (size_t)t * g.N + n;
+    const float gate = valid ? a.g_l[(size_t)bh * g.L + l] : 0.f;
+    const bf16_t* dob = a.d_out + (((size_t)bidx * g.L + l) * g.H + h) * D + vb * 32;
+    const f32x4* gq = reinterpret_cast<const f32x4*>(&gms[vb * 32 + 4 * hg]);
+    float y[16], u_[16], dgv = 0.f, uy = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      u32x2 x = {0, 0};
+      if (valid) x = *reinterpret_cast<const u32x2*>(dob + 8 * i4 + 4 * hg);
+      const float dv4[4] = {bf16_to_f32((bf16_t)(x[0] & 0xFFFFu)), bf16_to_f32((bf16_t)(x[0] >> 16)),
+                            bf16_to_f32((bf16_t)(x[1] & 0xFFFFu)), bf16_to_f32((bf16_t)(x[1] >> 16))};
+      const f32x4 gm4 = gq[2 * i4];                    // gamma of channels 8 i4 + 4 hg + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * i4 + r;
+        y[i] = valid ? o[i] * inv : 0.f;
+        u_[i] = gate * gm4[r] * dv4[r];
+        dgv = fmaf(dv4[r] * gm4[r], y[i], dgv);
+        uy = fmaf(u_[i], y[i], uy);
+        gacc[i] = fmaf(dv4[r] * gate, y[i], gacc[i]);
+      }
+    }
+    dgv = half_sum(dgv);
+    uy = half_sum(uy);
+    if (hg == 0) {
+      red2[wave][l32][0] = dgv;
+      red2[wave][l32][1] = uy;
+    }
+    lds_barrier();
+    float dgt = 0.f, uyt = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      dgt += red2[ts * NB + b][l32][0];
+      uyt += red2[ts * NB + b][l32][1];
+    }
+    if (vb == 0 && hg == 0 && valid && a.dg_l) a.dg_l[(size_t)bh * g.L + l] = dgt;
+    const float muy = uyt / (float)D;
+    // dO of this block -> LDS, row-major and transposed, hi + lo
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      uint32_t ph[2], pl[2];
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        float hv[2], lv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 4 * i4 + 2 * r2 + e;
+          const float d = valid ? inv * (u_[i] - y[i] * muy) : 0.f;
+          const bf16_t hb = f32_to_bf16(d);
+          hv[e] = bf16_to_f32(hb);
+          lv[e] = d - hv[e];
+          const int vrow = vb * 32 + mfma32_row(i, hg);
+          u.t.dth[vrow * QP + nl] = hb;
+          u.t.dtl[vrow * QP + nl] = f32_to_bf16(lv[e]);
+        }
+        ph[r2] = pack_bf16x2(hv[0], hv[1]);
+        pl[r2] = pack_bf16x2(lv[0], lv[1]);
+      }
+      const int c0 = vb * 32 + 8 * i4 + 4 * hg;
+      *reinterpret_cast<u32x2*>(&u.t.doh[nl * DP + c0]) = u32x2{ph[0], ph[1]};
+      *reinterpret_cast<u32x2*>(&u.t.dol[nl * DP + c0]) = u32x2{pl[0], pl[1]};
+    }
+    __syncthreads();
+    // dq^T rows k of block vb for the sub-tile's tokens
+    f32x16 dq = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 bh_ = as_bf16x8(ld16(&u.t.doh[nl * DP + kk * 16 + hg * 8]));
+      const bf16x8 bl_ = as_bf16x8(ld16(&u.t.dol[nl * DP + kk * 16 + hg * 8]));
+      dq = mfma32x32x16(mh[kk], bh_, dq);
+      dq = mfma32x32x16(ml[kk], bh_, dq);
+      dq = mfma32x32x16(mh[kk], bl_, dq);
+    }
+    if (valid) {
+      bf16_t* dqr = a.dq + (tok0 + n) * D + vb * 32;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(dq[4 * i4 + 0], dq[4 * i4 + 1]);
+        pk[1] = pack_bf16x2(dq[4 * i4 + 2], dq[4 * i4 + 3]);
+        *reinterpret_cast<u32x2*>(dqr + 8 * i4 + 4 * hg) = pk;
+      }
+    }
+    // G += Q^T dO over the step's tokens
+#pragma unroll
+    for (int b = 0; b < NGB; ++b) {
+      const int blk = wave + 4 * b;
+      const int kb = blk / NB, vbg = blk % NB;
+#pragma unroll
+      for (int ns = 0; ns < TPS / 16; ++ns) {
+        const bf16x8 aq = as_bf16x8(ld16(&u.t.qt[(kb * 32 + l32) * QP + ns * 16 + hg * 8]));
+        const bf16x8 bh_ = as_bf16x8(ld16(&u.t.dth[(vbg * 32 + l32) * QP + ns * 16 + hg * 8]));
+        const bf16x8 bl_ = as_bf16x8(ld16(&u.t.dtl[(vbg * 32 + l32) * QP + ns * 16 + hg * 8]));
+        G[b] = mfma32x32x16(aq, bh_, G[b]);
+        G[b] = mfma32x32x16(aq, bl_, G[b]);
+      }
+    }
+    __syncthreads();
+  }
+  // G -> memory and LDS; bridge adjoints dD = rowsum(G * P)
+  float* Go = a.G + ((size_t)bh * g.F + t) * DD;
+#pragma unroll
+  for (int b = 0; b < NGB; ++b) {
+    const int blk = wave + 4 * b;
+    const int kb = blk / NB, vbg = blk % NB;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = kb * 32 + mfma32_row(i, hg), v = vbg * 32 + l32;
+      Go[(size_t)k * D + v] = G[b][i];
+      u.pd[k * (D + 1) + v] = G[b][i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gsum[ts][vb * 32 + mfma32_row(i, hg)][l32] = gacc[i];
+  __syncthreads();
+  for (int r = wave; r < D; r += 4) {
+    float sf = 0.f, sr = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      const float x = u.pd[r * (D + 1) + c];
+      sf = fmaf(x, pf[(size_t)r * D + c], sf);
+      sr = fmaf(x, pr[(size_t)r * D + c], sr);
+    }
+    sf = sum64(sf);
+    sr = sum64(sr);
+    if (lane == 0) {
+      a.dDbr[(((size_t)bh * 2 + 0) * g.F + t) * D + r] = sf;
+      a.dDbr[(((size_t)bh * 2 + 1) * g.F + t) * D + r] = sr;
+    }
+  }
+  if (a.dgp) {
+    for (int c = tid; c < D; c += 256) {
+      float sg = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < SUBT; ++s2)
+        for (int j = 0; j < 32; ++j) sg += gsum[s2][c][j];
+      a.dgp[((size_t)bh * g.F + t) * D + c] = sg;
     }
   }
 }
@@ -591,101 +858,119 @@ __global__ __launch_bounds__(256) void vda_bwd_frame_adjoint_kernel(VdaBwdArgs<T
 // ---------------------------------------------------------------------------
 // 7. Per frame (and the text frame): dA_sym = -(Z0 S0^T + Z1 S1^T) + transpose,
 //    dW = Z0 + Z1, the scan's alpha term, then the token gradients.  One
-//    workgroup (256 threads) per (b, h, frame); dA_sym and dW sit in LDS
-//    with pitch D + 1.
+//    workgroup (256 threads) per (b, h, frame).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void vda_bwd_token_kernel(VdaBwdArgs<T> a) {
-  constexpr int CPT = D / 16, TOK = 16, MP = D + 1, VC = 16, ZP = D + 4;
-  __shared__ float Am[D * MP];
-  __shared__ float Wm[D * MP];
-  struct ZS { float z[VC][ZP]; float s[VC][ZP]; };
-  struct KV { float k[TOK][MP]; float v[TOK][MP]; float b[TOK]; };
-  __shared__ union { ZS zs; KV kv; } u;
-
-  const Geometry& g = a.g;
-  const int nfr = g.F + (g.T > 0 ? 1 : 0);
-  const int f = blockIdx.x % nfr;
-  const int bh = blockIdx.x / nfr;
-  const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
-  const int wave = tid >> 6, lane = tid & 63;
-  const size_t DD = (size_t)D * D;
-  const bool text = f == g.F;
-  const float* Z0 = text ? a.ZT + (size_t)bh * DD : a.Zst + (((size_t)bh * 2 + 0) * g.F + f) * DD;
-  const float* Z1 = text ? nullptr : a.Zst + (((size_t)bh * 2 + 1) * g.F + f) * DD;
-  const float* S0 = text ? a.St + (size_t)bh * DD : a.Sst + (((size_t)bh * 2 + 0) * (g.F + 1) + f + 1) * DD;
-  const float* S1 = text ? nullptr : a.Sst + (((size_t)bh * 2 + 1) * (g.F + 1) + f) * DD;
-
-  // the scan's alpha term: rowsum(Z0 * S_fwd before f) + rowsum(Z1 * S_rev after f + 1)
-  if (!text) {
-    const float* P0 = a.Sst + (((size_t)bh * 2 + 0) * (g.F + 1) + f) * DD;
-    const float* P1 = a.Sst + (((size_t)bh * 2 + 1) * (g.F + 1) + f + 1) * DD;
-    for (int r = wave; r < D; r += 4) {
-      float s = 0.f;
-      for (int c = lane; c < D; c += 64)
-        s += Z0[(size_t)r * D + c] * P0[(size_t)r * D + c] + Z1[(size_t)r * D + c] * P1[(size_t)r * D + c];
-      s = sum64(s);
-      if (lane == 0) a.dalpha[((size_t)bh * g.F + f) * D + r] += s;
-    }
-  }
+template <typename T>
+struct FrameTok {
+  bool text, anchor;
+  const float *Z0, *Z1, *S0, *S1;      // Z1 = S1 = nullptr for the text frame
   long long ntok;
-  size_t tok0;
   const T *kp, *vp;
   const float* bp;
   T *dkp, *dvp;
   float* dbp;
-  if (text) {
-    ntok = g.T;
-    tok0 = 0;
-    kp = a.k_text + (size_t)bh * g.T * D;
-    vp = a.v_text + (size_t)bh * g.T * D;
-    bp = a.beta_text + (size_t)bh * g.T;
-    dkp = a.dk_text + (size_t)bh * g.T * D;
-    dvp = a.dv_text + (size_t)bh * g.T * D;
-    dbp = a.dbeta_text + (size_t)bh * g.T;
-  } else {
-    ntok = g.N;
-    tok0 = (size_t)bh * g.L + (size_t)f * g.N;
-    kp = a.k + tok0 * D;
-    vp = a.v + tok0 * D;
-    bp = a.beta + tok0;
-    dkp = a.dk + tok0 * D;
-    dvp = a.dv + tok0 * D;
-    dbp = a.dbeta + tok0;
-  }
-  if (!text && is_anchor_frame(g, f)) {            // no write: zero gradients
-    for (long long e = tid; e < ntok * D; e += 256) {
-      Elem<T>::store(dkp, e, 0.f);
-      Elem<T>::store(dvp, e, 0.f);
-    }
-    for (long long n = tid; n < ntok; n += 256) dbp[n] = 0.f;
-    return;
-  }
+};
 
-  // dA = -(Z0 S0^T + Z1 S1^T): thread owns rows grp + 16 i, columns sub + 16 j
-  float acc[CPT][CPT];
+template <typename T, int D>
+__device__ __forceinline__ FrameTok<T> frame_tok(const VdaBwdArgs<T>& a, int bh, int f) {
+  const Geometry& g = a.g;
+  const size_t DD = (size_t)D * D;
+  FrameTok<T> r;
+  r.text = f == g.F;
+  r.anchor = !r.text && is_anchor_frame(g, f);
+  if (r.text) {
+    r.Z0 = a.ZT + (size_t)bh * DD;
+    r.S0 = a.St + (size_t)bh * DD;
+    r.Z1 = r.S1 = nullptr;
+    r.ntok = g.T;
+    r.kp = a.k_text + (size_t)bh * g.T * D;
+    r.vp = a.v_text + (size_t)bh * g.T * D;
+    r.bp = a.beta_text + (size_t)bh * g.T;
+    r.dkp = a.dk_text + (size_t)bh * g.T * D;
+    r.dvp = a.dv_text + (size_t)bh * g.T * D;
+    r.dbp = a.dbeta_text + (size_t)bh * g.T;
+  } else {
+    r.Z0 = a.Zst + (((size_t)bh * 2 + 0) * g.F + f) * DD;
+    r.Z1 = a.Zst + (((size_t)bh * 2 + 1) * g.F + f) * DD;
+    r.S0 = a.Sst + (((size_t)bh * 2 + 0) * (g.F + 1) + f + 1) * DD;   // forward state after f
+    r.S1 = a.Sst + (((size_t)bh * 2 + 1) * (g.F + 1) + f) * DD;       // reverse state after f
+    r.ntok = g.N;
+    const size_t tok0 = (size_t)bh * g.L + (size_t)f * g.N;
+    r.kp = a.k + tok0 * D;
+    r.vp = a.v + tok0 * D;
+    r.bp = a.beta + tok0;
+    r.dkp = a.dk + tok0 * D;
+    r.dvp = a.dv + tok0 * D;
+    r.dbp = a.dbeta + tok0;
+  }
+  return r;
+}
+
+// The scan's alpha term of a video frame, added to dalpha (initialised by
+// the bridge kernel): rowsum(Z0 * forward state before f) + rowsum(Z1 *
+// reverse state after f + 1).  One wave per row, lanes over columns.
+template <typename T, int D>
+__device__ __forceinline__ void alpha_scan_term(const VdaBwdArgs<T>& a, const FrameTok<T>& ft, int bh,
+                                                int f) {
+  const Geometry& g = a.g;
+  const size_t DD = (size_t)D * D;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float* P0 = a.Sst + (((size_t)bh * 2 + 0) * (g.F + 1) + f) * DD;
+  const float* P1 = a.Sst + (((size_t)bh * 2 + 1) * (g.F + 1) + f + 1) * DD;
+  for (int r = wave; r < D; r += 4) {
+    float s = 0.f;
+    for (int c = lane; c < D; c += 64)
+      s += ft.Z0[(size_t)r * D + c] * P0[(size_t)r * D + c] + ft.Z1[(size_t)r * D + c] * P1[(size_t)r * D + c];
+    s = sum64(s);
+    if (lane == 0) a.dalpha[((size_t)bh * g.F + f) * D + r] += s;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void zero_tokens(const FrameTok<T>& ft, int D) {
+  for (long long e = threadIdx.x; e < ft.ntok * D; e += 256) {
+    Elem<T>::store(ft.dkp, e, 0.f);
+    Elem<T>::store(ft.dvp, e, 0.f);
+  }
+  for (long long n = threadIdx.x; n < ft.ntok; n += 256) ft.dbp[n] = 0.f;
+}
+
+// Staging of Z and S column slices for the dA product.
+template <int D>
+struct ZSStage {
+  static constexpr int VC = 16, ZP = D + 4;
+  float z[VC][ZP];
+  float s[VC][ZP];
+};
+
+// acc[i][j] = (Z0 S0^T + Z1 S1^T)[grp + 16 i][sub + 16 j] (fp32, 256 threads).
+template <int D>
+__device__ __forceinline__ void frame_zst(const float* Z0, const float* S0, const float* Z1, const float* S1,
+                                          ZSStage<D>& st, float (&acc)[D / 16][D / 16]) {
+  constexpr int CPT = D / 16, VC = ZSStage<D>::VC;
+  const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
 #pragma unroll
     for (int j = 0; j < CPT; ++j) acc[i][j] = 0.f;
-  for (int src = 0; src < (text ? 1 : 2); ++src) {
+  for (int src = 0; src < (Z1 ? 2 : 1); ++src) {
     const float* Zs = src ? Z1 : Z0;
     const float* Ss = src ? S1 : S0;
     for (int v0 = 0; v0 < D; v0 += VC) {
       __syncthreads();
       for (int e = tid; e < D * VC; e += 256) {
         const int r = e / VC, c = e % VC;
-        u.zs.z[c][r] = Zs[(size_t)r * D + v0 + c];
-        u.zs.s[c][r] = Ss[(size_t)r * D + v0 + c];
+        st.z[c][r] = Zs[(size_t)r * D + v0 + c];
+        st.s[c][r] = Ss[(size_t)r * D + v0 + c];
       }
       __syncthreads();
 #pragma unroll 4
       for (int c = 0; c < VC; ++c) {
         float zi[CPT], sj[CPT];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) zi[i] = u.zs.z[c][grp + 16 * i];
+        for (int i = 0; i < CPT; ++i) zi[i] = st.z[c][grp + 16 * i];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) sj[j] = u.zs.s[c][sub + 16 * j];
+        for (int j = 0; j < CPT; ++j) sj[j] = st.s[c][sub + 16 * j];
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
 #pragma unroll
@@ -693,13 +978,39 @@ __global__ __launch_bounds__(256) void vda_bwd_token_kernel(VdaBwdArgs<T> a) {
       }
     }
   }
+}
+
+// Generic kernel (any D, fp32 or bf16 storage): dA_sym and dW in LDS with
+// pitch D + 1; thread (grp, sub) takes token grp of a 16-token tile and the
+// columns sub + 16 j.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vda_bwd_token_kernel(VdaBwdArgs<T> a) {
+  constexpr int CPT = D / 16, TOK = 16, MP = D + 1;
+  __shared__ float Am[D * MP];
+  __shared__ float Wm[D * MP];
+  struct KV { float k[TOK][MP]; float v[TOK][MP]; float b[TOK]; };
+  __shared__ union { ZSStage<D> zs; KV kv; } u;
+
+  const Geometry& g = a.g;
+  const int nfr = g.F + (g.T > 0 ? 1 : 0);
+  const int f = blockIdx.x % nfr;
+  const int bh = blockIdx.x / nfr;
+  const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
+  const FrameTok<T> ft = frame_tok<T, D>(a, bh, f);
+  if (!ft.text) alpha_scan_term<T, D>(a, ft, bh, f);
+  if (ft.anchor) {                                   // no write: zero gradients
+    zero_tokens(ft, D);
+    return;
+  }
+  float acc[CPT][CPT];
+  frame_zst<D>(ft.Z0, ft.S0, ft.Z1, ft.S1, u.zs, acc);
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
 #pragma unroll
     for (int j = 0; j < CPT; ++j) Am[(grp + 16 * i) * MP + sub + 16 * j] = -acc[i][j];
   for (int e = tid; e < D * D; e += 256) {
     const int r = e / D, c = e % D;
-    Wm[r * MP + c] = Z0[e] + (Z1 ? Z1[e] : 0.f);
+    Wm[r * MP + c] = ft.Z0[e] + (ft.Z1 ? ft.Z1[e] : 0.f);
   }
   __syncthreads();
 #pragma unroll
@@ -716,15 +1027,15 @@ __global__ __launch_bounds__(256) void vda_bwd_token_kernel(VdaBwdArgs<T> a) {
     for (int j = 0; j < CPT; ++j) Am[(grp + 16 * i) * MP + sub + 16 * j] = acc[i][j];
 
   // tokens: E = k dA_sym, Fm = k dW, Gm = v dW^T
-  for (long long n0 = 0; n0 < ntok; n0 += TOK) {
+  for (long long n0 = 0; n0 < ft.ntok; n0 += TOK) {
     __syncthreads();
     for (int e = tid; e < TOK * D; e += 256) {
       const int r = e / D, c = e % D;
-      const bool ok = n0 + r < ntok;
-      u.kv.k[r][c] = ok ? Elem<T>::load(kp, (size_t)(n0 + r) * D + c) : 0.f;
-      u.kv.v[r][c] = ok ? Elem<T>::load(vp, (size_t)(n0 + r) * D + c) : 0.f;
+      const bool ok = n0 + r < ft.ntok;
+      u.kv.k[r][c] = ok ? Elem<T>::load(ft.kp, (size_t)(n0 + r) * D + c) : 0.f;
+      u.kv.v[r][c] = ok ? Elem<T>::load(ft.vp, (size_t)(n0 + r) * D + c) : 0.f;
     }
-    if (tid < TOK) u.kv.b[tid] = n0 + tid < ntok ? bp[n0 + tid] : 0.f;
+    if (tid < TOK) u.kv.b[tid] = n0 + tid < ft.ntok ? ft.bp[n0 + tid] : 0.f;
     __syncthreads();
     float E[CPT], Fm[CPT], Gm[CPT];
 #pragma unroll
@@ -748,14 +1059,160 @@ __global__ __launch_bounds__(256) void vda_bwd_token_kernel(VdaBwdArgs<T> a) {
     }
     db = sum16(db);
     const long long n = n0 + grp;
-    if (n < ntok) {
+    if (n < ft.ntok) {
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int c = sub + 16 * j;
-        Elem<T>::store(dkp, (size_t)n * D + c, b * (E[j] + Gm[j]));
-        Elem<T>::store(dvp, (size_t)n * D + c, b * Fm[j]);
+        Elem<T>::store(ft.dkp, (size_t)n * D + c, b * (E[j] + Gm[j]));
+        Elem<T>::store(ft.dvp, (size_t)n * D + c, b * Fm[j]);
       }
-      if (sub == 0) dbp[n] = db;
+      if (sub == 0) ft.dbp[n] = db;
+    }
+  }
+}
+
+// bf16 kernel (D = 64, 128) on v_mfma_f32_32x32x16_bf16.  Wave w owns the
+// 32-channel block cb = w % (D/32) and the 32-token sub-tile w / (D/32) of
+// each step.  Its rows of dA_sym, dW^T and dW stay in registers for the
+// whole frame as bf16 hi + lo fragments (A operands); K and V rows come
+// straight from global memory as B operands, the next step's while the
+// current one is multiplied.  Per token (column n) and channel c:
+//   acc1 = (dA_sym k + dW v)[c],  acc2 = (dW^T k)[c],
+//   dk = beta acc1,  dv = beta acc2,  dbeta = 1/2 (acc1 . k + acc2 . v)
+// (the last since k dW v = v dW^T k).
+template <int D>
+__global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16_t> a) {
+  constexpr int CPT = D / 16, MP = D + 1, NB = D / 32, NKK = D / 16;
+  constexpr int SUBT = 4 / NB;            // token sub-tiles per step
+  constexpr int TPS = 32 * SUBT;          // tokens per step
+  __shared__ __attribute__((aligned(16))) union {
+    ZSStage<D> zs;
+    float am[D * MP];
+  } u;
+  __shared__ float red[2][4][32];
+
+  const Geometry& g = a.g;
+  const int nfr = g.F + (g.T > 0 ? 1 : 0);
+  const int f = blockIdx.x % nfr;
+  const int bh = blockIdx.x / nfr;
+  const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
+  const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const FrameTok<bf16_t> ft = frame_tok<bf16_t, D>(a, bh, f);
+  if (!ft.text) alpha_scan_term<bf16_t, D>(a, ft, bh, f);
+  if (ft.anchor) {
+    zero_tokens(ft, D);
+    return;
+  }
+  {
+    float acc[CPT][CPT];
+    frame_zst<D>(ft.Z0, ft.S0, ft.Z1, ft.S1, u.zs, acc);
+    __syncthreads();                           // staging dead: u.am takes its place
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) u.am[(grp + 16 * i) * MP + sub + 16 * j] = -acc[i][j];
+  }
+  __syncthreads();
+  // A-operand fragments of the wave's channel rows
+  const int cb = wave % NB, ts = wave / NB;
+  const int c = cb * 32 + l32;
+  bf16x8 ash[NKK], asl[NKK], wth[NKK], wtl[NKK], wh[NKK], wl[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int k0 = kk * 16 + hg * 8;
+    float xs[8], xt[8], xw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      xs[j] = u.am[c * MP + k] + u.am[k * MP + c];
+      xw[j] = ft.Z0[(size_t)c * D + k] + (ft.Z1 ? ft.Z1[(size_t)c * D + k] : 0.f);
+      xt[j] = ft.Z0[(size_t)k * D + c] + (ft.Z1 ? ft.Z1[(size_t)k * D + c] : 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16_t hs = f32_to_bf16(xs[j]), hw = f32_to_bf16(xw[j]), ht = f32_to_bf16(xt[j]);
+      ash[kk][j] = __builtin_bit_cast(__bf16, hs);
+      asl[kk][j] = static_cast<__bf16>(xs[j] - bf16_to_f32(hs));
+      wh[kk][j] = __builtin_bit_cast(__bf16, hw);
+      wl[kk][j] = static_cast<__bf16>(xw[j] - bf16_to_f32(hw));
+      wth[kk][j] = __builtin_bit_cast(__bf16, ht);
+      wtl[kk][j] = static_cast<__bf16>(xt[j] - bf16_to_f32(ht));
+    }
+  }
+
+  const long long ntok = ft.ntok;
+  bf16x8 bk[NKK], bv[NKK], bkn[NKK], bvn[NKK];
+  auto load_b = [&](long long n, bf16x8* dk_, bf16x8* dv_) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+      if (n < ntok) {
+        x = ld16(ft.kp + (size_t)n * D + kk * 16 + hg * 8);
+        y = ld16(ft.vp + (size_t)n * D + kk * 16 + hg * 8);
+      }
+      dk_[kk] = as_bf16x8(x);
+      dv_[kk] = as_bf16x8(y);
+    }
+  };
+  load_b(ts * 32 + l32, bk, bv);
+  int it = 0;
+  for (long long n0 = 0; n0 < ntok; n0 += TPS, ++it) {
+    const long long n = n0 + ts * 32 + l32;
+    load_b(n + TPS, bkn, bvn);
+    f32x16 acc1 = f32x16{}, acc2 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      acc1 = mfma32x32x16(ash[kk], bk[kk], acc1);
+      acc1 = mfma32x32x16(asl[kk], bk[kk], acc1);
+      acc1 = mfma32x32x16(wh[kk], bv[kk], acc1);
+      acc1 = mfma32x32x16(wl[kk], bv[kk], acc1);
+      acc2 = mfma32x32x16(wth[kk], bk[kk], acc2);
+      acc2 = mfma32x32x16(wtl[kk], bk[kk], acc2);
+    }
+    const bool valid = n < ntok;
+    float db = 0.f;
+    if (valid) {
+      const float b = ft.bp[n];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int c0 = cb * 32 + 8 * i4 + 4 * hg;
+        const u32x2 kx = *reinterpret_cast<const u32x2*>(ft.kp + (size_t)n * D + c0);
+        const u32x2 vx = *reinterpret_cast<const u32x2*>(ft.vp + (size_t)n * D + c0);
+        float kc[4], vc[4];
+        kc[0] = bf16_to_f32((bf16_t)(kx[0] & 0xFFFFu)); kc[1] = bf16_to_f32((bf16_t)(kx[0] >> 16));
+        kc[2] = bf16_to_f32((bf16_t)(kx[1] & 0xFFFFu)); kc[3] = bf16_to_f32((bf16_t)(kx[1] >> 16));
+        vc[0] = bf16_to_f32((bf16_t)(vx[0] & 0xFFFFu)); vc[1] = bf16_to_f32((bf16_t)(vx[0] >> 16));
+        vc[2] = bf16_to_f32((bf16_t)(vx[1] & 0xFFFFu)); vc[3] = bf16_to_f32((bf16_t)(vx[1] >> 16));
+        u32x2 pk, pv;
+        float e1[4], e2[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e1[r] = acc1[4 * i4 + r];
+          e2[r] = acc2[4 * i4 + r];
+          db = fmaf(e1[r], kc[r], db);
+          db = fmaf(e2[r], vc[r], db);
+        }
+        pk[0] = pack_bf16x2(b * e1[0], b * e1[1]);
+        pk[1] = pack_bf16x2(b * e1[2], b * e1[3]);
+        pv[0] = pack_bf16x2(b * e2[0], b * e2[1]);
+        pv[1] = pack_bf16x2(b * e2[2], b * e2[3]);
+        *reinterpret_cast<u32x2*>(ft.dkp + (size_t)n * D + c0) = pk;
+        *reinterpret_cast<u32x2*>(ft.dvp + (size_t)n * D + c0) = pv;
+      }
+    }
+    db = half_sum(db);
+    if (hg == 0) red[it & 1][wave][l32] = db;
+    lds_barrier();
+    if (cb == 0 && hg == 0 && valid) {
+      float s = 0.f;
+#pragma unroll
+      for (int b2 = 0; b2 < NB; ++b2) s += red[it & 1][ts * NB + b2][l32];
+      ft.dbp[n] = 0.5f * s;
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      bk[kk] = bkn[kk];
+      bv[kk] = bvn[kk];
     }
   }
 }
@@ -777,13 +1234,20 @@ hipError_t launch_all(const VdaBwdArgs<T>& a, const float* Tf, const float* Uf, 
   const Geometry& g = a.g;
   const unsigned BH = (unsigned)(g.B * g.H);
   constexpr int NCB = (D + kBCB - 1) / kBCB;
-  vda_bwd_readout_kernel<T, D><<<BH * g.F, 256, 0, s>>>(a);
+  if constexpr (std::is_same<T, bf16_t>::value && (D == 64 || D == 128))
+    vda_bwd_readout_mfma_kernel<D><<<BH * g.F, 256, 0, s>>>(a);
+  else
+    vda_bwd_readout_kernel<T, D><<<BH * g.F, 256, 0, s>>>(a);
   vda_bwd_dp_kernel<T, D><<<BH * 2 * (g.C + 1), 256, 0, s>>>(a);
   vda_bwd_alpha_bridge_kernel<T, D><<<BH, 128, 0, s>>>(a);
   vda_bwd_chunk_adjoint_kernel<T, D><<<BH * 2 * NCB, 256, 0, s>>>(a);
   if (g.T > 0) vda_bwd_text_kernel<T, D><<<BH * NCB, 256, 0, s>>>(a);
   vda_bwd_frame_adjoint_kernel<T, D><<<BH * 2 * g.C * NCB, 256, 0, s>>>(a, Tf, Uf);
-  vda_bwd_token_kernel<T, D><<<BH * (g.F + (g.T > 0 ? 1 : 0)), 256, 0, s>>>(a);
+  const unsigned nfr = BH * (g.F + (g.T > 0 ? 1 : 0));
+  if constexpr (std::is_same<T, bf16_t>::value && (D == 64 || D == 128))
+    vda_bwd_token_mfma_kernel<D><<<nfr, 256, 0, s>>>(a);
+  else
+    vda_bwd_token_kernel<T, D><<<nfr, 256, 0, s>>>(a);
   if (dgamma && a.dgp) vda_bwd_dgamma_kernel<D><<<1, 128, 0, s>>>(a.dgp, (long long)BH * g.F, dgamma);
   return hipGetLastError();
 }

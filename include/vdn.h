@@ -270,7 +270,8 @@ size_t vdn_softmax_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p
  *  dgamma                [d]       float  output, nullable (summed over
  *                                          batch, heads and tokens)
  *  workspace             vda_bwd_workspace_bytes(dims, p, dt) bytes
- * Errors as for vdn_attn_fwd.  Deterministic (no atomics).
+ * Errors as for vdn_attn_fwd; F > 1024 -> VDN_ERR_UNSUPPORTED.  Deterministic
+ * (no atomics).
  */
 vdn_status vda_bwd(const void* q, const void* k, const void* v, const float* beta,
                    const float* alpha, const void* k_text, const void* v_text,

@@ -47,6 +47,7 @@ namespace vdn {
 namespace {
 
 constexpr int kBCB = 32;   // state columns per workgroup in the chain kernels
+constexpr int kBridgeCh = 2;   // channels per workgroup of the bridge-alpha kernel (<= 56 F bytes of LDS)
 
 template <typename T>
 struct VdaBwdArgs {
@@ -352,14 +353,24 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     }
   };
   const int nl = ts * 32 + l32;                 // token within the step
+  // dOhat of this lane's token and 16 channels, the next step's requested early
+  u32x2 dx[4], dxn[4];
+  auto load_do = [&](int n, u32x2* dst) {
+    const bf16_t* dob = a.d_out + (((size_t)bidx * g.L + (size_t)t * g.N + n) * g.H + h) * D + vb * 32;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      dst[i4] = n < g.N ? *reinterpret_cast<const u32x2*>(dob + 8 * i4 + 4 * hg) : u32x2{0, 0};
+  };
+  load_do(nl, dx);
   for (int n0 = 0; n0 < g.N; n0 += TPS) {
     const int n = n0 + nl;
     const bool valid = n < g.N;
     load_q(n, qf);
+    load_do(n + TPS, dxn);
     // Q^T tile: this wave writes its two k-steps
 #pragma unroll
-    for (int kq = 0; kq < 2; ++kq) {
-      const int kk = vb * 2 + kq;
+    for (int kk = 0; kk < NKK; ++kk) {
+      if ((kk >> 1) != vb) continue;      // wave-uniform: keeps the register index static
       const u32x4 w = __builtin_bit_cast(u32x4, qf[kk]);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -384,13 +395,11 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     const float inv = rsqrtf(sst / (float)D + a.eps);
     const size_t l = (size_t)t * g.N + n;
     const float gate = valid ? a.g_l[(size_t)bh * g.L + l] : 0.f;
-    const bf16_t* dob = a.d_out + (((size_t)bidx * g.L + l) * g.H + h) * D + vb * 32;
     const f32x4* gq = reinterpret_cast<const f32x4*>(&gms[vb * 32 + 4 * hg]);
     float y[16], u_[16], dgv = 0.f, uy = 0.f;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      u32x2 x = {0, 0};
-      if (valid) x = *reinterpret_cast<const u32x2*>(dob + 8 * i4 + 4 * hg);
+      const u32x2 x = dx[i4];
       const float dv4[4] = {bf16_to_f32((bf16_t)(x[0] & 0xFFFFu)), bf16_to_f32((bf16_t)(x[0] >> 16)),
                             bf16_to_f32((bf16_t)(x[1] & 0xFFFFu)), bf16_to_f32((bf16_t)(x[1] >> 16))};
       const f32x4 gm4 = gq[2 * i4];                    // gamma of channels 8 i4 + 4 hg + r
@@ -479,6 +488,8 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
         G[b] = mfma32x32x16(aq, bl_, G[b]);
       }
     }
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) dx[i4] = dxn[i4];
     __syncthreads();
   }
   // G -> memory and LDS; bridge adjoints dD = rowsum(G * P)
@@ -563,67 +574,89 @@ __global__ __launch_bounds__(256) void vda_bwd_dp_kernel(VdaBwdArgs<T> a) {
 //    sharing a bridge start a (one group) contribute to alpha_f, f >= a,
 //      pre(f) * R(f),  pre(f) = prod_{a..f-1} alpha,
 //      R(f) = [f in group] dD_f + alpha_{f+1} R(f+1)   (f up to the group's last query);
-//    the reverse bridges t..we mirror this.  One thread per channel; R is
-//    kept in a per-thread column of Rscr.  Writes (initialises) dalpha.
+//    the reverse bridges t..we mirror this.  A workgroup takes 2 channels of
+//    one (b, h): alpha, dD, R and the dalpha sums for all frames sit in LDS
+//    (5 F floats per channel), one thread per channel runs the recurrences.
+//    Writes (initialises) dalpha.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(128) void vda_bwd_alpha_bridge_kernel(VdaBwdArgs<T> a) {
+__global__ __launch_bounds__(64) void vda_bwd_alpha_bridge_kernel(VdaBwdArgs<T> a) {
+  // LDS: alpha, dD_fwd, dD_rev, R, sums (kBridgeCh floats per frame each),
+  // then ws and we per frame and the groups' last / first query (ints)
+  extern __shared__ float bsm[];
   const Geometry& g = a.g;
-  const int bh = blockIdx.x;
+  constexpr int NG = D / kBridgeCh;
+  const int grp = blockIdx.x % NG, bh = blockIdx.x / NG;
+  const int c0 = grp * kBridgeCh;
+  const int F = g.F, C = g.C;
+  float* al = bsm;
+  float* dDf = al + F * kBridgeCh;
+  float* dDr = dDf + F * kBridgeCh;
+  float* R = dDr + F * kBridgeCh;
+  float* das = R + F * kBridgeCh;
+  int* wsA = reinterpret_cast<int*>(das + F * kBridgeCh);
+  int* weA = wsA + F;
+  int* tmaxA = weA + F;            // [C]: last query with ws = i * cf
+  int* tminA = tmaxA + C;          // [C + 1]: first query with we = min(i * cf, F) - 1
+  const float* alg = a.alpha + (size_t)bh * F * D + c0;
+  const float* dDfg = a.dDbr + ((size_t)bh * 2 + 0) * F * D + c0;
+  const float* dDrg = a.dDbr + ((size_t)bh * 2 + 1) * F * D + c0;
+  for (int e = threadIdx.x; e < F * kBridgeCh; e += 64) {
+    const int f = e / kBridgeCh, c = e % kBridgeCh;
+    al[e] = alg[(size_t)f * D + c];
+    dDf[e] = dDfg[(size_t)f * D + c];
+    dDr[e] = dDrg[(size_t)f * D + c];
+    das[e] = 0.f;
+  }
+  for (int t = threadIdx.x; t < F; t += 64) {
+    int i_f, ws, i_r, we;
+    readout_indices(g, t, i_f, ws, i_r, we);
+    wsA[t] = ws;
+    weA[t] = we;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < C; ++i) tmaxA[i] = -1;
+    for (int i = 0; i <= C; ++i) tminA[i] = F;
+    for (int t = 0; t < F; ++t) tmaxA[wsA[t] / g.cf] = t;                   // ascending: the last wins
+    for (int t = F - 1; t >= 0; --t) tminA[(weA[t] + 1 + g.cf - 1) / g.cf] = t;
+  }
+  __syncthreads();
   const int c = threadIdx.x;
-  if (c >= D) return;
-  const float* al = a.alpha + (size_t)bh * g.F * D + c;
-  float* da = a.dalpha + (size_t)bh * g.F * D + c;
-  float* R = a.Rscr + (size_t)bh * g.F * D + c;
-  const float* dDf = a.dDbr + ((size_t)bh * 2 + 0) * g.F * D + c;
-  const float* dDr = a.dDbr + ((size_t)bh * 2 + 1) * g.F * D + c;
-  for (int f = 0; f < g.F; ++f) da[(size_t)f * D] = 0.f;
+  if (c >= kBridgeCh) return;
+  auto A = [&](int f) { return al[f * kBridgeCh + c]; };
   // forward bridges: groups by start ws = i * cf
-  for (int i = 0; i < g.C; ++i) {
-    const int start = i * g.cf;
-    int tmax = -1;
-    for (int t = 0; t < g.F; ++t) {
-      int i_f, ws, i_r, we;
-      readout_indices(g, t, i_f, ws, i_r, we);
-      if (ws == start) tmax = t;
-    }
+  for (int i = 0; i < C; ++i) {
+    const int start = i * g.cf, tmax = tmaxA[i];
     if (tmax < start) continue;
     float r = 0.f;
     for (int f = tmax; f >= start; --f) {
-      int i_f, ws, i_r, we;
-      readout_indices(g, f, i_f, ws, i_r, we);
-      r = (f < tmax ? al[(size_t)(f + 1) * D] * r : 0.f) + (ws == start ? dDf[(size_t)f * D] : 0.f);
-      R[(size_t)f * D] = r;
+      r = (f < tmax ? A(f + 1) * r : 0.f) + (wsA[f] == start ? dDf[f * kBridgeCh + c] : 0.f);
+      R[f * kBridgeCh + c] = r;
     }
     float pre = 1.f;
     for (int f = start; f <= tmax; ++f) {
-      da[(size_t)f * D] += pre * R[(size_t)f * D];
-      pre *= al[(size_t)f * D];
+      das[f * kBridgeCh + c] += pre * R[f * kBridgeCh + c];
+      pre *= A(f);
     }
   }
   // reverse bridges: groups by end we = min(i * cf, F) - 1
-  for (int i = 1; i <= g.C; ++i) {
-    const int end = min(i * g.cf, g.F) - 1;
-    int tmin = g.F;
-    for (int t = g.F - 1; t >= 0; --t) {
-      int i_f, ws, i_r, we;
-      readout_indices(g, t, i_f, ws, i_r, we);
-      if (we == end) tmin = t;
-    }
+  for (int i = 1; i <= C; ++i) {
+    const int end = min(i * g.cf, F) - 1, tmin = tminA[i];
     if (tmin > end) continue;
     float r = 0.f;
     for (int f = tmin; f <= end; ++f) {
-      int i_f, ws, i_r, we;
-      readout_indices(g, f, i_f, ws, i_r, we);
-      r = (f > tmin ? al[(size_t)(f - 1) * D] * r : 0.f) + (we == end ? dDr[(size_t)f * D] : 0.f);
-      R[(size_t)f * D] = r;
+      r = (f > tmin ? A(f - 1) * r : 0.f) + (weA[f] == end ? dDr[f * kBridgeCh + c] : 0.f);
+      R[f * kBridgeCh + c] = r;
     }
     float suf = 1.f;
     for (int f = end; f >= tmin; --f) {
-      da[(size_t)f * D] += suf * R[(size_t)f * D];
-      suf *= al[(size_t)f * D];
+      das[f * kBridgeCh + c] += suf * R[f * kBridgeCh + c];
+      suf *= A(f);
     }
   }
+  float* da = a.dalpha + (size_t)bh * F * D + c0 + c;
+  for (int f = 0; f < F; ++f) da[(size_t)f * D] = das[f * kBridgeCh + c];
 }
 
 // ---------------------------------------------------------------------------
@@ -856,6 +889,205 @@ __global__ __launch_bounds__(256) void vda_bwd_frame_adjoint_kernel(VdaBwdArgs<T
 }
 
 // ---------------------------------------------------------------------------
+// fp32 MFMA chains for kernels 4 and 6 (D = 64, 128), on
+// v_mfma_f32_32x32x2f32.  A workgroup owns a 32-column block Y of the
+// state (or adjoint), kept transposed in LDS (Yt[n][k]); wave w < D/32 owns
+// rows 32w..32w+31 of each left factor, loaded from global memory straight
+// into registers -- the next step's while the current product runs.  Lane
+// half g takes k = 8j + 4g .. 8j + 4g + 3 of each 8-wide group on both
+// operands.
+// ---------------------------------------------------------------------------
+template <int D>
+struct ChainMfma {
+  static constexpr int NB = D / 32, YP = D + 4, NK8 = D / 8;
+  float* Yt;
+  int col0, wave, hg, l32;
+  bool mw;
+
+  __device__ __forceinline__ ChainMfma(float* yt, int c0) : Yt(yt), col0(c0) {
+    const int tid = threadIdx.x;
+    wave = tid >> 6;
+    hg = (tid & 63) >> 5;
+    l32 = tid & 31;
+    mw = wave < NB;
+  }
+  // rows of L (row-major) or of L^T (transposed: columns of L)
+  __device__ __forceinline__ void load_left(const float* Lm, bool transposed, f32x4 (&dst)[NK8]) const {
+    const int mrow = wave * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < NK8; ++j) {
+      if (!mw) { dst[j] = f32x4{}; continue; }
+      const int k0 = 8 * j + 4 * hg;
+      if (transposed)
+        dst[j] = f32x4{Lm[(size_t)k0 * D + mrow], Lm[(size_t)(k0 + 1) * D + mrow],
+                       Lm[(size_t)(k0 + 2) * D + mrow], Lm[(size_t)(k0 + 3) * D + mrow]};
+      else
+        dst[j] = *reinterpret_cast<const f32x4*>(Lm + (size_t)mrow * D + k0);
+    }
+  }
+  __device__ __forceinline__ void y_from(const float* src, float scale = 1.f) const {
+    for (int e = threadIdx.x; e < D * 32; e += 256) {
+      const int k = e / 32, n = e % 32;
+      Yt[n * YP + k] = scale * src[(size_t)k * D + col0 + n];
+    }
+  }
+  __device__ __forceinline__ f32x16 product(const f32x4 (&lf)[NK8]) const {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int j = 0; j < NK8; ++j) {
+      const f32x4 yb = *reinterpret_cast<const f32x4*>(&Yt[l32 * YP + 8 * j + 4 * hg]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = mfma32x32x2f32(lf[j][q], yb[q], acc);
+    }
+    return acc;
+  }
+  __device__ __forceinline__ f32x16 y_rows() const {     // the wave's rows of Y, accumulator layout
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = Yt[l32 * YP + wave * 32 + mfma32_row(i, hg)];
+    return acc;
+  }
+  __device__ __forceinline__ int row(int i) const { return wave * 32 + mfma32_row(i, hg); }
+  __device__ __forceinline__ void to_y(const f32x16& acc) const {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 v = {acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
+      *reinterpret_cast<f32x4*>(&Yt[l32 * YP + wave * 32 + 8 * i4 + 4 * hg]) = v;
+    }
+  }
+  __device__ __forceinline__ void to_global(const f32x16& acc, float* dst) const {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[(size_t)row(i) * D + col0 + l32] = acc[i];
+  }
+};
+
+// Kernel 4 on MFMA: grid (b, h, direction, column block).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vda_bwd_chunk_adjoint_mfma_kernel(VdaBwdArgs<T> a) {
+  using CM = ChainMfma<D>;
+  __shared__ __attribute__((aligned(16))) float Yt[32 * CM::YP];
+  constexpr int NCB = D / 32;
+  const Geometry& g = a.g;
+  int id = blockIdx.x;
+  const int cb = id % NCB; id /= NCB;
+  const int dir = id % 2;
+  const int bh = id / 2;
+  const size_t DD = (size_t)D * D;
+  CM cm(Yt, cb * 32);
+  const float* dP = a.dP + ((size_t)bh * 2 + dir) * (g.C + 1) * DD;
+  float* mu = a.mu + ((size_t)bh * 2 + dir) * (g.C + 1) * DD;
+  const float* Tc = a.Tc + ((size_t)bh * 2 + dir) * g.C * DD;
+  const int first = dir == 0 ? g.C : 0;
+  cm.y_from(dP + (size_t)first * DD);
+  for (int e = threadIdx.x; e < D * 32; e += 256) {
+    const int k = e / 32, n = e % 32;
+    mu[(size_t)first * DD + (size_t)k * D + cm.col0 + n] = dP[(size_t)first * DD + (size_t)k * D + cm.col0 + n];
+  }
+  f32x4 lf[CM::NK8], ln[CM::NK8];
+  auto chunk = [&](int n) { return dir == 0 ? g.C - 1 - n : n; };
+  cm.load_left(Tc + (size_t)chunk(0) * DD, true, lf);
+  for (int n = 0; n < g.C; ++n) {
+    const int c = chunk(n);
+    const int slot = dir == 0 ? c : c + 1;
+    if (n + 1 < g.C) cm.load_left(Tc + (size_t)chunk(n + 1) * DD, true, ln);
+    __syncthreads();
+    f32x16 acc = f32x16{};
+    if (cm.mw) {
+      acc = cm.product(lf);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += dP[(size_t)slot * DD + (size_t)cm.row(i) * D + cm.col0 + cm.l32];
+    }
+    __syncthreads();
+    if (cm.mw) {
+      cm.to_y(acc);
+      cm.to_global(acc, mu + (size_t)slot * DD);
+    }
+#pragma unroll
+    for (int j = 0; j < CM::NK8; ++j) lf[j] = ln[j];
+  }
+}
+
+// Kernel 6 on MFMA: grid (b, h, direction, chunk, column block).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vda_bwd_frame_adjoint_mfma_kernel(VdaBwdArgs<T> a,
+                                                                         const float* __restrict__ Tf,
+                                                                         const float* __restrict__ Uf) {
+  using CM = ChainMfma<D>;
+  __shared__ __attribute__((aligned(16))) float Yt[32 * CM::YP];
+  constexpr int NCB = D / 32;
+  const Geometry& g = a.g;
+  int id = blockIdx.x;
+  const int cb = id % NCB; id /= NCB;
+  const int c = id % g.C; id /= g.C;
+  const int dir = id % 2;
+  const int bh = id / 2;
+  const size_t DD = (size_t)D * D;
+  CM cm(Yt, cb * 32);
+  const int f0 = c * g.cf, f1 = f0 + g.cf - 1;
+  float* S = a.Sst + ((size_t)bh * 2 + dir) * (g.F + 1) * DD;
+  float* Z = a.Zst + ((size_t)bh * 2 + dir) * g.F * DD;
+  const float* P = (dir == 0 ? a.Pf : a.Pr) + (size_t)bh * (g.C + 1) * DD;
+  const float* Tb = Tf + (size_t)bh * g.F * DD;
+  const float* Ub = Uf + (size_t)bh * g.F * DD;
+  const float* Xb = a.Xf + (size_t)bh * (g.F + 1) * DD;
+  const float* al = a.alpha + (size_t)bh * g.F * D;
+
+  // boundary copies: S[f0] = P[c]; the last chunk also writes S[F] = P[C]
+  for (int e = threadIdx.x; e < D * 32; e += 256) {
+    const size_t o = (size_t)(e / 32) * D + cm.col0 + e % 32;
+    S[(size_t)f0 * DD + o] = P[(size_t)c * DD + o];
+    if (c == g.C - 1) S[(size_t)g.F * DD + o] = P[(size_t)g.C * DD + o];
+  }
+  // ---- states inside the chunk ----
+  const int nst = g.cf - 1;
+  auto sframe = [&](int s2) { return dir == 0 ? f0 + s2 : f1 - s2; };
+  f32x4 lf[CM::NK8], ln[CM::NK8];
+  cm.y_from(P + (size_t)(dir == 0 ? c : c + 1) * DD);
+  if (nst > 0) cm.load_left(Tb + (size_t)sframe(0) * DD, false, lf);
+  for (int s2 = 0; s2 < nst; ++s2) {
+    const int f = sframe(s2);
+    if (s2 + 1 < nst) cm.load_left(Tb + (size_t)sframe(s2 + 1) * DD, false, ln);
+    __syncthreads();
+    f32x16 acc = f32x16{};
+    if (cm.mw) {
+      acc = cm.product(lf);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += Ub[(size_t)f * DD + (size_t)cm.row(i) * D + cm.col0 + cm.l32];
+    }
+    __syncthreads();
+    if (cm.mw) {
+      cm.to_y(acc);
+      cm.to_global(acc, S + (size_t)(dir == 0 ? f + 1 : f) * DD);
+    }
+#pragma unroll
+    for (int j = 0; j < CM::NK8; ++j) lf[j] = ln[j];
+  }
+  // ---- adjoints: Z_f = X_f lambda_f (lambda_f for anchors), lambda <- diag(alpha_f) Z_f ----
+  const float* mu = a.mu + ((size_t)bh * 2 + dir) * (g.C + 1) * DD;
+  auto aframe = [&](int n) { return dir == 0 ? f1 - n : f0 + n; };
+  __syncthreads();
+  cm.y_from(mu + (size_t)(dir == 0 ? c + 1 : c) * DD);
+  if (!is_anchor_frame(g, aframe(0))) cm.load_left(Xb + (size_t)aframe(0) * DD, false, lf);
+  for (int n = 0; n < g.cf; ++n) {
+    const int f = aframe(n);
+    if (n + 1 < g.cf && !is_anchor_frame(g, aframe(n + 1)))
+      cm.load_left(Xb + (size_t)aframe(n + 1) * DD, false, ln);
+    __syncthreads();
+    f32x16 acc = f32x16{};
+    if (cm.mw) acc = is_anchor_frame(g, f) ? cm.y_rows() : cm.product(lf);
+    __syncthreads();
+    if (cm.mw) {
+      cm.to_global(acc, Z + (size_t)f * DD);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] *= al[(size_t)f * D + cm.row(i)];
+      cm.to_y(acc);
+    }
+#pragma unroll
+    for (int j = 0; j < CM::NK8; ++j) lf[j] = ln[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 7. Per frame (and the text frame): dA_sym = -(Z0 S0^T + Z1 S1^T) + transpose,
 //    dW = Z0 + Z1, the scan's alpha term, then the token gradients.  One
 //    workgroup (256 threads) per (b, h, frame).
@@ -908,22 +1140,26 @@ __device__ __forceinline__ FrameTok<T> frame_tok(const VdaBwdArgs<T>& a, int bh,
 
 // The scan's alpha term of a video frame, added to dalpha (initialised by
 // the bridge kernel): rowsum(Z0 * forward state before f) + rowsum(Z1 *
-// reverse state after f + 1).  One wave per row, lanes over columns.
+// reverse state after f + 1).  256 / D threads per row, each a contiguous
+// slice of columns; all loads are independent.
 template <typename T, int D>
 __device__ __forceinline__ void alpha_scan_term(const VdaBwdArgs<T>& a, const FrameTok<T>& ft, int bh,
                                                 int f) {
+  constexpr int TPR = 256 / D, CW = D / TPR;
   const Geometry& g = a.g;
   const size_t DD = (size_t)D * D;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float* P0 = a.Sst + (((size_t)bh * 2 + 0) * (g.F + 1) + f) * DD;
-  const float* P1 = a.Sst + (((size_t)bh * 2 + 1) * (g.F + 1) + f + 1) * DD;
-  for (int r = wave; r < D; r += 4) {
-    float s = 0.f;
-    for (int c = lane; c < D; c += 64)
-      s += ft.Z0[(size_t)r * D + c] * P0[(size_t)r * D + c] + ft.Z1[(size_t)r * D + c] * P1[(size_t)r * D + c];
-    s = sum64(s);
-    if (lane == 0) a.dalpha[((size_t)bh * g.F + f) * D + r] += s;
-  }
+  const int r = threadIdx.x / TPR, part = threadIdx.x % TPR;
+  const size_t o = (size_t)r * D + part * CW;
+  const float* z0 = ft.Z0 + o;
+  const float* z1 = ft.Z1 + o;
+  const float* p0 = a.Sst + (((size_t)bh * 2 + 0) * (g.F + 1) + f) * DD + o;
+  const float* p1 = a.Sst + (((size_t)bh * 2 + 1) * (g.F + 1) + f + 1) * DD + o;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) s = fmaf(z0[c], p0[c], fmaf(z1[c], p1[c], s));
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, TPR);
+  if (part == 0) a.dalpha[((size_t)bh * g.F + f) * D + r] += s;
 }
 
 template <typename T>
@@ -1082,11 +1318,10 @@ __global__ __launch_bounds__(256) void vda_bwd_token_kernel(VdaBwdArgs<T> a) {
 // (the last since k dW v = v dW^T k).
 template <int D>
 __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16_t> a) {
-  constexpr int CPT = D / 16, MP = D + 1, NB = D / 32, NKK = D / 16;
+  constexpr int MP = D + 1, NB = D / 32, NKK = D / 16;
   constexpr int SUBT = 4 / NB;            // token sub-tiles per step
   constexpr int TPS = 32 * SUBT;          // tokens per step
-  __shared__ __attribute__((aligned(16))) union {
-    ZSStage<D> zs;
+  __shared__ __attribute__((aligned(16))) struct {
     float am[D * MP];
   } u;
   __shared__ float red[2][4][32];
@@ -1095,7 +1330,7 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
   const int nfr = g.F + (g.T > 0 ? 1 : 0);
   const int f = blockIdx.x % nfr;
   const int bh = blockIdx.x / nfr;
-  const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
   const FrameTok<bf16_t> ft = frame_tok<bf16_t, D>(a, bh, f);
   if (!ft.text) alpha_scan_term<bf16_t, D>(a, ft, bh, f);
@@ -1104,13 +1339,35 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
     return;
   }
   {
-    float acc[CPT][CPT];
-    frame_zst<D>(ft.Z0, ft.S0, ft.Z1, ft.S1, u.zs, acc);
-    __syncthreads();                           // staging dead: u.am takes its place
+    // dA = -(Z0 S0^T + Z1 S1^T) on v_mfma_f32_32x32x2f32, operands straight
+    // from memory: rows of Z (A) and of S (B), 4 consecutive columns per
+    // lane half and load.  Wave w computes the 32 x 32 blocks w + 4 b.
+    constexpr int NGB = NB * NB / 4, NK8 = D / 8;
+    f32x16 acc[NGB];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
+    for (int b = 0; b < NGB; ++b) acc[b] = f32x16{};
+    for (int src = 0; src < (ft.Z1 ? 2 : 1); ++src) {
+      const float* Zs = src ? ft.Z1 : ft.Z0;
+      const float* Ss = src ? ft.S1 : ft.S0;
+#pragma unroll 2
+      for (int j = 0; j < NK8; ++j) {
+        const int v0 = 8 * j + 4 * hg;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) u.am[(grp + 16 * i) * MP + sub + 16 * j] = -acc[i][j];
+        for (int b = 0; b < NGB; ++b) {
+          const int blk = wave + 4 * b, ib = blk / NB, jb = blk % NB;
+          const f32x4 za = *reinterpret_cast<const f32x4*>(Zs + (size_t)(ib * 32 + l32) * D + v0);
+          const f32x4 sb = *reinterpret_cast<const f32x4*>(Ss + (size_t)(jb * 32 + l32) * D + v0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[b] = mfma32x32x2f32(za[q], sb[q], acc[b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NGB; ++b) {
+      const int blk = wave + 4 * b, ib = blk / NB, jb = blk % NB;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u.am[(ib * 32 + mfma32_row(i, hg)) * MP + jb * 32 + l32] = -acc[b][i];
+    }
   }
   __syncthreads();
   // A-operand fragments of the wave's channel rows
@@ -1217,15 +1474,21 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
   }
 }
 
-// 8. dgamma = sum of the per-(b, h, frame) partial sums.
-template <int D>
-__global__ __launch_bounds__(128) void vda_bwd_dgamma_kernel(const float* __restrict__ dgp, long long rows,
-                                                             float* __restrict__ dgamma) {
-  const int c = threadIdx.x;
-  if (c >= D) return;
+// 8. dgamma = sum of the per-(b, h, frame) partial sums: one workgroup per
+//    channel, a fixed-order tree over the rows.
+__global__ __launch_bounds__(256) void vda_bwd_dgamma_kernel(const float* __restrict__ dgp, long long rows,
+                                                             int D, float* __restrict__ dgamma) {
+  __shared__ float part[256];
+  const int c = blockIdx.x;
   float s = 0.f;
-  for (long long r = 0; r < rows; ++r) s += dgp[r * D + c];
-  dgamma[c] = s;
+  for (long long r = threadIdx.x; r < rows; r += 256) s += dgp[r * D + c];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dgamma[c] = part[0];
 }
 
 template <typename T, int D>
@@ -1239,16 +1502,23 @@ hipError_t launch_all(const VdaBwdArgs<T>& a, const float* Tf, const float* Uf, 
   else
     vda_bwd_readout_kernel<T, D><<<BH * g.F, 256, 0, s>>>(a);
   vda_bwd_dp_kernel<T, D><<<BH * 2 * (g.C + 1), 256, 0, s>>>(a);
-  vda_bwd_alpha_bridge_kernel<T, D><<<BH, 128, 0, s>>>(a);
-  vda_bwd_chunk_adjoint_kernel<T, D><<<BH * 2 * NCB, 256, 0, s>>>(a);
+  vda_bwd_alpha_bridge_kernel<T, D><<<BH * (D / kBridgeCh), 64,
+                                      ((size_t)5 * g.F * kBridgeCh + 2 * g.F + 2 * g.C + 1) * 4, s>>>(a);
+  if constexpr (D == 64 || D == 128)
+    vda_bwd_chunk_adjoint_mfma_kernel<T, D><<<BH * 2 * NCB, 256, 0, s>>>(a);
+  else
+    vda_bwd_chunk_adjoint_kernel<T, D><<<BH * 2 * NCB, 256, 0, s>>>(a);
   if (g.T > 0) vda_bwd_text_kernel<T, D><<<BH * NCB, 256, 0, s>>>(a);
-  vda_bwd_frame_adjoint_kernel<T, D><<<BH * 2 * g.C * NCB, 256, 0, s>>>(a, Tf, Uf);
+  if constexpr (D == 64 || D == 128)
+    vda_bwd_frame_adjoint_mfma_kernel<T, D><<<BH * 2 * g.C * NCB, 256, 0, s>>>(a, Tf, Uf);
+  else
+    vda_bwd_frame_adjoint_kernel<T, D><<<BH * 2 * g.C * NCB, 256, 0, s>>>(a, Tf, Uf);
   const unsigned nfr = BH * (g.F + (g.T > 0 ? 1 : 0));
   if constexpr (std::is_same<T, bf16_t>::value && (D == 64 || D == 128))
     vda_bwd_token_mfma_kernel<D><<<nfr, 256, 0, s>>>(a);
   else
     vda_bwd_token_kernel<T, D><<<nfr, 256, 0, s>>>(a);
-  if (dgamma && a.dgp) vda_bwd_dgamma_kernel<D><<<1, 128, 0, s>>>(a.dgp, (long long)BH * g.F, dgamma);
+  if (dgamma && a.dgp) vda_bwd_dgamma_kernel<<<D, 256, 0, s>>>(a.dgp, (long long)BH * g.F, D, dgamma);
   return hipGetLastError();
 }
 

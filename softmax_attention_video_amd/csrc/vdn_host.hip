@@ -687,6 +687,7 @@ vdn_status vda_bwd(const void* q, const void* k, const void* v, const float* bet
   if (g.T > 0) {
     NEED(k_text); NEED(v_text); NEED(beta_text); NEED(dk_text); NEED(dv_text); NEED(dbeta_text);
   }
+  if (g.F > 1024) return fail(VDN_ERR_UNSUPPORTED, "F=%d: the linear-branch backward supports F <= 1024", g.F);
   const VdaBwdLayout lay = vda_bwd_layout(g);
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;

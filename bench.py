@@ -305,6 +305,63 @@ def measure_bwd(cfg, t, reps: int = 3) -> dict:
             "note": "S and dP are computed in both kernels: 14 d MFMA flops per pair against the 10 d counted"}
 
 
+def measure_vda_bwd(cfg, t, reps: int = 5) -> dict:
+    """Backward of the linear branch (vda_bwd) on the layer's inputs with a
+    seeded random gradient of Ohat_l: HIP-event time of the whole call and,
+    through the library's kernel timer, of its longest kernel, the readout
+    adjoint (recompute q M, RMSNorm/gate adjoint, dq = dO M^T, G = Q^T dO).
+    That kernel is bound by HBM (6 N d^2 flops per frame against the bytes
+    of q, dOhat, dq and G): its algorithmic bytes per launch are q and
+    dOhat read once, dq written once (2 B each per element), G written (fp32
+    d x d per frame) and the chunk-boundary states read once (fp32)."""
+    import torch
+
+    import softmax_attention_video_amd as vdn
+
+    B, H, L, d = t["q"].shape
+    dev = t["q"].device
+    if t["q"].dtype != torch.bfloat16:
+        return {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    dout = torch.randn((B, L, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dims = vdn.Dims(B, H, cfg.F, cfg.N, cfg.T, d, d, H * d)
+    p = vdn.Params().c()
+    ws = torch.empty(vdn.lib().vda_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p), vdn.VDN_BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        return vdn.vda_bwd(t["q"], t["k"], t["v"], t["beta"], t["alpha"], t["k_text"], t["v_text"],
+                           t["beta_text"], t["g_l"], dout, gamma=t["gamma"], want_dg=True,
+                           want_dgamma=True, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    timer = vdn.KernelTimer(reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    k_ms = timer.read()
+    timer.close()
+    ms = e0.elapsed_time(e1) / reps
+    C = cfg.F // 5
+    nbytes = 3.0 * B * H * L * d * 2 + B * H * cfg.F * d * d * 4 + 2.0 * B * H * (C + 1) * d * d * 4
+    flops = 6.0 * B * H * L * d * d
+    kms = float(k_ms.mean())
+    gbps = nbytes / (kms / 1e3) / 1e9
+    del ws, dout
+    return {"entry": "vda_bwd (dq, dk, dv, dbeta, dalpha, text gradients, dg_l, dgamma)",
+            "workload": f"{cfg.name}: linear-branch backward, B={B} H={H} d={d} F={cfg.F} N={cfg.N} T={cfg.T}",
+            "ms": ms, "tokens_per_s": B * L / (ms / 1e3),
+            "kernel": f"vda_bwd_readout_mfma_kernel<{d}>", "kernel_ms": kms, "bound": "hbm",
+            "achieved": gbps, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBS,
+            "algorithmic_bytes": nbytes, "kernel_flops": flops,
+            "kernel_tflops": flops / (kms / 1e3) / 1e12}
+
+
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 / MX-FP8 MFMA (2 x the bf16 peak)
 
 
@@ -376,6 +433,8 @@ def main() -> int:
                     help="skip the separate text-keys-in-Softmax measurement")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the separate MX-FP8 merge measurement")
+    ap.add_argument("--no-vda-bwd", action="store_true",
+                    help="skip the linear-branch backward leg")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the separate Softmax-backward measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -523,6 +582,11 @@ def main() -> int:
         r = res["softmax_bwd"]
         print(f"[bench] Softmax backward: {r['ms']:.3f} ms, kernels {r['kernel_ms']:.3f} ms, "
               f"{r['achieved']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_vda_bwd and cfg.dtype == "bf16":
+        res["vda_bwd"] = measure_vda_bwd(cfg, t)
+        r = res["vda_bwd"]
+        print(f"[bench] linear-branch backward: {r['ms']:.3f} ms, readout adjoint {r['kernel_ms']:.3f} ms, "
+              f"{r['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(res), flush=True)

@@ -1493,14 +1493,17 @@ __global__ __launch_bounds__(256) void vda_bwd_dgamma_kernel(const float* __rest
 
 template <typename T, int D>
 hipError_t launch_all(const VdaBwdArgs<T>& a, const float* Tf, const float* Uf, float* dgamma,
-                      hipStream_t s) {
+                      int stage, hipStream_t s) {
   const Geometry& g = a.g;
   const unsigned BH = (unsigned)(g.B * g.H);
   constexpr int NCB = (D + kBCB - 1) / kBCB;
-  if constexpr (std::is_same<T, bf16_t>::value && (D == 64 || D == 128))
-    vda_bwd_readout_mfma_kernel<D><<<BH * g.F, 256, 0, s>>>(a);
-  else
-    vda_bwd_readout_kernel<T, D><<<BH * g.F, 256, 0, s>>>(a);
+  if (stage == 0) {
+    if constexpr (std::is_same<T, bf16_t>::value && (D == 64 || D == 128))
+      vda_bwd_readout_mfma_kernel<D><<<BH * g.F, 256, 0, s>>>(a);
+    else
+      vda_bwd_readout_kernel<T, D><<<BH * g.F, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   vda_bwd_dp_kernel<T, D><<<BH * 2 * (g.C + 1), 256, 0, s>>>(a);
   vda_bwd_alpha_bridge_kernel<T, D><<<BH * (D / kBridgeCh), 64,
                                       ((size_t)5 * g.F * kBridgeCh + 2 * g.F + 2 * g.C + 1) * 4, s>>>(a);
@@ -1527,16 +1530,17 @@ hipError_t launch_all(const VdaBwdArgs<T>& a, const float* Tf, const float* Uf, 
 template <typename T>
 hipError_t launch_vda_bwd(const Geometry& g, const VdaBwdPtrs& p, const T* q, const T* k, const T* v,
                           const T* k_text, const T* v_text, const T* d_out, T* dq, T* dk, T* dv,
-                          T* dk_text, T* dv_text, float eps, float init_scale, hipStream_t s) {
+                          T* dk_text, T* dv_text, float eps, float init_scale, int stage,
+                          hipStream_t s) {
   VdaBwdArgs<T> a{g, q, k, v, p.beta, p.alpha, k_text, v_text, p.beta_text, p.g_l, p.gamma, d_out,
                   eps, init_scale, p.Pf, p.Pr, p.St, p.Xf, p.Tc, p.G, p.Dbr, p.dDbr,
                   p.dgamma ? p.dgp : nullptr, p.dP, p.mu, p.Sst, p.Zst, p.ZT, p.Rscr, dq, dk, dv,
                   p.dbeta, p.dalpha, dk_text, dv_text, p.dbeta_text, p.dg_l};
   switch (g.D) {
-    case 16: return launch_all<T, 16>(a, p.Tf, p.Uf, p.dgamma, s);
-    case 32: return launch_all<T, 32>(a, p.Tf, p.Uf, p.dgamma, s);
-    case 64: return launch_all<T, 64>(a, p.Tf, p.Uf, p.dgamma, s);
-    case 128: return launch_all<T, 128>(a, p.Tf, p.Uf, p.dgamma, s);
+    case 16: return launch_all<T, 16>(a, p.Tf, p.Uf, p.dgamma, stage, s);
+    case 32: return launch_all<T, 32>(a, p.Tf, p.Uf, p.dgamma, stage, s);
+    case 64: return launch_all<T, 64>(a, p.Tf, p.Uf, p.dgamma, stage, s);
+    case 128: return launch_all<T, 128>(a, p.Tf, p.Uf, p.dgamma, stage, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1544,10 +1548,10 @@ hipError_t launch_vda_bwd(const Geometry& g, const VdaBwdPtrs& p, const T* q, co
 template hipError_t launch_vda_bwd<float>(const Geometry&, const VdaBwdPtrs&, const float*, const float*,
                                           const float*, const float*, const float*, const float*,
                                           float*, float*, float*, float*, float*, float, float,
-                                          hipStream_t);
+                                          int, hipStream_t);
 template hipError_t launch_vda_bwd<bf16_t>(const Geometry&, const VdaBwdPtrs&, const bf16_t*,
                                            const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*,
                                            const bf16_t*, bf16_t*, bf16_t*, bf16_t*, bf16_t*, bf16_t*,
-                                           float, float, hipStream_t);
+                                           float, float, int, hipStream_t);
 
 }  // namespace vdn

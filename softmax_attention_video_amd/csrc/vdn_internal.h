@@ -104,7 +104,8 @@ hipError_t launch_vda_readout(const Geometry& g, const T* q, const float* alpha,
 // ---- linear-branch backward ----
 // Workspace and fp32 arguments of launch_vda_bwd (device pointers).  The
 // forward recompute (Tf, Uf, Pf, Pr, St, Xf, Tc) must be in place before the
-// launch; the rest is scratch or output.
+// launch; the rest is scratch or output.  stage 0 launches the readout
+// adjoint, stage 1 everything after it.
 struct VdaBwdPtrs {
   const float *beta, *alpha, *beta_text, *g_l, *gamma;
   const float *Tf, *Uf, *Pf, *Pr, *St, *Xf, *Tc;
@@ -114,7 +115,8 @@ struct VdaBwdPtrs {
 template <typename T>
 hipError_t launch_vda_bwd(const Geometry& g, const VdaBwdPtrs& p, const T* q, const T* k, const T* v,
                           const T* k_text, const T* v_text, const T* d_out, T* dq, T* dk, T* dv,
-                          T* dk_text, T* dv_text, float eps, float init_scale, hipStream_t s);
+                          T* dk_text, T* dv_text, float eps, float init_scale, int stage,
+                          hipStream_t s);
 
 // ---- merge ----
 // out[M,Dm] = A0[M,K] W0[K,Dm] + A1[M,K] W1[K,Dm]   (bf16 path via W^T)

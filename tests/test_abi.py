@@ -299,3 +299,40 @@ def test_softmax_bwd_validation():
     assert fn(*args, fake, big, ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED
     need = L.vdn_softmax_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16)
     assert need >= 2 * 20 * 16 * 64 * 2 + 2 * 20 * 16 * 4
+
+
+def test_vda_bwd_validation():
+    """Host-side checks of vda_bwd: required pointers, text pointers when
+    T > 0, workspace size, the frame limit, and the workspace query."""
+    L = vdn.lib()
+    fake = ctypes.c_void_p(0x100000)
+    d = _dims()                       # T = 4
+    p = vdn.Params().c()
+    big = ctypes.c_size_t(1 << 40)
+    args = [fake] * 21                # q k v beta alpha k_text v_text beta_text g_l gamma d_out dq dk dv
+    fn = L.vda_bwd                    # dbeta dalpha dk_text dv_text dbeta_text dg_l dgamma
+    for i in (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 12, 13, 14, 15, 16, 17, 18):
+        a = list(args)
+        a[i] = None
+        assert fn(*a, fake, big, ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG, i
+    for i in (9, 19, 20):             # gamma, dg_l, dgamma are optional: the call gets past the checks
+        a = list(args)
+        a[i] = None
+        assert fn(*a, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16,
+                  None) == vdn.VDN_ERR_WORKSPACE, i
+    d0 = _dims()
+    d0.T = 0                          # no text: its pointers may be NULL
+    a = list(args)
+    for i in (5, 6, 7, 16, 17, 18):
+        a[i] = None
+    assert fn(*a, fake, ctypes.c_size_t(16), ctypes.byref(d0), ctypes.byref(p), vdn.VDN_BF16,
+              None) == vdn.VDN_ERR_WORKSPACE
+    dbig = _dims()
+    dbig.F, dbig.N = 1030, 1          # 206 chunks of 5: beyond the frame limit
+    assert fn(*args, fake, big, ctypes.byref(dbig), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED
+    need = L.vda_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16)
+    BH, F, D, C = d.B * d.H, d.F, d.d_k, d.F // 5
+    assert need >= 4 * BH * D * D * (3 * F + 1 + 4 * C + 2 * (C + 1) + F + 4 * (C + 1) + 2 * (F + 1) + 2 * F)
+    bad = _dims()
+    bad.d_k = bad.d_v = 48
+    assert L.vda_bwd_workspace_bytes(ctypes.byref(bad), ctypes.byref(p), vdn.VDN_BF16) == 0

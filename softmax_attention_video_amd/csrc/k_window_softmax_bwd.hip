@@ -11,8 +11,8 @@
 // where lse is the forward's log-sum-exp, so P needs no renormalisation.
 //
 // Work split: a query-stationary pass computes dQ over the same items as the
-// forward (query groups and their key spans); a key-stationary pass computes
-// dK and dV.  Visibility is symmetric, so the forward's items read with the
+// forward (query groups and their key spans); two key-stationary passes
+// compute dV and dK.  Visibility is symmetric, so the forward's items read with the
 // roles swapped (the group's frames as keys, its spans as the queries that
 // see them) cover every (query, key) pair exactly once, and every output row
 // is written by one workgroup: no atomics.
@@ -267,7 +267,7 @@ struct BwdArgs {
 };
 
 constexpr int kBwdQW = 8;          // dQ kernel: waves (32 queries each)
-constexpr int kBwdKW = 4;          // dK/dV kernel: key blocks of 32 per workgroup (two waves each)
+constexpr int kBwdKW = 8;          // dK / dV kernels: key blocks of 32 per workgroup (one wave each)
 constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per staged tile (dK/dV)
 
 template <int D>
@@ -401,30 +401,35 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
     }
 }
 
-// dK, dV (key-stationary; the item's frames are the keys, its spans the
-// queries that see them): 8 waves, two per block of 32 keys -- waves 0..3
-// accumulate dV, waves 4..7 dK -- so each wave holds one accumulator set and
-// two waves share each SIMD.  Per 32-query block:
+// dK or dV (key-stationary; the item's frames are the keys, its spans the
+// queries that see them), one role per kernel so each gets its own register
+// budget: 8 waves, one per block of 32 keys, two waves per SIMD.  Per
+// 32-query block:
 //   S   = Q K^T         (A: Q rows from LDS in key_perm order, B: K fragments)
 //   P = exp2(S scale log2e - lse log2e)
-//   dV waves:  dV^T += dO^T P   (A: dO^T rows from LDS, B: P from registers)
-//   dK waves:  dP = dO V^T      (A: dO rows from LDS, B: V fragments)
-//              dS = P (dP - Dq),  dK^T += Q^T dS  (A: Q^T rows, B: dS)
+//   ROLE 0 (dV):  dV^T += dO^T P   (A: dO^T rows from LDS, B: P from registers)
+//   ROLE 1 (dK):  dP = dO V^T      (A: dO rows from LDS, B: V fragments)
+//                 dS = P (dP - Dq),  dK^T += Q^T dS  (A: Q^T rows, B: dS)
 // A lane holds one key and 16 queries; the block's lse and Dq come from LDS
-// (queries past the span: lse = +inf, so P = 0).
-template <int D>
-__global__ __launch_bounds__(2 * kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
-  constexpr int NT = 2 * kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
+// (queries past the span: lse = +inf, so P = 0).  In the dV kernel the
+// tile's two query blocks are software-pipelined (block 1's S among block
+// 0's exponentials, block 0's accumulation among block 1's).  The next tile
+// is staged in two pieces: the row tiles after block 0's products, the
+// transposed tile and lse / Dq at the end.
+template <int D, int ROLE>
+__global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
+  constexpr int NT = kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
   constexpr int KP = D + 8, TP = BQ + 8;
   constexpr int NKK = D / 16, NDB = D / 32, NB = BQ / 32;
   constexpr int RCH = BQ * D / 8 / NT, TCH = D * BQ / 8 / NT;
   static_assert(RCH * NT * 8 == BQ * D && TCH * NT * 8 == D * BQ, "tile split");
+  static_assert(NB == 2, "two query blocks per tile");
+  constexpr bool DK = ROLE == 1;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Ds[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Qts[2][D * TP];
-  __shared__ __attribute__((aligned(16))) bf16_t Dts[2][D * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Ds[DK ? 2 : 1][DK ? BQ * KP : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t Ts[2][D * TP];     // dO^T (dV) or Q^T (dK)
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Dd[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Dd[DK ? 2 : 1][BQ];
   const Geometry& g = a.g;
   Item it;
   int k0;
@@ -434,147 +439,179 @@ __global__ __launch_bounds__(2 * kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(
   const size_t hb = (size_t)it.bh * L * D;
   const bf16_t* Q = a.q + hb;
   const bf16_t* dO = a.dO + hb;
-  const bf16_t* Qt = a.qt + hb;
-  const bf16_t* dOt = a.dOt + hb;
+  const bf16_t* Tg = (DK ? a.qt : a.dOt) + hb;
   const float* lse = a.lse + (size_t)it.bh * L;
   const float* Dq = a.Dq + (size_t)it.bh * L;
-  const bool kwave = wave >= kBwdKW;          // this wave accumulates dK (else dV)
-  const int krow = k0 + (wave % kBwdKW) * 32 + l32;
+  const int krow = k0 + wave * 32 + l32;
   const bool kvalid = krow < it.q_end;
-  bf16x8 kf[NKK], vf[NKK];
+  bf16x8 kf[NKK], vf[DK ? NKK : 1];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (kvalid) {
-      x = ld16(a.k + hb + (size_t)krow * D + kk * 16 + hg * 8);
-      if (kwave) y = ld16(a.v + hb + (size_t)krow * D + kk * 16 + hg * 8);
-    }
+    u32x4 x = {0, 0, 0, 0};
+    if (kvalid) x = ld16(a.k + hb + (size_t)krow * D + kk * 16 + hg * 8);
     kf[kk] = as_bf16x8(x);
-    vf[kk] = as_bf16x8(y);
+    if constexpr (DK) {
+      u32x4 y = {0, 0, 0, 0};
+      if (kvalid) y = ld16(a.v + hb + (size_t)krow * D + kk * 16 + hg * 8);
+      vf[kk] = as_bf16x8(y);
+    }
   }
   f32x16 acc[NDB];
 #pragma unroll
   for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
   const SpanWalk<BQ, 3> walk(it);
   const uint32_t t_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
-  u32x4 cr[2 * RCH + 2 * TCH];
+  u32x4 c0r[(DK ? 2 : 1) * RCH], c1r[TCH];
   float cl = 0.f, cd = 0.f;
-  auto load_tile = [&](int j) {
+  auto load_piece0 = [&](int j) {      // Q rows (and dO rows)
     int qs, nq;
     walk.tile(j, qs, nq);
     const rsrc_t rq = make_rsrc(Q + (size_t)qs * D, (uint32_t)nq * D * 2);
     const rsrc_t rd = make_rsrc(dO + (size_t)qs * D, (uint32_t)nq * D * 2);
-    const rsrc_t rqt = make_rsrc(Qt + qs, t_bytes - (uint32_t)qs * 2);
-    const rsrc_t rdt = make_rsrc(dOt + qs, t_bytes - (uint32_t)qs * 2);
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = tid + NT * i;
       const uint32_t off = (uint32_t)((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
-      cr[i] = buf_ld16(rq, off);
-      cr[RCH + i] = buf_ld16(rd, off);
-    }
-#pragma unroll
-    for (int i = 0; i < TCH; ++i) {
-      const int c = tid + NT * i;
-      const int r = c / (BQ / 8), c8 = c % (BQ / 8);
-      const uint32_t off = c8 * 8 < nq ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u;
-      cr[2 * RCH + i] = buf_ld16(rqt, off);
-      cr[2 * RCH + TCH + i] = buf_ld16(rdt, off);
-    }
-    if (tid < BQ) {
-      cl = tid < nq ? lse[qs + tid] * kLog2e : INFINITY;
-      cd = tid < nq ? Dq[qs + tid] : 0.f;
+      c0r[i] = buf_ld16(rq, off);
+      if constexpr (DK) c0r[RCH + i] = buf_ld16(rd, off);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_piece0 = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = tid + NT * i;
       const int off = (c / (D / 8)) * KP + (c % (D / 8)) * 8;
-      st16(&Qs[buf][off], cr[i]);
-      st16(&Ds[buf][off], cr[RCH + i]);
+      st16(&Qs[buf][off], c0r[i]);
+      if constexpr (DK) st16(&Ds[buf][off], c0r[RCH + i]);
     }
+  };
+  auto load_piece1 = [&](int j) {      // the transposed tile, lse and Dq
+    int qs, nq;
+    walk.tile(j, qs, nq);
+    const rsrc_t rt = make_rsrc(Tg + qs, t_bytes - (uint32_t)qs * 2);
 #pragma unroll
     for (int i = 0; i < TCH; ++i) {
       const int c = tid + NT * i;
-      const int off = (c / (BQ / 8)) * TP + (c % (BQ / 8)) * 8;
-      st16(&Qts[buf][off], cr[2 * RCH + i]);
-      st16(&Dts[buf][off], cr[2 * RCH + TCH + i]);
+      const int r = c / (BQ / 8), c8 = c % (BQ / 8);
+      c1r[i] = buf_ld16(rt, c8 * 8 < nq ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u);
+    }
+    if (tid < BQ) {
+      cl = tid < nq ? lse[qs + tid] * kLog2e : INFINITY;
+      if constexpr (DK) cd = tid < nq ? Dq[qs + tid] : 0.f;
+    }
+  };
+  auto store_piece1 = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TCH; ++i) {
+      const int c = tid + NT * i;
+      st16(&Ts[buf][(c / (BQ / 8)) * TP + (c % (BQ / 8)) * 8], c1r[i]);
     }
     if (tid < BQ) {
       Ls[buf][tid] = cl;
-      Dd[buf][tid] = cd;
+      if constexpr (DK) Dd[buf][tid] = cd;
     }
   };
   const int rperm = key_perm(l32);
+  auto qk = [&](int buf, int blk, const bf16x8* frag, const bf16_t* base) {
+    f32x16 x = {};
+    const bf16_t* r = base + (blk * 32 + rperm) * KP + hg * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) x = mfma32x32x16(as_bf16x8(ld16(r + kk * 16)), frag[kk], x);
+    return x;
+  };
+  auto accum = [&](int buf, int blk, const bf16x8* pb) {
+    const int col = blk * 32 + hg * 16;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) {
+        const bf16x8 tf = as_bf16x8(ld16(Ts[buf] + (b * 32 + l32) * TP + col + h2 * 8));
+        acc[b] = mfma32x32x16(tf, pb[h2], acc[b]);
+      }
+  };
+  // P (dV) or dS = P (dP - Dq) (dK) of one block, as bf16 MFMA operands
+  auto probs = [&](int buf, int blk, const f32x16& sv, const f32x16& dpv, bf16x8* pb) {
+    const int col = blk * 32 + hg * 16;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][col + 4 * i4]);
+      f32x4 d4 = {};
+      if constexpr (DK) d4 = *reinterpret_cast<const f32x4*>(&Dd[buf][col + 4 * i4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        const float pv = fast_exp2(fmaf(sv[i], a.scale_log2, -l4[e]));
+        pb[i >> 3][i & 7] = static_cast<__bf16>(DK ? pv * (dpv[i] - d4[e]) : pv);
+      }
+    }
+  };
   if (walk.n > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_piece0(0);
+    load_piece1(0);
+    store_piece0(0);
+    store_piece1(0);
   }
   __syncthreads();
   for (int j = 0; j < walk.n; ++j) {
     const int buf = j & 1;
-    if (j + 1 < walk.n) load_tile(j + 1);
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      const bf16_t* qr = Qs[buf] + (blk * 32 + rperm) * KP + hg * 8;
-      const bf16_t* dr = Ds[buf] + (blk * 32 + rperm) * KP + hg * 8;
-      const int col = blk * 32 + hg * 16;   // the 16 queries this lane half holds
-      if (!kwave) {
-        f32x16 s = {};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) s = mfma32x32x16(as_bf16x8(ld16(qr + kk * 16)), kf[kk], s);
-        bf16x8 pb[2];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][col + 4 * i4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            pb[i >> 3][i & 7] = static_cast<__bf16>(fast_exp2(fmaf(s[i], a.scale_log2, -l4[e])));
-          }
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int b = 0; b < NDB; ++b) {
-            const bf16x8 dtf = as_bf16x8(ld16(Dts[buf] + (b * 32 + l32) * TP + col + h2 * 8));
-            acc[b] = mfma32x32x16(dtf, pb[h2], acc[b]);
-          }
-      } else {
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          s = mfma32x32x16(as_bf16x8(ld16(qr + kk * 16)), kf[kk], s);
-          dp = mfma32x32x16(as_bf16x8(ld16(dr + kk * 16)), vf[kk], dp);
-        }
-        bf16x8 sb[2];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][col + 4 * i4]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dd[buf][col + 4 * i4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const float p = fast_exp2(fmaf(s[i], a.scale_log2, -l4[e]));
-            sb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - d4[e]));
-          }
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int b = 0; b < NDB; ++b) {
-            const bf16x8 qtf = as_bf16x8(ld16(Qts[buf] + (b * 32 + l32) * TP + col + h2 * 8));
-            acc[b] = mfma32x32x16(qtf, sb[h2], acc[b]);
-          }
+    const bool more = j + 1 < walk.n;
+    if (more) load_piece0(j + 1);
+    bf16x8 p0[2], p1[2];
+    if constexpr (!DK) {
+      const f32x16 s0 = qk(buf, 0, kf, Qs[buf]);
+      if (more) {                               // that buffer was released by the last barrier
+        store_piece0(buf ^ 1);
+        load_piece1(j + 1);
       }
+      const f32x16 s1 = qk(buf, 1, kf, Qs[buf]);
+      probs(buf, 0, s0, s0, p0);
+      accum(buf, 0, p0);
+      probs(buf, 1, s1, s1, p1);
+      accum(buf, 1, p1);
+      // issue order: block 0's S; the next tile's row stores; block 1's S
+      // among block 0's exponentials; block 0's products among block 1's
+      // exponentials; block 1's products
+#pragma unroll
+      for (int u = 0; u < NKK; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, RCH, 0);
+#pragma unroll
+      for (int u = 0; u < NKK; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 2 * NDB; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    } else {
+      // one block after the other: the dK waves' registers (K and V fragments,
+      // S, dP, dS, the dK accumulators) leave no room for a second block in
+      // flight at two waves per SIMD
+      const f32x16 s0 = qk(buf, 0, kf, Qs[buf]);
+      const f32x16 dp0 = qk(buf, 0, vf, Ds[buf]);
+      if (more) {                               // that buffer was released by the last barrier
+        store_piece0(buf ^ 1);
+        load_piece1(j + 1);
+      }
+      probs(buf, 0, s0, dp0, p0);
+      accum(buf, 0, p0);
+      const f32x16 s1 = qk(buf, 1, kf, Qs[buf]);
+      const f32x16 dp1 = qk(buf, 1, vf, Ds[buf]);
+      probs(buf, 1, s1, dp1, p1);
+      accum(buf, 1, p1);
     }
-    if (j + 1 < walk.n) store_tile(buf ^ 1);
+    if (more) store_piece1(buf ^ 1);
     __syncthreads();
   }
   if (!kvalid) return;
-  bf16_t* orow = (kwave ? a.dk : a.dv) + hb + (size_t)krow * D;
-  const float sc = kwave ? a.scale : 1.f;
+  bf16_t* orow = (DK ? a.dk : a.dv) + hb + (size_t)krow * D;
+  const float sc = DK ? a.scale : 1.f;
 #pragma unroll
   for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -608,10 +645,12 @@ hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const u
   if (a.w.grid == 0) return hipSuccess;
   if (g.D == 128) {
     softmax_bwd_dq_mfma_kernel<128><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv_mfma_kernel<128><<<b.w.grid, 2 * kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<128, 0><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<128, 1><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
   } else {
     softmax_bwd_dq_mfma_kernel<64><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv_mfma_kernel<64><<<b.w.grid, 2 * kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<64, 0><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<64, 1><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
   }
   return hipGetLastError();
 }

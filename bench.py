@@ -305,7 +305,7 @@ def measure_bwd(cfg, t, reps: int = 3) -> dict:
             "note": "S is computed in all three kernels and dP in two: 16 d MFMA flops per pair against the 10 d counted"}
 
 
-def measure_vda_bwd(cfg, t, reps: int = 5) -> dict:
+def measure_vda_bwd(cfg, t, reps: int = 5, cpu: bool = True) -> dict:
     """Backward of the linear branch (vda_bwd) on the layer's inputs with a
     seeded random gradient of Ohat_l: HIP-event time of the whole call and,
     through the library's kernel timer, of its longest kernel, the readout
@@ -352,6 +352,23 @@ def measure_vda_bwd(cfg, t, reps: int = 5) -> dict:
     flops = 6.0 * B * H * L * d * d
     kms = float(k_ms.mean())
     gbps = nbytes / (kms / 1e3) / 1e9
+    cpu_res = None
+    if cpu:
+        # the oracle on head (0, 0) of the same inputs, in full, scaled to all heads
+        import numpy as np
+        import threadpoolctl
+        from oracle import vda_bwd as VB
+        f64 = lambda x: x.detach().float().cpu().numpy().astype(np.float64)
+        hd = {key: f64(t[key][0, 0]) for key in ("q", "k", "v", "beta", "alpha", "k_text", "v_text",
+                                                 "beta_text", "g_l")}
+        t0 = time.perf_counter()
+        VB.linear_branch_bwd(hd["q"], hd["k"], hd["v"], hd["beta"], hd["alpha"], hd["k_text"], hd["v_text"],
+                             hd["beta_text"], hd["g_l"], f64(t["gamma"]), f64(dout[0, :, 0]))
+        t_head = time.perf_counter() - t0
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        cpu_res = {"value": B * L / (t_head * B * H), "unit": "tokens/s", "cores": int(threads),
+                   "kind": "oracle",
+                   "sample": f"head (b=0,h=0) in full ({t_head:.2f} s), scaled to {B * H} heads"}
     del ws, dout
     return {"entry": "vda_bwd (dq, dk, dv, dbeta, dalpha, text gradients, dg_l, dgamma)",
             "workload": f"{cfg.name}: linear-branch backward, B={B} H={H} d={d} F={cfg.F} N={cfg.N} T={cfg.T}",
@@ -359,7 +376,7 @@ def measure_vda_bwd(cfg, t, reps: int = 5) -> dict:
             "kernel": f"vda_bwd_readout_mfma_kernel<{d}>", "kernel_ms": kms, "bound": "hbm",
             "achieved": gbps, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBS,
             "algorithmic_bytes": nbytes, "kernel_flops": flops,
-            "kernel_tflops": flops / (kms / 1e3) / 1e12}
+            "kernel_tflops": flops / (kms / 1e3) / 1e12, "cpu_baseline": cpu_res}
 
 
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 / MX-FP8 MFMA (2 x the bf16 peak)
@@ -583,7 +600,7 @@ def main() -> int:
         print(f"[bench] Softmax backward: {r['ms']:.3f} ms, kernels {r['kernel_ms']:.3f} ms, "
               f"{r['achieved']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_vda_bwd and cfg.dtype == "bf16":
-        res["vda_bwd"] = measure_vda_bwd(cfg, t)
+        res["vda_bwd"] = measure_vda_bwd(cfg, t, cpu=not args.no_cpu_baseline)
         r = res["vda_bwd"]
         print(f"[bench] linear-branch backward: {r['ms']:.3f} ms, readout adjoint {r['kernel_ms']:.3f} ms, "
               f"{r['achieved']:.0f} GB/s", file=sys.stderr, flush=True)

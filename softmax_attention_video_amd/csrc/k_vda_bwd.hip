@@ -287,6 +287,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     float pd[D * (D + 1)];    // G at the end of the frame
   } u;
   __shared__ float gsum[SUBT][D][33];
+  __shared__ __attribute__((aligned(16))) bf16_t qrow[2][TPS * DP];   // the step's Q rows
   __shared__ float red1[4][32], red2[4][32][2];
   __shared__ float dfs[D], drs[D];
   __shared__ __attribute__((aligned(16))) float gms[D];
@@ -344,12 +345,23 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
   for (int i = 0; i < 16; ++i) gacc[i] = 0.f;
 
   bf16x8 qf[NKK];
-  auto load_q = [&](int n, bf16x8* dst) {
+  // the next step's Q rows travel global -> registers -> LDS (qrow) while
+  // the current step runs: CQ 16-byte chunks per thread
+  constexpr int CQ = TPS * D / 8 / 256;
+  u32x4 qst[CQ];
+  auto fetch_q = [&](int n0) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 x = {0, 0, 0, 0};
-      if (n < g.N) x = ld16(a.q + (tok0 + n) * D + kk * 16 + hg * 8);
-      dst[kk] = as_bf16x8(x);
+    for (int i = 0; i < CQ; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c / (D / 8), c8 = c % (D / 8);
+      qst[i] = n0 + r < g.N ? ld16(a.q + (tok0 + n0 + r) * D + c8 * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto stage_q = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < CQ; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      st16(&qrow[b][(c / (D / 8)) * DP + (c % (D / 8)) * 8], qst[i]);
     }
   };
   const int nl = ts * 32 + l32;                 // token within the step
@@ -362,10 +374,16 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
       dst[i4] = n < g.N ? *reinterpret_cast<const u32x2*>(dob + 8 * i4 + 4 * hg) : u32x2{0, 0};
   };
   load_do(nl, dx);
-  for (int n0 = 0; n0 < g.N; n0 += TPS) {
+  fetch_q(0);
+  stage_q(0);
+  __syncthreads();
+  for (int n0 = 0, st = 0; n0 < g.N; n0 += TPS, st ^= 1) {
     const int n = n0 + nl;
     const bool valid = n < g.N;
-    load_q(n, qf);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(ld16(&qrow[st][nl * DP + kk * 16 + hg * 8]));
+    const bool more = n0 + TPS < g.N;
+    if (more) fetch_q(n0 + TPS);
     load_do(n + TPS, dxn);
     // Q^T tile: this wave writes its two k-steps
 #pragma unroll
@@ -490,6 +508,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) dx[i4] = dxn[i4];
+    if (more) stage_q(st ^ 1);      // that buffer was last read before the previous barrier
     __syncthreads();
   }
   // G -> memory and LDS; bridge adjoints dD = rowsum(G * P)

@@ -1446,32 +1446,62 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
       acc2 = mfma32x32x16(wtl[kk], bk[kk], acc2);
     }
     const bool valid = n < ntok;
+    // k and v at the accumulator positions (channels cb*32 + 8 i4 + 4 hg + r)
+    // come from the step's B fragments: k-steps 2 cb and 2 cb + 1 hold them,
+    // half in this lane and half in its partner (lane ^ 32); one
+    // v_permlane32_swap per fragment word exchanges them.
+    float kc[16], vc[16];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if ((kk >> 1) != cb) continue;       // wave-uniform: keeps the register index static
+      const int m = kk & 1;
+      const u32x4 wk = __builtin_bit_cast(u32x4, bk[kk]);
+      const u32x4 wv = __builtin_bit_cast(u32x4, bv[kk]);
+      uint32_t ok[4], pk_[4], ov[4], pv_[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const auto rk = __builtin_amdgcn_permlane32_swap(wk[w], wk[w], false, false);
+        const auto rv = __builtin_amdgcn_permlane32_swap(wv[w], wv[w], false, false);
+        ok[w] = hg ? rk[1] : rk[0];          // own word
+        pk_[w] = hg ? rk[0] : rk[1];         // the partner's
+        ov[w] = hg ? rv[1] : rv[0];
+        pv_[w] = hg ? rv[0] : rv[1];
+      }
+#pragma unroll
+      for (int odd = 0; odd < 2; ++odd) {
+        const int i4 = 2 * m + odd;
+        const bool own = hg == odd;
+        // words 0,1 (lower half's slots 0..3) for hg = 0, words 2,3 for hg = 1
+        const uint32_t k0w = own ? (hg ? ok[2] : ok[0]) : (hg ? pk_[2] : pk_[0]);
+        const uint32_t k1w = own ? (hg ? ok[3] : ok[1]) : (hg ? pk_[3] : pk_[1]);
+        const uint32_t v0w = own ? (hg ? ov[2] : ov[0]) : (hg ? pv_[2] : pv_[0]);
+        const uint32_t v1w = own ? (hg ? ov[3] : ov[1]) : (hg ? pv_[3] : pv_[1]);
+        kc[4 * i4 + 0] = bf16_to_f32((bf16_t)(k0w & 0xFFFFu));
+        kc[4 * i4 + 1] = bf16_to_f32((bf16_t)(k0w >> 16));
+        kc[4 * i4 + 2] = bf16_to_f32((bf16_t)(k1w & 0xFFFFu));
+        kc[4 * i4 + 3] = bf16_to_f32((bf16_t)(k1w >> 16));
+        vc[4 * i4 + 0] = bf16_to_f32((bf16_t)(v0w & 0xFFFFu));
+        vc[4 * i4 + 1] = bf16_to_f32((bf16_t)(v0w >> 16));
+        vc[4 * i4 + 2] = bf16_to_f32((bf16_t)(v1w & 0xFFFFu));
+        vc[4 * i4 + 3] = bf16_to_f32((bf16_t)(v1w >> 16));
+      }
+    }
     float db = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      db = fmaf(acc1[i], kc[i], db);
+      db = fmaf(acc2[i], vc[i], db);
+    }
     if (valid) {
       const float b = ft.bp[n];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int c0 = cb * 32 + 8 * i4 + 4 * hg;
-        const u32x2 kx = *reinterpret_cast<const u32x2*>(ft.kp + (size_t)n * D + c0);
-        const u32x2 vx = *reinterpret_cast<const u32x2*>(ft.vp + (size_t)n * D + c0);
-        float kc[4], vc[4];
-        kc[0] = bf16_to_f32((bf16_t)(kx[0] & 0xFFFFu)); kc[1] = bf16_to_f32((bf16_t)(kx[0] >> 16));
-        kc[2] = bf16_to_f32((bf16_t)(kx[1] & 0xFFFFu)); kc[3] = bf16_to_f32((bf16_t)(kx[1] >> 16));
-        vc[0] = bf16_to_f32((bf16_t)(vx[0] & 0xFFFFu)); vc[1] = bf16_to_f32((bf16_t)(vx[0] >> 16));
-        vc[2] = bf16_to_f32((bf16_t)(vx[1] & 0xFFFFu)); vc[3] = bf16_to_f32((bf16_t)(vx[1] >> 16));
         u32x2 pk, pv;
-        float e1[4], e2[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e1[r] = acc1[4 * i4 + r];
-          e2[r] = acc2[4 * i4 + r];
-          db = fmaf(e1[r], kc[r], db);
-          db = fmaf(e2[r], vc[r], db);
-        }
-        pk[0] = pack_bf16x2(b * e1[0], b * e1[1]);
-        pk[1] = pack_bf16x2(b * e1[2], b * e1[3]);
-        pv[0] = pack_bf16x2(b * e2[0], b * e2[1]);
-        pv[1] = pack_bf16x2(b * e2[2], b * e2[3]);
+        pk[0] = pack_bf16x2(b * acc1[4 * i4 + 0], b * acc1[4 * i4 + 1]);
+        pk[1] = pack_bf16x2(b * acc1[4 * i4 + 2], b * acc1[4 * i4 + 3]);
+        pv[0] = pack_bf16x2(b * acc2[4 * i4 + 0], b * acc2[4 * i4 + 1]);
+        pv[1] = pack_bf16x2(b * acc2[4 * i4 + 2], b * acc2[4 * i4 + 3]);
         *reinterpret_cast<u32x2*>(ft.dkp + (size_t)n * D + c0) = pk;
         *reinterpret_cast<u32x2*>(ft.dvp + (size_t)n * D + c0) = pv;
       }

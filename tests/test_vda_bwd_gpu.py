@@ -97,3 +97,14 @@ def test_vda_bwd_full_size_h3_sampled():
     rhs, mag = float(np.sum(terms)), float(np.sum(np.abs(terms)))
     log(f"[vda_bwd] h3 sum gamma*dgamma = {lhs:.6e}, sum g*dg = {rhs:.6e} (sum |g*dg| = {mag:.3e})")
     assert abs(lhs - rhs) <= 1e-4 * mag
+
+
+@pytest.mark.parametrize("name,heads", [("medium", [(0, 0), (0, 15)]), ("long", [(0, 0)])])
+def test_vda_bwd_config_sampled(name, heads):
+    """The medium configuration (5% of frames duplicated from their
+    predecessor: correlated writes) and the long one (F = 600, 120 chunks:
+    long anchor bridges, many scan groups), whole heads against the oracle."""
+    cfg = CONFIGS[name]
+    inp, dOl, got = _run(cfg)
+    ref = VB.vda_bwd(inp, dOl, oracle_params(None), heads=heads)
+    _compare(got, ref, GRADS, TOL[cfg.dtype], name, heads=heads)

@@ -119,10 +119,12 @@ __device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, f32x16
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, sa, OPSEL, sb);
 }
 
-// 8 waves (two per SIMD): wave (wm 0..3, wn 0..1) owns a 64 x 128 block of
-// the 256 x 256 tile, computed as out^T blocks (W^T rows are the MFMA's
-// first operand).  K2 (the concatenated contraction) is a multiple of 128.
-__global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __restrict__ a,
+// 4 waves (one per SIMD): wave (wm 0..1, wn 0..1) owns a 128 x 128 block of
+// the 256 x 256 tile (16 accumulator blocks), computed as out^T blocks (W^T
+// rows are the MFMA's first operand), so each fragment read from LDS feeds
+// four MFMAs; the next 64-deep step's fragments are read while the current
+// step's MFMAs run.  K2 (the concatenated contraction) is a multiple of 128.
+__global__ __launch_bounds__(256) void merge_gemm_mx_kernel(const uint8_t* __restrict__ a,
                                                             const uint8_t* __restrict__ a_sc,
                                                             const uint8_t* __restrict__ bt,
                                                             const uint8_t* __restrict__ b_sc,
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __res
                                                             int tiles_n, int rpx) {
   constexpr int BM = kMxBM, BN = kMxBN, BK = kMxBK;
   constexpr int P = BK + 16;                 // LDS row pitch in bytes
-  constexpr int CH = BM * BK / 16 / 512;     // 16-byte chunks per thread per operand and K step (4)
+  constexpr int CH = BM * BK / 16 / 256;     // 16-byte chunks per thread per operand and K step (8)
   constexpr int NSUB = BK / 64;              // 64-deep MFMA steps per K step (2)
   constexpr int CPS = CH / NSUB;             // chunks per operand staged per MFMA step (2)
   __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * P];
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __res
   const long long m0 = (long long)row * BM;
   const int n0 = col * BN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;   // 4 waves, each 128 x 128
   const int nkt = K2 / BK;
   const int nsc = K2 / 32;                   // scale bytes per row
   const rsrc_t ra = make_rsrc(a + (size_t)m0 * K2, rsrc_bytes(a + (size_t)m0 * K2, a + (size_t)M * K2));
@@ -160,23 +162,23 @@ __global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __res
   int soff[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = tid + 512 * i;
+    const int c = tid + 256 * i;
     const int r = c / (BK / 16), c16 = c % (BK / 16);
     voff[i] = (uint32_t)(r * K2 + c16 * 16);
     soff[i] = r * P + c16 * 16;
   }
-  // scale dwords of this lane's rows: A rows wm*64 + mb*32 + l32, W^T rows wn*128 + nb*32 + l32
-  uint32_t sa_off[2], sb_off[4];
+  // scale dwords of this lane's rows: A rows wm*128 + mb*32 + l32, W^T rows wn*128 + nb*32 + l32
+  uint32_t sa_off[4], sb_off[4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) sa_off[mb] = (uint32_t)((wm * 64 + mb * 32 + l32) * nsc);
+  for (int mb = 0; mb < 4; ++mb) sa_off[mb] = (uint32_t)((wm * 128 + mb * 32 + l32) * nsc);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) sb_off[nb] = (uint32_t)((wn * 128 + nb * 32 + l32) * nsc);
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   u32x4 pa[CH], pb[CH];
   auto load_piece = [&](int i, int kt) {    // K steps past the end re-read the last one
     kt = min(kt, nkt - 1);
@@ -188,12 +190,12 @@ __global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __res
     st16(&As[buf][soff[i]], pa[i]);
     st16(&Bs[buf][soff[i]], pb[i]);
   };
-  uint32_t sa[2], sb[4], sa_n[2], sb_n[4];
+  uint32_t sa[4], sb[4], sa_n[4], sb_n[4];
   auto load_scales = [&](uint32_t* da, uint32_t* db, int kt) {
     kt = min(kt, nkt - 1);
     const int kb = kt * 4;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
       da[mb] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsa, (int)sa_off[mb], kb, 0);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -209,11 +211,11 @@ __global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __res
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     load_scales(sa_n, sb_n, kt + 1);
-    const uint8_t* Ab = As[kt & 1] + (wm * 64 + l32) * P + hg * 16;
+    const uint8_t* Ab = As[kt & 1] + (wm * 128 + l32) * P + hg * 16;
     const uint8_t* Bb = Bs[kt & 1] + (wn * 128 + l32) * P + hg * 16;
-    uint32_t ssa[2], ssb[4];
+    uint32_t ssa[4], ssb[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) ssa[mb] = sa[mb] >> (8 * hg);
+    for (int mb = 0; mb < 4; ++mb) ssa[mb] = sa[mb] >> (8 * hg);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) ssb[nb] = sb[nb] >> (8 * hg);
     auto frag = [&](const uint8_t* base, int ks) {
@@ -224,21 +226,30 @@ __global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __res
       f[4] = (int)hi[0]; f[5] = (int)hi[1]; f[6] = (int)hi[2]; f[7] = (int)hi[3];
       return f;
     };
+    i32x8 fm[2][4], fn[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fm[0][i] = frag(Ab + i * 32 * P, 0);
+      fn[0][i] = frag(Bb + i * 32 * P, 0);
+    }
 #pragma unroll
     for (int ks = 0; ks < NSUB; ++ks) {
-      i32x8 fm[2], fn[4];
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < NSUB) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fm[i] = frag(Ab + i * 32 * P, ks);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fn[i] = frag(Bb + i * 32 * P, ks);
+        for (int i = 0; i < 4; ++i) {
+          fm[nxt][i] = frag(Ab + i * 32 * P, ks + 1);
+          fn[nxt][i] = frag(Bb + i * 32 * P, ks + 1);
+        }
+      }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 4; ++mb) {
           if (ks == 0)
-            acc[nb][mb] = mfma_mx<0>(fn[nb], fm[mb], acc[nb][mb], (int)ssb[nb], (int)ssa[mb]);
+            acc[nb][mb] = mfma_mx<0>(fn[cur][nb], fm[cur][mb], acc[nb][mb], (int)ssb[nb], (int)ssa[mb]);
           else
-            acc[nb][mb] = mfma_mx<2>(fn[nb], fm[mb], acc[nb][mb], (int)ssb[nb], (int)ssa[mb]);
+            acc[nb][mb] = mfma_mx<2>(fn[cur][nb], fm[cur][mb], acc[nb][mb], (int)ssb[nb], (int)ssa[mb]);
         }
       // stage chunks of the next K step, request them for the one after
 #pragma unroll
@@ -249,14 +260,14 @@ __global__ __launch_bounds__(512) void merge_gemm_mx_kernel(const uint8_t* __res
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) sa[mb] = sa_n[mb];
+    for (int mb = 0; mb < 4; ++mb) sa[mb] = sa_n[mb];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) sb[nb] = sb_n[nb];
     lds_barrier();
   }
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const long long m = m0 + wm * 64 + mb * 32 + l32;
+  for (int mb = 0; mb < 4; ++mb) {
+    const long long m = m0 + wm * 128 + mb * 32 + l32;
     if (m >= M) continue;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -281,7 +292,7 @@ hipError_t launch_merge_gemm_mx(const uint8_t* a, const uint8_t* a_sc, const uin
   const int rpx = (tm + kNumXcd - 1) / kNumXcd;
   const int groups = (rpx + kMxGroupRows - 1) / kMxGroupRows;
   const long long grid = (long long)kNumXcd * groups * kMxGroupRows * tn;
-  merge_gemm_mx_kernel<<<(unsigned)grid, 512, 0, s>>>(a, a_sc, bt, b_sc, out, M, K2, Dm, tm, tn, rpx);
+  merge_gemm_mx_kernel<<<(unsigned)grid, 256, 0, s>>>(a, a_sc, bt, b_sc, out, M, K2, Dm, tm, tn, rpx);
   return hipGetLastError();
 }
 

@@ -136,6 +136,9 @@ __global__ __launch_bounds__(256) void vda_chunk_compose_kernel(Geometry g, cons
 //   of the next frames for part U; the final Y is T_c / U_c.
 // Mode scan: grid (b, h, dir, column block); Y0 = init_scale * S_text,
 //   L_s = T_c, A_s = U_c in scan order; Y is written to P after every step.
+// Mode frame scan: the same grid and Y0, but L_s = T_f, A_s = U_f of the
+//   frames themselves in scan order (no composition), Y written to P at
+//   every chunk boundary.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void vda_chain_mfma_kernel(Geometry g, const float* __restrict__ Tf,
@@ -182,11 +185,18 @@ __global__ __launch_bounds__(256) void vda_chain_mfma_kernel(Geometry g, const f
     out_final = (part == 0 ? Tc : Uc) + (((size_t)bh * 2 + dir) * g.C + c) * DD;
   } else {
     float* P = dir == 0 ? P_fwd : P_rev;
-    nsteps = g.C;
-    const int c0 = dir == 0 ? 0 : g.C - 1;
     lstride = (dir == 0 ? 1 : -1) * (ptrdiff_t)DD;
-    L0 = Tc + (((size_t)bh * 2 + dir) * g.C + c0) * DD;
-    A0 = Uc + (((size_t)bh * 2 + dir) * g.C + c0) * DD;
+    if (mode == 1) {
+      nsteps = g.C;
+      const int c0 = dir == 0 ? 0 : g.C - 1;
+      L0 = Tc + (((size_t)bh * 2 + dir) * g.C + c0) * DD;
+      A0 = Uc + (((size_t)bh * 2 + dir) * g.C + c0) * DD;
+    } else {
+      nsteps = g.F;
+      const int f0 = dir == 0 ? 0 : g.F - 1;
+      L0 = Tf + ((size_t)bh * g.F + f0) * DD;
+      A0 = Uf + ((size_t)bh * g.F + f0) * DD;
+    }
     ysrc = S_text + (size_t)bh * DD;
     yscale = init_scale;
     Pb = P + (size_t)bh * (g.C + 1) * DD;
@@ -232,8 +242,13 @@ __global__ __launch_bounds__(256) void vda_chain_mfma_kernel(Geometry g, const f
         f32x4 v = {acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
         *reinterpret_cast<f32x4*>(&Yt[l32 * YP + wave * 32 + 8 * i4 + 4 * hg]) = v;
       }
-      if (Pb) {
-        const int slot = dir == 0 ? st + 1 : g.C - 1 - st;
+      // P slot completed by this step (-1: none, frame scan inside a chunk)
+      int slot = dir == 0 ? st + 1 : g.C - 1 - st;
+      if (mode == 2) {
+        const int f = dir == 0 ? st : g.F - 1 - st;
+        slot = dir == 0 ? ((f + 1) % g.cf == 0 ? (f + 1) / g.cf : -1) : (f % g.cf == 0 ? f / g.cf : -1);
+      }
+      if (Pb && slot >= 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           Pb[(size_t)slot * DD + (size_t)(wave * 32 + mfma32_row(i, hg)) * D + col0 + l32] = acc[i];
@@ -322,6 +337,22 @@ __global__ __launch_bounds__(256) void vda_chunk_scan_kernel(Geometry g, const f
     }
     float* t = yin; yin = yout; yout = t;
   }
+}
+
+// Frame-level scans straight from the frame maps (D = 64, 128): P_fwd and P_rev
+// at the chunk boundaries without composing the chunks first.
+hipError_t launch_vda_frame_scan(const Geometry& g, const float* Tf, const float* Uf,
+                                 const float* S_text, float init_scale, float* P_fwd, float* P_rev,
+                                 hipStream_t s) {
+  const int dirs = (P_fwd ? 1 : 0) | (P_rev ? 2 : 0);
+  const unsigned grid = (unsigned)(g.B * g.H * 2 * (g.D / 32));
+  if (g.D == 128)
+    vda_chain_mfma_kernel<128><<<grid, 256, 0, s>>>(g, Tf, Uf, nullptr, nullptr, S_text, init_scale, P_fwd, P_rev, 2, dirs);
+  else if (g.D == 64)
+    vda_chain_mfma_kernel<64><<<grid, 256, 0, s>>>(g, Tf, Uf, nullptr, nullptr, S_text, init_scale, P_fwd, P_rev, 2, dirs);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_vda_chunk_scan(const Geometry& g, const float* Tc, const float* Uc,

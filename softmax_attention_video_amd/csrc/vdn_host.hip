@@ -237,6 +237,14 @@ vdn_status run_scan(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, c
     VDN_HIP(vdn::launch_vda_frame_solve<float>(g, (const float*)k, (const float*)v, beta, alpha,
                                                (const float*)kt, (const float*)vt, bt, Tf, Uf, St,
                                                s));
+  // With all heads on one GPU the frame-level scan does fewer products than
+  // composing chunks first and scanning those, and occupies far fewer
+  // compute units (192 workgroups at H3 against ~9,200) beside the Softmax;
+  // composition pays off once heads are sharded over GPUs.
+  if (g.D == 64 || g.D == 128) {
+    VDN_HIP(vdn::launch_vda_frame_scan(g, Tf, Uf, St, p->text_init_scale, P_fwd, P_rev, s));
+    return VDN_OK;
+  }
   const int dirs = (P_fwd ? 1 : 0) | (P_rev ? 2 : 0);
   VDN_HIP(vdn::launch_vda_chunk_compose(g, Tf, Uf, Tc, Uc, dirs, s));
   VDN_HIP(vdn::launch_vda_chunk_scan(g, Tc, Uc, St, p->text_init_scale, P_fwd, P_rev, s));

@@ -90,6 +90,10 @@ hipError_t launch_vda_frame_solve(const Geometry& g, const T* k, const T* v, con
 hipError_t launch_vda_chunk_compose(const Geometry& g, const float* Tf, const float* Uf,
                                     float* Tc, float* Uc, int dirs_mask, hipStream_t s);
 // P [B,H,C+1,D,D] for each requested direction (nullable).
+// Frame-level scans from the frame maps directly (D = 64, 128 only).
+hipError_t launch_vda_frame_scan(const Geometry& g, const float* Tf, const float* Uf,
+                                 const float* S_text, float init_scale, float* P_fwd, float* P_rev,
+                                 hipStream_t s);
 hipError_t launch_vda_chunk_scan(const Geometry& g, const float* Tc, const float* Uc,
                                  const float* S_text, float init_scale, float* P_fwd,
                                  float* P_rev, hipStream_t s);

@@ -11,8 +11,8 @@
 // where lse is the forward's log-sum-exp, so P needs no renormalisation.
 //
 // Work split: a query-stationary pass computes dQ over the same items as the
-// forward (query groups and their key spans); two key-stationary passes
-// compute dV and dK.  Visibility is symmetric, so the forward's items read with the
+// forward (query groups and their key spans); a key-stationary pass computes
+// dK and dV together.  Visibility is symmetric, so the forward's items read with the
 // roles swapped (the group's frames as keys, its spans as the queries that
 // see them) cover every (query, key) pair exactly once, and every output row
 // is written by one workgroup: no atomics.
@@ -234,8 +234,9 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernels (D = 64, 128; N % 16 == 0), v_mfma_f32_32x32x16_bf16 with
-// fp32 accumulation.  Tiles are staged global -> registers -> LDS one tile
+// bf16 MFMA kernels (D = 64, 128; N % 16 == 0) with fp32 accumulation: dQ on
+// v_mfma_f32_32x32x16_bf16, dK and dV on v_mfma_f32_16x16x32_bf16 (below).
+// Tiles are staged global -> registers -> LDS one tile
 // ahead with one workgroup barrier per tile; rows past a span's end read as
 // zero through the buffer descriptors.
 //
@@ -267,8 +268,7 @@ struct BwdArgs {
 };
 
 constexpr int kBwdQW = 8;          // dQ kernel: waves (32 queries each)
-constexpr int kBwdKW = 8;          // dK / dV kernels: key blocks of 32 per workgroup (one wave each)
-constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per staged tile (dK/dV)
+constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per staged tile (dK, dV)
 
 template <int D>
 __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArgs a) {
@@ -401,69 +401,82 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
     }
 }
 
-// dK or dV (key-stationary; the item's frames are the keys, its spans the
-// queries that see them), one role per kernel so each gets its own register
-// budget: 8 waves, one per block of 32 keys, two waves per SIMD.  Per
-// 32-query block:
-//   S   = Q K^T         (A: Q rows from LDS in key_perm order, B: K fragments)
-//   P = exp2(S scale log2e - lse log2e)
-//   ROLE 0 (dV):  dV^T += dO^T P   (A: dO^T rows from LDS, B: P from registers)
-//   ROLE 1 (dK):  dP = dO V^T      (A: dO rows from LDS, B: V fragments)
-//                 dS = P (dP - Dq),  dK^T += Q^T dS  (A: Q^T rows, B: dS)
-// A lane holds one key and 16 queries; the block's lse and Dq come from LDS
-// (queries past the span: lse = +inf, so P = 0).  In the dV kernel the
-// tile's two query blocks are software-pipelined (block 1's S among block
-// 0's exponentials, block 0's accumulation among block 1's).  The next tile
-// is staged in two pieces: the row tiles after block 0's products, the
-// transposed tile and lse / Dq at the end.
-template <int D, int ROLE>
-__global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
-  constexpr int NT = kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
-  constexpr int KP = D + 8, TP = BQ + 8;
-  constexpr int NKK = D / 16, NDB = D / 32, NB = BQ / 32;
+// v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies row l % 16 of A and
+// column l % 16 of B, each with contraction slots 8 (l / 16) .. 8 (l / 16) + 7;
+// the 16 x 16 result holds column l % 16, rows 4 (l / 16) .. 4 (l / 16) + 3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kBwdFW = 8;          // fused dK / dV kernel: waves, 16 keys each
+
+// dK and dV together (key-stationary: the item's frames are the keys, its
+// spans the queries that see them), one wave per 16 keys on
+// 16 x 16 x 32 products, so that S and dP are formed once for both
+// gradients (8 d flops per visible pair) and the wave's K and V fragments,
+// S, dP and both accumulators fit two waves per SIMD.  Per 32-query block:
+//   S  = Q K^T,  dP = dO V^T      (A: Q / dO rows from LDS, B: K / V fragments)
+//   P = exp2(S scale log2e - lse log2e),  dS = P (dP - Dq)
+//   dV^T += dO^T P,  dK^T += Q^T dS   (A: dO^T / Q^T rows from LDS, B: P / dS)
+// A lane of S holds one key and the queries 16 r + 4 (l / 16) + i of row
+// tile r = 0, 1; taken in that order as the eight contraction slots of the
+// accumulation they are its B operand directly, and the transposed tiles are
+// stored with each block's columns in the same order (two 8-byte pieces per
+// staged 16-byte chunk), so the A operand is one 16-byte read per lane.
+template <int D>
+__global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs a) {
+  constexpr int NT = kBwdFW * 64, BKEY = kBwdFW * 16, BQ = kBwdBK;
+  // row pitches of 32 bytes times an odd number: the 32 lanes that one LDS
+  // cycle serves (16 rows, two 16-byte column groups) then cover all banks
+  constexpr int KP = D + 16, TP = BQ + 16;
+  static_assert((KP * 2 / 32) % 2 == 1 && (TP * 2 / 32) % 2 == 1, "row pitch");
+  constexpr int NKS = D / 32, NDT = D / 16, NB = BQ / 32;
   constexpr int RCH = BQ * D / 8 / NT, TCH = D * BQ / 8 / NT;
   static_assert(RCH * NT * 8 == BQ * D && TCH * NT * 8 == D * BQ, "tile split");
   static_assert(NB == 2, "two query blocks per tile");
-  constexpr bool DK = ROLE == 1;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Ds[DK ? 2 : 1][DK ? BQ * KP : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t Ts[2][D * TP];     // dO^T (dV) or Q^T (dK)
+  __shared__ __attribute__((aligned(16))) bf16_t Ds[2][BQ * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[2][D * TP];
+  __shared__ __attribute__((aligned(16))) bf16_t Dt[2][D * TP];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Dd[DK ? 2 : 1][BQ];
+  __shared__ __attribute__((aligned(16))) float Dd[2][BQ];
   const Geometry& g = a.g;
   Item it;
   int k0;
   if (!decode_item<false>(g, a.w, BKEY, blockIdx.x, 0, it, k0)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, l16 = lane & 15;
   const long long L = g.L;
   const size_t hb = (size_t)it.bh * L * D;
   const bf16_t* Q = a.q + hb;
   const bf16_t* dO = a.dO + hb;
-  const bf16_t* Tg = (DK ? a.qt : a.dOt) + hb;
+  const bf16_t* QT = a.qt + hb;
+  const bf16_t* dOT = a.dOt + hb;
   const float* lse = a.lse + (size_t)it.bh * L;
   const float* Dq = a.Dq + (size_t)it.bh * L;
-  const int krow = k0 + wave * 32 + l32;
+  const int krow = k0 + wave * 16 + l16;
   const bool kvalid = krow < it.q_end;
-  bf16x8 kf[NKK], vf[DK ? NKK : 1];
+  bf16x8 kf[NKS], vf[NKS];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    u32x4 x = {0, 0, 0, 0};
-    if (kvalid) x = ld16(a.k + hb + (size_t)krow * D + kk * 16 + hg * 8);
-    kf[kk] = as_bf16x8(x);
-    if constexpr (DK) {
-      u32x4 y = {0, 0, 0, 0};
-      if (kvalid) y = ld16(a.v + hb + (size_t)krow * D + kk * 16 + hg * 8);
-      vf[kk] = as_bf16x8(y);
+  for (int ks = 0; ks < NKS; ++ks) {
+    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (kvalid) {
+      x = ld16(a.k + hb + (size_t)krow * D + ks * 32 + grp * 8);
+      y = ld16(a.v + hb + (size_t)krow * D + ks * 32 + grp * 8);
     }
+    kf[ks] = as_bf16x8(x);
+    vf[ks] = as_bf16x8(y);
   }
-  f32x16 acc[NDB];
+  f32x4 accK[NDT], accV[NDT];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
+  for (int t = 0; t < NDT; ++t) {
+    accK[t] = f32x4{};
+    accV[t] = f32x4{};
+  }
   const SpanWalk<BQ, 3> walk(it);
   const uint32_t t_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
-  u32x4 c0r[(DK ? 2 : 1) * RCH], c1r[TCH];
+  u32x4 c0r[2 * RCH], c1r[2 * TCH];
   float cl = 0.f, cd = 0.f;
-  auto load_piece0 = [&](int j) {      // Q rows (and dO rows)
+  auto load_piece0 = [&](int j) {      // Q and dO rows
     int qs, nq;
     walk.tile(j, qs, nq);
     const rsrc_t rq = make_rsrc(Q + (size_t)qs * D, (uint32_t)nq * D * 2);
@@ -473,7 +486,7 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
       const int c = tid + NT * i;
       const uint32_t off = (uint32_t)((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
       c0r[i] = buf_ld16(rq, off);
-      if constexpr (DK) c0r[RCH + i] = buf_ld16(rd, off);
+      c0r[RCH + i] = buf_ld16(rd, off);
     }
   };
   auto store_piece0 = [&](int buf) {
@@ -482,67 +495,84 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
       const int c = tid + NT * i;
       const int off = (c / (D / 8)) * KP + (c % (D / 8)) * 8;
       st16(&Qs[buf][off], c0r[i]);
-      if constexpr (DK) st16(&Ds[buf][off], c0r[RCH + i]);
+      st16(&Ds[buf][off], c0r[RCH + i]);
     }
   };
-  auto load_piece1 = [&](int j) {      // the transposed tile, lse and Dq
+  auto load_piece1 = [&](int j) {      // Q^T and dO^T, lse and Dq
     int qs, nq;
     walk.tile(j, qs, nq);
-    const rsrc_t rt = make_rsrc(Tg + qs, t_bytes - (uint32_t)qs * 2);
+    const rsrc_t rt = make_rsrc(QT + qs, t_bytes - (uint32_t)qs * 2);
+    const rsrc_t ru = make_rsrc(dOT + qs, t_bytes - (uint32_t)qs * 2);
 #pragma unroll
     for (int i = 0; i < TCH; ++i) {
       const int c = tid + NT * i;
       const int r = c / (BQ / 8), c8 = c % (BQ / 8);
-      c1r[i] = buf_ld16(rt, c8 * 8 < nq ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u);
+      const uint32_t off = c8 * 8 < nq ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u;
+      c1r[i] = buf_ld16(rt, off);
+      c1r[TCH + i] = buf_ld16(ru, off);
     }
     if (tid < BQ) {
       cl = tid < nq ? lse[qs + tid] * kLog2e : INFINITY;
-      if constexpr (DK) cd = tid < nq ? Dq[qs + tid] : 0.f;
+      cd = tid < nq ? Dq[qs + tid] : 0.f;
     }
   };
+  // a staged chunk holds queries 8 m .. 8 m + 7 of a block (m = 0..3); its
+  // halves go to the slot positions 16 (m % 2) + 4 (m / 2) and that + 8
   auto store_piece1 = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TCH; ++i) {
       const int c = tid + NT * i;
-      st16(&Ts[buf][(c / (BQ / 8)) * TP + (c % (BQ / 8)) * 8], c1r[i]);
+      const int r = c / (BQ / 8), c8 = c % (BQ / 8), m = c8 & 3;
+      const int p = r * TP + (c8 >> 2) * 32 + 16 * (m & 1) + 4 * (m >> 1);
+      const u32x2 lo = {c1r[i][0], c1r[i][1]}, hi = {c1r[i][2], c1r[i][3]};
+      *reinterpret_cast<u32x2*>(&Qt[buf][p]) = lo;
+      *reinterpret_cast<u32x2*>(&Qt[buf][p + 8]) = hi;
+      const u32x2 lo2 = {c1r[TCH + i][0], c1r[TCH + i][1]}, hi2 = {c1r[TCH + i][2], c1r[TCH + i][3]};
+      *reinterpret_cast<u32x2*>(&Dt[buf][p]) = lo2;
+      *reinterpret_cast<u32x2*>(&Dt[buf][p + 8]) = hi2;
     }
     if (tid < BQ) {
       Ls[buf][tid] = cl;
-      if constexpr (DK) Dd[buf][tid] = cd;
+      Dd[buf][tid] = cd;
     }
   };
-  const int rperm = key_perm(l32);
-  auto qk = [&](int buf, int blk, const bf16x8* frag, const bf16_t* base) {
-    f32x16 x = {};
-    const bf16_t* r = base + (blk * 32 + rperm) * KP + hg * 8;
+  // S and dP of query block qb: row tile r holds queries qb 32 + 16 r + ...
+  auto sdp = [&](int buf, int qb, f32x4* sv, f32x4* dpv) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) x = mfma32x32x16(as_bf16x8(ld16(r + kk * 16)), frag[kk], x);
-    return x;
-  };
-  auto accum = [&](int buf, int blk, const bf16x8* pb) {
-    const int col = blk * 32 + hg * 16;
+    for (int r = 0; r < 2; ++r) {
+      sv[r] = f32x4{};
+      dpv[r] = f32x4{};
+    }
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int b = 0; b < NDB; ++b) {
-        const bf16x8 tf = as_bf16x8(ld16(Ts[buf] + (b * 32 + l32) * TP + col + h2 * 8));
-        acc[b] = mfma32x32x16(tf, pb[h2], acc[b]);
+      for (int r = 0; r < 2; ++r) {
+        const int off = (qb * 32 + r * 16 + l16) * KP + ks * 32 + grp * 8;
+        sv[r] = mfma16x16x32(as_bf16x8(ld16(&Qs[buf][off])), kf[ks], sv[r]);
+        dpv[r] = mfma16x16x32(as_bf16x8(ld16(&Ds[buf][off])), vf[ks], dpv[r]);
       }
   };
-  // P (dV) or dS = P (dP - Dq) (dK) of one block, as bf16 MFMA operands
-  auto probs = [&](int buf, int blk, const f32x16& sv, const f32x16& dpv, bf16x8* pb) {
-    const int col = blk * 32 + hg * 16;
+  // P and dS as bf16 operands, slot 4 r + i = query qb 32 + 16 r + 4 grp + i
+  auto probs = [&](int buf, int qb, const f32x4* sv, const f32x4* dpv, bf16x8& pb, bf16x8& db) {
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][col + 4 * i4]);
-      f32x4 d4 = {};
-      if constexpr (DK) d4 = *reinterpret_cast<const f32x4*>(&Dd[buf][col + 4 * i4]);
+    for (int r = 0; r < 2; ++r) {
+      const int q = qb * 32 + 16 * r + 4 * grp;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][q]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dd[buf][q]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 4 * i4 + e;
-        const float pv = fast_exp2(fmaf(sv[i], a.scale_log2, -l4[e]));
-        pb[i >> 3][i & 7] = static_cast<__bf16>(DK ? pv * (dpv[i] - d4[e]) : pv);
+        const float pv = fast_exp2(fmaf(sv[r][e], a.scale_log2, -l4[e]));
+        pb[4 * r + e] = static_cast<__bf16>(pv);
+        db[4 * r + e] = static_cast<__bf16>(pv * (dpv[r][e] - d4[e]));
       }
+    }
+  };
+  auto accum = [&](int buf, int qb, const bf16x8& pb, const bf16x8& db) {
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      const int off = (16 * t + l16) * TP + qb * 32 + 8 * grp;
+      accV[t] = mfma16x16x32(as_bf16x8(ld16(&Dt[buf][off])), pb, accV[t]);
+      accK[t] = mfma16x16x32(as_bf16x8(ld16(&Qt[buf][off])), db, accK[t]);
     }
   };
   if (walk.n > 0) {
@@ -556,72 +586,35 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
     const int buf = j & 1;
     const bool more = j + 1 < walk.n;
     if (more) load_piece0(j + 1);
-    bf16x8 p0[2], p1[2];
-    if constexpr (!DK) {
-      const f32x16 s0 = qk(buf, 0, kf, Qs[buf]);
-      if (more) {                               // that buffer was released by the last barrier
-        store_piece0(buf ^ 1);
-        load_piece1(j + 1);
-      }
-      const f32x16 s1 = qk(buf, 1, kf, Qs[buf]);
-      probs(buf, 0, s0, s0, p0);
-      accum(buf, 0, p0);
-      probs(buf, 1, s1, s1, p1);
-      accum(buf, 1, p1);
-      // issue order: block 0's S; the next tile's row stores; block 1's S
-      // among block 0's exponentials; block 0's products among block 1's
-      // exponentials; block 1's products
-#pragma unroll
-      for (int u = 0; u < NKK; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x200, RCH, 0);
-#pragma unroll
-      for (int u = 0; u < NKK; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 2 * NDB; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-    } else {
-      // one block after the other: the dK waves' registers (K and V fragments,
-      // S, dP, dS, the dK accumulators) leave no room for a second block in
-      // flight at two waves per SIMD
-      const f32x16 s0 = qk(buf, 0, kf, Qs[buf]);
-      const f32x16 dp0 = qk(buf, 0, vf, Ds[buf]);
-      if (more) {                               // that buffer was released by the last barrier
-        store_piece0(buf ^ 1);
-        load_piece1(j + 1);
-      }
-      probs(buf, 0, s0, dp0, p0);
-      accum(buf, 0, p0);
-      const f32x16 s1 = qk(buf, 1, kf, Qs[buf]);
-      const f32x16 dp1 = qk(buf, 1, vf, Ds[buf]);
-      probs(buf, 1, s1, dp1, p1);
-      accum(buf, 1, p1);
+    f32x4 s0[2], d0[2], s1[2], d1[2];
+    bf16x8 p0, g0, p1, g1;
+    sdp(buf, 0, s0, d0);
+    if (more) {                               // that buffer was released by the last barrier
+      store_piece0(buf ^ 1);
+      load_piece1(j + 1);
     }
+    sdp(buf, 1, s1, d1);
+    probs(buf, 0, s0, d0, p0, g0);
+    accum(buf, 0, p0, g0);
+    probs(buf, 1, s1, d1, p1, g1);
+    accum(buf, 1, p1, g1);
     if (more) store_piece1(buf ^ 1);
     __syncthreads();
   }
   if (!kvalid) return;
-  bf16_t* orow = (DK ? a.dk : a.dv) + hb + (size_t)krow * D;
-  const float sc = DK ? a.scale : 1.f;
+  bf16_t* krk = a.dk + hb + (size_t)krow * D;
+  bf16_t* krv = a.dv + hb + (size_t)krow * D;
 #pragma unroll
-  for (int b = 0; b < NDB; ++b)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = b * 32 + 8 * i4 + 4 * hg;
-      u32x2 pk;
-      pk[0] = pack_bf16x2(acc[b][i4 * 4 + 0] * sc, acc[b][i4 * 4 + 1] * sc);
-      pk[1] = pack_bf16x2(acc[b][i4 * 4 + 2] * sc, acc[b][i4 * 4 + 3] * sc);
-      *reinterpret_cast<u32x2*>(orow + d) = pk;
-    }
+  for (int t = 0; t < NDT; ++t) {
+    const int d = 16 * t + 4 * grp;
+    u32x2 pk, pv;
+    pk[0] = pack_bf16x2(accK[t][0] * a.scale, accK[t][1] * a.scale);
+    pk[1] = pack_bf16x2(accK[t][2] * a.scale, accK[t][3] * a.scale);
+    pv[0] = pack_bf16x2(accV[t][0], accV[t][1]);
+    pv[1] = pack_bf16x2(accV[t][2], accV[t][3]);
+    *reinterpret_cast<u32x2*>(krk + d) = pk;
+    *reinterpret_cast<u32x2*>(krv + d) = pv;
+  }
 }
 
 bool softmax_bwd_mfma_ok(const Geometry& g) {
@@ -641,16 +634,14 @@ hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const u
   a.scale_log2 = scale * kLog2e;
   BwdArgs b = a;
   a.w = window_work(g, kBwdQW * 32);
-  b.w = window_work(g, kBwdKW * 32);
+  b.w = window_work(g, kBwdFW * 16);
   if (a.w.grid == 0) return hipSuccess;
   if (g.D == 128) {
     softmax_bwd_dq_mfma_kernel<128><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv_mfma_kernel<128, 0><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
-    softmax_bwd_dkdv_mfma_kernel<128, 1><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv16_kernel<128><<<b.w.grid, kBwdFW * 64, 0, s>>>(b);
   } else {
     softmax_bwd_dq_mfma_kernel<64><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv_mfma_kernel<64, 0><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
-    softmax_bwd_dkdv_mfma_kernel<64, 1><<<b.w.grid, kBwdKW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv16_kernel<64><<<b.w.grid, kBwdFW * 64, 0, s>>>(b);
   }
   return hipGetLastError();
 }

@@ -584,21 +584,47 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
   __syncthreads();
   for (int j = 0; j < walk.n; ++j) {
     const int buf = j & 1;
-    const bool more = j + 1 < walk.n;
-    if (more) load_piece0(j + 1);
+    // the next tile is requested now and stored at the end (into the buffer
+    // the last barrier released); the last tile restages itself there, which
+    // keeps the body one straight-line block for the issue order below
+    const int jn = j + 1 < walk.n ? j + 1 : j;
+    load_piece0(jn);
+    load_piece1(jn);
     f32x4 s0[2], d0[2], s1[2], d1[2];
     bf16x8 p0, g0, p1, g1;
     sdp(buf, 0, s0, d0);
-    if (more) {                               // that buffer was released by the last barrier
-      store_piece0(buf ^ 1);
-      load_piece1(j + 1);
-    }
     sdp(buf, 1, s1, d1);
     probs(buf, 0, s0, d0, p0, g0);
     accum(buf, 0, p0, g0);
     probs(buf, 1, s1, d1, p1, g1);
     accum(buf, 1, p1, g1);
-    if (more) store_piece1(buf ^ 1);
+    store_piece0(buf ^ 1);
+    store_piece1(buf ^ 1);
+    // issue order: block 0's S and dP; block 1's among block 0's
+    // probabilities; block 0's accumulation among block 1's probabilities;
+    // block 1's accumulation
+#pragma unroll
+    for (int u = 0; u < 4 * NKS; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4 * NKS; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2 * NDT; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2 * NDT; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
     __syncthreads();
   }
   if (!kvalid) return;

@@ -139,9 +139,15 @@ __global__ __launch_bounds__(256) void vda_chunk_compose_kernel(Geometry g, cons
 // Mode frame scan: the same grid and Y0, but L_s = T_f, A_s = U_f of the
 //   frames themselves in scan order (no composition), Y written to P at
 //   every chunk boundary.
+// A workgroup holds kChainG column blocks of one chain, 256 threads each:
+// the chains are latency-bound (one dependent product per step), so sharing
+// a compute unit interleaves their matrix-core work on each SIMD instead of
+// holding one compute unit per column block for the same time (two per
+// workgroup keep the register budget for the left factors' prefetch).
 // ---------------------------------------------------------------------------
+constexpr int kChainG = 2;
 template <int D>
-__global__ __launch_bounds__(256) void vda_chain_mfma_kernel(Geometry g, const float* __restrict__ Tf,
+__global__ __launch_bounds__(256 * kChainG) void vda_chain_mfma_kernel(Geometry g, const float* __restrict__ Tf,
                                                              const float* __restrict__ Uf,
                                                              float* __restrict__ Tc, float* __restrict__ Uc,
                                                              const float* __restrict__ S_text,
@@ -152,11 +158,15 @@ __global__ __launch_bounds__(256) void vda_chain_mfma_kernel(Geometry g, const f
   constexpr int NCB = D / 32;           // 32-column blocks of Y
   constexpr int YP = D + 4;             // pitch of Yt (floats)
   constexpr int NK8 = D / 8;            // 8-wide k groups
-  __shared__ __attribute__((aligned(16))) float Yt[32 * YP];
+  static_assert(NCB % kChainG == 0, "column blocks per workgroup");
+  __shared__ __attribute__((aligned(16))) float Yts[kChainG][32 * YP];
   const size_t DD = (size_t)D * D;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int grp = threadIdx.x >> 8;     // 256-thread group: one column block
+  float* Yt = Yts[grp];
+  const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
   int id = blockIdx.x;
-  const int cb = id % NCB; id /= NCB;
+  const int cb = (id % (NCB / kChainG)) * kChainG + grp;
+  id /= NCB / kChainG;
   int part = 0, c = 0, dir, bh;
   if (mode == 0) {
     part = id % 2; id /= 2;
@@ -274,11 +284,11 @@ __global__ __launch_bounds__(256) void vda_chain_mfma_kernel(Geometry g, const f
 hipError_t launch_vda_chunk_compose(const Geometry& g, const float* Tf, const float* Uf, float* Tc,
                                     float* Uc, int dirs_mask, hipStream_t s) {
   if (g.D == 64 || g.D == 128) {
-    const unsigned grid = (unsigned)(g.B * g.H * 2 * g.C * 2 * (g.D / 32));
+    const unsigned grid = (unsigned)(g.B * g.H * 2 * g.C * 2 * (g.D / 32 / kChainG));
     if (g.D == 128)
-      vda_chain_mfma_kernel<128><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, nullptr, 0.f, nullptr, nullptr, 0, dirs_mask);
+      vda_chain_mfma_kernel<128><<<grid, 256 * kChainG, 0, s>>>(g, Tf, Uf, Tc, Uc, nullptr, 0.f, nullptr, nullptr, 0, dirs_mask);
     else
-      vda_chain_mfma_kernel<64><<<grid, 256, 0, s>>>(g, Tf, Uf, Tc, Uc, nullptr, 0.f, nullptr, nullptr, 0, dirs_mask);
+      vda_chain_mfma_kernel<64><<<grid, 256 * kChainG, 0, s>>>(g, Tf, Uf, Tc, Uc, nullptr, 0.f, nullptr, nullptr, 0, dirs_mask);
     return hipGetLastError();
   }
   const int NCB = 2 * ((g.D + kCB - 1) / kCB);
@@ -345,11 +355,11 @@ hipError_t launch_vda_frame_scan(const Geometry& g, const float* Tf, const float
                                  const float* S_text, float init_scale, float* P_fwd, float* P_rev,
                                  hipStream_t s) {
   const int dirs = (P_fwd ? 1 : 0) | (P_rev ? 2 : 0);
-  const unsigned grid = (unsigned)(g.B * g.H * 2 * (g.D / 32));
+  const unsigned grid = (unsigned)(g.B * g.H * 2 * (g.D / 32 / kChainG));
   if (g.D == 128)
-    vda_chain_mfma_kernel<128><<<grid, 256, 0, s>>>(g, Tf, Uf, nullptr, nullptr, S_text, init_scale, P_fwd, P_rev, 2, dirs);
+    vda_chain_mfma_kernel<128><<<grid, 256 * kChainG, 0, s>>>(g, Tf, Uf, nullptr, nullptr, S_text, init_scale, P_fwd, P_rev, 2, dirs);
   else if (g.D == 64)
-    vda_chain_mfma_kernel<64><<<grid, 256, 0, s>>>(g, Tf, Uf, nullptr, nullptr, S_text, init_scale, P_fwd, P_rev, 2, dirs);
+    vda_chain_mfma_kernel<64><<<grid, 256 * kChainG, 0, s>>>(g, Tf, Uf, nullptr, nullptr, S_text, init_scale, P_fwd, P_rev, 2, dirs);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -360,11 +370,11 @@ hipError_t launch_vda_chunk_scan(const Geometry& g, const float* Tc, const float
                                  hipStream_t s) {
   const int dirs = (P_fwd ? 1 : 0) | (P_rev ? 2 : 0);
   if (g.D == 64 || g.D == 128) {
-    const unsigned grid = (unsigned)(g.B * g.H * 2 * (g.D / 32));
+    const unsigned grid = (unsigned)(g.B * g.H * 2 * (g.D / 32 / kChainG));
     if (g.D == 128)
-      vda_chain_mfma_kernel<128><<<grid, 256, 0, s>>>(g, nullptr, nullptr, const_cast<float*>(Tc), const_cast<float*>(Uc), S_text, init_scale, P_fwd, P_rev, 1, dirs);
+      vda_chain_mfma_kernel<128><<<grid, 256 * kChainG, 0, s>>>(g, nullptr, nullptr, const_cast<float*>(Tc), const_cast<float*>(Uc), S_text, init_scale, P_fwd, P_rev, 1, dirs);
     else
-      vda_chain_mfma_kernel<64><<<grid, 256, 0, s>>>(g, nullptr, nullptr, const_cast<float*>(Tc), const_cast<float*>(Uc), S_text, init_scale, P_fwd, P_rev, 1, dirs);
+      vda_chain_mfma_kernel<64><<<grid, 256 * kChainG, 0, s>>>(g, nullptr, nullptr, const_cast<float*>(Tc), const_cast<float*>(Uc), S_text, init_scale, P_fwd, P_rev, 1, dirs);
     return hipGetLastError();
   }
   const int NCB = (g.D + kCB - 1) / kCB;

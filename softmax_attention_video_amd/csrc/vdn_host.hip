@@ -239,7 +239,7 @@ vdn_status run_scan(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, c
                                                s));
   // With all heads on one GPU the frame-level scan does fewer products than
   // composing chunks first and scanning those, and occupies far fewer
-  // compute units (192 workgroups at H3 against ~9,200) beside the Softmax;
+  // compute units (96 workgroups at H3 against ~4,600) beside the Softmax;
   // composition pays off once heads are sharded over GPUs.
   if (g.D == 64 || g.D == 128) {
     VDN_HIP(vdn::launch_vda_frame_scan(g, Tf, Uf, St, p->text_init_scale, P_fwd, P_rev, s));

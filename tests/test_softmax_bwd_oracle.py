@@ -113,3 +113,64 @@ def test_rows_evaluation_matches_full():
         np.testing.assert_allclose(rq, fl(dq)[qrows], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(rk, fl(dk)[krows], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(rv, fl(dv)[krows], rtol=1e-10, atol=1e-12)
+
+
+# ---- the text-keys option: the T text tokens are keys of every query ----
+
+def _torch_grads_text(q, k, v, g, do, kt, vt, p):
+    F, N, d = q.shape
+    T = kt.shape[0]
+    vis = np.repeat(np.repeat(O.visibility(F, p).astype(bool), N, 0), N, 1)
+    mask = np.concatenate([vis, np.ones((F * N, T), bool)], axis=1)
+    tq, tk, tv, tg = (torch.tensor(x.reshape(F * N, -1) if x.ndim == 3 else x.reshape(F * N),
+                                   dtype=torch.float64, requires_grad=True) for x in (q, k, v, g))
+    tkt, tvt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (kt, vt))
+    scale = 1.0 / math.sqrt(d) if p.softmax_scale is None else p.softmax_scale
+    s = (tq @ torch.cat([tk, tkt]).T) * scale
+    s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    out = tg[:, None] * (torch.softmax(s, dim=1) @ torch.cat([tv, tvt]))
+    out.backward(torch.from_numpy(do.reshape(F * N, d)))
+    return [x.grad.numpy() for x in (tq, tk, tv, tg, tkt, tvt)]
+
+
+@pytest.mark.parametrize("F,N,d,T,anchors", [(20, 3, 8, 5, True), (12, 2, 4, 3, False), (7, 4, 6, 1, True)])
+def test_text_keys_match_torch_autograd(F, N, d, T, anchors):
+    p = O.Params(anchors=anchors, text_softmax=True)
+    q, k, v, g, do = _case(F, N, d, F * 7 + T)
+    rng = np.random.default_rng(T)
+    kt, vt = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    got = SB.softmax_branch_bwd(q, k, v, g, do, p, K_text=kt, V_text=vt)
+    want = _torch_grads_text(q, k, v, g, do, kt, vt, p)
+    shapes = [(F * N, d)] * 3 + [(F * N,), (T, d), (T, d)]
+    for a, b, sh in zip(got, want, shapes):
+        np.testing.assert_allclose(a.reshape(sh), b, rtol=1e-10, atol=1e-12)
+
+
+def test_text_keys_value_gradients_sum_to_output_gradients():
+    F, N, d, T = 25, 3, 4, 6
+    p = O.Params(text_softmax=True)
+    q, k, v, g, do = _case(F, N, d, 19)
+    rng = np.random.default_rng(2)
+    _, _, dv, _, _, dvt = SB.softmax_branch_bwd(q, k, v, g, do, p, K_text=rng.standard_normal((T, d)),
+                                                V_text=rng.standard_normal((T, d)))
+    np.testing.assert_allclose(dv.sum(axis=(0, 1)) + dvt.sum(axis=0),
+                               (g[..., None] * do).sum(axis=(0, 1)), rtol=1e-12)
+
+
+def test_text_keys_rows_evaluation_matches_full():
+    F, N, d, T = 25, 3, 4, 4
+    p = O.Params(text_softmax=True)
+    q, k, v, g, do = _case(F, N, d, 23)
+    rng = np.random.default_rng(3)
+    kt, vt = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    dq, dk, dv, _, _, _ = SB.softmax_branch_bwd(q, k, v, g, do, p, K_text=kt, V_text=vt)
+    L = F * N
+    fl = lambda x: x.reshape(L, -1)
+    qrows = np.array([0, 5, 40, 74])
+    for kframe in (0, 12):
+        krows = kframe * N + np.array([1, 2])
+        rq, rk, rv = SB.softmax_bwd_rows(fl(q), fl(k), fl(v), g.reshape(L), fl(do), F, qrows, kframe,
+                                         krows, p, K_text=kt, V_text=vt)
+        np.testing.assert_allclose(rq, fl(dq)[qrows], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rk, fl(dk)[krows], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rv, fl(dv)[krows], rtol=1e-10, atol=1e-12)

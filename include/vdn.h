@@ -210,8 +210,7 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
                          const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream);
 
 /*
- * vdn_window_softmax_bwd -- gradients of the Softmax branch (a7), video keys
- * only (p->text_softmax = 0).
+ * vdn_window_softmax_bwd -- gradients of the Softmax branch (a7).
  *
  * Paper, method (local Softmax window; branch calibration) defines the
  * forward Ohat_s = g_s * softmax(scale q k^T) v over the visible keys; the
@@ -219,22 +218,32 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
  *   dO = g_s * d_out,  Dq = rowsum(dO * o),  P = exp(scale q.k - lse),
  *   dS = P * (dO.v - Dq),  dq = scale * sum_k dS k,  dk = scale * sum_q dS q,
  *   dv = sum_q P dO,  dg_s = rowsum(d_out * o).
+ * With p->text_softmax = 1 and dims->T > 0 (method, bidirectional linear
+ * attention: the text stays visible to the Softmax branch) the T text tokens
+ * are keys of every query in the same softmax, and their gradients are
+ * summed over all queries.
  *
  *  q, k, v     [B,H,L,d] dt     the forward's inputs
+ *  k_text, v_text [B,H,T,d] dt  the text keys and values (read only with text keys)
  *  o           [B,L,H,d] dt     the ungated Softmax output O_s
- *                               (vdn_window_softmax_fwd with g_s = NULL)
+ *                               (vdn_window_softmax_fwd with g_s = NULL, same p)
  *  lse         [B,H,L]   float  the forward's log-sum-exp (same call)
  *  g_s         [B,H,L]   float  the gate, NULL = 1
  *  d_out       [B,L,H,d] dt     gradient of the gated output Ohat_s
  *  dq, dk, dv  [B,H,L,d] dt     outputs (fully written)
+ *  dk_text, dv_text [B,H,T,d] dt  outputs with text keys (fully written), else unused
  *  dg_s        [B,H,L]   float  output gradient of g_s, nullable
  *  workspace   vdn_softmax_bwd_workspace_bytes(dims, p, dt) bytes
+ * Errors: VDN_ERR_INVALID_ARG for a NULL required pointer (k_text, v_text,
+ * dk_text, dv_text are required with text keys) or invalid dims;
+ * VDN_ERR_WORKSPACE for a short workspace.
  */
-vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, const void* o,
+vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v,
+                                  const void* k_text, const void* v_text, const void* o,
                                   const float* lse, const float* g_s, const void* d_out, void* dq,
-                                  void* dk, void* dv, float* dg_s, void* workspace,
-                                  size_t workspace_bytes, const vdn_dims* dims, const vdn_params* p,
-                                  vdn_dtype dt, void* stream);
+                                  void* dk, void* dv, void* dk_text, void* dv_text, float* dg_s,
+                                  void* workspace, size_t workspace_bytes, const vdn_dims* dims,
+                                  const vdn_params* p, vdn_dtype dt, void* stream);
 
 /* Workspace bytes of vdn_window_softmax_bwd (0 if the arguments are invalid). */
 size_t vdn_softmax_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);

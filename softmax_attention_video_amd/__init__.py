@@ -143,7 +143,7 @@ def lib() -> ctypes.CDLL:
     L.vdn_merge_fwd.restype = I
     L.vdn_mx_quantize.argtypes = [P, P, P, ctypes.c_longlong, I, P]
     L.vdn_mx_quantize.restype = I
-    L.vdn_window_softmax_bwd.argtypes = [P] * 12 + [S, dp, pp, I, P]
+    L.vdn_window_softmax_bwd.argtypes = [P] * 16 + [S, dp, pp, I, P]
     L.vdn_window_softmax_bwd.restype = I
     L.vdn_softmax_bwd_workspace_bytes.argtypes = [dp, pp, I]
     L.vdn_softmax_bwd_workspace_bytes.restype = S
@@ -390,13 +390,16 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
 
 
 def window_softmax_bwd(q, k, v, o, lse, d_out, F: int, g_s=None, want_dg: bool = False,
-                       params: Params | None = None, workspace=None, stream=None):
-    """Gradients of the Softmax branch (vdn_window_softmax_bwd), video keys only.
+                       params: Params | None = None, workspace=None, stream=None, k_text=None,
+                       v_text=None):
+    """Gradients of the Softmax branch (vdn_window_softmax_bwd).
 
     q, k, v [B,H,L,d]; o [B,L,H,d] the ungated output and lse [B,H,L] of
-    window_softmax_fwd(..., g_s=None, want_lse=True); d_out [B,L,H,d] the
-    gradient of the gated output; g_s [B,H,L] or None.
-    Returns (dq, dk, dv [B,H,L,d], dg [B,H,L] or None)."""
+    window_softmax_fwd(..., g_s=None, want_lse=True) with the same params
+    and text keys; d_out [B,L,H,d] the gradient of the gated output; g_s
+    [B,H,L] or None.  With params.text_softmax, k_text and v_text [B,H,T,d]
+    are keys of every query.  Returns (dq, dk, dv [B,H,L,d], dg [B,H,L] or
+    None), followed by (dk_text, dv_text [B,H,T,d]) with text keys."""
     torch = _torch()
     params = params or Params()
     B, H, L, d = q.shape
@@ -406,7 +409,9 @@ def window_softmax_bwd(q, k, v, o, lse, d_out, F: int, g_s=None, want_dg: bool =
     code = _dtype_code(q)
     dev = q.device
     f32 = torch.float32
-    dims = Dims(B, H, F, L // F, 0, d, d, H * d)
+    T = k_text.shape[2] if k_text is not None else 0
+    text = bool(params.text_softmax) and T > 0
+    dims = Dims(B, H, F, L // F, T, d, d, H * d)
     p = params.c()
     need = int(lib().vdn_softmax_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p), code))
     if workspace is None:
@@ -415,14 +420,22 @@ def window_softmax_bwd(q, k, v, o, lse, d_out, F: int, g_s=None, want_dg: bool =
         raise ValueError(f"workspace of {workspace.numel()} bytes < {need}")
     dq, dk, dv = (torch.empty((B, H, L, d), dtype=dt, device=dev) for _ in range(3))
     dg = torch.empty((B, H, L), dtype=f32, device=dev) if want_dg else None
+    dkt, dvt = ((torch.empty((B, H, T, d), dtype=dt, device=dev) for _ in range(2)) if text
+                else (None, None))
     _check(lib().vdn_window_softmax_bwd(
         _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
-        _ptr(v, "v", dt, (B, H, L, d), dev), _ptr(o, "o", dt, (B, L, H, d), dev),
+        _ptr(v, "v", dt, (B, H, L, d), dev),
+        _ptr(k_text if text else None, "k_text", dt, (B, H, T, d), dev, allow_none=True),
+        _ptr(v_text if text else None, "v_text", dt, (B, H, T, d), dev, allow_none=True),
+        _ptr(o, "o", dt, (B, L, H, d), dev),
         _ptr(lse, "lse", f32, (B, H, L), dev), _ptr(g_s, "g_s", f32, (B, H, L), dev, allow_none=True),
         _ptr(d_out, "d_out", dt, (B, L, H, d), dev), _ptr(dq, "dq"), _ptr(dk, "dk"), _ptr(dv, "dv"),
+        _ptr(dkt, "dk_text", allow_none=True), _ptr(dvt, "dv_text", allow_none=True),
         _ptr(dg, "dg", allow_none=True),
         ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
         ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    if text:
+        return dq, dk, dv, dg, dkt, dvt
     return dq, dk, dv, dg
 
 

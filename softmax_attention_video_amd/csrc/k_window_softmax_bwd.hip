@@ -16,6 +16,12 @@
 // roles swapped (the group's frames as keys, its spans as the queries that
 // see them) cover every (query, key) pair exactly once, and every output row
 // is written by one workgroup: no atomics.
+//
+// Text keys (method, bidirectional linear attention: the text stays visible
+// to the Softmax branch): the T text tokens are keys of every query in the
+// same softmax.  The query-stationary pass walks them as one more key span;
+// the key-stationary pass gets extra items, blocks of text keys whose query
+// span is the whole video.
 #include "vdn_common.h"
 #include "vdn_internal.h"
 #include "window_items.h"
@@ -78,6 +84,36 @@ hipError_t launch_softmax_bwd_prep(const Geometry& g, const T* o, const T* dout,
   return hipGetLastError();
 }
 
+// Key-stationary work items of the text keys: blocks of bk text keys, each
+// seen by every video query ([0, L) as one span).  They lead the grid (as
+// long as the anchor items, so they start first), padded to a multiple of
+// the XCD count so the video items keep their XCD placement.
+__host__ __device__ inline int text_key_blocks(const Geometry& g, int bk) {
+  return g.Ts > 0 ? g.B * g.H * ((g.Ts + bk - 1) / bk) : 0;
+}
+__host__ __device__ inline int text_items_padded(const Geometry& g, int bk) {
+  return (text_key_blocks(g, bk) + kNumXcd - 1) / kNumXcd * kNumXcd;
+}
+// Decodes workgroup bid of a key-stationary kernel whose first ntext
+// workgroups take text key blocks; text: the item's keys are text keys
+// (key range [k0, Ts) of it.q_begin .. it.q_end).
+__device__ __forceinline__ bool decode_key_item(const Geometry& g, const SoftmaxWork& w, int bk,
+                                                int ntext, int bid, Item& it, int& k0, bool& text) {
+  text = bid < ntext;
+  if (!text) return decode_item<false>(g, w, bk, bid - ntext, 0, it, k0);
+  const int nb = (g.Ts + bk - 1) / bk;
+  if (bid >= g.B * g.H * nb) return false;
+  it.bh = bid / nb;
+  k0 = (bid % nb) * bk;
+  it.q_begin = 0;
+  it.q_end = g.Ts;
+  it.nspan = 1;
+  it.kb0 = 0;
+  it.ke0 = (int)g.L;
+  it.kb1 = it.ke1 = it.kb2 = it.ke2 = it.kb3 = it.ke3 = 0;
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // Generic SIMT kernels (fp32 or bf16 storage, any D <= 128, any N).
 // dQ: one thread per query, key tiles of 32 staged through LDS.
@@ -85,14 +121,16 @@ hipError_t launch_softmax_bwd_prep(const Geometry& g, const T* o, const T* dout,
 template <typename T, int DMAX>
 __global__ __launch_bounds__(128) void softmax_bwd_dq_simt_kernel(
     Geometry g, SoftmaxWork w, const T* __restrict__ qp, const T* __restrict__ kp,
-    const T* __restrict__ vp, const T* __restrict__ dop, const float* __restrict__ lse,
-    const float* __restrict__ Dq, T* __restrict__ dq, float scale) {
+    const T* __restrict__ vp, const T* __restrict__ ktp, const T* __restrict__ vtp,
+    const T* __restrict__ dop, const float* __restrict__ lse, const float* __restrict__ Dq,
+    T* __restrict__ dq, float scale) {
   constexpr int BQ = 128, BK = 32;
   __shared__ float Ks[BK][DMAX + 1];
   __shared__ float Vs[BK][DMAX + 1];
   Item it;
   int q0;
-  if (!decode_item<false>(g, w, BQ, blockIdx.x, 0, it, q0)) return;
+  // text keys (g.Ts > 0) are a fourth span, walk positions L .. L + Ts - 1
+  if (!decode_item<true>(g, w, BQ, blockIdx.x, g.Ts, it, q0)) return;
   const int D = g.D;
   const long long L = g.L;
   const int qrow = q0 + threadIdx.x;
@@ -107,15 +145,19 @@ __global__ __launch_bounds__(128) void softmax_bwd_dq_simt_kernel(
   }
   const float lq = qvalid ? lse[(size_t)it.bh * L + qrow] : 0.f;
   const float dq_ = qvalid ? Dq[(size_t)it.bh * L + qrow] : 0.f;
-  const SpanWalk<BK, 3> walk(it);
+  const SpanWalk<BK, 4> walk(it);
   for (int jt = 0; jt < walk.n; ++jt) {
     int ks, nk;
     walk.tile(jt, ks, nk);
+    const bool tx = ks >= L;
+    const T* kb = tx ? ktp : kp;
+    const T* vb = tx ? vtp : vp;
+    const size_t kbase = tx ? ((size_t)it.bh * g.Ts + (ks - L)) * D : base + (size_t)ks * D;
     __syncthreads();
     for (int e = threadIdx.x; e < BK * D; e += blockDim.x) {
       const int r = e / D, c = e % D;
-      Ks[r][c] = r < nk ? Elem<T>::load(kp, base + (size_t)(ks + r) * D + c) : 0.f;
-      Vs[r][c] = r < nk ? Elem<T>::load(vp, base + (size_t)(ks + r) * D + c) : 0.f;
+      Ks[r][c] = r < nk ? Elem<T>::load(kb, kbase + (size_t)r * D + c) : 0.f;
+      Vs[r][c] = r < nk ? Elem<T>::load(vb, kbase + (size_t)r * D + c) : 0.f;
     }
     __syncthreads();
     for (int r = 0; r < nk; ++r) {
@@ -144,26 +186,35 @@ __global__ __launch_bounds__(128) void softmax_bwd_dq_simt_kernel(
 // lse and Dq staged through LDS.
 template <typename T, int DMAX>
 __global__ __launch_bounds__(128) void softmax_bwd_dkdv_simt_kernel(
-    Geometry g, SoftmaxWork w, const T* __restrict__ qp, const T* __restrict__ kp,
-    const T* __restrict__ vp, const T* __restrict__ dop, const float* __restrict__ lse,
-    const float* __restrict__ Dq, T* __restrict__ dk, T* __restrict__ dv, float scale) {
+    Geometry g, SoftmaxWork w, int ntext, const T* __restrict__ qp, const T* __restrict__ kp,
+    const T* __restrict__ vp, const T* __restrict__ ktp, const T* __restrict__ vtp,
+    const T* __restrict__ dop, const float* __restrict__ lse, const float* __restrict__ Dq,
+    T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ dkt, T* __restrict__ dvt,
+    float scale) {
   constexpr int BK = 128, BQ = 32;
   __shared__ float Qs[BQ][DMAX + 1];
   __shared__ float Ds[BQ][DMAX + 1];
   __shared__ float Ls[BQ], Dd[BQ];
   Item it;
   int k0;
-  if (!decode_item<false>(g, w, BK, blockIdx.x, 0, it, k0)) return;
+  bool text;
+  if (!decode_key_item(g, w, BK, ntext, blockIdx.x, it, k0, text)) return;
   const int D = g.D;
   const long long L = g.L;
   const int krow = k0 + threadIdx.x;
   const bool kvalid = krow < it.q_end;
   const size_t base = (size_t)it.bh * L * D;
+  // the item's keys: video rows of this head, or its text keys
+  const size_t kbase = text ? (size_t)it.bh * g.Ts * D : base;
+  const T* kb = text ? ktp : kp;
+  const T* vb = text ? vtp : vp;
+  T* dkb = text ? dkt : dk;
+  T* dvb = text ? dvt : dv;
   float kv[DMAX], vv[DMAX], ak[DMAX], av[DMAX];
 #pragma unroll
   for (int j = 0; j < DMAX; ++j) {
-    kv[j] = (j < D && kvalid) ? Elem<T>::load(kp, base + (size_t)krow * D + j) : 0.f;
-    vv[j] = (j < D && kvalid) ? Elem<T>::load(vp, base + (size_t)krow * D + j) : 0.f;
+    kv[j] = (j < D && kvalid) ? Elem<T>::load(kb, kbase + (size_t)krow * D + j) : 0.f;
+    vv[j] = (j < D && kvalid) ? Elem<T>::load(vb, kbase + (size_t)krow * D + j) : 0.f;
     ak[j] = 0.f;
     av[j] = 0.f;
   }
@@ -205,21 +256,27 @@ __global__ __launch_bounds__(128) void softmax_bwd_dkdv_simt_kernel(
 #pragma unroll
   for (int j = 0; j < DMAX; ++j)
     if (j < D) {
-      Elem<T>::store(dk, base + (size_t)krow * D + j, ak[j] * scale);
-      Elem<T>::store(dv, base + (size_t)krow * D + j, av[j]);
+      Elem<T>::store(dkb, kbase + (size_t)krow * D + j, ak[j] * scale);
+      Elem<T>::store(dvb, kbase + (size_t)krow * D + j, av[j]);
     }
 }
 
 template <typename T>
 hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, const T* v,
                                    const T* do_hm, const float* lse, const float* Dq, T* dq, T* dk,
-                                   T* dv, float scale, hipStream_t s) {
+                                   T* dv, const SoftmaxBwdText& tx, float scale, hipStream_t s) {
+  if (g.Ts > 0 && (!tx.k_text || !tx.v_text || !tx.dk_text || !tx.dv_text)) return hipErrorInvalidValue;
   const SoftmaxWork wq = window_work(g, 128);
   const SoftmaxWork wk = window_work(g, 128);
   if (wq.grid == 0) return hipSuccess;
+  const int ntext = text_items_padded(g, 128);
+  const T* kt = (const T*)tx.k_text;
+  const T* vt = (const T*)tx.v_text;
+  T* dkt = (T*)tx.dk_text;
+  T* dvt = (T*)tx.dv_text;
 #define VDN_BWD_SIMT(DM)                                                                           \
-  softmax_bwd_dq_simt_kernel<T, DM><<<wq.grid, 128, 0, s>>>(g, wq, q, k, v, do_hm, lse, Dq, dq, scale); \
-  softmax_bwd_dkdv_simt_kernel<T, DM><<<wk.grid, 128, 0, s>>>(g, wk, q, k, v, do_hm, lse, Dq, dk, dv, scale)
+  softmax_bwd_dq_simt_kernel<T, DM><<<wq.grid, 128, 0, s>>>(g, wq, q, k, v, kt, vt, do_hm, lse, Dq, dq, scale); \
+  softmax_bwd_dkdv_simt_kernel<T, DM><<<ntext + wk.grid, 128, 0, s>>>(g, wk, ntext, q, k, v, kt, vt, do_hm, lse, Dq, dk, dv, dkt, dvt, scale)
   if (g.D <= 16) {
     VDN_BWD_SIMT(16);
   } else if (g.D <= 32) {
@@ -264,13 +321,25 @@ struct BwdArgs {
   bf16_t* dq;
   bf16_t* dk;
   bf16_t* dv;
+  // text keys (g.Ts > 0): k_text, v_text [B,H,Ts,D], their transpose
+  // [B,H,D,Tp] (Tp = Ts rounded up to 16, zero columns past Ts) and the
+  // gradients dk_text, dv_text [B,H,Ts,D]
+  const bf16_t* k_text;
+  const bf16_t* v_text;
+  const bf16_t* ktt;
+  bf16_t* dk_text;
+  bf16_t* dv_text;
+  int tpitch;           // Tp
+  int ntext;            // leading workgroups of the dK/dV kernel that take text keys
   float scale, scale_log2;
 };
+
+
 
 constexpr int kBwdQW = 8;          // dQ kernel: waves (32 queries each)
 constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per staged tile (dK, dV)
 
-template <int D>
+template <int D, bool TEXT>
 __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArgs a) {
   constexpr int NT = kBwdQW * 64, BQ = kBwdQW * 32, BK = kBwdBK;
   constexpr int KP = D + 8, TP = BK + 8;
@@ -283,13 +352,18 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
   const Geometry& g = a.g;
   Item it;
   int q0;
-  if (!decode_item<false>(g, a.w, BQ, blockIdx.x, 0, it, q0)) return;
+  if (!decode_item<TEXT>(g, a.w, BQ, blockIdx.x, TEXT ? g.Ts : 0, it, q0)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
   const long long L = g.L;
   const size_t hb = (size_t)it.bh * L * D;
   const bf16_t* K = a.k + hb;
   const bf16_t* V = a.v + hb;
   const bf16_t* Kt = a.kt + hb;
+  // text keys (walk positions from L on)
+  const size_t hbt = TEXT ? (size_t)it.bh * g.Ts * D : 0;
+  const bf16_t* KT = TEXT ? a.k_text + hbt : nullptr;
+  const bf16_t* VT = TEXT ? a.v_text + hbt : nullptr;
+  const bf16_t* KTt = TEXT ? a.ktt + (size_t)it.bh * D * a.tpitch : nullptr;
   const int qrow = q0 + wave * 32 + l32;
   const bool qvalid = qrow < it.q_end;
   bf16x8 qf[NKK], df[NKK];
@@ -308,15 +382,19 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
   f32x16 acc[NDB];
 #pragma unroll
   for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
-  const SpanWalk<BK, 3> walk(it);
+  const SpanWalk<BK, TEXT ? 4 : 3> walk(it);
   const uint32_t kt_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
   u32x4 cr[2 * RCH + TCH];
   auto load_tile = [&](int j) {
     int ks, nk;
     walk.tile(j, ks, nk);
-    const rsrc_t rk = make_rsrc(K + (size_t)ks * D, (uint32_t)nk * D * 2);
-    const rsrc_t rv = make_rsrc(V + (size_t)ks * D, (uint32_t)nk * D * 2);
-    const rsrc_t rt = make_rsrc(Kt + ks, kt_bytes - (uint32_t)ks * 2);
+    const bool tx = TEXT && ks >= L;
+    const int kr = tx ? ks - (int)L : ks;                // row in its own key array
+    const long long pitch = tx ? a.tpitch : L;           // row pitch of the transposed keys
+    const rsrc_t rk = make_rsrc((tx ? KT : K) + (size_t)kr * D, (uint32_t)nk * D * 2);
+    const rsrc_t rv = make_rsrc((tx ? VT : V) + (size_t)kr * D, (uint32_t)nk * D * 2);
+    const rsrc_t rt = tx ? make_rsrc(KTt + kr, (uint32_t)(D * pitch - kr) * 2)
+                         : make_rsrc(Kt + ks, kt_bytes - (uint32_t)ks * 2);
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = tid + NT * i;
@@ -328,7 +406,7 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
     for (int i = 0; i < TCH; ++i) {
       const int c = tid + NT * i;
       const int r = c / (BK / 8), c8 = c % (BK / 8);
-      cr[2 * RCH + i] = buf_ld16(rt, c8 * 8 < nk ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u);
+      cr[2 * RCH + i] = buf_ld16(rt, c8 * 8 < nk ? (uint32_t)(r * pitch + c8 * 8) * 2 : 0x80000000u);
     }
   };
   auto store_tile = [&](int buf) {
@@ -369,11 +447,13 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
         s = mfma32x32x16(as_bf16x8(ld16(kr + kk * 16)), qf[kk], s);
         dp = mfma32x32x16(as_bf16x8(ld16(vr + kk * 16)), df[kk], dp);
       }
-      const bool valid = blk * 32 + hg * 16 < nk;   // whole 16-key groups
+      // video spans hold whole 16-key groups; the text span may end inside one
+      const bool valid = blk * 32 + hg * 16 < nk;
       bf16x8 pb[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = valid ? fast_exp2(fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
+        const bool vk = TEXT ? blk * 32 + hg * 16 + i < nk : valid;
+        const float p = vk ? fast_exp2(fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
         pb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - dqv));
       }
 #pragma unroll
@@ -443,10 +523,17 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
   const Geometry& g = a.g;
   Item it;
   int k0;
-  if (!decode_item<false>(g, a.w, BKEY, blockIdx.x, 0, it, k0)) return;
+  bool text;
+  if (!decode_key_item(g, a.w, BKEY, a.ntext, blockIdx.x, it, k0, text)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, l16 = lane & 15;
   const long long L = g.L;
   const size_t hb = (size_t)it.bh * L * D;
+  // the item's keys: video rows of this head, or its text keys
+  const size_t hk = text ? (size_t)it.bh * g.Ts * D : hb;
+  const bf16_t* Kk = text ? a.k_text : a.k;
+  const bf16_t* Vk = text ? a.v_text : a.v;
+  bf16_t* dKk = text ? a.dk_text : a.dk;
+  bf16_t* dVk = text ? a.dv_text : a.dv;
   const bf16_t* Q = a.q + hb;
   const bf16_t* dO = a.dO + hb;
   const bf16_t* QT = a.qt + hb;
@@ -460,8 +547,8 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
   for (int ks = 0; ks < NKS; ++ks) {
     u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (kvalid) {
-      x = ld16(a.k + hb + (size_t)krow * D + ks * 32 + grp * 8);
-      y = ld16(a.v + hb + (size_t)krow * D + ks * 32 + grp * 8);
+      x = ld16(Kk + hk + (size_t)krow * D + ks * 32 + grp * 8);
+      y = ld16(Vk + hk + (size_t)krow * D + ks * 32 + grp * 8);
     }
     kf[ks] = as_bf16x8(x);
     vf[ks] = as_bf16x8(y);
@@ -628,8 +715,8 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
     __syncthreads();
   }
   if (!kvalid) return;
-  bf16_t* krk = a.dk + hb + (size_t)krow * D;
-  bf16_t* krv = a.dv + hb + (size_t)krow * D;
+  bf16_t* krk = dKk + hk + (size_t)krow * D;
+  bf16_t* krv = dVk + hk + (size_t)krow * D;
 #pragma unroll
   for (int t = 0; t < NDT; ++t) {
     const int d = 16 * t + 4 * grp;
@@ -651,23 +738,34 @@ hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const u
                                    const uint16_t* v, const uint16_t* do_hm, const uint16_t* kt,
                                    const uint16_t* qt, const uint16_t* dot, const float* lse,
                                    const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                                   float scale, hipStream_t s) {
+                                   const SoftmaxBwdText& tx, float scale, hipStream_t s) {
+  if (g.Ts > 0 && (!tx.k_text || !tx.v_text || !tx.ktt || !tx.dk_text || !tx.dv_text ||
+                   tx.tpitch < (g.Ts + 15) / 16 * 16))
+    return hipErrorInvalidValue;
   BwdArgs a;
   a.g = g;
   a.q = q; a.k = k; a.v = v; a.dO = do_hm; a.kt = kt; a.qt = qt; a.dOt = dot;
   a.lse = lse; a.Dq = Dq; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.k_text = (const bf16_t*)tx.k_text; a.v_text = (const bf16_t*)tx.v_text; a.ktt = tx.ktt;
+  a.dk_text = (bf16_t*)tx.dk_text; a.dv_text = (bf16_t*)tx.dv_text; a.tpitch = tx.tpitch;
+  a.ntext = 0;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   BwdArgs b = a;
   a.w = window_work(g, kBwdQW * 32);
   b.w = window_work(g, kBwdFW * 16);
+  b.ntext = text_items_padded(g, kBwdFW * 16);
   if (a.w.grid == 0) return hipSuccess;
+  const unsigned gk = (unsigned)(b.ntext + b.w.grid);
+  const bool tq = g.Ts > 0;
   if (g.D == 128) {
-    softmax_bwd_dq_mfma_kernel<128><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv16_kernel<128><<<b.w.grid, kBwdFW * 64, 0, s>>>(b);
+    if (tq) softmax_bwd_dq_mfma_kernel<128, true><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
+    else softmax_bwd_dq_mfma_kernel<128, false><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
+    softmax_bwd_dkdv16_kernel<128><<<gk, kBwdFW * 64, 0, s>>>(b);
   } else {
-    softmax_bwd_dq_mfma_kernel<64><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv16_kernel<64><<<b.w.grid, kBwdFW * 64, 0, s>>>(b);
+    if (tq) softmax_bwd_dq_mfma_kernel<64, true><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
+    else softmax_bwd_dq_mfma_kernel<64, false><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
+    softmax_bwd_dkdv16_kernel<64><<<gk, kBwdFW * 64, 0, s>>>(b);
   }
   return hipGetLastError();
 }
@@ -679,11 +777,11 @@ template hipError_t launch_softmax_bwd_prep<bf16_t>(const Geometry&, const bf16_
                                                     hipStream_t);
 template hipError_t launch_softmax_bwd_simt<float>(const Geometry&, const float*, const float*,
                                                    const float*, const float*, const float*,
-                                                   const float*, float*, float*, float*, float,
-                                                   hipStream_t);
+                                                   const float*, float*, float*, float*,
+                                                   const SoftmaxBwdText&, float, hipStream_t);
 template hipError_t launch_softmax_bwd_simt<bf16_t>(const Geometry&, const bf16_t*, const bf16_t*,
                                                     const bf16_t*, const bf16_t*, const float*,
-                                                    const float*, bf16_t*, bf16_t*, bf16_t*, float,
-                                                    hipStream_t);
+                                                    const float*, bf16_t*, bf16_t*, bf16_t*,
+                                                    const SoftmaxBwdText&, float, hipStream_t);
 
 }  // namespace vdn

@@ -109,8 +109,11 @@ Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt, bool mx) {
 // Workspace of the Softmax backward: g_s * dOhat in head-major order, Dq,
 // and on the MFMA path K^T, Q^T and dO^T.
 struct BwdLayout {
-  size_t dohm, Dq, kt, qt, dot, total;
+  size_t dohm, Dq, kt, qt, dot, ktt, total;
 };
+
+// Row pitch of the transposed text keys of the Softmax backward.
+long long bwd_text_pitch(const vdn::Geometry& g) { return ((long long)g.Ts + 15) / 16 * 16; }
 
 BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
   const size_t es = dt == VDN_BF16 ? 2 : 4;
@@ -124,6 +127,7 @@ BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
   l.kt = take(mf ? rows * g.D * es : 0);
   l.qt = take(mf ? rows * g.D * es : 0);
   l.dot = take(mf ? rows * g.D * es : 0);
+  l.ktt = take(mf && g.Ts > 0 ? (size_t)g.B * g.H * g.D * bwd_text_pitch(g) * es : 0);
   l.total = o;
   return l;
 }
@@ -621,9 +625,10 @@ size_t vdn_softmax_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p
   return bwd_layout(g, dt).total;
 }
 
-vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, const void* o,
-                                  const float* lse, const float* g_s, const void* d_out, void* dq,
-                                  void* dk, void* dv, float* dg_s, void* workspace,
+vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, const void* k_text,
+                                  const void* v_text, const void* o, const float* lse,
+                                  const float* g_s, const void* d_out, void* dq, void* dk, void* dv,
+                                  void* dk_text, void* dv_text, float* dg_s, void* workspace,
                                   size_t workspace_bytes, const vdn_dims* dims, const vdn_params* p,
                                   vdn_dtype dt, void* stream) {
   g_err[0] = 0;
@@ -631,7 +636,7 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
   vdn_status st = check_geometry(dims, p, dt, &g);
   if (st != VDN_OK) return st;
   NEED(q); NEED(k); NEED(v); NEED(o); NEED(lse); NEED(d_out); NEED(dq); NEED(dk); NEED(dv);
-  if (g.Ts > 0) return fail(VDN_ERR_UNSUPPORTED, "the Softmax backward covers video keys only (text_softmax = 0)");
+  if (g.Ts > 0) { NEED(k_text); NEED(v_text); NEED(dk_text); NEED(dv_text); }
   const BwdLayout lay = bwd_layout(g, dt);
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
@@ -639,6 +644,10 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
   char* ws = (char*)workspace;
   float* Dq = (float*)(ws + lay.Dq);
   const float sc = softmax_scale(p, g.D);
+  vdn::SoftmaxBwdText tx;
+  if (g.Ts > 0) {
+    tx.k_text = k_text; tx.v_text = v_text; tx.dk_text = dk_text; tx.dv_text = dv_text;
+  }
   if (dt == VDN_BF16) {
     uint16_t* dohm = (uint16_t*)(ws + lay.dohm);
     VDN_HIP(vdn::launch_softmax_bwd_prep<uint16_t>(g, (const uint16_t*)o, (const uint16_t*)d_out, g_s,
@@ -651,16 +660,24 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
       VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)k, kt, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
       VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)q, qt, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
       VDN_HIP(vdn::launch_transpose_bf16(dohm, dot, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
+      if (g.Ts > 0) {
+        uint16_t* ktt = (uint16_t*)(ws + lay.ktt);
+        const long long Tp = bwd_text_pitch(g);
+        VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)k_text, ktt, Tp, g.Ts, g.D, Tp, Tp * g.D,
+                                           BH, s));
+        tx.ktt = ktt;
+        tx.tpitch = (int)Tp;
+      }
       VDN_HIP(timer_mark(s, true));
       VDN_HIP(vdn::launch_softmax_bwd_mfma(g, (const uint16_t*)q, (const uint16_t*)k,
                                            (const uint16_t*)v, dohm, kt, qt, dot, lse, Dq,
-                                           (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, sc, s));
+                                           (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, tx, sc, s));
       VDN_HIP(timer_mark(s, false));
     } else {
       VDN_HIP(vdn::launch_softmax_bwd_simt<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k,
                                                      (const uint16_t*)v, dohm, lse, Dq,
                                                      (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv,
-                                                     sc, s));
+                                                     tx, sc, s));
     }
   } else {
     float* dohm = (float*)(ws + lay.dohm);
@@ -668,7 +685,7 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
                                                 Dq, dg_s, s));
     VDN_HIP(vdn::launch_softmax_bwd_simt<float>(g, (const float*)q, (const float*)k, (const float*)v,
                                                 dohm, lse, Dq, (float*)dq, (float*)dk, (float*)dv,
-                                                sc, s));
+                                                tx, sc, s));
   }
   return VDN_OK;
 }

@@ -139,11 +139,23 @@ hipError_t launch_add(const T* a, const T* b, T* out, long long n, hipStream_t s
 template <typename T>
 hipError_t launch_softmax_bwd_prep(const Geometry& g, const T* o, const T* dout, const float* g_s,
                                    T* do_hm, float* Dq, float* dg, hipStream_t s);
+// Text keys of the backward (g.Ts > 0): k_text, v_text [B,H,Ts,D] (storage
+// type of the call) are keys of every query; dk_text, dv_text [B,H,Ts,D]
+// receive their gradients.  The MFMA path also reads ktt = k_text^T
+// [B,H,D,tpitch], tpitch >= Ts rounded up to 16, zero columns past Ts.
+struct SoftmaxBwdText {
+  const void* k_text = nullptr;
+  const void* v_text = nullptr;
+  const uint16_t* ktt = nullptr;
+  void* dk_text = nullptr;
+  void* dv_text = nullptr;
+  int tpitch = 0;
+};
 // q, k, v, do_hm [B,H,L,D]; lse, Dq [B,H,L]; dq, dk, dv [B,H,L,D].
 template <typename T>
 hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, const T* v,
                                    const T* do_hm, const float* lse, const float* Dq, T* dq, T* dk,
-                                   T* dv, float scale, hipStream_t s);
+                                   T* dv, const SoftmaxBwdText& tx, float scale, hipStream_t s);
 
 // bf16 MFMA path (D = 64, 128; N % 16 == 0): kt, qt, dot = K^T, Q^T, dO^T [B,H,D,L].
 bool softmax_bwd_mfma_ok(const Geometry& g);
@@ -151,7 +163,7 @@ hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const u
                                    const uint16_t* v, const uint16_t* do_hm, const uint16_t* kt,
                                    const uint16_t* qt, const uint16_t* dot, const float* lse,
                                    const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                                   float scale, hipStream_t s);
+                                   const SoftmaxBwdText& tx, float scale, hipStream_t s);
 
 // ---- MX-FP8 merge (OCP MX: blocks of 32 along rows, E8M0 scales, E4M3) ----
 // src bf16 [rows, cols] -> codes[r * dst_ld + dst_col0 + c], scales[r * dst_ld/32 + (dst_col0 + c)/32].

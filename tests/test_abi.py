@@ -282,23 +282,38 @@ def test_merge_fwd_and_quantize_validation():
 
 
 def test_softmax_bwd_validation():
+    """Host-side checks of vdn_window_softmax_bwd: required pointers (the
+    text ones only with text keys), workspace size and the workspace query."""
     L = vdn.lib()
     fake = ctypes.c_void_p(0x100000)
     d = _dims()                       # T = 4
     p = vdn.Params().c()
     big = ctypes.c_size_t(1 << 40)
-    args = [fake] * 11
+    # q k v k_text v_text o lse g_s d_out dq dk dv dk_text dv_text dg_s
+    args = [fake] * 15
     fn = L.vdn_window_softmax_bwd
-    for i in (0, 3, 4, 6, 7):         # q, o, lse, d_out, dq
+    for i in (0, 1, 2, 5, 6, 8, 9, 10, 11):
         a = list(args)
         a[i] = None
-        assert fn(*a, fake, big, ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
-    assert fn(*args, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16,
+        assert fn(*a, fake, big, ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG, i
+    # without text keys the text pointers, g_s and dg_s may be NULL
+    a = list(args)
+    for i in (3, 4, 7, 12, 13, 14):
+        a[i] = None
+    assert fn(*a, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16,
               None) == vdn.VDN_ERR_WORKSPACE
+    # with text keys they are required
     pt = vdn.Params(text_softmax=1).c()
-    assert fn(*args, fake, big, ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED
+    for i in (3, 4, 12, 13):
+        a = list(args)
+        a[i] = None
+        assert fn(*a, fake, big, ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG, i
+    assert fn(*args, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16,
+              None) == vdn.VDN_ERR_WORKSPACE
     need = L.vdn_softmax_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16)
     assert need >= 2 * 20 * 16 * 64 * 2 + 2 * 20 * 16 * 4
+    need_t = L.vdn_softmax_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16)
+    assert need_t >= need
 
 
 def test_vda_bwd_validation():

@@ -254,7 +254,7 @@ def measure_text(cfg, t, reps: int = 5) -> dict:
             "frac": ach / PEAK_BF16_TFLOPS, "softmax_flops": sm_flops}
 
 
-def measure_bwd(cfg, t, reps: int = 3) -> dict:
+def measure_bwd(cfg, t, reps: int = 3, text: bool = False) -> dict:
     """Backward of the Softmax branch (vdn_window_softmax_bwd) on the layer's
     q, k, v and gate, with a seeded random output gradient: the forward
     (g_s = NULL, with lse) supplies O_s and lse outside the timed region.
@@ -267,18 +267,23 @@ def measure_bwd(cfg, t, reps: int = 3) -> dict:
     dev = t["q"].device
     if t["q"].dtype != torch.bfloat16:
         return {}
-    o, lse = vdn.window_softmax_fwd(t["q"], t["k"], t["v"], cfg.F, want_lse=True)
+    params = vdn.Params(text_softmax=1) if text else vdn.Params()
+    kt_, vt_ = (t["k_text"], t["v_text"]) if text else (None, None)
+    T = kt_.shape[2] if text else 0
+    o, lse = vdn.window_softmax_fwd(t["q"], t["k"], t["v"], cfg.F, want_lse=True, params=params,
+                                    k_text=kt_, v_text=vt_)
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
     dout = torch.randn((B, L, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    dims = vdn.Dims(B, H, cfg.F, cfg.N, 0, d, d, H * d)
-    p = vdn.Params().c()
+    dims = vdn.Dims(B, H, cfg.F, cfg.N, T, d, d, H * d)
+    p = params.c()
     ws = torch.empty(vdn.lib().vdn_softmax_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p),
                                                               vdn.VDN_BF16), dtype=torch.uint8, device=dev)
 
     def run():
         return vdn.window_softmax_bwd(t["q"], t["k"], t["v"], o, lse, dout, cfg.F, g_s=t["g_s"],
-                                      want_dg=True, workspace=ws)
+                                      want_dg=True, workspace=ws, params=params, k_text=kt_,
+                                      v_text=vt_)
 
     run()
     torch.cuda.synchronize()
@@ -293,9 +298,16 @@ def measure_bwd(cfg, t, reps: int = 3) -> dict:
     timer.close()
     ms = e0.elapsed_time(e1) / reps
     pairs = int(vdn.window_plan(cfg.F)[0].sum())
-    flops = 10.0 * d * pairs * cfg.N * cfg.N * H * B      # S, dP, dV, dQ, dK: 5 products of 2 d per pair
+    # S, dP, dV, dQ, dK: 5 products of 2 d per visible (query, key) pair; text keys are seen by every query
+    flops = 10.0 * d * (pairs * cfg.N * cfg.N + cfg.L * T) * H * B
     ach = flops / (float(k_ms.mean()) / 1e3) / 1e12
     del ws, o, lse, dout
+    if text:
+        return {"entry": "vdn_window_softmax_bwd with text_softmax = 1 (also dk_text, dv_text)",
+                "workload": f"{cfg.name}: Softmax branch backward with its T={T} text keys",
+                "ms": ms, "kernel_ms": float(k_ms.mean()), "bound": "mfma", "achieved": ach,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "algorithmic_flops": flops}
     return {"entry": "vdn_window_softmax_bwd (dq, dk, dv, dg_s)",
             "workload": f"{cfg.name}: Softmax branch backward, B={B} H={H} d={d} F={cfg.F} N={cfg.N}",
             "ms": ms, "kernel": f"softmax_bwd_dq_mfma_kernel<{d}> + softmax_bwd_dkdv16_kernel<{d}>",
@@ -599,6 +611,10 @@ def main() -> int:
         r = res["softmax_bwd"]
         print(f"[bench] Softmax backward: {r['ms']:.3f} ms, kernels {r['kernel_ms']:.3f} ms, "
               f"{r['achieved']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        if "text_softmax" in res:
+            res["text_softmax"]["bwd"] = r = measure_bwd(cfg, t, text=True)
+            print(f"[bench] Softmax backward with text keys: {r['ms']:.3f} ms, kernels {r['kernel_ms']:.3f} ms, "
+                  f"{r['achieved']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_vda_bwd and cfg.dtype == "bf16":
         res["vda_bwd"] = measure_vda_bwd(cfg, t, cpu=not args.no_cpu_baseline)
         r = res["vda_bwd"]

@@ -210,6 +210,36 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
                          const vdn_dims* dims, const vdn_params* p, vdn_dtype dt, void* stream);
 
 /*
+ * vdn_merge_bwd -- gradients of the merge (a8).
+ *
+ * Paper, method, branch calibration defines out = Ohat_s W_s + Ohat_l W_l
+ * (heads concatenated); the experiments train through it.  For the output
+ * gradient d_out the gradients of the two matrix products are
+ *   d_ohat_s = d_out W_s^T,  d_ohat_l = d_out W_l^T,
+ *   dW_s = Ohat_s^T d_out,   dW_l = Ohat_l^T d_out    (summed over all B*L tokens),
+ * in bf16 with fp32 accumulation.  Without projections (W_s = W_l = NULL,
+ * out = Ohat_s + Ohat_l) d_ohat_s = d_ohat_l = d_out.  Only dims->B, H, F,
+ * N, d_k, d_v and D are used.
+ *
+ *  ohat_s, ohat_l [B,L,H,d_v] dt   the forward's branch outputs (read only for dW)
+ *  W_s, W_l       [H*d_v, D]  dt   or both NULL
+ *  d_out          [B,L,D]     dt
+ *  d_ohat_s, d_ohat_l [B,L,H,d_v] dt  outputs
+ *  dW_s, dW_l     [H*d_v, D]  dt   outputs, or both NULL to skip the weight gradients
+ *  workspace      vdn_merge_bwd_workspace_bytes(dims, p, dt) bytes (used only for dW)
+ * Errors: VDN_ERR_UNSUPPORTED with projections unless dt is bf16, D % 128 == 0,
+ * H*d_v % 8 == 0, each operand below 2 GiB and, for dW, B*L % 128 == 0;
+ * VDN_ERR_INVALID_ARG for NULL required pointers or an unpaired W / dW;
+ * VDN_ERR_WORKSPACE for a short workspace.
+ */
+vdn_status vdn_merge_bwd(const void* ohat_s, const void* ohat_l, const void* W_s, const void* W_l,
+                         const void* d_out, void* d_ohat_s, void* d_ohat_l, void* dW_s, void* dW_l,
+                         void* workspace, size_t workspace_bytes, const vdn_dims* dims,
+                         const vdn_params* p, vdn_dtype dt, void* stream);
+/* Workspace bytes of vdn_merge_bwd (0 if the arguments are invalid). */
+size_t vdn_merge_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
+
+/*
  * vdn_window_softmax_bwd -- gradients of the Softmax branch (a7).
  *
  * Paper, method (local Softmax window; branch calibration) defines the

@@ -36,7 +36,7 @@ EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_status_string", "vdn_last_error", "vdn_timer_enable", "vdn_timer_read",
            "vdn_timer_disable", "vda_prep_default_params", "vda_prep_fwd", "vdn_merge_fwd",
            "vdn_mx_quantize", "vdn_window_softmax_bwd", "vdn_softmax_bwd_workspace_bytes",
-           "vda_bwd", "vda_bwd_workspace_bytes")
+           "vda_bwd", "vda_bwd_workspace_bytes", "vdn_merge_bwd", "vdn_merge_bwd_workspace_bytes")
 
 
 class VdnError(RuntimeError):
@@ -147,6 +147,10 @@ def lib() -> ctypes.CDLL:
     L.vdn_window_softmax_bwd.restype = I
     L.vdn_softmax_bwd_workspace_bytes.argtypes = [dp, pp, I]
     L.vdn_softmax_bwd_workspace_bytes.restype = S
+    L.vdn_merge_bwd.argtypes = [P] * 10 + [S, dp, pp, I, P]
+    L.vdn_merge_bwd.restype = I
+    L.vdn_merge_bwd_workspace_bytes.argtypes = [dp, pp, I]
+    L.vdn_merge_bwd_workspace_bytes.restype = S
     L.vda_bwd.argtypes = [P] * 22 + [S, dp, pp, I, P]
     L.vda_bwd.restype = I
     L.vda_bwd_workspace_bytes.argtypes = [dp, pp, I]
@@ -526,6 +530,43 @@ def merge_fwd(ohat_s, ohat_l, W_s, W_l, F: int, params: Params | None = None, ou
         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
         ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
     return out
+
+
+
+def merge_bwd(d_out, ohat_s, ohat_l, W_s, W_l, F: int, want_dw: bool = True,
+              params: Params | None = None, workspace=None, stream=None):
+    """Gradients of the merge (vdn_merge_bwd).  d_out [B,L,D]; ohat_* [B,L,H,d];
+    W_* [H*d, D] or both None (identity).  Returns (d_ohat_s, d_ohat_l
+    [B,L,H,d], dW_s, dW_l [H*d, D] or None)."""
+    torch = _torch()
+    params = params or Params()
+    B, L, H, d = ohat_s.shape
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    dt = ohat_s.dtype
+    code = _dtype_code(ohat_s)
+    dev = ohat_s.device
+    Dm = W_s.shape[1] if W_s is not None else H * d
+    dims = Dims(B, H, F, L // F, 0, d, d, Dm)
+    p = params.c()
+    want_dw = want_dw and W_s is not None
+    need = int(lib().vdn_merge_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p), code)) if want_dw else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace of {workspace.numel()} bytes < {need}")
+    dos, dol = (torch.empty((B, L, H, d), dtype=dt, device=dev) for _ in range(2))
+    dws, dwl = ((torch.empty((H * d, Dm), dtype=dt, device=dev) for _ in range(2)) if want_dw
+                else (None, None))
+    _check(lib().vdn_merge_bwd(
+        _ptr(ohat_s, "ohat_s", dt, (B, L, H, d), dev), _ptr(ohat_l, "ohat_l", dt, (B, L, H, d), dev),
+        _ptr(W_s, "W_s", dt, (H * d, Dm), dev, allow_none=True),
+        _ptr(W_l, "W_l", dt, (H * d, Dm), dev, allow_none=True),
+        _ptr(d_out, "d_out", dt, (B, L, Dm), dev), _ptr(dos, "d_ohat_s"), _ptr(dol, "d_ohat_l"),
+        _ptr(dws, "dW_s", allow_none=True), _ptr(dwl, "dW_l", allow_none=True),
+        ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+        ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return dos, dol, dws, dwl
 
 
 def mx_quantize(x, stream=None):

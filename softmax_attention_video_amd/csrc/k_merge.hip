@@ -15,6 +15,7 @@
 // features of one token (8-byte stores).
 #include "vdn_common.h"
 #include "vdn_internal.h"
+#include "gemm_nt.h"
 
 namespace vdn {
 
@@ -35,13 +36,20 @@ constexpr int kGroupRows = 4;
 // walks it in groups of kGroupRows rows, column by column inside a group, so
 // the workgroups resident on one XCD share A row panels and W^T column
 // panels in that XCD's L2.
+//
+// LD = false: the operands are packed (row pitch K).  LD = true: rows of all
+// four operands have pitch ld >= K, which lets one product with a
+// contraction of 2K be split into two halves of the same rows (a1 = a0 + K,
+// bt1 = bt0 + K, ld = 2K): the backward's GEMMs.
+template <bool LD>
 __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __restrict__ a0,
                                                               const bf16_t* __restrict__ a1,
                                                               const bf16_t* __restrict__ bt0,
                                                               const bf16_t* __restrict__ bt1,
                                                               bf16_t* __restrict__ out,
                                                               long long M, int K, int N,
-                                                              int tiles_m, int tiles_n, int rpx) {
+                                                              int tiles_m, int tiles_n, int rpx,
+                                                              long long ld_) {
   constexpr int BM = kGBM, BN = kGBN, BK = kGBK;
   constexpr int P = BK + 8;
   constexpr int CH = BM * BK / 8 / 512;   // 16-byte chunks per thread per operand and K step (4)
@@ -64,17 +72,20 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
   const int nkt = 2 * K / BK;   // K % BK == 0
-  const rsrc_t ra0 = make_rsrc(a0 + (size_t)m0 * K, rsrc_bytes(a0 + (size_t)m0 * K, a0 + (size_t)M * K));
-  const rsrc_t ra1 = make_rsrc(a1 + (size_t)m0 * K, rsrc_bytes(a1 + (size_t)m0 * K, a1 + (size_t)M * K));
-  const rsrc_t rb0 = make_rsrc(bt0 + (size_t)n0 * K, rsrc_bytes(bt0 + (size_t)n0 * K, bt0 + (size_t)N * K));
-  const rsrc_t rb1 = make_rsrc(bt1 + (size_t)n0 * K, rsrc_bytes(bt1 + (size_t)n0 * K, bt1 + (size_t)N * K));
+  // row pitch; each descriptor ends at the end of its operand's last row
+  const size_t ld = LD ? (size_t)ld_ : (size_t)K;
+  const size_t ea = (size_t)(M - 1) * ld + K, eb = (size_t)(N - 1) * ld + K;
+  const rsrc_t ra0 = make_rsrc(a0 + (size_t)m0 * ld, rsrc_bytes(a0 + (size_t)m0 * ld, a0 + ea));
+  const rsrc_t ra1 = make_rsrc(a1 + (size_t)m0 * ld, rsrc_bytes(a1 + (size_t)m0 * ld, a1 + ea));
+  const rsrc_t rb0 = make_rsrc(bt0 + (size_t)n0 * ld, rsrc_bytes(bt0 + (size_t)n0 * ld, bt0 + eb));
+  const rsrc_t rb1 = make_rsrc(bt1 + (size_t)n0 * ld, rsrc_bytes(bt1 + (size_t)n0 * ld, bt1 + eb));
   uint32_t voff[CH];
   int soff[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = tid + 512 * i;
     const int r = c / (BK / 8), c8 = c % (BK / 8);
-    voff[i] = (uint32_t)((r * K + c8 * 8) * 2);
+    voff[i] = (uint32_t)((r * ld + c8 * 8) * 2);
     soff[i] = (r * P + c8 * 8);
   }
   f32x16 acc[4][2];
@@ -169,7 +180,22 @@ hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const 
   const int rpx = (tm + kNumXcd - 1) / kNumXcd;
   const int groups = (rpx + kGroupRows - 1) / kGroupRows;
   const long long grid = (long long)kNumXcd * groups * kGroupRows * tn;
-  merge_gemm_bf16_kernel<<<(unsigned)grid, 512, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm, tm, tn, rpx);
+  merge_gemm_bf16_kernel<false><<<(unsigned)grid, 512, 0, s>>>(a0, a1, w0t, w1t, out, M, K, Dm, tm,
+                                                               tn, rpx, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt_bf16(const uint16_t* a, const uint16_t* bt, uint16_t* out, long long M,
+                               long long Kc, int N, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (Kc % (2 * kGBK) != 0 || Kc / 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int K = (int)(Kc / 2);
+  const int tm = (int)((M + kGBM - 1) / kGBM), tn = (N + kGBN - 1) / kGBN;
+  const int rpx = (tm + kNumXcd - 1) / kNumXcd;
+  const int groups = (rpx + kGroupRows - 1) / kGroupRows;
+  const long long grid = (long long)kNumXcd * groups * kGroupRows * tn;
+  merge_gemm_bf16_kernel<true><<<(unsigned)grid, 512, 0, s>>>(a, a + K, bt, bt + K, out, M, K, N, tm,
+                                                              tn, rpx, Kc);
   return hipGetLastError();
 }
 // ---- generic SIMT GEMM (fp32 storage or odd shapes): 16x16 tiles ----

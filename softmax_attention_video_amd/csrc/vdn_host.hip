@@ -1,6 +1,7 @@
 // C-ABI of the VDN attention library: argument checks, workspace layout and
 // launch sequencing.  Every check runs on the host before the first HIP call.
 #include "../../include/vdn.h"
+#include "gemm_nt.h"
 #include "vdn_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -617,6 +618,88 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
   st = merge_prepare(g, p, dt, W_s, W_l, ohat_l, Dm, ws, lay, s);
   if (st != VDN_OK) return st;
   return merge_finish(g, p, dt, W_s, W_l, ohat_s, ohat_l, out, Dm, ws, lay, s);
+}
+
+// Merge backward: dOhat = dout W^T on the merge's GEMM; dW = Ohat^T dout
+// over the tokens, from transposed copies of dout and of each Ohat.
+struct MergeBwdLayout {
+  size_t doutT, ohT, total;
+};
+
+MergeBwdLayout merge_bwd_layout(const vdn::Geometry& g, int Dm) {
+  const size_t M = (size_t)g.B * g.L, K = (size_t)g.H * g.D;
+  MergeBwdLayout l{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+  l.doutT = take(M * Dm * 2);
+  l.ohT = take(M * K * 2);
+  l.total = o;
+  return l;
+}
+
+size_t vdn_merge_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
+  vdn::Geometry g;
+  if (check_geometry(dims, p, dt, &g) != VDN_OK || dims->D < 1) return 0;
+  return merge_bwd_layout(g, dims->D).total;
+}
+
+vdn_status vdn_merge_bwd(const void* ohat_s, const void* ohat_l, const void* W_s, const void* W_l,
+                         const void* d_out, void* d_ohat_s, void* d_ohat_l, void* dW_s, void* dW_l,
+                         void* workspace, size_t workspace_bytes, const vdn_dims* dims,
+                         const vdn_params* p, vdn_dtype dt, void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(d_out); NEED(d_ohat_s); NEED(d_ohat_l);
+  const int Dm = dims->D;
+  if ((W_s == nullptr) != (W_l == nullptr))
+    return fail(VDN_ERR_INVALID_ARG, "W_s and W_l must both be given or both be NULL");
+  if ((dW_s == nullptr) != (dW_l == nullptr))
+    return fail(VDN_ERR_INVALID_ARG, "dW_s and dW_l must both be given or both be NULL");
+  const long long M = (long long)g.B * g.L;
+  const int K = g.H * g.D;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t es = dt == VDN_BF16 ? 2 : 4;
+  if (!W_s) {   // out = Ohat_s + Ohat_l
+    if (Dm != K) return fail(VDN_ERR_INVALID_ARG, "without projections D=%d must equal H*d_v=%d", Dm, K);
+    if (dW_s) return fail(VDN_ERR_INVALID_ARG, "no projections: dW_s, dW_l must be NULL");
+    VDN_HIP(hipMemcpyAsync(d_ohat_s, d_out, (size_t)M * K * es, hipMemcpyDeviceToDevice, s));
+    VDN_HIP(hipMemcpyAsync(d_ohat_l, d_out, (size_t)M * K * es, hipMemcpyDeviceToDevice, s));
+    return VDN_OK;
+  }
+  if (dt != VDN_BF16) return fail(VDN_ERR_UNSUPPORTED, "the merge backward needs bf16 storage");
+  if (Dm % 128 != 0 || K % 8 != 0)
+    return fail(VDN_ERR_UNSUPPORTED, "the merge backward needs D %% 128 == 0 and H*d_v %% 8 == 0");
+  if ((long long)M * Dm * 2 > 0x7FFFFFF0ll || (long long)M * K * 2 > 0x7FFFFFF0ll)
+    return fail(VDN_ERR_UNSUPPORTED, "the merge backward's operands must stay below 2 GiB");
+  if (dW_s) {
+    NEED(ohat_s); NEED(ohat_l);
+    if (M % 128 != 0) return fail(VDN_ERR_UNSUPPORTED, "dW needs B*L %% 128 == 0 (B*L=%lld)", M);
+  }
+  const MergeBwdLayout lay = merge_bwd_layout(g, Dm);
+  if (dW_s) {
+    st = check_workspace(workspace, workspace_bytes, lay.total);
+    if (st != VDN_OK) return st;
+  }
+  // dOhat_* [M, K] = dout [M, D] W_*^T (W_* [K, D] is the contraction-contiguous right operand)
+  VDN_HIP(vdn::launch_gemm_nt_bf16((const uint16_t*)d_out, (const uint16_t*)W_s, (uint16_t*)d_ohat_s,
+                                   M, Dm, K, s));
+  VDN_HIP(vdn::launch_gemm_nt_bf16((const uint16_t*)d_out, (const uint16_t*)W_l, (uint16_t*)d_ohat_l,
+                                   M, Dm, K, s));
+  if (!dW_s) return VDN_OK;
+  // dW_* [K, D] = Ohat_*^T dout: both operands transposed to token-contiguous rows
+  char* ws = (char*)workspace;
+  uint16_t* doutT = (uint16_t*)(ws + lay.doutT);
+  uint16_t* ohT = (uint16_t*)(ws + lay.ohT);
+  VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)d_out, doutT, M, M, Dm, M, M * Dm, 1, s));
+  const void* oh[2] = {ohat_s, ohat_l};
+  void* dw[2] = {dW_s, dW_l};
+  for (int i = 0; i < 2; ++i) {
+    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)oh[i], ohT, M, M, K, M, M * K, 1, s));
+    VDN_HIP(vdn::launch_gemm_nt_bf16(ohT, doutT, (uint16_t*)dw[i], K, M, Dm, s));
+  }
+  return VDN_OK;
 }
 
 size_t vdn_softmax_bwd_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {

@@ -351,3 +351,32 @@ def test_vda_bwd_validation():
     bad = _dims()
     bad.d_k = bad.d_v = 48
     assert L.vda_bwd_workspace_bytes(ctypes.byref(bad), ctypes.byref(p), vdn.VDN_BF16) == 0
+
+
+def test_merge_bwd_validation():
+    """Host-side checks of vdn_merge_bwd: required pointers, paired W and dW,
+    the supported storage and shapes, the workspace, and its query."""
+    L = vdn.lib()
+    fake = ctypes.c_void_p(0x100000)
+    d = _dims(N=32, D=256)           # B*L = 640, a multiple of 128
+    p = vdn.Params().c()
+    big = ctypes.c_size_t(1 << 40)
+    args = [fake] * 9                 # ohat_s ohat_l W_s W_l d_out d_ohat_s d_ohat_l dW_s dW_l
+    fn = L.vdn_merge_bwd
+    for i in (4, 5, 6):
+        a = list(args)
+        a[i] = None
+        assert fn(*a, fake, big, ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG, i
+    for i in (2, 7):                  # unpaired W or dW
+        a = list(args)
+        a[i] = None
+        assert fn(*a, fake, big, ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG, i
+    assert fn(*args, fake, big, ctypes.byref(d), ctypes.byref(p), vdn.VDN_F32, None) == vdn.VDN_ERR_UNSUPPORTED
+    d_odd = _dims(D=200)
+    assert fn(*args, fake, big, ctypes.byref(d_odd), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED
+    assert fn(*args, fake, ctypes.c_size_t(16), ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16,
+              None) == vdn.VDN_ERR_WORKSPACE
+    need = L.vdn_merge_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16)
+    assert need >= (20 * 32) * (256 + 128) * 2
+    d_rag = _dims(D=256)              # B*L = 320: no weight gradients for it
+    assert fn(*args, fake, big, ctypes.byref(d_rag), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED

@@ -317,6 +317,48 @@ def measure_bwd(cfg, t, reps: int = 3, text: bool = False) -> dict:
             "note": "S and dP are computed in both kernels: 14 d MFMA flops per pair against the 10 d counted"}
 
 
+def measure_merge_bwd(cfg, t, reps: int = 3) -> dict:
+    """Backward of the merge (vdn_merge_bwd) at the layer's shape with seeded
+    random branch outputs and output gradient: HIP-event time of the call
+    (four GEMMs and the three token-contiguous transposes dW needs)."""
+    import torch
+
+    import softmax_attention_video_amd as vdn
+
+    B, H, L, d = t["q"].shape
+    dev = t["q"].device
+    D = t["W_s"].shape[1]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    r = lambda *s_: torch.randn(*s_, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    os_, ol_, dout = r(B, L, H, d), r(B, L, H, d), r(B, L, D)
+    dims = vdn.Dims(B, H, cfg.F, cfg.N, 0, d, d, D)
+    p = vdn.Params().c()
+    ws = torch.empty(vdn.lib().vdn_merge_bwd_workspace_bytes(ctypes.byref(dims), ctypes.byref(p), vdn.VDN_BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        return vdn.merge_bwd(dout, os_, ol_, t["W_s"], t["W_l"], cfg.F, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4 * 2.0 * B * L * (H * d) * D
+    ach = flops / (ms / 1e3) / 1e12
+    del ws, os_, ol_, dout
+    return {"entry": "vdn_merge_bwd (d_ohat_s, d_ohat_l, dW_s, dW_l)",
+            "workload": f"{cfg.name} merge backward: M={B * L} tokens, K={H * d}, D={D}",
+            "ms": ms, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flops": flops,
+            "note": "time of the whole call, the three transposes for dW included"}
+
+
 def measure_vda_bwd(cfg, t, reps: int = 5, cpu: bool = True) -> dict:
     """Backward of the linear branch (vda_bwd) on the layer's inputs with a
     seeded random gradient of Ohat_l: HIP-event time of the whole call and,
@@ -615,6 +657,10 @@ def main() -> int:
             res["text_softmax"]["bwd"] = r = measure_bwd(cfg, t, text=True)
             print(f"[bench] Softmax backward with text keys: {r['ms']:.3f} ms, kernels {r['kernel_ms']:.3f} ms, "
                   f"{r['achieved']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_bwd and cfg.proj and cfg.dtype == "bf16" and (cfg.B * cfg.L) % 128 == 0:
+        res["merge_bwd"] = r = measure_merge_bwd(cfg, t)
+        print(f"[bench] merge backward: {r['ms']:.3f} ms, {r['achieved']:.0f} TFLOP/s", file=sys.stderr,
+              flush=True)
     if not args.no_vda_bwd and cfg.dtype == "bf16":
         res["vda_bwd"] = measure_vda_bwd(cfg, t, cpu=not args.no_cpu_baseline)
         r = res["vda_bwd"]

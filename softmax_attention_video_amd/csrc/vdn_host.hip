@@ -682,23 +682,45 @@ vdn_status vdn_merge_bwd(const void* ohat_s, const void* ohat_l, const void* W_s
     st = check_workspace(workspace, workspace_bytes, lay.total);
     if (st != VDN_OK) return st;
   }
-  // dOhat_* [M, K] = dout [M, D] W_*^T (W_* [K, D] is the contraction-contiguous right operand)
-  VDN_HIP(vdn::launch_gemm_nt_bf16((const uint16_t*)d_out, (const uint16_t*)W_s, (uint16_t*)d_ohat_s,
-                                   M, Dm, K, s));
-  VDN_HIP(vdn::launch_gemm_nt_bf16((const uint16_t*)d_out, (const uint16_t*)W_l, (uint16_t*)d_ohat_l,
-                                   M, Dm, K, s));
-  if (!dW_s) return VDN_OK;
-  // dW_* [K, D] = Ohat_*^T dout: both operands transposed to token-contiguous rows
-  char* ws = (char*)workspace;
-  uint16_t* doutT = (uint16_t*)(ws + lay.doutT);
-  uint16_t* ohT = (uint16_t*)(ws + lay.ohT);
-  VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)d_out, doutT, M, M, Dm, M, M * Dm, 1, s));
-  const void* oh[2] = {ohat_s, ohat_l};
-  void* dw[2] = {dW_s, dW_l};
-  for (int i = 0; i < 2; ++i) {
-    VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)oh[i], ohT, M, M, K, M, M * K, 1, s));
-    VDN_HIP(vdn::launch_gemm_nt_bf16(ohT, doutT, (uint16_t*)dw[i], K, M, Dm, s));
+  // dW_* [K, D] = Ohat_*^T dout, on the side stream: both operands transposed
+  // to token-contiguous rows.  Its GEMMs have few output tiles (K/256 x D/256)
+  // and a long contraction, so they leave compute units free for the dOhat
+  // GEMMs on the caller's stream.
+  SideStream* ss = nullptr;
+  hipError_t ej = hipSuccess;
+  if (dW_s) {
+    VDN_HIP(side_stream(&ss));
+    VDN_HIP(hipEventRecord(ss->fork, s));
+    VDN_HIP(hipStreamWaitEvent(ss->stream, ss->fork, 0));
+    char* ws = (char*)workspace;
+    uint16_t* doutT = (uint16_t*)(ws + lay.doutT);
+    uint16_t* ohT = (uint16_t*)(ws + lay.ohT);
+    hipError_t e = vdn::launch_transpose_bf16((const uint16_t*)d_out, doutT, M, M, Dm, M, M * Dm, 1,
+                                              ss->stream);
+    const void* oh[2] = {ohat_s, ohat_l};
+    void* dw[2] = {dW_s, dW_l};
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      e = vdn::launch_transpose_bf16((const uint16_t*)oh[i], ohT, M, M, K, M, M * K, 1, ss->stream);
+      if (e == hipSuccess) e = vdn::launch_gemm_nt_bf16(ohT, doutT, (uint16_t*)dw[i], K, M, Dm, ss->stream);
+    }
+    // the join is recorded even after a failure, so the caller's stream
+    // never runs ahead of work already queued on the side stream
+    ej = hipEventRecord(ss->join, ss->stream);
+    if (e != hipSuccess) st = fail(VDN_ERR_HIP, "weight-gradient launch failed: %s", hipGetErrorString(e));
   }
+  // dOhat_* [M, K] = dout [M, D] W_*^T (W_* [K, D] is the contraction-contiguous right operand)
+  hipError_t e2 = hipSuccess;
+  if (st == VDN_OK) {
+    e2 = vdn::launch_gemm_nt_bf16((const uint16_t*)d_out, (const uint16_t*)W_s, (uint16_t*)d_ohat_s, M,
+                                  Dm, K, s);
+    if (e2 == hipSuccess)
+      e2 = vdn::launch_gemm_nt_bf16((const uint16_t*)d_out, (const uint16_t*)W_l, (uint16_t*)d_ohat_l,
+                                    M, Dm, K, s);
+  }
+  const hipError_t ew = ss ? (ej == hipSuccess ? hipStreamWaitEvent(s, ss->join, 0) : ej) : hipSuccess;
+  if (st != VDN_OK) return st;
+  if (e2 != hipSuccess) return fail(VDN_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e2));
+  if (ew != hipSuccess) return fail(VDN_ERR_HIP, "side-stream join failed: %s", hipGetErrorString(ew));
   return VDN_OK;
 }
 

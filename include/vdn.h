@@ -382,20 +382,55 @@ vdn_status vda_prep_fwd(const void* q, const void* k, const void* v,
                         const vdn_dims* dims, const vda_prep_params* p, vdn_dtype dt,
                         void* stream);
 
-/* Workspace bytes that suffice for every entry point above at these sizes;
- * 0 if the arguments are invalid. */
+/* Workspace bytes that suffice for every entry point above at these sizes
+ * (vdn_attn_fwd's full layout); 0 if the arguments are invalid.  vdn_attn_fwd
+ * needs the full amount only when it keeps Ohat_s / Ohat_l in the workspace:
+ * with both ohat_s and ohat_l given, those two regions (the last ones) are not
+ * required. */
 size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
+/* What one entry point alone requires (0 if the arguments are invalid):
+ *  vdn_scan_workspace_bytes     vda_scan_fwd / vda_scan_rev: the fp32 frame
+ *                               maps T_f, U_f, S_text (+ the chunk maps for
+ *                               d = 16, 32)
+ *  vdn_softmax_workspace_bytes  vdn_window_softmax_fwd: V^T (and the text
+ *                               values) on the bf16 MFMA path, else 0
+ *  vdn_merge_workspace_bytes    vdn_merge_fwd: W_s^T, W_l^T (+ MX-FP8 operands) */
+size_t vdn_scan_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
+size_t vdn_softmax_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
+size_t vdn_merge_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt);
 
 /*
- * vdn_window_plan -- host-only helper: the frame roles the kernels use.
- *  vis   [F*F] row = query frame, 1 = key frame visible to Softmax (nullable)
+ * vdn_window_plan -- host-only helper: the frame roles the kernels use
+ * (method, local Softmax window and boundary anchors; bidirectional linear
+ * attention: the states gathered just outside the window and the decay
+ * bridge over the skipped span).
+ *  vis   [F*F] row = query frame, 1 = key frame visible to Softmax (nullable);
+ *        built by running the Softmax kernels' own work-item decoder over
+ *        their whole grid (one head, one token per frame)
  *  i_fwd, ws, i_rev, we [F] (each nullable): query frame t reads
  *        P_fwd[i_fwd[t]] decayed over frames ws[t]..t and P_rev[i_rev[t]]
- *        decayed over frames t..we[t].
- * Host memory, caller owned.  No device is touched.
+ *        decayed over frames t..we[t]; the readout kernels' own function.
+ * Host memory, caller owned.  No device is touched.  Fails with
+ * VDN_ERR_UNSUPPORTED if the work items do not cover every query frame
+ * exactly once.
  */
 vdn_status vdn_window_plan(int F, const vdn_params* p, uint8_t* vis,
                            int32_t* i_fwd, int32_t* ws, int32_t* i_rev, int32_t* we);
+
+/*
+ * vdn_window_row_keys -- host-only helper: how many keys each query row's
+ * softmax runs over, in the launch vdn_window_softmax_fwd makes for these
+ * dims, params and dtype (method, local Softmax window: N tokens of every
+ * visible frame, plus the T text keys with text_softmax).  The library runs
+ * that launch's work-item decoder over its whole grid on the host.
+ *  keys [B*H*L] int64, host memory, caller owned: keys[(b*H + h)*L + l] for
+ *       query row l of head (b, h); -1 where the row is covered by no work
+ *       item or by more than one.
+ * No device is touched.  Argument errors as for vdn_window_softmax_fwd;
+ * VDN_ERR_INVALID_ARG if B*H*L exceeds 2^31.
+ */
+vdn_status vdn_window_row_keys(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                               int64_t* keys);
 
 /*
  * Kernel timer (instrumentation for roofline measurements).

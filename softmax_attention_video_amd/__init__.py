@@ -15,6 +15,7 @@ Entry points (same names as the C-ABI):
   mx_quantize(x)              -> codes, scales  (vdn_mx_quantize)
   prep_fwd(...)               -> q', k', v'     (vda_prep_fwd)
   window_plan(F, params)      -> host tables    (vdn_window_plan)
+  window_row_keys(dims, ...)  -> keys per row   (vdn_window_row_keys)
   workspace_bytes(...)
 """
 from __future__ import annotations
@@ -36,7 +37,9 @@ EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_status_string", "vdn_last_error", "vdn_timer_enable", "vdn_timer_read",
            "vdn_timer_disable", "vda_prep_default_params", "vda_prep_fwd", "vdn_merge_fwd",
            "vdn_mx_quantize", "vdn_window_softmax_bwd", "vdn_softmax_bwd_workspace_bytes",
-           "vda_bwd", "vda_bwd_workspace_bytes", "vdn_merge_bwd", "vdn_merge_bwd_workspace_bytes")
+           "vda_bwd", "vda_bwd_workspace_bytes", "vdn_merge_bwd", "vdn_merge_bwd_workspace_bytes",
+           "vdn_window_row_keys", "vdn_scan_workspace_bytes", "vdn_softmax_workspace_bytes",
+           "vdn_merge_workspace_bytes")
 
 
 class VdnError(RuntimeError):
@@ -121,10 +124,14 @@ def lib() -> ctypes.CDLL:
         getattr(L, n).restype = I
     L.vdn_window_softmax_fwd.argtypes = [P] * 9 + [S, dp, pp, I, P]
     L.vdn_window_softmax_fwd.restype = I
-    L.vdn_workspace_bytes.argtypes = [dp, pp, I]
-    L.vdn_workspace_bytes.restype = S
+    for n in ("vdn_workspace_bytes", "vdn_scan_workspace_bytes", "vdn_softmax_workspace_bytes",
+              "vdn_merge_workspace_bytes"):
+        getattr(L, n).argtypes = [dp, pp, I]
+        getattr(L, n).restype = S
     L.vdn_window_plan.argtypes = [I, pp, P, P, P, P, P]
     L.vdn_window_plan.restype = I
+    L.vdn_window_row_keys.argtypes = [dp, pp, I, P]
+    L.vdn_window_row_keys.restype = I
     L.vdn_status_string.argtypes = [I]
     L.vdn_status_string.restype = ctypes.c_char_p
     L.vdn_last_error.argtypes = []
@@ -181,6 +188,15 @@ def window_plan(F: int, params: Params | None = None):
     _check(lib().vdn_window_plan(F, ctypes.byref(p), vis.ctypes.data,
                                  *[a.ctypes.data for a in t]))
     return vis, *t
+
+
+def window_row_keys(dims: Dims, params: Params | None = None, dtype: int = VDN_BF16):
+    """Keys per query row of the forward Softmax launch ([B*H*L] int64; -1 =
+    row not covered exactly once)."""
+    p = (params or Params()).c()
+    keys = np.zeros(dims.B * dims.H * dims.F * dims.N, np.int64)
+    _check(lib().vdn_window_row_keys(ctypes.byref(dims), ctypes.byref(p), dtype, keys.ctypes.data))
+    return keys
 
 
 class KernelTimer:
@@ -250,9 +266,15 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(dims, params, code, device, workspace):
+_WS_QUERY = {"attn": "vdn_workspace_bytes", "scan": "vdn_scan_workspace_bytes",
+             "softmax": "vdn_softmax_workspace_bytes", "merge": "vdn_merge_workspace_bytes"}
+
+
+def _workspace(dims, params, code, device, workspace, entry="attn"):
+    """The caller's workspace, or a new one of the size the entry point needs."""
     torch = _torch()
-    need = workspace_bytes(dims, params, code)
+    p = (params or Params()).c()
+    need = int(getattr(lib(), _WS_QUERY[entry])(ctypes.byref(dims), ctypes.byref(p), code))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     if workspace.numel() < need:
@@ -329,7 +351,7 @@ def _scan(which, k, v, beta, alpha, k_text, v_text, beta_text, params, workspace
         P = torch.empty((B, H, C + 1, d, d), dtype=f32, device=dev)
     if S_text is None:
         S_text = torch.empty((B, H, d, d), dtype=f32, device=dev)
-    ws = _workspace(dims, params, code, dev, workspace)
+    ws = _workspace(dims, params, code, dev, workspace, "scan")
     p = params.c()
     fn = lib().vda_scan_fwd if which == "fwd" else lib().vda_scan_rev
     _check(fn(_ptr(k, "k", dt, (B, H, L, d), dev), _ptr(v, "v", dt, (B, H, L, d), dev),
@@ -378,7 +400,7 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
     if out is None:
         out = torch.empty((B, L, H, d), dtype=dt, device=dev)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=dev) if want_lse else None
-    ws = _workspace(dims, params, code, dev, workspace)
+    ws = _workspace(dims, params, code, dev, workspace, "softmax")
     p = params.c()
     _check(lib().vdn_window_softmax_fwd(
         _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
@@ -520,7 +542,7 @@ def merge_fwd(ohat_s, ohat_l, W_s, W_l, F: int, params: Params | None = None, ou
     dims = Dims(B, H, F, L // F, 0, d, d, Dm)
     if out is None:
         out = torch.empty((B, L, Dm), dtype=dt, device=dev)
-    ws = _workspace(dims, params, code, dev, workspace)
+    ws = _workspace(dims, params, code, dev, workspace, "merge")
     p = params.c()
     _check(lib().vdn_merge_fwd(
         _ptr(ohat_s, "ohat_s", dt, (B, L, H, d), dev), _ptr(ohat_l, "ohat_l", dt, (B, L, H, d), dev),

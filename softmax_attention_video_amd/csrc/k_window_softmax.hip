@@ -33,28 +33,6 @@
 
 namespace vdn {
 
-SoftmaxWork window_work(const Geometry& g, int bq) {
-  SoftmaxWork w{};
-  w.GA = g.anchors ? 2 * g.B * g.H : 0;
-  w.GC = g.B * g.H * g.C;
-  w.tA = (g.N + bq - 1) / bq;
-  w.tC = (g.cf * g.N + bq - 1) / bq;
-  w.pa = (w.GA + kNumXcd - 1) / kNumXcd;
-  w.pc = (w.GC + kNumXcd - 1) / kNumXcd;
-  int mx = 0;
-  for (int x = 0; x < kNumXcd; ++x) {
-    int na = w.GA - x * w.pa;
-    na = na < 0 ? 0 : (na > w.pa ? w.pa : na);
-    int nc = w.GC - x * w.pc;
-    nc = nc < 0 ? 0 : (nc > w.pc ? w.pc : nc);
-    int items = na * w.tA + nc * w.tC;
-    mx = items > mx ? items : mx;
-  }
-  w.grid = mx * kNumXcd;
-  return w;
-}
-
-
 // -------------------------------------------------------------------------
 // bf16 MFMA flash kernel.  512 threads = 8 waves of 32 queries each (256
 // queries per workgroup), two waves per SIMD.  The kernel is compiled with
@@ -96,6 +74,7 @@ struct WinArgs {
 
 constexpr int kWinNW = 8;                  // waves per workgroup, 32 queries each
 constexpr int kWinBQ = kWinNW * 32;        // queries per workgroup
+static_assert(kWinBQ == kWinMfmaBQ, "query rows per workgroup");
 constexpr float kLazySum = 256.f;
 
 
@@ -497,7 +476,7 @@ __global__ __launch_bounds__(128) void window_softmax_simt_kernel(Geometry g, So
                                                                   T* __restrict__ out,
                                                                   float* __restrict__ lse,
                                                                   float scale_log2) {
-  constexpr int BQ = 128, BK = 32;
+  constexpr int BQ = kWinSimtBQ, BK = 32;
   __shared__ float Ks[BK][DMAX + 1];
   __shared__ float Vs[BK][DMAX + 1];
   Item it;
@@ -565,7 +544,7 @@ hipError_t launch_window_softmax_simt(const Geometry& g, const T* q, const T* k,
                                       const T* k_text, const T* v_text, const float* g_s, T* out,
                                       float* lse, float scale, hipStream_t s) {
   if (g.Ts > 0 && (!k_text || !v_text)) return hipErrorInvalidValue;
-  const SoftmaxWork w = window_work(g, 128);
+  const SoftmaxWork w = window_work(g, kWinSimtBQ);
   if (w.grid == 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (g.D <= 16)

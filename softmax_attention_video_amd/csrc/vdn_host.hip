@@ -3,6 +3,7 @@
 #include "../../include/vdn.h"
 #include "gemm_nt.h"
 #include "vdn_internal.h"
+#include "window_items.h"
 
 #include <hip/hip_runtime.h>
 
@@ -72,37 +73,51 @@ hipError_t side_stream(SideStream** out) {
   return hipSuccess;
 }
 
-// Workspace carve-up (offsets in bytes, each 256-aligned).
+// Workspace carve-up (offsets in bytes, each 256-aligned).  Each entry point
+// takes only the regions it uses; vdn_attn_fwd takes them all, with the
+// branch outputs Ohat_s, Ohat_l last so that a caller who passes its own
+// buffers for them needs no room for them.
 struct Layout {
-  size_t vt, wt0, wt1, Tf, Uf, St, Tc, Uc, Pf, Pr, ohs, ohl;
+  size_t vt, wt0, wt1, Tf, Uf, St, Tc, Uc, Pf, Pr;
   size_t mxa, mxas, mxw, mxws;   // MX-FP8 merge operands: codes and scales of A and W^T
+  size_t ohs, ohl;
   size_t total;
 };
 
+enum class Entry { Attn, Scan, Softmax, Merge };
+
 // mx: the merge runs in MX-FP8 (vdn_params.merge_mxfp8 on the bf16 path).
-Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt, bool mx) {
+Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt, bool mx, Entry e) {
   const size_t es = dt == VDN_BF16 ? 2 : 4;
   const size_t BH = (size_t)g.B * g.H, DD = (size_t)g.D * g.D;
   const size_t M = (size_t)g.B * g.L, K2 = 2 * (size_t)g.H * g.D;
+  const bool attn = e == Entry::Attn;
+  const bool sm = attn || e == Entry::Softmax;
+  const bool scan = attn || e == Entry::Scan;
+  const bool merge = attn || e == Entry::Merge;
+  const bool bf16 = dt == VDN_BF16;
+  // chunk maps exist only where the chunk-composed scan runs (d = 16, 32);
+  // d = 64, 128 scan the frame maps directly
+  const bool compose = g.D != 64 && g.D != 128;
   Layout l{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
-  l.vt = take(dt == VDN_BF16 ? BH * (size_t)vdn::softmax_vt_pitch(g) * g.D * es : 0);
-  l.wt0 = take(dt == VDN_BF16 ? (size_t)g.H * g.D * Dm * es : 0);
-  l.wt1 = take(dt == VDN_BF16 ? (size_t)g.H * g.D * Dm * es : 0);
-  l.Tf = take(BH * g.F * DD * 4);
-  l.Uf = take(BH * g.F * DD * 4);
-  l.St = take(BH * DD * 4);
-  l.Tc = take(BH * 2 * g.C * DD * 4);
-  l.Uc = take(BH * 2 * g.C * DD * 4);
-  l.Pf = take(BH * (g.C + 1) * DD * 4);
-  l.Pr = take(BH * (g.C + 1) * DD * 4);
-  l.ohs = take(BH * g.L * g.D * es);
-  l.ohl = take(BH * g.L * g.D * es);
-  l.mxa = take(mx ? M * K2 : 0);
-  l.mxas = take(mx ? M * K2 / 32 : 0);
-  l.mxw = take(mx ? (size_t)Dm * K2 : 0);
-  l.mxws = take(mx ? (size_t)Dm * K2 / 32 : 0);
+  l.vt = take(sm && bf16 && vdn::window_softmax_mfma_ok(g) ? BH * (size_t)vdn::softmax_vt_pitch(g) * g.D * es : 0);
+  l.wt0 = take(merge && bf16 ? (size_t)g.H * g.D * Dm * es : 0);
+  l.wt1 = take(merge && bf16 ? (size_t)g.H * g.D * Dm * es : 0);
+  l.Tf = take(scan ? BH * g.F * DD * 4 : 0);
+  l.Uf = take(scan ? BH * g.F * DD * 4 : 0);
+  l.St = take(scan ? BH * DD * 4 : 0);
+  l.Tc = take(scan && compose ? BH * 2 * g.C * DD * 4 : 0);
+  l.Uc = take(scan && compose ? BH * 2 * g.C * DD * 4 : 0);
+  l.Pf = take(attn ? BH * (g.C + 1) * DD * 4 : 0);
+  l.Pr = take(attn ? BH * (g.C + 1) * DD * 4 : 0);
+  l.mxa = take(merge && mx ? M * K2 : 0);
+  l.mxas = take(merge && mx ? M * K2 / 32 : 0);
+  l.mxw = take(merge && mx ? (size_t)Dm * K2 : 0);
+  l.mxws = take(merge && mx ? (size_t)Dm * K2 / 32 : 0);
+  l.ohs = take(attn ? BH * g.L * g.D * es : 0);
+  l.ohl = take(attn ? BH * g.L * g.D * es : 0);
   l.total = o;
   return l;
 }
@@ -393,7 +408,7 @@ vdn_status scan_entry(const void* k, const void* v, const float* beta, const flo
   NEED(k); NEED(v); NEED(beta); NEED(alpha);
   if (g.T > 0) { NEED(k_text); NEED(v_text); NEED(beta_text); }
   if (!P_fwd && !P_rev) return fail(VDN_ERR_INVALID_ARG, "output state pointer is NULL");
-  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt, use_mx(p, dt));
+  const Layout lay = make_layout(g, g.H * g.D, dt, false, Entry::Scan);
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -472,7 +487,25 @@ size_t vdn_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype 
   vdn::Geometry g;
   if (check_geometry(dims, p, dt, &g) != VDN_OK) return 0;
   const int Dm = dims->D > 0 ? dims->D : g.H * g.D;
-  return make_layout(g, Dm, dt, use_mx(p, dt)).total;
+  return make_layout(g, Dm, dt, use_mx(p, dt), Entry::Attn).total;
+}
+
+size_t vdn_scan_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
+  vdn::Geometry g;
+  if (check_geometry(dims, p, dt, &g) != VDN_OK) return 0;
+  return make_layout(g, g.H * g.D, dt, false, Entry::Scan).total;
+}
+
+size_t vdn_softmax_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
+  vdn::Geometry g;
+  if (check_geometry(dims, p, dt, &g) != VDN_OK) return 0;
+  return make_layout(g, g.H * g.D, dt, false, Entry::Softmax).total;
+}
+
+size_t vdn_merge_workspace_bytes(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt) {
+  vdn::Geometry g;
+  if (check_geometry(dims, p, dt, &g) != VDN_OK || dims->D < 1) return 0;
+  return make_layout(g, dims->D, dt, use_mx(p, dt), Entry::Merge).total;
 }
 
 vdn_status vdn_window_plan(int F, const vdn_params* p, uint8_t* vis, int32_t* i_fwd, int32_t* ws,
@@ -484,25 +517,84 @@ vdn_status vdn_window_plan(int F, const vdn_params* p, uint8_t* vis, int32_t* i_
     return fail(VDN_ERR_INVALID_ARG, "bad chunk_frames/window_chunks/anchors");
   if (F % p->chunk_frames != 0)
     return fail(VDN_ERR_INVALID_ARG, "F=%d is not a multiple of chunk_frames=%d", F, p->chunk_frames);
-  const int cf = p->chunk_frames, wc = p->window_chunks, C = F / cf;
-  for (int t = 0; t < F; ++t) {
-    const bool anc = p->anchors && (t == 0 || t == F - 1);
-    const int c = t / cf;
-    int lo = c - wc < 0 ? 0 : c - wc;
-    int hi = c + wc + 1 > C ? C : c + wc + 1;     // chunk range [lo, hi)
-    if (vis) {
-      for (int f = 0; f < F; ++f) {
-        const int cfr = f / cf;
-        bool v = anc || (cfr >= lo && cfr < hi) || (p->anchors && (f == 0 || f == F - 1));
-        vis[(size_t)t * F + f] = v ? 1 : 0;
+  // One head with one token per frame: the Softmax kernels' own item decoder
+  // run over their whole grid gives every query frame's key frames.
+  vdn::Geometry g{};
+  g.B = 1; g.H = 1; g.F = F; g.N = 1; g.T = 0; g.D = 0;
+  g.cf = p->chunk_frames; g.wc = p->window_chunks; g.anchors = p->anchors;
+  g.C = F / g.cf; g.L = F; g.Ts = 0;
+  if (vis) {
+    memset(vis, 0, (size_t)F * F);
+    const vdn::SoftmaxWork w = vdn::window_work(g, vdn::kWinMfmaBQ);
+    int* covered = new int[F]();
+    for (int bid = 0; bid < w.grid; ++bid) {
+      vdn::Item it;
+      int q0;
+      if (!vdn::decode_item<false>(g, w, vdn::kWinMfmaBQ, bid, 0, it, q0)) continue;
+      const int q1 = q0 + vdn::kWinMfmaBQ < it.q_end ? q0 + vdn::kWinMfmaBQ : it.q_end;
+      const int kb[3] = {it.kb0, it.kb1, it.kb2}, ke[3] = {it.ke0, it.ke1, it.ke2};
+      for (int t = q0; t < q1; ++t) {
+        ++covered[t];
+        for (int s = 0; s < it.nspan; ++s)
+          for (int f = kb[s]; f < ke[s]; ++f) vis[(size_t)t * F + f] = 1;
       }
     }
-    int a = anc ? 0 : lo, b = anc ? C : hi;
-    if (i_fwd) i_fwd[t] = a;
-    if (ws) ws[t] = a * cf;
-    if (i_rev) i_rev[t] = b;
-    if (we) we[t] = (b * cf < F ? b * cf : F) - 1;
+    int bad = -1;
+    for (int t = 0; t < F && bad < 0; ++t)
+      if (covered[t] != 1) bad = t;
+    const int nbad = bad >= 0 ? covered[bad] : 0;
+    delete[] covered;
+    if (bad >= 0)
+      return fail(VDN_ERR_UNSUPPORTED, "work items cover query frame %d %d times", bad, nbad);
   }
+  // gather indices and bridge ends: the readout kernels' own function
+  for (int t = 0; t < F; ++t) {
+    int a, s, b, e;
+    vdn::readout_indices(g, t, a, s, b, e);
+    if (i_fwd) i_fwd[t] = a;
+    if (ws) ws[t] = s;
+    if (i_rev) i_rev[t] = b;
+    if (we) we[t] = e;
+  }
+  return VDN_OK;
+}
+
+vdn_status vdn_window_row_keys(const vdn_dims* dims, const vdn_params* p, vdn_dtype dt,
+                               int64_t* keys) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(keys);
+  const long long rows = (long long)g.B * g.H * g.L;
+  if (rows > (1ll << 31)) return fail(VDN_ERR_INVALID_ARG, "too many rows (%lld)", rows);
+  // the launch vdn_window_softmax_fwd makes for these sizes
+  const bool mfma = dt == VDN_BF16 && vdn::window_softmax_mfma_ok(g);
+  const int bq = mfma ? vdn::kWinMfmaBQ : vdn::kWinSimtBQ;
+  // the MFMA kernel walks the text keys in whole 16-key groups and takes
+  // the last Ts % 16 as one masked block after the walk
+  const int nt = mfma ? (g.Ts & ~15) : g.Ts;
+  const int rem = g.Ts - nt;
+  const vdn::SoftmaxWork w = vdn::window_work(g, bq);
+  int* covered = new int[rows]();
+  memset(keys, 0, (size_t)rows * sizeof(int64_t));
+  for (int bid = 0; bid < w.grid; ++bid) {
+    vdn::Item it;
+    int q0;
+    if (!vdn::decode_item<true>(g, w, bq, bid, nt, it, q0)) continue;
+    const int kb[4] = {it.kb0, it.kb1, it.kb2, it.kb3}, ke[4] = {it.ke0, it.ke1, it.ke2, it.ke3};
+    long long n = rem;
+    for (int s = 0; s < it.nspan; ++s) n += ke[s] - kb[s];
+    const int q1 = q0 + bq < it.q_end ? q0 + bq : it.q_end;
+    for (int l = q0; l < q1; ++l) {
+      const long long r = (long long)it.bh * g.L + l;
+      ++covered[r];
+      keys[r] += n;
+    }
+  }
+  for (long long r = 0; r < rows; ++r)
+    if (covered[r] != 1) keys[r] = -1;
+  delete[] covered;
   return VDN_OK;
 }
 
@@ -535,7 +627,7 @@ vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v,
   if (st != VDN_OK) return st;
   NEED(q); NEED(k); NEED(v); NEED(out);
   if (g.Ts > 0) { NEED(k_text); NEED(v_text); }
-  const Layout lay = make_layout(g, dims->D > 0 ? dims->D : g.H * g.D, dt, use_mx(p, dt));
+  const Layout lay = make_layout(g, g.H * g.D, dt, false, Entry::Softmax);
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
   return run_softmax(g, p, dt, q, k, v, k_text, v_text, g_s, out, lse, (char*)workspace, lay,
@@ -557,8 +649,9 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   const int Dm = dims->D;
   st = check_merge(g, p, dt, W_s, W_l, Dm);
   if (st != VDN_OK) return st;
-  const Layout lay = make_layout(g, Dm, dt, use_mx(p, dt));
-  st = check_workspace(workspace, workspace_bytes, lay.total);
+  const Layout lay = make_layout(g, Dm, dt, use_mx(p, dt), Entry::Attn);
+  // the branch-output regions come last: not needed when the caller passes both
+  st = check_workspace(workspace, workspace_bytes, ohat_s && ohat_l ? lay.ohs : lay.total);
   if (st != VDN_OK) return st;
 
   hipStream_t s = (hipStream_t)stream;
@@ -610,7 +703,7 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
   const int Dm = dims->D;
   st = check_merge(g, p, dt, W_s, W_l, Dm);
   if (st != VDN_OK) return st;
-  const Layout lay = make_layout(g, Dm, dt, use_mx(p, dt));
+  const Layout lay = make_layout(g, Dm, dt, use_mx(p, dt), Entry::Merge);
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
   hipStream_t s = (hipStream_t)stream;

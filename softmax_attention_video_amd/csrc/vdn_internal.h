@@ -43,7 +43,8 @@ inline long long softmax_vt_pitch(const Geometry& g) {
   return g.L + (g.Ts > 0 ? ((long long)g.Ts + 15) / 16 * 16 : 0);
 }
 
-// Work split of the window Softmax over query groups (see window_work()).
+// Work split of the window Softmax over query groups (window_work() in
+// window_items.h).
 struct SoftmaxWork {
   int GA, GC;    // anchor-frame groups, chunk groups
   int tA, tC;    // query tiles per anchor group / chunk group
@@ -53,7 +54,9 @@ struct SoftmaxWork {
 
 constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dealt round-robin
 
-SoftmaxWork window_work(const Geometry& g, int bq);
+// Query rows per workgroup of the forward window Softmax kernels.
+constexpr int kWinMfmaBQ = 256;   // bf16 MFMA kernel: 8 waves x 32 queries
+constexpr int kWinSimtBQ = 128;   // generic kernel: one thread per query
 
 // ---- window Softmax (Softmax branch) ----
 // q,k [B,H,L,D]; k_text [B,H,Ts,D] (read only when Ts > 0); vt [B,H,D,Lp]

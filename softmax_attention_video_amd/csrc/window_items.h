@@ -58,7 +58,7 @@ struct SpanWalk {
 };
 
 // Appends the text span [L, L + nt) after the item's video spans.
-__device__ __forceinline__ void add_text_span(const Geometry& g, int nt, Item& it) {
+__host__ __device__ inline void add_text_span(const Geometry& g, int nt, Item& it) {
   it.kb3 = it.ke3 = 0;
   if (nt <= 0) return;
   const int tb = (int)g.L, te = (int)(g.L + nt);
@@ -72,10 +72,76 @@ __device__ __forceinline__ void add_text_span(const Geometry& g, int nt, Item& i
   ++it.nspan;
 }
 
+// Frame roles of one chunk group, in frames: the non-anchor query frames
+// [f0, f1) of chunk c and their key frames, at most three contiguous frame
+// spans in ascending order -- [anchor 0] window [anchor F-1].  The window is
+// the chunks c - wc .. c + wc clipped to the clip; an anchor frame is a
+// separate span only when it lies outside the window.  Returns false when
+// the chunk has no non-anchor frame.  This is the one definition of the
+// visibility rule: the Softmax kernels decode their work items through it
+// and the host-side plan (vdn_window_plan) builds its frame mask from it.
+struct ChunkRoles {
+  int f0, f1;
+  int nspan;
+  int b0, e0, b1, e1, b2, e2;
+};
+__host__ __device__ inline bool chunk_roles(int F, int cf, int wc, int anchors, int c,
+                                            ChunkRoles& r) {
+  int f0 = c * cf, f1 = (c + 1) * cf;
+  if (f1 > F) f1 = F;
+  if (anchors) {
+    if (f0 == 0) f0 = 1;
+    if (f1 == F) f1 = F - 1;
+  }
+  r.f0 = f0;
+  r.f1 = f1;
+  int lo = c - wc;
+  lo = (lo < 0 ? 0 : lo) * cf;
+  int hi = (c + wc + 1) * cf;
+  hi = hi > F ? F : hi;
+  const bool a_lo = anchors && lo > 0, a_hi = anchors && hi < F;
+  r.b0 = a_lo ? 0 : lo;
+  r.e0 = a_lo ? 1 : hi;
+  r.b1 = a_lo ? lo : F - 1;
+  r.e1 = a_lo ? hi : F;
+  r.b2 = F - 1;
+  r.e2 = F;
+  r.nspan = 1 + (a_lo ? 1 : 0) + (a_hi ? 1 : 0);
+  return f1 > f0;
+}
+
+// Work split of the window Softmax over query groups.  An "anchor group" is
+// one anchor frame of one head (its keys: the whole clip); a "chunk group"
+// the non-anchor frames of one chunk of one head.  Groups are cut into
+// query tiles of bq rows.  MI355X deals workgroups round-robin to its 8
+// XCDs (workgroup b runs on XCD b % 8), so each XCD gets a contiguous slice
+// of the groups -- anchor groups first -- and the grid is 8 x the longest
+// slice.
+inline SoftmaxWork window_work(const Geometry& g, int bq) {
+  SoftmaxWork w{};
+  w.GA = g.anchors ? 2 * g.B * g.H : 0;
+  w.GC = g.B * g.H * g.C;
+  w.tA = (g.N + bq - 1) / bq;
+  w.tC = (g.cf * g.N + bq - 1) / bq;
+  w.pa = (w.GA + kNumXcd - 1) / kNumXcd;
+  w.pc = (w.GC + kNumXcd - 1) / kNumXcd;
+  int mx = 0;
+  for (int x = 0; x < kNumXcd; ++x) {
+    int na = w.GA - x * w.pa;
+    na = na < 0 ? 0 : (na > w.pa ? w.pa : na);
+    int nc = w.GC - x * w.pc;
+    nc = nc < 0 ? 0 : (nc > w.pc ? w.pc : nc);
+    int items = na * w.tA + nc * w.tC;
+    mx = items > mx ? items : mx;
+  }
+  w.grid = mx * kNumXcd;
+  return w;
+}
+
 // Decode workgroup id -> (query range, key spans).  Returns false if idle.
 // TEXT: append a span of the first nt text keys (none if nt == 0).
 template <bool TEXT>
-__device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork& w, int bq,
+__host__ __device__ inline bool decode_item(const Geometry& g, const SoftmaxWork& w, int bq,
                                             int bid, int nt, Item& it, int& q0) {
   const int x = bid % kNumXcd;
   int k = bid / kNumXcd;
@@ -103,30 +169,18 @@ __device__ __forceinline__ bool decode_item(const Geometry& g, const SoftmaxWork
   const int tile = k % w.tC;
   if (gc >= w.GC || gc >= (x + 1) * w.pc) return false;
   it.bh = gc / g.C;
-  const int c = gc % g.C;
-  int f0 = c * g.cf, f1 = (c + 1) * g.cf;
-  if (f1 > g.F) f1 = g.F;
-  if (g.anchors) {
-    if (f0 == 0) f0 = 1;
-    if (f1 == g.F) f1 = g.F - 1;
-  }
-  if (f1 <= f0) return false;
-  it.q_begin = (int)(f0 * N);
-  it.q_end = (int)(f1 * N);
-  int lo = c - g.wc;
-  lo = (lo < 0 ? 0 : lo) * g.cf;
-  int hi = (c + g.wc + 1) * g.cf;
-  hi = hi > g.F ? g.F : hi;
-  // spans in ascending key order: [anchor 0] window [anchor F-1]
+  ChunkRoles r;
+  if (!chunk_roles(g.F, g.cf, g.wc, g.anchors, gc % g.C, r)) return false;
   const int nN = (int)N;
-  const bool a_lo = g.anchors && lo > 0, a_hi = g.anchors && hi < g.F;
-  it.kb0 = a_lo ? 0 : lo * nN;
-  it.ke0 = a_lo ? nN : hi * nN;
-  it.kb1 = a_lo ? lo * nN : (g.F - 1) * nN;
-  it.ke1 = a_lo ? hi * nN : g.F * nN;
-  it.kb2 = (g.F - 1) * nN;
-  it.ke2 = g.F * nN;
-  it.nspan = 1 + (a_lo ? 1 : 0) + (a_hi ? 1 : 0);
+  it.q_begin = r.f0 * nN;
+  it.q_end = r.f1 * nN;
+  it.kb0 = r.b0 * nN;
+  it.ke0 = r.e0 * nN;
+  it.kb1 = r.b1 * nN;
+  it.ke1 = r.e1 * nN;
+  it.kb2 = r.b2 * nN;
+  it.ke2 = r.e2 * nN;
+  it.nspan = r.nspan;
   it.kb3 = it.ke3 = 0;
   if (TEXT) add_text_span(g, nt, it);
   q0 = it.q_begin + tile * bq;

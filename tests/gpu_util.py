@@ -86,6 +86,21 @@ def oracle_params(params):
                     text_softmax=bool(params.text_softmax))
 
 
+def block_errors(got, exp, F):
+    """Largest rel-L2 over the heads and over the (batch, head, frame) blocks
+    of a [B, L, H, d] output."""
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    B, L, H, d = exp.shape
+    N = L // F
+    g5 = got.reshape(B, F, N, H, d)
+    e5 = exp.reshape(B, F, N, H, d)
+    head = max(rel_l2(got[b, :, h], exp[b, :, h]) for b in range(B) for h in range(H))
+    frame = max(rel_l2(g5[b, f, :, h], e5[b, f, :, h])
+                for b in range(B) for h in range(H) for f in range(F))
+    return head, frame
+
+
 TOL = {"f32": 1e-4, "bf16": 1e-2}
 TOL_STATE = 1e-4
 
@@ -115,10 +130,25 @@ def check_full(cfg, params=None, tol=None):
         "lse": rel_l2(got["lse"], ref["lse"]),
         "out": rel_l2(got["out"].reshape(ref["out"].shape), ref["out"]),
     }
+    # per head and per (head, frame) maxima beside the pooled figures, so
+    # that one wrong head or frame cannot hide behind the others
+    F = inp["alpha"].shape[2]
+    for key, g_, r_ in (("Ohat_s", got["Ohat_s"], ref["Ohat_s"].transpose(0, 2, 1, 3)),
+                        ("Ohat_l", got["Ohat_l"], ref["Ohat_l"].transpose(0, 2, 1, 3)),
+                        ("sm", got["sm"], ref["Ohat_s"].transpose(0, 2, 1, 3))):
+        errs[key + "_head_max"], errs[key + "_frame_max"] = block_errors(g_, r_, F)
+    o_g = got["out"].reshape(ref["out"].shape)
+    errs["out_frame_max"] = max(rel_l2(o_g[b, f * (L // F):(f + 1) * (L // F)],
+                                       ref["out"][b, f * (L // F):(f + 1) * (L // F)])
+                                for b in range(B) for f in range(F))
     log(f"[parity] rel-L2 {errs}")
     for key in ("P_fwd", "P_rev", "S_text"):
         assert errs[key] <= TOL_STATE, (key, errs)
     for key in ("Ohat_s", "Ohat_l", "sm", "out"):
         assert errs[key] <= tol, (key, errs)
+    for key in ("Ohat_s", "Ohat_l", "sm"):
+        assert errs[key + "_head_max"] <= tol, (key, errs)
+        assert errs[key + "_frame_max"] <= tol, (key, errs)
+    assert errs["out_frame_max"] <= tol, errs
     assert errs["lse"] <= 1e-5, errs
     return errs

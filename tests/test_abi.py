@@ -42,11 +42,18 @@ def test_status_strings():
         assert L.vdn_status_string(code) == name
 
 
-@pytest.mark.parametrize("F", list(range(2, 61)))
-@pytest.mark.parametrize("params", [O.Params(), O.Params(chunk_frames=3, window_chunks=2),
-                                    O.Params(anchors=False), O.Params(chunk_frames=1, window_chunks=0),
-                                    O.Params(chunk_frames=2, window_chunks=3)])
+PLAN_PARAMS = [O.Params(), O.Params(chunk_frames=3, window_chunks=2), O.Params(anchors=False),
+               O.Params(chunk_frames=1, window_chunks=0), O.Params(chunk_frames=2, window_chunks=3),
+               O.Params(chunk_frames=4, window_chunks=0, anchors=False),
+               O.Params(chunk_frames=10, window_chunks=2)]
+
+
+@pytest.mark.parametrize("F", list(range(2, 61)) + [100, 120, 240, 600])
+@pytest.mark.parametrize("params", PLAN_PARAMS)
 def test_window_plan_bit_exact(F, params):
+    """vis comes from the Softmax kernels' work-item decoder run over their
+    grid, the indices from the readout kernels' function: both bit-exact
+    against the oracle's literal rule."""
     if F % params.chunk_frames:
         with pytest.raises(vdn.VdnError) as e:
             vdn.window_plan(F, vdn.Params(chunk_frames=params.chunk_frames))
@@ -58,6 +65,50 @@ def test_window_plan_bit_exact(F, params):
     np.testing.assert_array_equal(vis, O.visibility(F, params))
     for got, exp in zip((i_f, ws, i_r, we), O.scan_indices(F, params)):
         np.testing.assert_array_equal(got, exp)
+
+
+def _row_keys_expected(B, H, F, N, T, params: O.Params):
+    vis = O.visibility(F, params).astype(np.int64)
+    per_frame = vis.sum(axis=1) * N + (T if params.text_softmax else 0)
+    return np.tile(np.repeat(per_frame, N), B * H)
+
+
+@pytest.mark.parametrize("B,H,F,N,T,d,dt", [
+    (1, 1, 20, 16, 8, 16, vdn.VDN_F32),          # tiny fp32 (generic kernel)
+    (1, 8, 60, 256, 64, 64, vdn.VDN_BF16),       # small bf16 (MFMA kernel)
+    (1, 16, 100, 384, 512, 128, vdn.VDN_BF16),   # medium
+    (1, 24, 120, 1536, 512, 128, vdn.VDN_BF16),  # H3-scale layer
+    (1, 16, 600, 768, 256, 128, vdn.VDN_BF16),   # long clip
+    (2, 3, 20, 80, 5, 64, vdn.VDN_BF16),         # ragged tiles, two batches
+    (1, 2, 10, 37, 3, 64, vdn.VDN_BF16),         # N % 16 != 0: generic kernel
+    (1, 2, 35, 112, 21, 128, vdn.VDN_BF16),
+    (3, 5, 15, 16, 0, 32, vdn.VDN_BF16),
+])
+@pytest.mark.parametrize("params", [O.Params(), O.Params(text_softmax=True), O.Params(anchors=False),
+                                    O.Params(chunk_frames=3, window_chunks=2, text_softmax=True),
+                                    O.Params(chunk_frames=1, window_chunks=0, anchors=False)])
+def test_window_row_keys_bit_exact(B, H, F, N, T, d, dt, params):
+    """Every query row of every head is covered by exactly one work item of
+    the forward Softmax launch, and that item walks exactly N*|Vis(t)| video
+    keys (+ T text keys with text_softmax): the launch's own decoder, run over
+    its whole grid, against the oracle's visibility rule."""
+    if F % params.chunk_frames:
+        pytest.skip("F not a multiple of chunk_frames")
+    dims = vdn.Dims(B, H, F, N, T, d, d, H * d)
+    vp = vdn.Params(chunk_frames=params.chunk_frames, window_chunks=params.window_chunks,
+                    anchors=int(params.anchors), text_softmax=int(params.text_softmax))
+    got = vdn.window_row_keys(dims, vp, dt)
+    np.testing.assert_array_equal(got, _row_keys_expected(B, H, F, N, T, params))
+
+
+def test_window_row_keys_rejects_bad_args():
+    L = vdn.lib()
+    p = vdn.Params().c()
+    keys = np.zeros(20 * 16, np.int64)
+    assert L.vdn_window_row_keys(ctypes.byref(_dims(F=22)), ctypes.byref(p), vdn.VDN_BF16,
+                                 keys.ctypes.data) == vdn.VDN_ERR_INVALID_ARG
+    assert L.vdn_window_row_keys(ctypes.byref(_dims()), ctypes.byref(p), vdn.VDN_BF16,
+                                 None) == vdn.VDN_ERR_INVALID_ARG
 
 
 def test_window_plan_rejects_bad_args():
@@ -126,9 +177,51 @@ def test_attn_unknown_dtype_and_params():
 
 
 def test_attn_workspace_too_small():
-    need = vdn.workspace_bytes(_dims())
+    d = _dims()
+    need = vdn.workspace_bytes(d)
     assert need > 0
-    assert _call_attn(_dims(), ws_bytes=need - 1) == vdn.VDN_ERR_WORKSPACE
+    # without caller buffers for the branch outputs the whole layout is needed
+    assert _call_attn(d, ws_bytes=need - 1, null=("ohat_s", "ohat_l")) == vdn.VDN_ERR_WORKSPACE
+    assert _call_attn(d, ws_bytes=need - 1, null=("ohat_s",)) == vdn.VDN_ERR_WORKSPACE
+    # with both given, their two regions (last in the layout) are not needed
+    oh = 2 * ((d.B * d.H * d.F * d.N * d.d_v * 2 + 255) // 256 * 256)
+    assert _call_attn(d, ws_bytes=need - oh - 1) == vdn.VDN_ERR_WORKSPACE
+
+
+def test_per_entry_workspace_queries():
+    """Each entry point needs only its own regions: the scan its frame maps
+    (and chunk maps for d = 16, 32), the Softmax the transposed values (bf16
+    MFMA path), the merge the transposed projections."""
+    L = vdn.lib()
+    p = vdn.Params()
+    pc = p.c()
+    for d_ in (32, 64):
+        d = _dims(d_k=d_, d_v=d_, D=2 * d_)
+        BH, F, C, DD = d.B * d.H, d.F, d.F // 5, d_ * d_
+        a256 = lambda x: (x + 255) // 256 * 256
+        scan = L.vdn_scan_workspace_bytes(ctypes.byref(d), ctypes.byref(pc), vdn.VDN_BF16)
+        maps = 2 * a256(BH * F * DD * 4) + a256(BH * DD * 4)
+        chunks = 2 * a256(BH * 2 * C * DD * 4) if d_ == 32 else 0
+        assert scan == maps + chunks
+        sm = L.vdn_softmax_workspace_bytes(ctypes.byref(d), ctypes.byref(pc), vdn.VDN_BF16)
+        assert sm == (a256(BH * d.F * d.N * d_ * 2) if d_ == 64 else 0)   # MFMA path: d = 64, 128
+        assert L.vdn_softmax_workspace_bytes(ctypes.byref(d), ctypes.byref(pc), vdn.VDN_F32) == 0
+        mg = L.vdn_merge_workspace_bytes(ctypes.byref(d), ctypes.byref(pc), vdn.VDN_BF16)
+        assert mg == 2 * a256(d.H * d_ * d.D * 2)
+        assert max(scan, sm, mg) < vdn.workspace_bytes(d, p)
+        fake = ctypes.c_void_p(0x100000)
+        for fn in (L.vda_scan_fwd, L.vda_scan_rev):
+            assert fn(*[fake] * 9, fake, ctypes.c_size_t(scan - 1), ctypes.byref(d), ctypes.byref(pc),
+                      vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+        if sm > 0:    # (a call that passes the check would launch kernels on fake pointers)
+            assert L.vdn_window_softmax_fwd(fake, fake, fake, None, None, None, fake, None, fake,
+                                            ctypes.c_size_t(sm - 1), ctypes.byref(d), ctypes.byref(pc),
+                                            vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+        assert L.vdn_merge_fwd(fake, fake, fake, fake, fake, fake, ctypes.c_size_t(mg - 1),
+                               ctypes.byref(d), ctypes.byref(pc), vdn.VDN_BF16, None) == vdn.VDN_ERR_WORKSPACE
+    bad = _dims(F=21)
+    for fn in (L.vdn_scan_workspace_bytes, L.vdn_softmax_workspace_bytes, L.vdn_merge_workspace_bytes):
+        assert fn(ctypes.byref(bad), ctypes.byref(pc), vdn.VDN_BF16) == 0
 
 
 def test_workspace_bytes_zero_for_invalid():

@@ -534,3 +534,60 @@ def test_full_operator_small_case_consistent():
     r2 = O.vdn_attn(inp, linear_form="bruteforce")
     np.testing.assert_allclose(r1["out"], r2["out"], rtol=1e-11, atol=1e-12)
     assert r1["out"].shape == (1, cfg.L, cfg.D)
+
+
+# ---------------------------------------------------------------------------
+# head_rows: the sampled-row evaluator behind the full-size GPU checks
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("p", [
+    O.Params(),
+    O.Params(chunk_frames=3, window_chunks=2, text_softmax=True, text_init_scale=0.8,
+             rms_eps=1e-3, softmax_scale=0.3),
+    O.Params(anchors=False, chunk_frames=4, window_chunks=0, text_softmax=True),
+])
+def test_head_rows_matches_full_head(p):
+    """head_rows at shuffled rows equals the full per-head evaluation: the
+    linear leg against each query frame's own masked recurrence
+    (vdn_head's brute-force form), the Softmax leg against torch's dense
+    softmax with the visibility mask and the text columns.  Gates g_s and
+    g_l differ, so using one for the other fails."""
+    rng = np.random.default_rng(11)
+    F, N, d, T = 24, 3, 4, 5
+    L = F * N
+    unit = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)
+    q = rng.standard_normal((L, d))
+    k = unit(rng.standard_normal((L, d)))
+    v = rng.standard_normal((L, d))
+    beta = rng.random(L)
+    alpha = rng.uniform(0.7, 1.0, (F, d))
+    kt, vt, bt = unit(rng.standard_normal((T, d))), rng.standard_normal((T, d)), rng.random(T)
+    g_s, g_l = rng.random(L), rng.random(L)
+    gamma = rng.uniform(0.5, 1.5, d)
+    rows = rng.permutation(L)[: L // 2]
+    got = O.head_rows(q, k, v, beta, alpha, kt, vt, bt, g_s, g_l, rows, gamma=gamma, p=p)
+    ref = O.vdn_head(q, k, v, beta, alpha, kt, vt, bt, g_s, g_l, gamma=gamma, p=p, F=F,
+                     linear_form="bruteforce", want_softmax=False)
+    np.testing.assert_allclose(got["O_l"], ref["O_l"][rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["Ohat_l"], ref["Ohat_l"][rows], rtol=1e-10, atol=1e-12)
+    # Softmax leg: dense masked softmax in torch (fp64)
+    scale = 1 / math.sqrt(d) if p.softmax_scale is None else p.softmax_scale
+    frame_mask = torch.from_numpy(O.visibility(F, p).astype(bool))
+    mask = frame_mask.repeat_interleave(N, 0).repeat_interleave(N, 1)       # [L, L]
+    Kall, Vall = torch.from_numpy(k), torch.from_numpy(v)
+    if p.text_softmax:
+        Kall = torch.cat([Kall, torch.from_numpy(kt)])
+        Vall = torch.cat([Vall, torch.from_numpy(vt)])
+        mask = torch.cat([mask, torch.ones(L, T, dtype=torch.bool)], dim=1)
+    logits = (torch.from_numpy(q) @ Kall.T) * scale
+    logits = logits.masked_fill(~mask, float("-inf"))
+    O_s = torch.softmax(logits, dim=1) @ Vall
+    lse = torch.logsumexp(logits, dim=1)
+    np.testing.assert_allclose(got["O_s"], O_s.numpy()[rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["Ohat_s"], g_s[rows, None] * O_s.numpy()[rows], rtol=1e-10,
+                               atol=1e-12)
+    np.testing.assert_allclose(got["lse"], lse.numpy()[rows], rtol=1e-12)
+    # the states are the full-head ones
+    full = O.vdn_head(q, k, v, beta, alpha, kt, vt, bt, g_s, g_l, gamma=gamma, p=p, F=F,
+                      want_softmax=False)
+    for key in ("P_fwd", "P_rev", "S_text"):
+        np.testing.assert_allclose(got[key], full[key], rtol=1e-12, atol=1e-14)

@@ -98,6 +98,9 @@ def test_full_size_sampled(name):
     r_ohl = np.stack([ref[h]["Ohat_l"] for h in range(H)], axis=1)
     errs["Ohat_s"] = rel_l2(g_ohs, r_ohs)
     errs["Ohat_l"] = rel_l2(g_ohl, r_ohl)
+    # per head over the sampled rows: one wrong head cannot hide in the pool
+    errs["Ohat_s_head_max"] = max(rel_l2(g_ohs[:, h], r_ohs[:, h]) for h in range(H))
+    errs["Ohat_l_head_max"] = max(rel_l2(g_ohl[:, h], r_ohl[:, h]) for h in range(H))
     r_out = O.merge(r_ohs[None], r_ohl[None], inp["W_s"], inp["W_l"])[0]
     errs["out"] = rel_l2(g_out, r_out)
     # per-row check as well: no single sampled row may be far off
@@ -115,6 +118,6 @@ def test_full_size_sampled(name):
     for key, v in errs.items():
         if key.startswith(("P_", "S_text")):
             assert v <= 1e-4, (key, errs)
-    for key in ("Ohat_s", "Ohat_l", "out"):
+    for key in ("Ohat_s", "Ohat_l", "out", "Ohat_s_head_max", "Ohat_l_head_max"):
         assert errs[key] <= 1e-2, (key, errs)
     assert errs["out_row_max"] <= 3e-2, errs

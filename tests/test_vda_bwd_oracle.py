@@ -36,6 +36,42 @@ def _oracle_grads(x, dO, p):
                                 x["v_text"], x["beta_text"], x["g_l"], x["gamma"], dO, p)
 
 
+def _torch_head_ohat(t_, F, p):
+    """Ohat_l [L, d] of one head in torch, in the brute-force form (method,
+    bidirectional linear attention: each query frame's own forward and
+    reverse masked recurrence).  t_: torch tensors of one head's inputs."""
+    L, d = t_["q"].shape
+    N = L // F
+    eye = torch.eye(d, dtype=torch.float64)
+
+    def update(S, K, V, b, al):
+        A = K.T @ (b[:, None] * K)
+        W = K.T @ (b[:, None] * V)
+        return torch.linalg.solve(eye + A, al[:, None] * S + W)
+
+    S_text = update(torch.zeros(d, d, dtype=torch.float64), t_["k_text"], t_["v_text"],
+                    t_["beta_text"], torch.ones(d, dtype=torch.float64))
+    S0 = p.text_init_scale * S_text
+    outs = []
+    for t in range(F):
+        fwd, rev = O.linear_regions(t, F, p)
+        rows = slice(t * N, (t + 1) * N)
+        mems = []
+        for region, order in ((fwd, range(0, t + 1)), (rev, range(F - 1, t - 1, -1))):
+            S = S0
+            for f in order:
+                fr = slice(f * N, (f + 1) * N)
+                if f in region:
+                    S = update(S, t_["k"][fr], t_["v"][fr], t_["beta"][fr], t_["alpha"][f])
+                else:
+                    S = t_["alpha"][f][:, None] * S
+            mems.append(S)
+        Ot = t_["q"][rows] @ (mems[0] + mems[1])
+        r = torch.sqrt(torch.mean(Ot * Ot, dim=1, keepdim=True) + p.rms_eps)
+        outs.append(t_["g_l"][rows][:, None] * t_["gamma"] * Ot / r)
+    return torch.cat(outs)
+
+
 def _torch_grads(x, dO, p):
     """Autograd through the brute-force forward (method, bidirectional linear
     attention: each query frame's own forward and reverse masked recurrence)."""
@@ -143,3 +179,46 @@ def test_zero_write_gate_blocks_video_key_value_gradients():
     g = _oracle_grads(x, dO, p)
     assert not g["dk"].any() and not g["dv"].any()
     assert np.abs(g["dbeta"]).max() > 0 and np.abs(g["dk_text"]).max() > 0
+
+
+def test_stacked_wrapper_matches_autograd_over_all_heads():
+    """vda_bwd over [B, H] stacked inputs with a [B, L, H, d] output gradient
+    against torch autograd through a stacked forward: every head's Ohat_l in
+    the brute-force form, laid out [B, L, H, d] like the operator's output,
+    with one gamma shared by all heads (its gradient sums over heads).  The
+    gradient is asymmetric in b, h and l, so slicing dOhat on the wrong axis
+    or overwriting dgamma per head fails."""
+    B, H, F, N, d, T = 2, 3, 20, 2, 3, 2        # four chunks: both regions non-empty
+    p = O.Params()
+    rng = np.random.default_rng(21)
+    L = F * N
+    unit = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)
+    inp = dict(q=rng.standard_normal((B, H, L, d)), k=unit(rng.standard_normal((B, H, L, d))),
+               v=rng.standard_normal((B, H, L, d)), beta=rng.random((B, H, L)),
+               alpha=rng.uniform(0.6, 1.0, (B, H, F, d)),
+               k_text=unit(rng.standard_normal((B, H, T, d))), v_text=rng.standard_normal((B, H, T, d)),
+               beta_text=rng.random((B, H, T)), g_s=rng.random((B, H, L)), g_l=rng.random((B, H, L)),
+               gamma=rng.uniform(0.5, 1.5, d))
+    dOhat = rng.standard_normal((B, L, H, d))
+    got = VB.vda_bwd(inp, dOhat, p)
+    per_head = [k for k in KEYS if k != "gamma"]
+    leaves = {k: torch.tensor(inp[k], dtype=torch.float64, requires_grad=True) for k in per_head}
+    gamma = torch.tensor(inp["gamma"], dtype=torch.float64, requires_grad=True)
+    rows = []
+    for b in range(B):
+        heads = []
+        for h in range(H):
+            t_ = {k: leaves[k][b, h] for k in per_head}
+            t_["gamma"] = gamma
+            heads.append(_torch_head_ohat(t_, F, p))          # [L, d]
+        rows.append(torch.stack(heads, dim=1))                 # [L, H, d]
+    Ohat = torch.stack(rows)                                   # [B, L, H, d]
+    torch.sum(Ohat * torch.from_numpy(dOhat)).backward()
+    for k in per_head:
+        np.testing.assert_allclose(got["d" + k], leaves[k].grad.numpy(), rtol=1e-9, atol=1e-11,
+                                   err_msg=k)
+    np.testing.assert_allclose(got["dgamma"], gamma.grad.numpy(), rtol=1e-9, atol=1e-11)
+    # a subset of heads leaves the others at zero
+    sub = VB.vda_bwd(inp, dOhat, p, heads=[(1, 2)])
+    np.testing.assert_allclose(sub["dq"][1, 2], got["dq"][1, 2], rtol=1e-12)
+    assert not sub["dq"][0].any() and not sub["dq"][1, :2].any()

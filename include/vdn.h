@@ -193,6 +193,25 @@ vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v,
                                   void* stream);
 
 /*
+ * vdn_window_softmax_fwd_noalloc -- vdn_window_softmax_fwd for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument and no device
+ * allocation.  Its scratch (V^T and the text values of the bf16 MFMA path,
+ * vdn_softmax_workspace_bytes() of them) lives in a device array of the
+ * library of at most 64 MiB, one per GPU, held until the process ends.
+ *  Arguments, outputs and results as vdn_window_softmax_fwd (same kernels).
+ *  Sizes whose scratch exceeds 64 MiB: VDN_ERR_UNSUPPORTED, nothing launched.
+ *  Every call on one GPU shares that array: calls that overlap on one GPU
+ *  (on different streams or threads without ordering) race.  Each call
+ *  rewrites every scratch element it reads, so no clearing is needed.
+ */
+vdn_status vdn_window_softmax_fwd_noalloc(const void* q, const void* k, const void* v,
+                                          const void* k_text, const void* v_text,
+                                          const float* g_s, void* out, float* lse,
+                                          const vdn_dims* dims, const vdn_params* p,
+                                          vdn_dtype dt, void* stream);
+
+/*
  * vdn_merge_fwd -- the merge alone (step a8 of vdn_attn_fwd).
  *
  * Paper, method, branch calibration: each branch has its own output

@@ -39,7 +39,7 @@ EXPORTS = ("vdn_default_params", "vdn_attn_fwd", "vda_scan_fwd", "vda_scan_rev",
            "vdn_mx_quantize", "vdn_window_softmax_bwd", "vdn_softmax_bwd_workspace_bytes",
            "vda_bwd", "vda_bwd_workspace_bytes", "vdn_merge_bwd", "vdn_merge_bwd_workspace_bytes",
            "vdn_window_row_keys", "vdn_scan_workspace_bytes", "vdn_softmax_workspace_bytes",
-           "vdn_merge_workspace_bytes")
+           "vdn_merge_workspace_bytes", "vdn_window_softmax_fwd_noalloc")
 
 
 class VdnError(RuntimeError):
@@ -124,6 +124,8 @@ def lib() -> ctypes.CDLL:
         getattr(L, n).restype = I
     L.vdn_window_softmax_fwd.argtypes = [P] * 9 + [S, dp, pp, I, P]
     L.vdn_window_softmax_fwd.restype = I
+    L.vdn_window_softmax_fwd_noalloc.argtypes = [P] * 8 + [dp, pp, I, P]
+    L.vdn_window_softmax_fwd_noalloc.restype = I
     for n in ("vdn_workspace_bytes", "vdn_scan_workspace_bytes", "vdn_softmax_workspace_bytes",
               "vdn_merge_workspace_bytes"):
         getattr(L, n).argtypes = [dp, pp, I]
@@ -412,6 +414,34 @@ def window_softmax_fwd(q, k, v, F: int, g_s=None, want_lse: bool = False, out=No
         _ptr(lse, "lse", torch.float32, (B, H, L), dev, allow_none=True),
         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
         ctypes.byref(dims), ctypes.byref(p), code, _stream(stream, dev)))
+    return out, lse
+
+
+def window_softmax_fwd_noalloc(q, k, v, F: int, out, lse=None, g_s=None,
+                               params: Params | None = None, stream=None, k_text=None,
+                               v_text=None):
+    """vdn_window_softmax_fwd_noalloc: the Softmax branch with the library's
+    own device scratch.  The caller supplies out [B,L,H,d] (and optionally
+    lse [B,H,L]); nothing is allocated here or in the library."""
+    torch = _torch()
+    params = params or Params()
+    B, H, L, d = q.shape
+    if L % F:
+        raise ValueError(f"L={L} is not a multiple of F={F}")
+    dt = q.dtype
+    dev = q.device
+    T = k_text.shape[2] if k_text is not None else 0
+    dims = Dims(B, H, F, L // F, T, d, d, H * d)
+    p = params.c()
+    _check(lib().vdn_window_softmax_fwd_noalloc(
+        _ptr(q, "q", dt, (B, H, L, d), dev), _ptr(k, "k", dt, (B, H, L, d), dev),
+        _ptr(v, "v", dt, (B, H, L, d), dev),
+        _ptr(k_text, "k_text", dt, (B, H, T, d), dev, allow_none=True),
+        _ptr(v_text, "v_text", dt, (B, H, T, d), dev, allow_none=T == 0),
+        _ptr(g_s, "g_s", torch.float32, (B, H, L), dev, allow_none=True),
+        _ptr(out, "out", dt, (B, L, H, d), dev),
+        _ptr(lse, "lse", torch.float32, (B, H, L), dev, allow_none=True),
+        ctypes.byref(dims), ctypes.byref(p), _dtype_code(q), _stream(stream, dev)))
     return out, lse
 
 

@@ -12,6 +12,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -389,6 +391,32 @@ vdn_status merge_finish(const vdn::Geometry& g, const vdn_params* p, vdn_dtype d
   return VDN_OK;
 }
 
+// Scratch of the allocation-free Softmax entry point: a file-scope device
+// array (each GPU the library runs on holds its own copy until the process
+// ends).  In host code `scratch` names a host-side stand-in, so its device
+// address is looked up once per device (with that device current) and kept.
+constexpr size_t kNoAllocScratchBytes = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[16];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+  ScratchAddr& sa = g_scratch[dev];
+  std::call_once(sa.once, [&sa] { sa.err = hipGetSymbolAddress(&sa.ptr, HIP_SYMBOL(scratch)); });
+  if (sa.err != hipSuccess) return sa.err;
+  *out = sa.ptr;
+  return hipSuccess;
+}
+
 vdn_status check_workspace(void* ws, size_t bytes, size_t need) {
   if (bytes < need)
     return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", bytes, need);
@@ -631,6 +659,31 @@ vdn_status vdn_window_softmax_fwd(const void* q, const void* k, const void* v,
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VDN_OK) return st;
   return run_softmax(g, p, dt, q, k, v, k_text, v_text, g_s, out, lse, (char*)workspace, lay,
+                     (hipStream_t)stream);
+}
+
+vdn_status vdn_window_softmax_fwd_noalloc(const void* q, const void* k, const void* v,
+                                          const void* k_text, const void* v_text, const float* g_s,
+                                          void* out, float* lse, const vdn_dims* dims,
+                                          const vdn_params* p, vdn_dtype dt, void* stream) {
+  g_err[0] = 0;
+  vdn::Geometry g;
+  vdn_status st = check_geometry(dims, p, dt, &g);
+  if (st != VDN_OK) return st;
+  NEED(q); NEED(k); NEED(v); NEED(out);
+  if (g.Ts > 0) { NEED(k_text); NEED(v_text); }
+  // the same regions vdn_window_softmax_fwd takes from its workspace (V^T
+  // and the text values, every element rewritten by each call), here in the
+  // device array
+  const Layout lay = make_layout(g, g.H * g.D, dt, false, Entry::Softmax);
+  if (lay.total > kNoAllocScratchBytes)
+    return fail(VDN_ERR_UNSUPPORTED,
+                "vdn_window_softmax_fwd_noalloc: these sizes need %zu bytes of scratch, more than "
+                "its %zu-byte device array; use vdn_window_softmax_fwd with a workspace",
+                lay.total, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (lay.total > 0) VDN_HIP(scratch_address(&ws));
+  return run_softmax(g, p, dt, q, k, v, k_text, v_text, g_s, out, lse, (char*)ws, lay,
                      (hipStream_t)stream);
 }
 

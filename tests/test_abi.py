@@ -473,3 +473,29 @@ def test_merge_bwd_validation():
     assert need >= (20 * 32) * (256 + 128) * 2
     d_rag = _dims(D=256)              # B*L = 320: no weight gradients for it
     assert fn(*args, fake, big, ctypes.byref(d_rag), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED
+
+
+def test_noalloc_softmax_validation():
+    """Host-side checks of vdn_window_softmax_fwd_noalloc: required pointers,
+    text pointers with text keys, and sizes beyond its scratch array, all
+    rejected before any HIP call."""
+    L = vdn.lib()
+    fake = ctypes.c_void_p(0x100000)
+    d = _dims()
+    p = vdn.Params().c()
+    fn = L.vdn_window_softmax_fwd_noalloc
+    # q k v k_text v_text g_s out lse
+    for i in (0, 1, 2, 6):
+        a = [fake] * 8
+        a[i] = None
+        assert fn(*a, ctypes.byref(d), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG, i
+    pt = vdn.Params(text_softmax=1).c()
+    for i in (3, 4):
+        a = [fake] * 8
+        a[i] = None
+        assert fn(*a, ctypes.byref(d), ctypes.byref(pt), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG, i
+    assert fn(*[fake] * 8, None, ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_INVALID_ARG
+    assert fn(*[fake] * 8, ctypes.byref(d), ctypes.byref(p), 7, None) == vdn.VDN_ERR_UNSUPPORTED
+    big = vdn.Dims(1, 24, 120, 1536, 0, 128, 128, 24 * 128)     # V^T of 1.1 GB
+    assert fn(*[fake] * 8, ctypes.byref(big), ctypes.byref(p), vdn.VDN_BF16, None) == vdn.VDN_ERR_UNSUPPORTED
+    assert b"scratch" in L.vdn_last_error()

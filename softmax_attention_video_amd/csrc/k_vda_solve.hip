@@ -10,22 +10,26 @@
 // in fp32.  The text state is the same solve on the text tokens from a zero
 // state (the leading virtual frame): S_text = (I + A_text)^{-1} W_text.
 //
-// Our design: one workgroup (256 threads, a 16 x 16 thread grid) per
-// (b, h, frame), frame index F being the text frame.  Thread (tr, tc) owns
-// rows tr*R..tr*R+R-1 of the augmented matrix [I + A | W] in columns
-// tc*R..tc*R+R-1 of each half (R = D / 16), i.e. 2 R^2 fp32 registers.
-// I + A is symmetric positive definite (eigenvalues >= 1), so the
-// elimination needs no pivoting; each pivot step broadcasts the pivot row
-// and column through double-buffered LDS with one barrier.
+// Our design: one workgroup (256 threads) per (b, h, frame), frame index F
+// being the text frame.  I + A is symmetric positive definite (eigenvalues
+// >= 1), so the elimination needs no pivoting.
 //
-// Statistics: the bf16 kernel (D = 64, 128) contracts over tokens on
-// v_mfma_f32_32x32x16_bf16.  Tokens must be the contracted (lane-contiguous)
-// index, so each 64-token tile is transposed into LDS ([channel][token]).
-// beta * K is formed in fp32 and split into bf16 hi + lo parts, so A and W
-// carry ~16 more mantissa bits than a single bf16 product.  The generic
-// kernel (fp32 storage, any D) accumulates in fp32 on the VALU.
+// bf16 kernel (D = 64, 128): statistics on v_mfma_f32_32x32x16_bf16 and a
+// blocked Gauss-Jordan (16-column panels factored in registers, rank-16
+// trailing updates on v_mfma_f32_32x32x2f32), both in one block ownership of
+// [I + A | W] (see the kernel).  Tokens must be the contracted
+// (lane-contiguous) index of the statistics, so each 64-token tile is
+// transposed into LDS ([channel][token]).  beta * K is formed in fp32 and
+// split into bf16 hi + lo parts, so A and W carry ~16 more mantissa bits than
+// a single bf16 product.
+//
+// Generic kernel (fp32 storage, any D): fp32 VALU statistics and an
+// unblocked elimination on a 16 x 16 thread grid (thread (tr, tc) owns an
+// 8 x 8 block of both halves; one barrier per pivot).
 #include "vdn_common.h"
 #include "vdn_internal.h"
+
+#include <utility>
 
 namespace vdn {
 
@@ -161,6 +165,12 @@ __device__ __forceinline__ void emit_solution(const Geometry& g, const float* al
     }
 }
 
+// alpha of video frame fr (unused for the text frame, fr == F).
+template <typename T>
+__device__ __forceinline__ const float* alpha_row(const SolveArgs<T>& a, int bh, int fr) {
+  return a.alpha + ((size_t)bh * a.g.F + (fr < a.g.F ? fr : 0)) * a.g.D;
+}
+
 template <typename T>
 __device__ __forceinline__ void frame_tokens(const SolveArgs<T>& a, int bh, int fr, bool text,
                                              const T*& kp, const T*& vp, const float*& bp,
@@ -251,34 +261,60 @@ __global__ __launch_bounds__(256) void vda_frame_solve_kernel(SolveArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: MFMA statistics (D = 64, 128).
+// bf16 kernel (D = 64, 128): MFMA statistics and a blocked Gauss-Jordan solve.
+//
+// Ownership: [I + A | W] is NB x 2NB blocks of 32 x 32 (NB = D / 32).  Wave w
+// owns BPW = NB * 2NB / 4 blocks of one block row rb (D = 128: the whole row
+// block w; D = 64: half of row block w / 2), as v_mfma 32 x 32 accumulators
+// (lane l: column l % 32, rows mfma32_row(i, l / 32)).  The statistics write
+// straight into that ownership, and so does the solve.
+//
+// Solve: panels of PW = 16 columns, left to right.  For panel k (columns
+// c0 .. c0 + 15) the in-place elimination of its 16 pivots is a left
+// multiplication by a matrix E_k that differs from I only in those columns,
+// G_k = E_k[:, panel].  Every wave factors the D x 16 panel redundantly in
+// registers (lane = row, pivot rows broadcast with v_readlane; no barrier),
+// giving G_k.  Then each wave applies the rank-16 update
+//   X[:, j] += (G_k - I_k) X[pivot rows, j]
+// to all of its blocks on v_mfma_f32_32x32x2f32; the panel's own columns are
+// preset to the identity pattern with B = I there, so they become G_k (the
+// in-place inverse).  After the last panel the left half holds
+// X = (I + A)^{-1} and the right half X W.  One barrier per panel (panel
+// columns and pivot rows are exchanged through double-buffered LDS).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf16_t> a) {
-  constexpr int R = D / 16;
   constexpr int TT = 64;            // tokens per tile
   constexpr int TP = TT + 8;        // transposed tile pitch (bf16)
   constexpr int NB = D / 32;        // 32-blocks per matrix side
-  constexpr int BPW = 2 * NB * NB / 4;   // output blocks per wave (A and W)
-  constexpr int XP = D + 1;         // fp32 transfer pitch
+  constexpr int NCB = 2 * NB;       // block columns of [I + A | W]
+  constexpr int BPW = NB * NCB / 4; // blocks per wave
   constexpr int PAIRS = TT / 2 * (D / 8) / 256;   // (token pair, 8-channel chunk) per thread
+  constexpr int PW = 16;            // panel width
+  constexpr int NP = D / PW;        // panels
+  constexpr int RS = D / 64;        // rows per lane in the panel factorization
+  constexpr int PP = PW + 4;        // LDS pitch of panel rows (floats): conflict-free 16-byte reads
+  static_assert(NCB % BPW == 0, "a wave's blocks lie in one block row");
   struct StatsTiles {
     bf16_t kt[D * TP];    // K^T
     bf16_t kh[D * TP];    // (beta K)^T, bf16 high part
     bf16_t kl[D * TP];    // (beta K)^T, bf16 low part
     bf16_t vt[D * TP];    // V^T
   };
+  struct SolveTiles {
+    float pnl[2][D * PP];        // panel columns, row-major [row][PP]
+    float prt[2][NCB * 32 * PP]; // pivot rows, transposed [column][PP], k-slots permuted
+  };
   union Smem {
     StatsTiles st;
-    float xfer[D * XP];
+    SolveTiles sv;
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
-  __shared__ GJShared sh;
 
   const Geometry& g = a.g;
   const int fr = blockIdx.x % (g.F + 1);
   const int bh = blockIdx.x / (g.F + 1);
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
   const bool text = (fr == g.F);
   if (!text && g.anchors && (fr == 0 || fr == g.F - 1)) {
@@ -290,6 +326,8 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
   long long ntok;
   frame_tokens(a, bh, fr, text, kp, vp, bp, ntok);
 
+  const int rb = wave * BPW / NCB;            // this wave's block row
+  const int cb0 = (wave * BPW) % NCB;         // its first block column
   f32x16 acc[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) acc[i] = f32x16{};
@@ -343,6 +381,9 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
     }
   };
 
+  // ---- statistics: block (rb, cb) of A = (beta K)^T K (cb < NB) or of
+  // W = (beta K)^T V (cb >= NB); the A operand (channels of block row rb)
+  // is shared by all of the wave's blocks
   if (ntok > 0) fetch(0);
   for (long long t0 = 0; t0 < ntok; t0 += TT) {
     __syncthreads();
@@ -351,51 +392,156 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
     if (t0 + TT < ntok) fetch(t0 + TT);
 #pragma unroll
     for (int ks = 0; ks < TT / 16; ++ks) {
+      const int col = ks * 16 + hg * 8;
+      const bf16x8 ah = as_bf16x8(ld16(&sm.st.kh[(rb * 32 + l32) * TP + col]));
+      const bf16x8 al = as_bf16x8(ld16(&sm.st.kl[(rb * 32 + l32) * TP + col]));
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        const int bi = wave * BPW + i;
-        const bool wblk = bi >= NB * NB;                 // block of W (else of A)
-        const int mb = (bi % (NB * NB)) / NB, nb = bi % NB;
-        const int col = ks * 16 + hg * 8;
-        const bf16x8 ah = as_bf16x8(ld16(&sm.st.kh[(mb * 32 + l32) * TP + col]));
-        const bf16x8 al = as_bf16x8(ld16(&sm.st.kl[(mb * 32 + l32) * TP + col]));
-        const bf16_t* bsrc = wblk ? sm.st.vt : sm.st.kt;
-        const bf16x8 bo = as_bf16x8(ld16(&bsrc[(nb * 32 + l32) * TP + col]));
-        acc[i] = mfma32x32x16(ah, bo, acc[i]);
-        acc[i] = mfma32x32x16(al, bo, acc[i]);
+      for (int j = 0; j < BPW; ++j) {
+        const int cb = cb0 + j;
+        const bf16_t* bsrc = cb < NB ? sm.st.kt : sm.st.vt;
+        const bf16x8 bo = as_bf16x8(ld16(&bsrc[((cb % NB) * 32 + l32) * TP + col]));
+        acc[j] = mfma32x32x16(ah, bo, acc[j]);
+        acc[j] = mfma32x32x16(al, bo, acc[j]);
       }
     }
   }
+  // I + A
+#pragma unroll
+  for (int j = 0; j < BPW; ++j)
+    if (cb0 + j == rb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (mfma32_row(i, hg) == l32) acc[j][i] += 1.f;
+    }
 
-  // accumulators -> GJ ownership, A first then W, through one fp32 buffer
-  float m[R][R], w[R][R];
+  // ---- blocked Gauss-Jordan.  The panel loop runs at run time in groups
+  // whose pivot rows share one register slot OS of the factor layout (rows
+  // lane + 64 OS), so every register index is a compile-time constant.
+  __syncthreads();   // the statistics tiles are dead before the union is reused
+  auto panel = [&](int k, auto osc) __attribute__((always_inline)) {
+    constexpr int OS = decltype(osc)::value;
+    const int c0 = k * PW;
+    const int cbk = c0 / 32, po = c0 % 32;   // the panel's block column (= pivot block row), offset
+    float* pnl = sm.sv.pnl[k & 1];
+    float* prt = sm.sv.prt[k & 1];
+    const bool in_panel = l32 >= po && l32 < po + PW;
+    // (1) publish the panel columns of this wave's blocks and, from block
+    // row cbk, the pivot rows (transposed; k-index kk in slot
+    // (kk % 2) * 8 + kk / 2; the identity in the panel's own columns).  Then
+    // preset the panel columns to the identity pattern: the update below
+    // turns them into G_k.
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    __syncthreads();
+    for (int j = 0; j < BPW; ++j) {
+      const int cb = cb0 + j;
+      if (cb == cbk && in_panel) {
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int bi = wave * BPW + i;
-      if ((bi >= NB * NB) != (pass == 1)) continue;
-      const int mb = (bi % (NB * NB)) / NB, nb = bi % NB;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sm.xfer[(mb * 32 + mfma32_row(r, hg)) * XP + nb * 32 + l32] = acc[i][r];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        const float x = sm.xfer[(tr * R + i) * XP + tc * R + j];
-        if (pass == 0) m[i][j] = x; else w[i][j] = x;
+        for (int i = 0; i < 16; ++i) pnl[(rb * 32 + mfma32_row(i, hg)) * PP + (l32 - po)] = acc[j][i];
       }
-  }
-  if (tr == tc) {
+      if (rb == cbk) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) m[i][i] += 1.f;
+        for (int i = 0; i < 16; ++i) {
+          const int kk = mfma32_row(i, hg) - po;
+          if (kk >= 0 && kk < PW) {
+            const float v = (cb == cbk && in_panel) ? (l32 - po == kk ? 1.f : 0.f) : acc[j][i];
+            prt[(cb * 32 + l32) * PP + (kk & 1) * 8 + (kk >> 1)] = v;
+          }
+        }
+      }
+      if (cb == cbk && in_panel) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[j][i] = (rb * 32 + mfma32_row(i, hg) == cbk * 32 + l32) ? 1.f : 0.f;
+      }
+    }
+    lds_barrier();
+    // (2) factor the D x 16 panel redundantly in every wave: lane holds rows
+    // lane + 64 s; pivot rows broadcast with v_readlane
+    float x[RS][PW];
+#pragma unroll
+    for (int s2 = 0; s2 < RS; ++s2)
+#pragma unroll
+      for (int c4 = 0; c4 < PW / 4; ++c4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&pnl[(lane + 64 * s2) * PP + c4 * 4]);
+        x[s2][c4 * 4 + 0] = v[0];
+        x[s2][c4 * 4 + 1] = v[1];
+        x[s2][c4 * 4 + 2] = v[2];
+        x[s2][c4 * 4 + 3] = v[3];
+      }
+#pragma unroll
+    for (int pv = 0; pv < PW; ++pv) {
+      const int ol = (c0 + pv) & 63;           // lane of the pivot row (its slot is OS)
+      float rowv[PW];                          // the pivot row's panel columns (uniform)
+#pragma unroll
+      for (int c = 0; c < PW; ++c) rowv[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[OS][c]), ol));
+      const float rp = 1.f / rowv[pv];
+#pragma unroll
+      for (int s2 = 0; s2 < RS; ++s2) {
+        const float f0 = x[s2][pv] * rp;       // multiplier of this row
+        // the pivot row itself: x - (1 - rp) x = rp x
+        const bool own = s2 == OS && lane == ol;
+        const float f = own ? 1.f - rp : f0;
+#pragma unroll
+        for (int c = 0; c < PW; ++c) x[s2][c] = fmaf(-f, rowv[c], x[s2][c]);
+        x[s2][pv] = own ? rp : -f0;
+      }
+    }
+    // (3) rank-16 update of this wave's blocks.  A operand: (G - I) at row
+    // rb * 32 + (l % 32), k-slot 2 s + l / 32; rows of block row rb sit in
+    // lane half rb % 2, slot rb / 2 of the factor layout
+    float aop[PW / 2];
+#pragma unroll
+    for (int s2 = 0; s2 < PW / 2; ++s2) {
+      const float e = RS == 1 || rb < 2 ? x[0][2 * s2] : x[RS - 1][2 * s2];
+      const float o = RS == 1 || rb < 2 ? x[0][2 * s2 + 1] : x[RS - 1][2 * s2 + 1];
+      float v;
+      if ((rb & 1) == 0) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o), __float_as_uint(o), false, false);
+        v = hg == 0 ? e : __uint_as_float(r[0]);
+      } else {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(e), __float_as_uint(e), false, false);
+        v = hg == 1 ? o : __uint_as_float(r[1]);
+      }
+      aop[s2] = (rb * 32 + l32 == c0 + 2 * s2 + hg) ? v - 1.f : v;
+    }
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const float* bsrc = &prt[((cb0 + j) * 32 + l32) * PP + hg * 8];
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bsrc);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(bsrc + 4);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acc[j] = mfma32x32x2f32(aop[s2], b0[s2], acc[j]);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acc[j] = mfma32x32x2f32(aop[4 + s2], b1[s2], acc[j]);
+    }
+  };
+  for (int k = 0; k < NP / RS; ++k) panel(k, std::integral_constant<int, 0>{});
+  if constexpr (RS == 2)
+    for (int k = NP / 2; k < NP; ++k) panel(k, std::integral_constant<int, 1>{});
+
+  // ---- emit: T = X diag(alpha), U = X W (video frame) or S_text = X W (text
+  // frame); X itself when Xf is set (the backward pass solves with it)
+  const size_t DD = (size_t)D * D;
+  const float* al = alpha_row(a, bh, fr);
+  float* Xo = a.Xf ? a.Xf + ((size_t)bh * (g.F + 1) + fr) * DD : nullptr;
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int cb = cb0 + j;
+    const int col = (cb % NB) * 32 + l32;
+    if (cb < NB) {
+      const float aj = text ? 1.f : al[col];
+      float* Tout = text ? nullptr : a.Tf + ((size_t)bh * g.F + fr) * DD;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const size_t e = (size_t)(rb * 32 + mfma32_row(i, hg)) * D + col;
+        if (Xo) Xo[e] = acc[j][i];
+        if (!text) Tout[e] = acc[j][i] * aj;
+      }
+    } else {
+      float* Uout = text ? a.S_text + (size_t)bh * DD : a.Uf + ((size_t)bh * g.F + fr) * DD;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Uout[(size_t)(rb * 32 + mfma32_row(i, hg)) * D + col] = acc[j][i];
+    }
   }
-  gauss_jordan<D>(m, w, sh, tr, tc);
-  emit_solution<D>(g, a.alpha, a.Tf, a.Uf, a.S_text, a.Xf, bh, fr, text, m, w, tr, tc);
 }
 
 template <typename T>

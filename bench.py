@@ -30,13 +30,20 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (AMD spec: 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
-def flop_counts(cfg, pairs: int) -> dict:
-    """Algorithmic flops of one forward (masked pairs not counted)."""
-    B, H, d, F, N, L, C = cfg.B, cfg.H, cfg.d, cfg.F, cfg.N, cfg.L, cfg.F // 5
+def flop_counts(cfg, pairs: int, chunk_frames: int = 5) -> dict:
+    """Algorithmic flops of one forward as the library runs it (masked pairs
+    not counted).  The scans: d = 64, 128 scan the frame maps directly
+    (S <- T_f S + U_f, 2 d^3 per frame and direction); d = 16, 32 compose
+    each chunk's maps (8 products of 2 d^3 per chunk and direction) and scan
+    the chunks (2 d^3 per chunk and direction)."""
+    B, H, d, F, N, L, T = cfg.B, cfg.H, cfg.d, cfg.F, cfg.N, cfg.L, cfg.T
+    C = F // chunk_frames
     softmax = 4.0 * d * pairs * N * N * H * B
+    scan = 2 * F * 2.0 * d ** 3 if d in (64, 128) else 2 * C * (16.0 + 2.0) * d ** 3
     vda = (6.0 * N * d * d * F          # A_f, W_f and the q.M readout
+           + 4.0 * T * d * d            # A_text, W_text
            + 4.0 * d ** 3 * (F + 1)     # frame solves (+ text frame)
-           + 2 * C * (16.0 + 2.0) * d ** 3) * H * B   # compose + scan, both directions
+           + scan) * H * B              # both directions
     merge = 4.0 * B * L * (H * d) * cfg.D if cfg.proj else 0.0
     return {"softmax": softmax, "vda": vda, "merge": merge, "total": softmax + vda + merge}
 

@@ -37,6 +37,7 @@ def hipcc() -> str:
 # results in arch VGPRs (two waves per SIMD fit in 256 registers; the
 # softmax arithmetic reads S without accumulator-register moves).
 EXTRA = {"k_window_softmax.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "k_vda_solve.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "k_window_softmax_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "k_merge.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

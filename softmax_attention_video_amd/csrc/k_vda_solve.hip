@@ -414,37 +414,42 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
         if (mfma32_row(i, hg) == l32) acc[j][i] += 1.f;
     }
 
-  // ---- blocked Gauss-Jordan.  The panel loop runs at run time in groups
-  // whose pivot rows share one register slot OS of the factor layout (rows
-  // lane + 64 OS), so every register index is a compile-time constant.
+  // ---- blocked Gauss-Jordan.  Panels are visited as (block column cbk,
+  // half PO) with cbk at run time and PO = 0, 16 compile-time; cbk runs in
+  // groups whose pivot rows share one register slot OS of the factor layout
+  // (rows lane + 64 OS).  Every register index and every row condition of
+  // the 32 x 32 accumulator layout is then a compile-time constant.
   __syncthreads();   // the statistics tiles are dead before the union is reused
-  auto panel = [&](int k, auto osc) __attribute__((always_inline)) {
+  int kpar = 0;      // panel parity: LDS buffer
+  auto panel = [&](int cbk, auto osc, auto poc) __attribute__((always_inline)) {
     constexpr int OS = decltype(osc)::value;
-    const int c0 = k * PW;
-    const int cbk = c0 / 32, po = c0 % 32;   // the panel's block column (= pivot block row), offset
-    float* pnl = sm.sv.pnl[k & 1];
-    float* prt = sm.sv.prt[k & 1];
-    const bool in_panel = l32 >= po && l32 < po + PW;
+    constexpr int PO = decltype(poc)::value;
+    const int c0 = cbk * 32 + PO;
+    float* pnl = sm.sv.pnl[kpar];
+    float* prt = sm.sv.prt[kpar];
+    kpar ^= 1;
+    const bool in_panel = l32 >= PO && l32 < PO + PW;
     // (1) publish the panel columns of this wave's blocks and, from block
     // row cbk, the pivot rows (transposed; k-index kk in slot
     // (kk % 2) * 8 + kk / 2; the identity in the panel's own columns).  Then
     // preset the panel columns to the identity pattern: the update below
-    // turns them into G_k.
+    // turns them into G_k.  Accumulator register i holds row
+    // 8 (i / 4) + 4 hg + i % 4, so the pivot rows PO .. PO + 15 are
+    // registers PO / 2 .. PO / 2 + 7 with kk = 8 (i / 4 - PO / 8) + 4 hg + i % 4.
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
       const int cb = cb0 + j;
       if (cb == cbk && in_panel) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pnl[(rb * 32 + mfma32_row(i, hg)) * PP + (l32 - po)] = acc[j][i];
+        for (int i = 0; i < 16; ++i) pnl[(rb * 32 + mfma32_row(i, hg)) * PP + (l32 - PO)] = acc[j][i];
       }
       if (rb == cbk) {
+        float* dst = &prt[(cb * 32 + l32) * PP];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = mfma32_row(i, hg) - po;
-          if (kk >= 0 && kk < PW) {
-            const float v = (cb == cbk && in_panel) ? (l32 - po == kk ? 1.f : 0.f) : acc[j][i];
-            prt[(cb * 32 + l32) * PP + (kk & 1) * 8 + (kk >> 1)] = v;
-          }
+        for (int i = PO / 2; i < PO / 2 + 8; ++i) {
+          const int kk = 8 * (i / 4 - PO / 8) + 4 * hg + (i & 3);
+          const float v = (cb == cbk && in_panel) ? (l32 - PO == kk ? 1.f : 0.f) : acc[j][i];
+          dst[(kk & 1) * 8 + (kk >> 1)] = v;
         }
       }
       if (cb == cbk && in_panel) {
@@ -514,9 +519,15 @@ __global__ __launch_bounds__(256) void vda_frame_solve_mfma_kernel(SolveArgs<bf1
       for (int s2 = 0; s2 < 4; ++s2) acc[j] = mfma32x32x2f32(aop[4 + s2], b1[s2], acc[j]);
     }
   };
-  for (int k = 0; k < NP / RS; ++k) panel(k, std::integral_constant<int, 0>{});
+  for (int cbk = 0; cbk < NB / RS; ++cbk) {
+    panel(cbk, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    panel(cbk, std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{});
+  }
   if constexpr (RS == 2)
-    for (int k = NP / 2; k < NP; ++k) panel(k, std::integral_constant<int, 1>{});
+    for (int cbk = NB / 2; cbk < NB; ++cbk) {
+      panel(cbk, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+      panel(cbk, std::integral_constant<int, 1>{}, std::integral_constant<int, 16>{});
+    }
 
   // ---- emit: T = X diag(alpha), U = X W (video frame) or S_text = X W (text
   // frame); X itself when Xf is set (the backward pass solves with it)

@@ -48,10 +48,20 @@ typedef enum {
   VDN_ERR_INVALID_ARG = -1,   /* null pointer, bad size or inconsistent shape */
   VDN_ERR_UNSUPPORTED = -2,   /* valid but not implemented (head dim, dtype)  */
   VDN_ERR_WORKSPACE = -3,     /* workspace smaller than vdn_workspace_bytes() */
-  VDN_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed   */
+  VDN_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed   */
+  /* range anchors, not codes: they give the type the range of int */
+  VDN_STATUS_INT_MIN_ = -2147483647 - 1, VDN_STATUS_INT_MAX_ = 2147483647
 } vdn_status;
 
-typedef enum { VDN_F32 = 0, VDN_BF16 = 1 } vdn_dtype;
+/* The range anchors are not dtypes: they make every int a valid value of the
+ * type, so an unknown code passed across the C-ABI is an ordinary value that
+ * the library rejects (VDN_ERR_UNSUPPORTED), not undefined behaviour. */
+typedef enum {
+  VDN_F32 = 0,
+  VDN_BF16 = 1,
+  VDN_DTYPE_INT_MIN_ = -2147483647 - 1,
+  VDN_DTYPE_INT_MAX_ = 2147483647
+} vdn_dtype;
 
 /* Problem sizes.  L = F*N video tokens per (b, h); D is the model width of
  * the projected output (D must equal H*d_v when no projections are given). */

@@ -27,7 +27,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvdn.so")
+# VDN_LIB overrides the library path (the host-sanitizer test loads its
+# instrumented build this way); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("VDN_LIB") or os.path.join(_HERE, "libvdn.so")
 
 VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE, VDN_ERR_HIP = 0, -1, -2, -3, -4
 VDN_F32, VDN_BF16 = 0, 1

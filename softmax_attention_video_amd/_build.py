@@ -68,6 +68,61 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizer build (a test build, never loaded by the product path):
+# vdn_host.hip -- argument checks, workspace carving, the host work-item and
+# plan loops -- with AddressSanitizer and UndefinedBehaviorSanitizer on the
+# host pass only; the kernel sources as in build().
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def build_sanitized(out_dir: str) -> str:
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = []
+    todo = []
+    for src in srcs:
+        name = os.path.basename(src)
+        if name == "vdn_host.hip":
+            todo.append((src, os.path.join(out_dir, name + ".san.o"), SAN_HOST))
+        else:
+            o = os.path.join(OBJ, name + ".o")
+            if os.path.exists(o) and os.path.getmtime(o) >= os.path.getmtime(src):
+                objs.append(o)
+            else:
+                todo.append((src, os.path.join(out_dir, name + ".o"), []))
+
+    def comp(job):
+        src, obj, extra = job
+        cmd = [hipcc(), *FLAGS, *EXTRA.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    jobs = min(len(todo), max(1, min(16, len(os.sched_getaffinity(0))))) or 1
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs += list(ex.map(comp, todo))
+    lib = os.path.join(out_dir, "libvdn_san.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fsanitize=address,undefined",
+           "-shared-libasan", *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
+def asan_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the HIP compiler."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        for c in glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"):
+            return c
+        raise RuntimeError("shared ASan runtime not found")
+    return path
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -464,6 +464,7 @@ const char* vdn_status_string(vdn_status s) {
     case VDN_ERR_UNSUPPORTED: return "VDN_ERR_UNSUPPORTED";
     case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE";
     case VDN_ERR_HIP: return "VDN_ERR_HIP";
+    default: break;
   }
   return "unknown vdn_status";
 }

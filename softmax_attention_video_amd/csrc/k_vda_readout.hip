@@ -123,14 +123,25 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
   int i_f, ws, i_r, we;
   readout_indices(g, t, i_f, ws, i_r, we);
   const float* al = alpha + (size_t)bh * g.F * D;
-  for (int k = tid; k < D; k += 256) {
-    float df = 1.f, dr = 1.f;
-    for (int f = ws; f <= t; ++f) df *= al[(size_t)f * D + k];
-    for (int f = t; f <= we; ++f) dr *= al[(size_t)f * D + k];
-    dfs[k] = df;
-    drs[k] = dr;
-    gms[k] = gamma ? gamma[k] : 1.f;
+  // decay bridges: thread (part, k) forms one channel's product over its
+  // span, loading 4 frames at a time so the loads are in flight together
+  if (tid < 2 * D) {
+    const int k = tid % D, part = tid / D;
+    const int f0 = part == 0 ? ws : t, f1 = part == 0 ? t : we;   // inclusive
+    float d = 1.f;
+    int f = f0;
+    for (; f + 3 <= f1; f += 4) {
+      const float a0 = al[(size_t)f * D + k], a1 = al[(size_t)(f + 1) * D + k];
+      const float a2 = al[(size_t)(f + 2) * D + k], a3 = al[(size_t)(f + 3) * D + k];
+      d *= a0;
+      d *= a1;
+      d *= a2;
+      d *= a3;
+    }
+    for (; f <= f1; ++f) d *= al[(size_t)f * D + k];
+    (part == 0 ? dfs : drs)[k] = d;
   }
+  for (int k = tid; k < D; k += 256) gms[k] = gamma ? gamma[k] : 1.f;
   __syncthreads();
   const size_t DD = (size_t)D * D;
   const float* pf = P_fwd + ((size_t)bh * (g.C + 1) + i_f) * DD;

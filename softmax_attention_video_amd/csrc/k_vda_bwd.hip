@@ -282,11 +282,18 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     bf16_t doh[TPS * DP];     // dO, hi / lo
     bf16_t dol[TPS * DP];
   };
+  // G goes through LDS in NPASS slices of RPP rows, so that the tiles, the
+  // slice and the dgamma partials share one region and two workgroups fit
+  // on a compute unit
+  constexpr int NPASS = D > 64 ? 2 : 1, RPP = D / NPASS;
+  struct Tail {
+    float pd[RPP * (D + 1)];  // a slice of G at the end of the frame
+    float gsum[SUBT][D][33];  // dgamma partials
+  };
   __shared__ __attribute__((aligned(16))) union {
     Tiles t;
-    float pd[D * (D + 1)];    // G at the end of the frame
+    Tail e;
   } u;
-  __shared__ float gsum[SUBT][D][33];
   __shared__ __attribute__((aligned(16))) bf16_t qrow[2][TPS * DP];   // the step's Q rows
   __shared__ float red1[4][32], red2[4][32][2];
   __shared__ float dfs[D], drs[D];
@@ -302,16 +309,26 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
   int i_f, ws, i_r, we;
   readout_indices(g, t, i_f, ws, i_r, we);
   const float* al = a.alpha + (size_t)bh * g.F * D;
-  for (int c = tid; c < D; c += 256) {
-    float df = 1.f, dr = 1.f;
-    for (int f = ws; f <= t; ++f) df *= al[(size_t)f * D + c];
-    for (int f = t; f <= we; ++f) dr *= al[(size_t)f * D + c];
-    dfs[c] = df;
-    drs[c] = dr;
-    gms[c] = a.gamma ? a.gamma[c] : 1.f;
-    a.Dbr[(((size_t)bh * 2 + 0) * g.F + t) * D + c] = df;
-    a.Dbr[(((size_t)bh * 2 + 1) * g.F + t) * D + c] = dr;
+  // bridges: thread (part, c) multiplies the decays of one direction's span
+  // in frame order, with four frames' loads in flight together
+  if (tid < 2 * D) {
+    const int c = tid % D, part = tid / D;
+    const int f0 = part == 0 ? ws : t, f1 = part == 0 ? t : we;   // inclusive
+    float d = 1.f;
+    int f = f0;
+    for (; f + 3 <= f1; f += 4) {
+      const float a0 = al[(size_t)f * D + c], a1 = al[(size_t)(f + 1) * D + c];
+      const float a2 = al[(size_t)(f + 2) * D + c], a3 = al[(size_t)(f + 3) * D + c];
+      d *= a0;
+      d *= a1;
+      d *= a2;
+      d *= a3;
+    }
+    for (; f <= f1; ++f) d *= al[(size_t)f * D + c];
+    (part == 0 ? dfs : drs)[c] = d;
+    a.Dbr[(((size_t)bh * 2 + part) * g.F + t) * D + c] = d;
   }
+  for (int c = tid; c < D; c += 256) gms[c] = a.gamma ? a.gamma[c] : 1.f;
   __syncthreads();
   const float* pf = a.Pf + ((size_t)bh * (g.C + 1) + i_f) * DD;
   const float* pr = a.Pr + ((size_t)bh * (g.C + 1) + i_r) * DD;
@@ -511,42 +528,50 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     if (more) stage_q(st ^ 1);      // that buffer was last read before the previous barrier
     __syncthreads();
   }
-  // G -> memory and LDS; bridge adjoints dD = rowsum(G * P)
+  // G -> memory and, a slice of rows at a time, LDS; bridge adjoints
+  // dD = rowsum(G * P).  The tiles were last read before the loop's final
+  // barrier, so the tail region is free.
   float* Go = a.G + ((size_t)bh * g.F + t) * DD;
 #pragma unroll
-  for (int b = 0; b < NGB; ++b) {
-    const int blk = wave + 4 * b;
-    const int kb = blk / NB, vbg = blk % NB;
+  for (int i = 0; i < 16; ++i) u.e.gsum[ts][vb * 32 + mfma32_row(i, hg)][l32] = gacc[i];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = kb * 32 + mfma32_row(i, hg), v = vbg * 32 + l32;
-      Go[(size_t)k * D + v] = G[b][i];
-      u.pd[k * (D + 1) + v] = G[b][i];
-    }
-  }
+  for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) gsum[ts][vb * 32 + mfma32_row(i, hg)][l32] = gacc[i];
-  __syncthreads();
-  for (int r = wave; r < D; r += 4) {
-    float sf = 0.f, sr = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      const float x = u.pd[r * (D + 1) + c];
-      sf = fmaf(x, pf[(size_t)r * D + c], sf);
-      sr = fmaf(x, pr[(size_t)r * D + c], sr);
+    for (int b = 0; b < NGB; ++b) {
+      const int blk = wave + 4 * b;
+      const int kb = blk / NB, vbg = blk % NB;
+      if (kb * 32 / RPP != ps) continue;      // wave-uniform
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k = kb * 32 + mfma32_row(i, hg), v = vbg * 32 + l32;
+        Go[(size_t)k * D + v] = G[b][i];
+        u.e.pd[(k - ps * RPP) * (D + 1) + v] = G[b][i];
+      }
     }
-    sf = sum64(sf);
-    sr = sum64(sr);
-    if (lane == 0) {
-      a.dDbr[(((size_t)bh * 2 + 0) * g.F + t) * D + r] = sf;
-      a.dDbr[(((size_t)bh * 2 + 1) * g.F + t) * D + r] = sr;
+    __syncthreads();
+    for (int rr = wave; rr < RPP; rr += 4) {
+      const int r = ps * RPP + rr;
+      float sf = 0.f, sr = 0.f;
+      for (int c = lane; c < D; c += 64) {
+        const float x = u.e.pd[rr * (D + 1) + c];
+        sf = fmaf(x, pf[(size_t)r * D + c], sf);
+        sr = fmaf(x, pr[(size_t)r * D + c], sr);
+      }
+      sf = sum64(sf);
+      sr = sum64(sr);
+      if (lane == 0) {
+        a.dDbr[(((size_t)bh * 2 + 0) * g.F + t) * D + r] = sf;
+        a.dDbr[(((size_t)bh * 2 + 1) * g.F + t) * D + r] = sr;
+      }
     }
+    if (ps + 1 < NPASS) __syncthreads();      // the slice is read before the next one lands
   }
   if (a.dgp) {
     for (int c = tid; c < D; c += 256) {
       float sg = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < SUBT; ++s2)
-        for (int j = 0; j < 32; ++j) sg += gsum[s2][c][j];
+        for (int j = 0; j < 32; ++j) sg += u.e.gsum[s2][c][j];
       a.dgp[((size_t)bh * g.F + t) * D + c] = sg;
     }
   }

@@ -41,6 +41,7 @@ template <typename T> struct Chunk8;
 template <> struct Chunk8<bf16_t> {   // 8 bf16 = one 16-byte access
   u32x4 r;
   __device__ __forceinline__ void load(const bf16_t* p) { r = ld16(p); }
+  __device__ __forceinline__ void store_raw(bf16_t* p) const { st16(p, r); }
   __device__ __forceinline__ void zero() { r = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ void to_f32(float* x) const {
 #pragma unroll
@@ -59,6 +60,7 @@ template <> struct Chunk8<bf16_t> {   // 8 bf16 = one 16-byte access
 template <> struct Chunk8<float> {    // 8 float = two 16-byte accesses
   u32x4 r0, r1;
   __device__ __forceinline__ void load(const float* p) { r0 = ld16(p); r1 = ld16(p + 4); }
+  __device__ __forceinline__ void store_raw(float* p) const { st16(p, r0); st16(p + 4, r1); }
   __device__ __forceinline__ void zero() { r0 = r1 = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ void to_f32(float* x) const {
 #pragma unroll
@@ -138,11 +140,13 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
   const int kh = KH > 0 ? KH : a.kh, kw = KW > 0 ? KW : a.kw;
   constexpr int TPT = (16 * C8 + kPrepThreads - 1) / kPrepThreads;   // column-pair tasks per thread (xt <= 32)
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  // LDS: staged rows [kh][xt + kw - 1][D] | spatial weights [kh*kw][D] | temporal weights by window slot [kTapsMax][D]
+  // LDS: spatial weights [kh*kw][D] | temporal weights by window slot
+  // [kTapsMax][D] | staged rows [kh][xt + kw - 1][D], kept in the storage
+  // type (the spatial sums convert to fp32 as they read)
   const int cols = a.xt + kw - 1;
-  float* in_s = sm;
-  float* ws_s = in_s + (size_t)kh * cols * D;
+  float* ws_s = sm;
   float* wt_s = ws_s + (size_t)kh * kw * D;
+  T* in_s = reinterpret_cast<T*>(wt_s + (size_t)kTapsMax * D);
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so XCD
   // x = blockIdx % 8 takes a contiguous run of the logical order (b, h,
@@ -199,13 +203,7 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
 #pragma unroll
     for (int i = 0; i < kPrefetchMax; ++i) {
       const int qq = tid + kPrepThreads * i;
-      if (qq < nchunk) {
-        float x[8];
-        pf[i].to_f32(x);
-        float* p = in_s + (size_t)(qq / C8) * D + (qq % C8) * 8;
-        st16(p, u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
-        st16(p + 4, u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
-      }
+      if (qq < nchunk) pf[i].store_raw(in_s + (size_t)(qq / C8) * D + (qq % C8) * 8);
     }
   };
 
@@ -246,13 +244,9 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
 #pragma unroll
           for (int cx = 0; cx <= KWM; ++cx) {
             if (KW == 0 && cx > kw) continue;
-            const float* xin = in_s + (size_t)(dy * cols + xl + cx) * D + c8 * 8;
-            const u32x4 v0 = ld16(xin), v1 = ld16(xin + 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              xc[cx][i] = __uint_as_float(v0[i]);
-              xc[cx][4 + i] = __uint_as_float(v1[i]);
-            }
+            Chunk8<T> xin;
+            xin.load(in_s + (size_t)(dy * cols + xl + cx) * D + c8 * 8);
+            xin.to_f32(xc[cx]);
           }
 #pragma unroll
           for (int dx = 0; dx < KWM; ++dx) {
@@ -321,7 +315,8 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
   static_assert(kRing == 5 && kRing >= kTapsMax, "the frame loop is unrolled kRing times");
 }
 
-// Largest even column tile (<= 32) whose LDS footprint stays within 64 KB;
+// Largest even column tile (<= 32) whose LDS footprint stays within 64 KB
+// with the rows staged as fp32 (bf16 rows take less);
 // a grid narrower than the tile rounds up to even (the extra column is
 // outside the grid and reads as zeros).
 int prep_tile_cols(int D, int kh, int kw, int gw) {
@@ -354,7 +349,7 @@ hipError_t launch_vda_prep(const void* q, const void* k, const void* v, const fl
   a.eps = eps;
   const long long kvtotal = (long long)B * H * gh * a.ntx * 2;
   const unsigned kvgrid = (unsigned)((kvtotal + kNumXcd - 1) / kNumXcd * kNumXcd);
-  const size_t lds = ((size_t)kh * (a.xt + kw - 1) * D + (size_t)kh * kw * D + (size_t)kTapsMax * D) * 4;
+  const size_t lds = (size_t)kh * (a.xt + kw - 1) * D * sizeof(T) + ((size_t)kh * kw * D + (size_t)kTapsMax * D) * 4;
 #define VDN_PREP_CASE(DD)                                                                          \
   case DD:                                                                                         \
     vda_prep_q_kernel<T, DD><<<qgrid, kPrepThreads, 0, s>>>((const T*)q, (T*)q_out, rows, H, L, eps); \

@@ -392,7 +392,8 @@ vdn_status vdn_mx_quantize(const void* src, void* codes, void* scales, long long
  *  q_out, k_out, v_out [B,H,L,d]   dt     frame-major, head-major features
  * Uses dims B, H, F, N and d_k (== d_v); T and D are ignored; F >= 1.  No
  * workspace.  Supported: d in {16,32,64,128}; kernel_h, kernel_w odd in [1,7];
- * taps in [1,5].  Outputs must not alias inputs.
+ * taps in [1,5]; one frame of all heads (N * H * d elements) at most 2 GiB
+ * (VDN_ERR_UNSUPPORTED otherwise).  Outputs must not alias inputs.
  */
 typedef struct {
   int grid_h, grid_w;      /* latent grid of one frame, N = grid_h * grid_w          */

@@ -42,6 +42,7 @@ template <> struct Chunk8<bf16_t> {   // 8 bf16 = one 16-byte access
   u32x4 r;
   __device__ __forceinline__ void load(const bf16_t* p) { r = ld16(p); }
   __device__ __forceinline__ void store_raw(bf16_t* p) const { st16(p, r); }
+  __device__ __forceinline__ void load_buf(rsrc_t rs, uint32_t off) { r = buf_ld16(rs, off); }
   __device__ __forceinline__ void zero() { r = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ void to_f32(float* x) const {
 #pragma unroll
@@ -61,6 +62,10 @@ template <> struct Chunk8<float> {    // 8 float = two 16-byte accesses
   u32x4 r0, r1;
   __device__ __forceinline__ void load(const float* p) { r0 = ld16(p); r1 = ld16(p + 4); }
   __device__ __forceinline__ void store_raw(float* p) const { st16(p, r0); st16(p + 4, r1); }
+  __device__ __forceinline__ void load_buf(rsrc_t rs, uint32_t off) {
+    r0 = buf_ld16(rs, off);
+    r1 = buf_ld16(rs, off + 16);   // an offset past the range stays past it
+  }
   __device__ __forceinline__ void zero() { r0 = r1 = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ void to_f32(float* x) const {
 #pragma unroll
@@ -180,30 +185,45 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
     wt_s[e] = tap >= 0 ? a.w_t[((size_t)h * D + c) * a.taps + tap] : 0.f;
   }
 
-  // staging: chunk q -> (row r, column cx, c8)
+  // staging: chunk q -> (row r, column cx, c8), at a fixed byte offset from
+  // the start of a frame's rows of head h; chunks outside the grid (and
+  // past the staged block) get an offset beyond the buffer range, which
+  // reads as zeros, so the frame loop carries no index arithmetic or
+  // bounds branches
   const int nchunk = kh * cols * C8;
+  uint32_t coff[kPrefetchMax];
+#pragma unroll
+  for (int i = 0; i < kPrefetchMax; ++i) {
+    const int qq = tid + kPrepThreads * i;
+    coff[i] = 0x80000000u;
+    if (qq < nchunk) {
+      const int c8 = qq % C8, rc = qq / C8;
+      const int cx = rc % cols, r = rc / cols;
+      const int yy = y + r - ry, xx = x0 + cx - rx;
+      if (yy >= 0 && yy < a.gh && xx >= 0 && xx < a.gw)
+        coff[i] = (uint32_t)((((size_t)yy * a.gw + xx) * a.H * D + c8 * 8) * sizeof(T));
+    }
+  }
+  const size_t frame_elems = (size_t)N * a.H * D;
+  const T* hbase = src + (size_t)b * a.L * a.H * D + (size_t)h * D;
+  const T* tend = src + (size_t)a.B * a.L * a.H * D;
   Chunk8<T> pf[kPrefetchMax];   // next frame's rows, fetched one frame ahead
   auto fetch = [&](Chunk8<T>* pf, int fi) {
+    if (fi < a.F) {
+      const T* fb = hbase + (size_t)fi * frame_elems;
+      const rsrc_t rs = make_rsrc(fb, rsrc_bytes(fb, tend));
 #pragma unroll
-    for (int i = 0; i < kPrefetchMax; ++i) {
-      const int qq = tid + kPrepThreads * i;
-      pf[i].zero();
-      if (qq < nchunk) {
-        const int c8 = qq % C8, rc = qq / C8;
-        const int cx = rc % cols, r = rc / cols;
-        const int yy = y + r - ry, xx = x0 + cx - rx;
-        if (fi < a.F && yy >= 0 && yy < a.gh && xx >= 0 && xx < a.gw) {
-          const long long l = (long long)fi * N + (long long)yy * a.gw + xx;
-          pf[i].load(src + (((size_t)b * a.L + l) * a.H + h) * D + c8 * 8);
-        }
-      }
+      for (int i = 0; i < kPrefetchMax; ++i) pf[i].load_buf(rs, coff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPrefetchMax; ++i) pf[i].zero();
     }
   };
   auto stage = [&](const Chunk8<T>* pf) {
 #pragma unroll
     for (int i = 0; i < kPrefetchMax; ++i) {
       const int qq = tid + kPrepThreads * i;
-      if (qq < nchunk) pf[i].store_raw(in_s + (size_t)(qq / C8) * D + (qq % C8) * 8);
+      if (qq < nchunk) pf[i].store_raw(in_s + (size_t)qq * 8);   // = row (qq / C8), channels 8 (qq % C8)
     }
   };
 
@@ -235,7 +255,8 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
       const int t = tid + kPrepThreads * j;
       const int xl = 2 * (t / C8), c8 = t % C8;
       const bool act[2] = {xl < a.xt && x0 + xl < a.gw, xl + 1 < a.xt && x0 + xl + 1 < a.gw};
-      float s[2][8] = {};
+      // the first tap of each sum multiplies (no zero-initialised accumulators)
+      float s[2][8];
       if (act[0]) {
 #pragma unroll
         for (int dy = 0; dy < KHM; ++dy) {
@@ -256,13 +277,25 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float wa = __uint_as_float(w0v[i]), wb = __uint_as_float(w1v[i]);
-              s[0][i] = fmaf(wa, xc[dx][i], s[0][i]);
-              s[0][4 + i] = fmaf(wb, xc[dx][4 + i], s[0][4 + i]);
-              s[1][i] = fmaf(wa, xc[dx + 1][i], s[1][i]);
-              s[1][4 + i] = fmaf(wb, xc[dx + 1][4 + i], s[1][4 + i]);
+              if (dy == 0 && dx == 0) {
+                s[0][i] = wa * xc[dx][i];
+                s[0][4 + i] = wb * xc[dx][4 + i];
+                s[1][i] = wa * xc[dx + 1][i];
+                s[1][4 + i] = wb * xc[dx + 1][4 + i];
+              } else {
+                s[0][i] = fmaf(wa, xc[dx][i], s[0][i]);
+                s[0][4 + i] = fmaf(wb, xc[dx][4 + i], s[0][4 + i]);
+                s[1][i] = fmaf(wa, xc[dx + 1][i], s[1][i]);
+                s[1][4 + i] = fmaf(wb, xc[dx + 1][4 + i], s[1][4 + i]);
+              }
             }
           }
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s[e][i] = 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e)
@@ -270,7 +303,7 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
         for (int i = 0; i < 8; ++i) win[j][u][e][i] = s[e][i];
       if (fo < 0) continue;
       // frame fi - k (slot (u - k) mod kRing) meets temporal weight slot kTapsMax - 1 - k
-      float o[2][8] = {};
+      float o[2][8];
 #pragma unroll
       for (int k = 0; k < kTapsMax; ++k) {
         const int sl = (u - k + kRing) % kRing;
@@ -280,8 +313,9 @@ __global__ __launch_bounds__(kPrepThreads) void vda_prep_kv_kernel(PrepArgs a) {
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            o[e][i] = fmaf(__uint_as_float(w0v[i]), win[j][sl][e][i], o[e][i]);
-            o[e][4 + i] = fmaf(__uint_as_float(w1v[i]), win[j][sl][e][4 + i], o[e][4 + i]);
+            const float wa = __uint_as_float(w0v[i]), wb = __uint_as_float(w1v[i]);
+            o[e][i] = k == 0 ? wa * win[j][sl][e][i] : fmaf(wa, win[j][sl][e][i], o[e][i]);
+            o[e][4 + i] = k == 0 ? wb * win[j][sl][e][4 + i] : fmaf(wb, win[j][sl][e][4 + i], o[e][4 + i]);
           }
       }
 #pragma unroll

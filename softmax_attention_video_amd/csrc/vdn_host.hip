@@ -1060,6 +1060,8 @@ vdn_status vda_prep_fwd(const void* q, const void* k, const void* v, const float
   const long long L = (long long)d.F * d.N;
   if (L > (1ll << 31) - 1 || (long long)d.B * L * d.H > (1ll << 40))
     return fail(VDN_ERR_INVALID_ARG, "sequence too long (L=%lld)", L);
+  if ((long long)d.N * d.H * d.d_k * (dt == VDN_BF16 ? 2 : 4) > 0x7FFFFFF0ll)
+    return fail(VDN_ERR_UNSUPPORTED, "one frame of all heads (N=%d H=%d d=%d) exceeds 2 GiB", d.N, d.H, d.d_k);
   if (vdn::prep_tile_cols(d.d_k, p->kernel_h, p->kernel_w, p->grid_w) <= 0)
     return fail(VDN_ERR_UNSUPPORTED, "filter %dx%d does not fit the kernel's LDS tile", p->kernel_h, p->kernel_w);
   hipStream_t s = (hipStream_t)stream;

@@ -273,13 +273,10 @@ template <int D>
 __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf16_t> a) {
   constexpr int NB = D / 32, NKK = D / 16;
   constexpr int SUBT = 4 / NB, TPS = 32 * SUBT;
-  constexpr int QP = TPS + 8, DP = D + 8;       // pitches (bf16) of the transposed / row tiles
+  constexpr int DP = D + 8;                     // pitch (bf16) of the row tiles
   constexpr int NGB = NB * NB / 4;              // G blocks per wave
   struct Tiles {
-    bf16_t qt[D * QP];        // Q^T of the step's tokens
-    bf16_t dth[D * QP];       // dO^T, hi / lo
-    bf16_t dtl[D * QP];
-    bf16_t doh[TPS * DP];     // dO, hi / lo
+    bf16_t doh[TPS * DP];     // dO, hi / lo (G reads them, and the Q rows, transposed)
     bf16_t dol[TPS * DP];
   };
   // G goes through LDS in NPASS slices of RPP rows, so that the tiles, the
@@ -390,6 +387,11 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     for (int i4 = 0; i4 < 4; ++i4)
       dst[i4] = n < g.N ? *reinterpret_cast<const u32x2*>(dob + 8 * i4 + 4 * hg) : u32x2{0, 0};
   };
+  // the gate of this lane's token, also requested a step early: a load
+  // issued and consumed within one step would make the step wait for every
+  // prefetch issued before it
+  auto load_gate = [&](int n) { return n < g.N ? a.g_l[(size_t)bh * g.L + (size_t)t * g.N + n] : 0.f; };
+  float gate_c = load_gate(nl), gate_n = 0.f;
   load_do(nl, dx);
   fetch_q(0);
   stage_q(0);
@@ -402,15 +404,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     const bool more = n0 + TPS < g.N;
     if (more) fetch_q(n0 + TPS);
     load_do(n + TPS, dxn);
-    // Q^T tile: this wave writes its two k-steps
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      if ((kk >> 1) != vb) continue;      // wave-uniform: keeps the register index static
-      const u32x4 w = __builtin_bit_cast(u32x4, qf[kk]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        u.t.qt[(kk * 16 + hg * 8 + j) * QP + nl] = (bf16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
-    }
+    gate_n = load_gate(n + TPS);
     // O^T block
     f32x16 o = f32x16{};
 #pragma unroll
@@ -429,7 +423,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     for (int b = 0; b < NB; ++b) sst += red1[ts * NB + b][l32];
     const float inv = rsqrtf(sst / (float)D + a.eps);
     const size_t l = (size_t)t * g.N + n;
-    const float gate = valid ? a.g_l[(size_t)bh * g.L + l] : 0.f;
+    const float gate = gate_c;
     const f32x4* gq = reinterpret_cast<const f32x4*>(&gms[vb * 32 + 4 * hg]);
     float y[16], u_[16], dgv = 0.f, uy = 0.f;
 #pragma unroll
@@ -474,12 +468,8 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
         for (int e = 0; e < 2; ++e) {
           const int i = 4 * i4 + 2 * r2 + e;
           const float d = valid ? inv * (u_[i] - y[i] * muy) : 0.f;
-          const bf16_t hb = f32_to_bf16(d);
-          hv[e] = bf16_to_f32(hb);
+          hv[e] = bf16_to_f32(f32_to_bf16(d));
           lv[e] = d - hv[e];
-          const int vrow = vb * 32 + mfma32_row(i, hg);
-          u.t.dth[vrow * QP + nl] = hb;
-          u.t.dtl[vrow * QP + nl] = f32_to_bf16(lv[e]);
         }
         ph[r2] = pack_bf16x2(hv[0], hv[1]);
         pl[r2] = pack_bf16x2(lv[0], lv[1]);
@@ -509,22 +499,34 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
         *reinterpret_cast<u32x2*>(dqr + 8 * i4 + 4 * hg) = pk;
       }
     }
-    // G += Q^T dO over the step's tokens
+    // G += Q^T dO over the step's tokens, both operands read transposed from
+    // the row tiles: lane group g (16 lanes) takes rows 16 (g % 2) + 0..15 of
+    // its block and contraction slots 8 (g / 2) + 0..7, four tokens a read
 #pragma unroll
     for (int b = 0; b < NGB; ++b) {
       const int blk = wave + 4 * b;
       const int kb = blk / NB, vbg = blk % NB;
+      const int grp = lane >> 4, sl = lane & 15;
+      const int trow = 8 * (grp >> 1) + (sl >> 2), tcol = 16 * (grp & 1) + 4 * (sl & 3);
 #pragma unroll
       for (int ns = 0; ns < TPS / 16; ++ns) {
-        const bf16x8 aq = as_bf16x8(ld16(&u.t.qt[(kb * 32 + l32) * QP + ns * 16 + hg * 8]));
-        const bf16x8 bh_ = as_bf16x8(ld16(&u.t.dth[(vbg * 32 + l32) * QP + ns * 16 + hg * 8]));
-        const bf16x8 bl_ = as_bf16x8(ld16(&u.t.dtl[(vbg * 32 + l32) * QP + ns * 16 + hg * 8]));
+        const int r0 = (ns * 16 + trow) * DP, r1 = r0 + 4 * DP;
+        const bf16_t* qa = &qrow[st][kb * 32 + tcol];
+        const bf16_t* dh = &u.t.doh[vbg * 32 + tcol];
+        const bf16_t* dl = &u.t.dol[vbg * 32 + tcol];
+        const u32x2 q0 = lds_read_tr16(qa + r0), q1 = lds_read_tr16(qa + r1);
+        const u32x2 h0 = lds_read_tr16(dh + r0), h1 = lds_read_tr16(dh + r1);
+        const u32x2 l0 = lds_read_tr16(dl + r0), l1 = lds_read_tr16(dl + r1);
+        const bf16x8 aq = as_bf16x8(u32x4{q0[0], q0[1], q1[0], q1[1]});
+        const bf16x8 bh_ = as_bf16x8(u32x4{h0[0], h0[1], h1[0], h1[1]});
+        const bf16x8 bl_ = as_bf16x8(u32x4{l0[0], l0[1], l1[0], l1[1]});
         G[b] = mfma32x32x16(aq, bh_, G[b]);
         G[b] = mfma32x32x16(aq, bl_, G[b]);
       }
     }
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) dx[i4] = dxn[i4];
+    gate_c = gate_n;
     if (more) stage_q(st ^ 1);      // that buffer was last read before the previous barrier
     __syncthreads();
   }

@@ -49,6 +49,21 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16, gfx950).  Each
+// lane names 8 bytes; within every group of 16 lanes the reads are
+// redistributed so that lane i of the group receives element i % 4 of the
+// reads of group lanes 4 e + i / 4, e = 0..3.  With group lane s pointing at
+// row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3 of a row-major 16-bit tile,
+// lane i receives column c0 + i of rows r0 .. r0 + 3: four consecutive
+// contraction slots of an MFMA operand read from a tile stored the other way
+// round.  p must be an LDS address, 8-byte aligned.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 // Raw buffer loads (gfx9 buffer descriptor: stride 0, num_records = bytes,
 // word 3 = 0x00020000).  A 16-byte load whose range lies past num_records
 // returns zeros, so tile loads need no bounds branches.

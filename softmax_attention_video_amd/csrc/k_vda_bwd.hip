@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     Tail e;
   } u;
   __shared__ __attribute__((aligned(16))) bf16_t qrow[2][TPS * DP];   // the step's Q rows
-  __shared__ float red1[4][32], red2[4][32][2];
+  __shared__ float red[4][32][3];
   __shared__ float dfs[D], drs[D];
   __shared__ __attribute__((aligned(16))) float gms[D];
 
@@ -412,20 +412,12 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
       o = mfma32x32x16(mth[kk], qf[kk], o);
       o = mfma32x32x16(mtl[kk], qf[kk], o);
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ss = fmaf(o[i], o[i], ss);
-    ss = half_sum(ss);
-    if (hg == 0) red1[wave][l32] = ss;
-    lds_barrier();
-    float sst = 0.f;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) sst += red1[ts * NB + b][l32];
-    const float inv = rsqrtf(sst / (float)D + a.eps);
-    const size_t l = (size_t)t * g.N + n;
+    // the token's three sums over its channels, from O directly (1 / r
+    // factors out of the last two), exchanged once: |o|^2, sum dOhat gamma o,
+    // sum u o with u = g_l gamma dOhat
     const float gate = gate_c;
     const f32x4* gq = reinterpret_cast<const f32x4*>(&gms[vb * 32 + 4 * hg]);
-    float y[16], u_[16], dgv = 0.f, uy = 0.f;
+    float u_[16], ss = 0.f, dgr = 0.f, uor = 0.f;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const u32x2 x = dx[i4];
@@ -435,31 +427,40 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * i4 + r;
-        y[i] = valid ? o[i] * inv : 0.f;
+        ss = fmaf(o[i], o[i], ss);
         u_[i] = gate * gm4[r] * dv4[r];
-        dgv = fmaf(dv4[r] * gm4[r], y[i], dgv);
-        uy = fmaf(u_[i], y[i], uy);
-        gacc[i] = fmaf(dv4[r] * gate, y[i], gacc[i]);
+        dgr = fmaf(dv4[r] * gm4[r], o[i], dgr);
+        uor = fmaf(u_[i], o[i], uor);
       }
     }
-    dgv = half_sum(dgv);
-    uy = half_sum(uy);
+    ss = half_sum(ss);
+    dgr = half_sum(dgr);
+    uor = half_sum(uor);
     if (hg == 0) {
-      red2[wave][l32][0] = dgv;
-      red2[wave][l32][1] = uy;
+      red[wave][l32][0] = ss;
+      red[wave][l32][1] = dgr;
+      red[wave][l32][2] = uor;
     }
     lds_barrier();
-    float dgt = 0.f, uyt = 0.f;
+    float sst = 0.f, dgt = 0.f, uyt = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      dgt += red2[ts * NB + b][l32][0];
-      uyt += red2[ts * NB + b][l32][1];
+      sst += red[ts * NB + b][l32][0];
+      dgt += red[ts * NB + b][l32][1];
+      uyt += red[ts * NB + b][l32][2];
     }
+    const float inv = rsqrtf(sst / (float)D + a.eps);
+    dgt *= inv;
+    uyt *= inv;
+    const size_t l = (size_t)t * g.N + n;
     if (vb == 0 && hg == 0 && valid && a.dg_l) a.dg_l[(size_t)bh * g.L + l] = dgt;
     const float muy = uyt / (float)D;
-    // dO of this block -> LDS, row-major and transposed, hi + lo
+    // y = o / r, the dgamma partials, dO of this block -> LDS as hi + lo
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
+      const u32x2 x = dx[i4];
+      const float dv4[4] = {bf16_to_f32((bf16_t)(x[0] & 0xFFFFu)), bf16_to_f32((bf16_t)(x[0] >> 16)),
+                            bf16_to_f32((bf16_t)(x[1] & 0xFFFFu)), bf16_to_f32((bf16_t)(x[1] >> 16))};
       uint32_t ph[2], pl[2];
 #pragma unroll
       for (int r2 = 0; r2 < 2; ++r2) {
@@ -467,7 +468,9 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int i = 4 * i4 + 2 * r2 + e;
-          const float d = valid ? inv * (u_[i] - y[i] * muy) : 0.f;
+          const float y = valid ? o[i] * inv : 0.f;
+          gacc[i] = fmaf(dv4[2 * r2 + e] * gate, y, gacc[i]);
+          const float d = valid ? inv * (u_[i] - y * muy) : 0.f;
           hv[e] = bf16_to_f32(f32_to_bf16(d));
           lv[e] = d - hv[e];
         }
@@ -478,7 +481,11 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
       *reinterpret_cast<u32x2*>(&u.t.doh[nl * DP + c0]) = u32x2{ph[0], ph[1]};
       *reinterpret_cast<u32x2*>(&u.t.dol[nl * DP + c0]) = u32x2{pl[0], pl[1]};
     }
-    __syncthreads();
+    // the next step's Q rows go to the other buffer (last read in the
+    // previous step, before this step's first barrier); the barrier below
+    // publishes them with dO
+    if (more) stage_q(st ^ 1);
+    lds_barrier();
     // dq^T rows k of block vb for the sub-tile's tokens
     f32x16 dq = f32x16{};
 #pragma unroll
@@ -527,9 +534,11 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) dx[i4] = dxn[i4];
     gate_c = gate_n;
-    if (more) stage_q(st ^ 1);      // that buffer was last read before the previous barrier
-    __syncthreads();
+    // no barrier here: the next writes to the dO tiles and the sums follow
+    // the next step's first barrier, which every wave reaches only after
+    // this step's reads
   }
+  __syncthreads();      // the tiles are read out before the tail reuses their space
   // G -> memory and, a slice of rows at a time, LDS; bridge adjoints
   // dD = rowsum(G * P).  The tiles were last read before the loop's final
   // barrier, so the tail region is free.

@@ -258,41 +258,48 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_kernel(VdaBwdArgs<T> a) {
   }
 }
 
-// bf16 kernel (D = 64, 128) on v_mfma_f32_32x32x16_bf16.  Wave w owns the
-// channel block vb = w % (D/32) of a 32-token sub-tile w / (D/32):
-//   O^T  = M^T Q^T   (rows v of its block; M^T rows as bf16 hi + lo fragments,
-//                     kept in registers for the whole frame),
-//   the RMSNorm / gate adjoint (per-token sums exchanged through LDS),
-//   dq^T = M dO^T    (rows k of block vb; M rows as hi + lo fragments; dO of
-//                     every channel block from LDS, hi + lo),
-//   G   += Q^T dO    (its G blocks, contracted over the step's tokens from
-//                     transposed Q and dO tiles in LDS).
+// bf16 kernel (D = 64, 128) on v_mfma_f32_32x32x16_bf16.  NW waves; wave w
+// owns the channel block vb = w % (D/32) of the 32-token sub-tile w / (D/32)
+// of a 64-token step.  M = diag(D_f) P_f + diag(D_r) P_r is formed once per
+// frame into LDS as bf16 hi + lo, row-major [k][v], so no wave holds
+// fragments of it for the whole frame:
+//   O^T  = M^T Q^T   (rows v of its block; M^T read from M with the
+//                     transposing LDS read),
+//   the RMSNorm / gate adjoint (three per-token sums exchanged through LDS),
+//   dq^T = M dO^T    (rows k of block vb straight from M; dO rows from LDS),
+//   G   += Q^T dO    (its G blocks, contracted over the step's tokens; both
+//                     operands read transposed from the Q and dO row tiles).
 // At the end G goes to memory and the bridge adjoints are row sums of
 // G * P; dgamma partials are reduced through LDS.
+template <int D> struct BwdReadoutShape {
+  static constexpr int NW = D == 128 ? 8 : 4;   // waves per workgroup
+};
 template <int D>
-__global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf16_t> a) {
-  constexpr int NB = D / 32, NKK = D / 16;
-  constexpr int SUBT = 4 / NB, TPS = 32 * SUBT;
-  constexpr int DP = D + 8;                     // pitch (bf16) of the row tiles
-  constexpr int NGB = NB * NB / 4;              // G blocks per wave
-  struct Tiles {
-    bf16_t doh[TPS * DP];     // dO, hi / lo (G reads them, and the Q rows, transposed)
+__global__ __launch_bounds__(BwdReadoutShape<D>::NW * 64) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf16_t> a) {
+  constexpr int NB = D / 32, NKK = D / 16, NW = BwdReadoutShape<D>::NW, NT = NW * 64;
+  constexpr int SUBT = NW / NB, TPS = 32 * SUBT;   // token sub-tiles and tokens per step
+  constexpr int DP = D + 8;                        // pitch (bf16) of the row tiles
+  constexpr int NGB = NB * NB / NW;                // G blocks per wave
+  static_assert(NGB * NW == NB * NB && TPS == 64, "work split");
+  // G goes through LDS in NPASS slices of RPP rows at the end of the frame,
+  // in the space the loop's tiles held
+  constexpr int NPASS = D > 64 ? 2 : 1, RPP = D / NPASS;
+  struct Loop {
+    bf16_t mh[D * DP];        // M hi / lo, row-major [k][v]
+    bf16_t ml[D * DP];
+    bf16_t doh[TPS * DP];     // dO of the step, hi / lo
     bf16_t dol[TPS * DP];
   };
-  // G goes through LDS in NPASS slices of RPP rows, so that the tiles, the
-  // slice and the dgamma partials share one region and two workgroups fit
-  // on a compute unit
-  constexpr int NPASS = D > 64 ? 2 : 1, RPP = D / NPASS;
   struct Tail {
-    float pd[RPP * (D + 1)];  // a slice of G at the end of the frame
+    float pd[RPP * (D + 1)];  // a slice of G
     float gsum[SUBT][D][33];  // dgamma partials
   };
   __shared__ __attribute__((aligned(16))) union {
-    Tiles t;
+    Loop t;
     Tail e;
   } u;
   __shared__ __attribute__((aligned(16))) bf16_t qrow[2][TPS * DP];   // the step's Q rows
-  __shared__ float red[4][32][3];
+  __shared__ float red[NW][32][3];
   __shared__ float dfs[D], drs[D];
   __shared__ __attribute__((aligned(16))) float gms[D];
 
@@ -301,6 +308,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
   const int bh = blockIdx.x / g.F;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int grp = lane >> 4, sl = lane & 15;       // 16-lane group of the transposing reads
   const int vb = wave % NB, ts = wave / NB;
   const size_t DD = (size_t)D * D;
   int i_f, ws, i_r, we;
@@ -325,29 +333,28 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     (part == 0 ? dfs : drs)[c] = d;
     a.Dbr[(((size_t)bh * 2 + part) * g.F + t) * D + c] = d;
   }
-  for (int c = tid; c < D; c += 256) gms[c] = a.gamma ? a.gamma[c] : 1.f;
+  for (int c = tid; c < D; c += NT) gms[c] = a.gamma ? a.gamma[c] : 1.f;
   __syncthreads();
   const float* pf = a.Pf + ((size_t)bh * (g.C + 1) + i_f) * DD;
   const float* pr = a.Pr + ((size_t)bh * (g.C + 1) + i_r) * DD;
-  // M fragments: mt* = rows v = 32 vb + l32 of M^T, m* = rows k = 32 vb + l32 of M
-  bf16x8 mth[NKK], mtl[NKK], mh[NKK], ml[NKK];
-  {
-    const int r = vb * 32 + l32;
+  // M[k][v] = D_f[k] P_f[k][v] + D_r[k] P_r[k][v] -> LDS as bf16 hi + lo,
+  // four columns per thread and item
+  for (int e = tid; e < D * D / 4; e += NT) {
+    const int k = e / (D / 4), v0 = (e % (D / 4)) * 4;
+    const f32x4 x4 = *reinterpret_cast<const f32x4*>(pf + (size_t)k * D + v0);
+    const f32x4 y4 = *reinterpret_cast<const f32x4*>(pr + (size_t)k * D + v0);
+    const float fk = dfs[k], rk = drs[k];
+    uint32_t hw[2], lw[2];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int k0 = kk * 16 + hg * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int k = k0 + j;
-        const float xt = dfs[k] * pf[(size_t)k * D + r] + drs[k] * pr[(size_t)k * D + r];   // M[k][r]
-        const float xm = dfs[r] * pf[(size_t)r * D + k] + drs[r] * pr[(size_t)r * D + k];   // M[r][k]
-        const bf16_t ht = f32_to_bf16(xt), hm = f32_to_bf16(xm);
-        mth[kk][j] = __builtin_bit_cast(__bf16, ht);
-        mtl[kk][j] = static_cast<__bf16>(xt - bf16_to_f32(ht));
-        mh[kk][j] = __builtin_bit_cast(__bf16, hm);
-        ml[kk][j] = static_cast<__bf16>(xm - bf16_to_f32(hm));
-      }
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const float m0 = fk * x4[2 * p2] + rk * y4[2 * p2];
+      const float m1 = fk * x4[2 * p2 + 1] + rk * y4[2 * p2 + 1];
+      const float h0 = bf16_to_f32(f32_to_bf16(m0)), h1 = bf16_to_f32(f32_to_bf16(m1));
+      hw[p2] = pack_bf16x2(h0, h1);
+      lw[p2] = pack_bf16x2(m0 - h0, m1 - h1);
     }
+    *reinterpret_cast<u32x2*>(&u.t.mh[k * DP + v0]) = u32x2{hw[0], hw[1]};
+    *reinterpret_cast<u32x2*>(&u.t.ml[k * DP + v0]) = u32x2{lw[0], lw[1]};
   }
   const int bidx = bh / g.H, h = bh % g.H;
   const size_t tok0 = (size_t)bh * g.L + (size_t)t * g.N;
@@ -358,15 +365,14 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
 #pragma unroll
   for (int i = 0; i < 16; ++i) gacc[i] = 0.f;
 
-  bf16x8 qf[NKK];
   // the next step's Q rows travel global -> registers -> LDS (qrow) while
   // the current step runs: CQ 16-byte chunks per thread
-  constexpr int CQ = TPS * D / 8 / 256;
+  constexpr int CQ = TPS * D / 8 / NT;
   u32x4 qst[CQ];
   auto fetch_q = [&](int n0) {
 #pragma unroll
     for (int i = 0; i < CQ; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       const int r = c / (D / 8), c8 = c % (D / 8);
       qst[i] = n0 + r < g.N ? ld16(a.q + (tok0 + n0 + r) * D + c8 * 8) : u32x4{0, 0, 0, 0};
     }
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
   auto stage_q = [&](int b) {
 #pragma unroll
     for (int i = 0; i < CQ; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       st16(&qrow[b][(c / (D / 8)) * DP + (c % (D / 8)) * 8], qst[i]);
     }
   };
@@ -396,11 +402,15 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
   fetch_q(0);
   stage_q(0);
   __syncthreads();
+  // transposing reads of M^T rows v of block vb: group lane sl points at row
+  // k = 16 kk + 8 (grp / 2) + sl / 4 (+ 4), columns v = 32 vb + 16 (grp % 2) + 4 (sl % 4)
+  const int mt_off = (8 * (grp >> 1) + (sl >> 2)) * DP + vb * 32 + 16 * (grp & 1) + 4 * (sl & 3);
+  // G operands: rows 16 (grp % 2) + 0..15 of a block, contraction slots
+  // 8 (grp / 2) + 0..7, four tokens a read
+  const int trow = 8 * (grp >> 1) + (sl >> 2), tcol = 16 * (grp & 1) + 4 * (sl & 3);
   for (int n0 = 0, st = 0; n0 < g.N; n0 += TPS, st ^= 1) {
     const int n = n0 + nl;
     const bool valid = n < g.N;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(ld16(&qrow[st][nl * DP + kk * 16 + hg * 8]));
     const bool more = n0 + TPS < g.N;
     if (more) fetch_q(n0 + TPS);
     load_do(n + TPS, dxn);
@@ -409,8 +419,13 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     f32x16 o = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      o = mfma32x32x16(mth[kk], qf[kk], o);
-      o = mfma32x32x16(mtl[kk], qf[kk], o);
+      const bf16x8 qf = as_bf16x8(ld16(&qrow[st][nl * DP + kk * 16 + hg * 8]));
+      const bf16_t* ph = &u.t.mh[kk * 16 * DP + mt_off];
+      const bf16_t* pl = &u.t.ml[kk * 16 * DP + mt_off];
+      const u32x2 h0 = lds_read_tr16(ph), h1 = lds_read_tr16(ph + 4 * DP);
+      const u32x2 l0 = lds_read_tr16(pl), l1 = lds_read_tr16(pl + 4 * DP);
+      o = mfma32x32x16(as_bf16x8(u32x4{h0[0], h0[1], h1[0], h1[1]}), qf, o);
+      o = mfma32x32x16(as_bf16x8(u32x4{l0[0], l0[1], l1[0], l1[1]}), qf, o);
     }
     // the token's three sums over its channels, from O directly (1 / r
     // factors out of the last two), exchanged once: |o|^2, sum dOhat gamma o,
@@ -490,11 +505,14 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     f32x16 dq = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
+      const int mo = (vb * 32 + l32) * DP + kk * 16 + hg * 8;
+      const bf16x8 mh_ = as_bf16x8(ld16(&u.t.mh[mo]));
+      const bf16x8 ml_ = as_bf16x8(ld16(&u.t.ml[mo]));
       const bf16x8 bh_ = as_bf16x8(ld16(&u.t.doh[nl * DP + kk * 16 + hg * 8]));
       const bf16x8 bl_ = as_bf16x8(ld16(&u.t.dol[nl * DP + kk * 16 + hg * 8]));
-      dq = mfma32x32x16(mh[kk], bh_, dq);
-      dq = mfma32x32x16(ml[kk], bh_, dq);
-      dq = mfma32x32x16(mh[kk], bl_, dq);
+      dq = mfma32x32x16(mh_, bh_, dq);
+      dq = mfma32x32x16(ml_, bh_, dq);
+      dq = mfma32x32x16(mh_, bl_, dq);
     }
     if (valid) {
       bf16_t* dqr = a.dq + (tok0 + n) * D + vb * 32;
@@ -506,15 +524,11 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
         *reinterpret_cast<u32x2*>(dqr + 8 * i4 + 4 * hg) = pk;
       }
     }
-    // G += Q^T dO over the step's tokens, both operands read transposed from
-    // the row tiles: lane group g (16 lanes) takes rows 16 (g % 2) + 0..15 of
-    // its block and contraction slots 8 (g / 2) + 0..7, four tokens a read
+    // G += Q^T dO over the step's tokens
 #pragma unroll
     for (int b = 0; b < NGB; ++b) {
-      const int blk = wave + 4 * b;
+      const int blk = wave + NW * b;
       const int kb = blk / NB, vbg = blk % NB;
-      const int grp = lane >> 4, sl = lane & 15;
-      const int trow = 8 * (grp >> 1) + (sl >> 2), tcol = 16 * (grp & 1) + 4 * (sl & 3);
 #pragma unroll
       for (int ns = 0; ns < TPS / 16; ++ns) {
         const int r0 = (ns * 16 + trow) * DP, r1 = r0 + 4 * DP;
@@ -540,8 +554,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
   }
   __syncthreads();      // the tiles are read out before the tail reuses their space
   // G -> memory and, a slice of rows at a time, LDS; bridge adjoints
-  // dD = rowsum(G * P).  The tiles were last read before the loop's final
-  // barrier, so the tail region is free.
+  // dD = rowsum(G * P)
   float* Go = a.G + ((size_t)bh * g.F + t) * DD;
 #pragma unroll
   for (int i = 0; i < 16; ++i) u.e.gsum[ts][vb * 32 + mfma32_row(i, hg)][l32] = gacc[i];
@@ -549,7 +562,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
   for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
     for (int b = 0; b < NGB; ++b) {
-      const int blk = wave + 4 * b;
+      const int blk = wave + NW * b;
       const int kb = blk / NB, vbg = blk % NB;
       if (kb * 32 / RPP != ps) continue;      // wave-uniform
 #pragma unroll
@@ -560,7 +573,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
       }
     }
     __syncthreads();
-    for (int rr = wave; rr < RPP; rr += 4) {
+    for (int rr = wave; rr < RPP; rr += NW) {
       const int r = ps * RPP + rr;
       float sf = 0.f, sr = 0.f;
       for (int c = lane; c < D; c += 64) {
@@ -578,7 +591,7 @@ __global__ __launch_bounds__(256) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf
     if (ps + 1 < NPASS) __syncthreads();      // the slice is read before the next one lands
   }
   if (a.dgp) {
-    for (int c = tid; c < D; c += 256) {
+    for (int c = tid; c < D; c += NT) {
       float sg = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < SUBT; ++s2)
@@ -1584,7 +1597,7 @@ hipError_t launch_all(const VdaBwdArgs<T>& a, const float* Tf, const float* Uf, 
   constexpr int NCB = (D + kBCB - 1) / kBCB;
   if (stage == 0) {
     if constexpr (std::is_same<T, bf16_t>::value && (D == 64 || D == 128))
-      vda_bwd_readout_mfma_kernel<D><<<BH * g.F, 256, 0, s>>>(a);
+      vda_bwd_readout_mfma_kernel<D><<<BH * g.F, BwdReadoutShape<D>::NW * 64, 0, s>>>(a);
     else
       vda_bwd_readout_kernel<T, D><<<BH * g.F, 256, 0, s>>>(a);
     return hipGetLastError();

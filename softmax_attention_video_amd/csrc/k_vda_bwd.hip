@@ -1375,24 +1375,40 @@ __global__ __launch_bounds__(256) void vda_bwd_token_kernel(VdaBwdArgs<T> a) {
   }
 }
 
-// bf16 kernel (D = 64, 128) on v_mfma_f32_32x32x16_bf16.  Wave w owns the
-// 32-channel block cb = w % (D/32) and the 32-token sub-tile w / (D/32) of
-// each step.  Its rows of dA_sym, dW^T and dW stay in registers for the
-// whole frame as bf16 hi + lo fragments (A operands); K and V rows come
-// straight from global memory as B operands, the next step's while the
-// current one is multiplied.  Per token (column n) and channel c:
+// bf16 kernel (D = 64, 128) on v_mfma_f32_32x32x16_bf16.  NW waves; wave w
+// owns the 32-channel block cb = w % (D/32) and the 32-token sub-tile
+// w / (D/32) of each 64-token step.  dA_sym and dW are formed once per frame
+// into LDS as bf16 hi + lo, row-major: the wave reads its rows of dA_sym and
+// dW as A operands and its rows of dW^T through the transposing read, so no
+// fragments stay in registers for the frame.  K and V rows come straight from
+// global memory as B operands, the next step's while the current one is
+// multiplied.  Per token (column n) and channel c:
 //   acc1 = (dA_sym k + dW v)[c],  acc2 = (dW^T k)[c],
 //   dk = beta acc1,  dv = beta acc2,  dbeta = 1/2 (acc1 . k + acc2 . v)
 // (the last since k dW v = v dW^T k).
 template <int D>
-__global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16_t> a) {
-  constexpr int MP = D + 1, NB = D / 32, NKK = D / 16;
-  constexpr int SUBT = 4 / NB;            // token sub-tiles per step
-  constexpr int TPS = 32 * SUBT;          // tokens per step
-  __shared__ __attribute__((aligned(16))) struct {
+__global__ __launch_bounds__(BwdReadoutShape<D>::NW * 64) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16_t> a) {
+  constexpr int NB = D / 32, NKK = D / 16, NW = BwdReadoutShape<D>::NW, NT = NW * 64;
+  constexpr int SUBT = NW / NB, TPS = 32 * SUBT;   // token sub-tiles and tokens per step
+  constexpr int MP = D + 1, DP = D + 8;
+  // region 0 holds dA (fp32) until dA_sym is formed, then dW hi + lo;
+  // region 1 holds dA_sym hi + lo
+  struct DaF32 {
     float am[D * MP];
-  } u;
-  __shared__ float red[2][4][32];
+  };
+  struct WHiLo {
+    bf16_t wh[D * DP];
+    bf16_t wl[D * DP];
+  };
+  __shared__ __attribute__((aligned(16))) union {
+    DaF32 f;
+    WHiLo w;
+  } r0;
+  __shared__ __attribute__((aligned(16))) struct {
+    bf16_t sh[D * DP];
+    bf16_t sl[D * DP];
+  } r1;
+  __shared__ float red[2][NW][32];
 
   const Geometry& g = a.g;
   const int nfr = g.F + (g.T > 0 ? 1 : 0);
@@ -1400,17 +1416,21 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
   const int bh = blockIdx.x / nfr;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int grp = lane >> 4, sl = lane & 15;       // 16-lane group of the transposing reads
   const FrameTok<bf16_t> ft = frame_tok<bf16_t, D>(a, bh, f);
-  if (!ft.text) alpha_scan_term<bf16_t, D>(a, ft, bh, f);
+  // the scan's alpha term and the anchor frames' zeros take the first 256
+  // threads (whole waves)
+  if (!ft.text && tid < 256) alpha_scan_term<bf16_t, D>(a, ft, bh, f);
   if (ft.anchor) {
-    zero_tokens(ft, D);
+    if (tid < 256) zero_tokens(ft, D);
     return;
   }
   {
     // dA = -(Z0 S0^T + Z1 S1^T) on v_mfma_f32_32x32x2f32, operands straight
     // from memory: rows of Z (A) and of S (B), 4 consecutive columns per
-    // lane half and load.  Wave w computes the 32 x 32 blocks w + 4 b.
-    constexpr int NGB = NB * NB / 4, NK8 = D / 8;
+    // lane half and load.  Wave w computes the 32 x 32 blocks w + NW b.
+    constexpr int NGB = NB * NB / NW, NK8 = D / 8;
+    static_assert(NGB * NW == NB * NB, "dA blocks");
     f32x16 acc[NGB];
 #pragma unroll
     for (int b = 0; b < NGB; ++b) acc[b] = f32x16{};
@@ -1422,7 +1442,7 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
         const int v0 = 8 * j + 4 * hg;
 #pragma unroll
         for (int b = 0; b < NGB; ++b) {
-          const int blk = wave + 4 * b, ib = blk / NB, jb = blk % NB;
+          const int blk = wave + NW * b, ib = blk / NB, jb = blk % NB;
           const f32x4 za = *reinterpret_cast<const f32x4*>(Zs + (size_t)(ib * 32 + l32) * D + v0);
           const f32x4 sb = *reinterpret_cast<const f32x4*>(Ss + (size_t)(jb * 32 + l32) * D + v0);
 #pragma unroll
@@ -1432,38 +1452,54 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
     }
 #pragma unroll
     for (int b = 0; b < NGB; ++b) {
-      const int blk = wave + 4 * b, ib = blk / NB, jb = blk % NB;
+      const int blk = wave + NW * b, ib = blk / NB, jb = blk % NB;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) u.am[(ib * 32 + mfma32_row(i, hg)) * MP + jb * 32 + l32] = -acc[b][i];
+      for (int i = 0; i < 16; ++i) r0.f.am[(ib * 32 + mfma32_row(i, hg)) * MP + jb * 32 + l32] = -acc[b][i];
     }
   }
   __syncthreads();
-  // A-operand fragments of the wave's channel rows
+  // dA_sym = dA + dA^T -> region 1 as bf16 hi + lo, four columns per item
+  for (int e = tid; e < D * D / 4; e += NT) {
+    const int c = e / (D / 4), k0 = (e % (D / 4)) * 4;
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const int k = k0 + 2 * p2;
+      const float x0 = r0.f.am[c * MP + k] + r0.f.am[k * MP + c];
+      const float x1 = r0.f.am[c * MP + k + 1] + r0.f.am[(k + 1) * MP + c];
+      const float h0 = bf16_to_f32(f32_to_bf16(x0)), h1 = bf16_to_f32(f32_to_bf16(x1));
+      hw[p2] = pack_bf16x2(h0, h1);
+      lw[p2] = pack_bf16x2(x0 - h0, x1 - h1);
+    }
+    *reinterpret_cast<u32x2*>(&r1.sh[c * DP + k0]) = u32x2{hw[0], hw[1]};
+    *reinterpret_cast<u32x2*>(&r1.sl[c * DP + k0]) = u32x2{lw[0], lw[1]};
+  }
+  __syncthreads();      // dA is read out before dW takes its space
+  // dW = Z0 + Z1 -> region 0 as bf16 hi + lo
+  for (int e = tid; e < D * D / 4; e += NT) {
+    const int c = e / (D / 4), k0 = (e % (D / 4)) * 4;
+    f32x4 z = *reinterpret_cast<const f32x4*>(ft.Z0 + (size_t)c * D + k0);
+    if (ft.Z1) {   // the text frame has one adjoint
+      const f32x4 z1 = *reinterpret_cast<const f32x4*>(ft.Z1 + (size_t)c * D + k0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] = z[j] + z1[j];
+    }
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const float h0 = bf16_to_f32(f32_to_bf16(z[2 * p2])), h1 = bf16_to_f32(f32_to_bf16(z[2 * p2 + 1]));
+      hw[p2] = pack_bf16x2(h0, h1);
+      lw[p2] = pack_bf16x2(z[2 * p2] - h0, z[2 * p2 + 1] - h1);
+    }
+    *reinterpret_cast<u32x2*>(&r0.w.wh[c * DP + k0]) = u32x2{hw[0], hw[1]};
+    *reinterpret_cast<u32x2*>(&r0.w.wl[c * DP + k0]) = u32x2{lw[0], lw[1]};
+  }
+  __syncthreads();
   const int cb = wave % NB, ts = wave / NB;
   const int c = cb * 32 + l32;
-  bf16x8 ash[NKK], asl[NKK], wth[NKK], wtl[NKK], wh[NKK], wl[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const int k0 = kk * 16 + hg * 8;
-    float xs[8], xt[8], xw[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = k0 + j;
-      xs[j] = u.am[c * MP + k] + u.am[k * MP + c];
-      xw[j] = ft.Z0[(size_t)c * D + k] + (ft.Z1 ? ft.Z1[(size_t)c * D + k] : 0.f);
-      xt[j] = ft.Z0[(size_t)k * D + c] + (ft.Z1 ? ft.Z1[(size_t)k * D + c] : 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16_t hs = f32_to_bf16(xs[j]), hw = f32_to_bf16(xw[j]), ht = f32_to_bf16(xt[j]);
-      ash[kk][j] = __builtin_bit_cast(__bf16, hs);
-      asl[kk][j] = static_cast<__bf16>(xs[j] - bf16_to_f32(hs));
-      wh[kk][j] = __builtin_bit_cast(__bf16, hw);
-      wl[kk][j] = static_cast<__bf16>(xw[j] - bf16_to_f32(hw));
-      wth[kk][j] = __builtin_bit_cast(__bf16, ht);
-      wtl[kk][j] = static_cast<__bf16>(xt[j] - bf16_to_f32(ht));
-    }
-  }
+  // transposing reads of dW^T rows c: group lane sl points at row
+  // k = 16 kk + 8 (grp / 2) + sl / 4 (+ 4), columns 32 cb + 16 (grp % 2) + 4 (sl % 4)
+  const int wt_off = (8 * (grp >> 1) + (sl >> 2)) * DP + cb * 32 + 16 * (grp & 1) + 4 * (sl & 3);
 
   const long long ntok = ft.ntok;
   bf16x8 bk[NKK], bv[NKK], bkn[NKK], bvn[NKK];
@@ -1487,12 +1523,19 @@ __global__ __launch_bounds__(256) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16
     f32x16 acc1 = f32x16{}, acc2 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      acc1 = mfma32x32x16(ash[kk], bk[kk], acc1);
-      acc1 = mfma32x32x16(asl[kk], bk[kk], acc1);
-      acc1 = mfma32x32x16(wh[kk], bv[kk], acc1);
-      acc1 = mfma32x32x16(wl[kk], bv[kk], acc1);
-      acc2 = mfma32x32x16(wth[kk], bk[kk], acc2);
-      acc2 = mfma32x32x16(wtl[kk], bk[kk], acc2);
+      const int ao = c * DP + kk * 16 + hg * 8;
+      const bf16x8 ash = as_bf16x8(ld16(&r1.sh[ao])), asl = as_bf16x8(ld16(&r1.sl[ao]));
+      const bf16x8 wh = as_bf16x8(ld16(&r0.w.wh[ao])), wl = as_bf16x8(ld16(&r0.w.wl[ao]));
+      const bf16_t* pth = &r0.w.wh[kk * 16 * DP + wt_off];
+      const bf16_t* ptl = &r0.w.wl[kk * 16 * DP + wt_off];
+      const u32x2 th0 = lds_read_tr16(pth), th1 = lds_read_tr16(pth + 4 * DP);
+      const u32x2 tl0 = lds_read_tr16(ptl), tl1 = lds_read_tr16(ptl + 4 * DP);
+      acc1 = mfma32x32x16(ash, bk[kk], acc1);
+      acc1 = mfma32x32x16(asl, bk[kk], acc1);
+      acc1 = mfma32x32x16(wh, bv[kk], acc1);
+      acc1 = mfma32x32x16(wl, bv[kk], acc1);
+      acc2 = mfma32x32x16(as_bf16x8(u32x4{th0[0], th0[1], th1[0], th1[1]}), bk[kk], acc2);
+      acc2 = mfma32x32x16(as_bf16x8(u32x4{tl0[0], tl0[1], tl1[0], tl1[1]}), bk[kk], acc2);
     }
     const bool valid = n < ntok;
     // k and v at the accumulator positions (channels cb*32 + 8 i4 + 4 hg + r)
@@ -1616,7 +1659,7 @@ hipError_t launch_all(const VdaBwdArgs<T>& a, const float* Tf, const float* Uf, 
     vda_bwd_frame_adjoint_kernel<T, D><<<BH * 2 * g.C * NCB, 256, 0, s>>>(a, Tf, Uf);
   const unsigned nfr = BH * (g.F + (g.T > 0 ? 1 : 0));
   if constexpr (std::is_same<T, bf16_t>::value && (D == 64 || D == 128))
-    vda_bwd_token_mfma_kernel<D><<<nfr, 256, 0, s>>>(a);
+    vda_bwd_token_mfma_kernel<D><<<nfr, BwdReadoutShape<D>::NW * 64, 0, s>>>(a);
   else
     vda_bwd_token_kernel<T, D><<<nfr, 256, 0, s>>>(a);
   if (dgamma && a.dgp) vda_bwd_dgamma_kernel<<<D, 256, 0, s>>>(a.dgp, (long long)BH * g.F, D, dgamma);

@@ -293,9 +293,9 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernels (D = 64, 128; N % 16 == 0) with fp32 accumulation: dQ on
 // v_mfma_f32_32x32x16_bf16, dK and dV on v_mfma_f32_16x16x32_bf16 (below).
-// Tiles are staged global -> registers -> LDS one tile
-// ahead with one workgroup barrier per tile; rows past a span's end read as
-// zero through the buffer descriptors.
+// Tiles are staged global -> registers -> LDS (dQ: requested two tiles
+// ahead; dK, dV: one) with one workgroup barrier per tile; rows past a
+// span's end read as zero through the buffer descriptors.
 //
 // dQ (query-stationary, 8 waves x 32 queries): per 32-key block
 //   S^T  = K Q^T        (A: K rows from LDS, B: the wave's Q fragments)
@@ -313,7 +313,6 @@ struct BwdArgs {
   const bf16_t* k;
   const bf16_t* v;
   const bf16_t* dO;     // g_s * dOhat, [B,H,L,D]
-  const bf16_t* kt;     // K^T  [B,H,D,L]
   const bf16_t* qt;     // Q^T  [B,H,D,L]
   const bf16_t* dOt;    // dO^T [B,H,D,L]
   const float* lse;     // [B,H,L], natural log
@@ -321,15 +320,12 @@ struct BwdArgs {
   bf16_t* dq;
   bf16_t* dk;
   bf16_t* dv;
-  // text keys (g.Ts > 0): k_text, v_text [B,H,Ts,D], their transpose
-  // [B,H,D,Tp] (Tp = Ts rounded up to 16, zero columns past Ts) and the
-  // gradients dk_text, dv_text [B,H,Ts,D]
+  // text keys (g.Ts > 0): k_text, v_text [B,H,Ts,D] and the gradients
+  // dk_text, dv_text [B,H,Ts,D]
   const bf16_t* k_text;
   const bf16_t* v_text;
-  const bf16_t* ktt;
   bf16_t* dk_text;
   bf16_t* dv_text;
-  int tpitch;           // Tp
   int ntext;            // leading workgroups of the dK/dV kernel that take text keys
   float scale, scale_log2;
 };
@@ -342,13 +338,12 @@ constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per st
 template <int D, bool TEXT>
 __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArgs a) {
   constexpr int NT = kBwdQW * 64, BQ = kBwdQW * 32, BK = kBwdBK;
-  constexpr int KP = D + 8, TP = BK + 8;
+  constexpr int KP = D + 8;
   constexpr int NKK = D / 16, NDB = D / 32, NB = BK / 32;
-  constexpr int RCH = BK * D / 8 / NT, TCH = D * BK / 8 / NT;   // 16-byte chunks per thread
-  static_assert(RCH * NT * 8 == BK * D && TCH * NT * 8 == D * BK, "tile split");
+  constexpr int RCH = BK * D / 8 / NT;   // 16-byte chunks per thread
+  static_assert(RCH * NT * 8 == BK * D, "tile split");
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BK * KP];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][BK * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Kts[2][D * TP];
   const Geometry& g = a.g;
   Item it;
   int q0;
@@ -358,12 +353,10 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
   const size_t hb = (size_t)it.bh * L * D;
   const bf16_t* K = a.k + hb;
   const bf16_t* V = a.v + hb;
-  const bf16_t* Kt = a.kt + hb;
   // text keys (walk positions from L on)
   const size_t hbt = TEXT ? (size_t)it.bh * g.Ts * D : 0;
   const bf16_t* KT = TEXT ? a.k_text + hbt : nullptr;
   const bf16_t* VT = TEXT ? a.v_text + hbt : nullptr;
-  const bf16_t* KTt = TEXT ? a.ktt + (size_t)it.bh * D * a.tpitch : nullptr;
   const int qrow = q0 + wave * 32 + l32;
   const bool qvalid = qrow < it.q_end;
   bf16x8 qf[NKK], df[NKK];
@@ -383,18 +376,14 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
 #pragma unroll
   for (int b = 0; b < NDB; ++b) acc[b] = f32x16{};
   const SpanWalk<BK, TEXT ? 4 : 3> walk(it);
-  const uint32_t kt_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
-  u32x4 cr[2 * RCH + TCH];
-  auto load_tile = [&](int j) {
+  u32x4 cA[2 * RCH], cB[2 * RCH];   // staging registers of even / odd tiles
+  auto load_tile = [&](u32x4* cr, int j) {
     int ks, nk;
     walk.tile(j, ks, nk);
     const bool tx = TEXT && ks >= L;
     const int kr = tx ? ks - (int)L : ks;                // row in its own key array
-    const long long pitch = tx ? a.tpitch : L;           // row pitch of the transposed keys
     const rsrc_t rk = make_rsrc((tx ? KT : K) + (size_t)kr * D, (uint32_t)nk * D * 2);
     const rsrc_t rv = make_rsrc((tx ? VT : V) + (size_t)kr * D, (uint32_t)nk * D * 2);
-    const rsrc_t rt = tx ? make_rsrc(KTt + kr, (uint32_t)(D * pitch - kr) * 2)
-                         : make_rsrc(Kt + ks, kt_bytes - (uint32_t)ks * 2);
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = tid + NT * i;
@@ -402,14 +391,8 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
       cr[i] = buf_ld16(rk, off);
       cr[RCH + i] = buf_ld16(rv, off);
     }
-#pragma unroll
-    for (int i = 0; i < TCH; ++i) {
-      const int c = tid + NT * i;
-      const int r = c / (BK / 8), c8 = c % (BK / 8);
-      cr[2 * RCH + i] = buf_ld16(rt, c8 * 8 < nk ? (uint32_t)(r * pitch + c8 * 8) * 2 : 0x80000000u);
-    }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const u32x4* cr, int buf) {
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = tid + NT * i;
@@ -417,26 +400,29 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
       st16(&Ks[buf][off], cr[i]);
       st16(&Vs[buf][off], cr[RCH + i]);
     }
-#pragma unroll
-    for (int i = 0; i < TCH; ++i) {
-      const int c = tid + NT * i;
-      st16(&Kts[buf][(c / (BK / 8)) * TP + (c % (BK / 8)) * 8], cr[2 * RCH + i]);
-    }
   };
+  // K^T operands of dQ^T += K^T dS^T come from the K rows through the
+  // transposing read: lane group g takes rows d = 32 b + 16 (g % 2) + 0..15
+  // and the keys 16 (g / 2) + 8 h2 + 0..7 of the block, four a read
+  const int grp = lane >> 4, sl = lane & 15;
+  const int kt_off = (16 * (grp >> 1) + (sl >> 2)) * KP + 16 * (grp & 1) + 4 * (sl & 3);
   const int rperm = key_perm(l32);
+  // tiles are requested two ahead of their LDS store: tile j + 2 into the
+  // register set of its parity at the start of tile j, tile j + 1 (requested
+  // a tile earlier) stored at its end
   if (walk.n > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_tile(cA, 0);
+    store_tile(cA, 0);
   }
+  if (walk.n > 1) load_tile(cB, 1);
   __syncthreads();
-  for (int j = 0; j < walk.n; ++j) {
+  auto tile_body = [&](int j, u32x4* c_next, u32x4* c_far) {
     const int buf = j & 1;
     int ks, nk;
     walk.tile(j, ks, nk);
-    if (j + 1 < walk.n) load_tile(j + 1);
+    if (j + 2 < walk.n) load_tile(c_far, j + 2);
     const bf16_t* Kb = Ks[buf];
     const bf16_t* Vb = Vs[buf];
-    const bf16_t* Tb = Kts[buf];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x16 s = {}, dp = {};
@@ -460,12 +446,17 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int b = 0; b < NDB; ++b) {
-          const bf16x8 kf = as_bf16x8(ld16(Tb + (b * 32 + l32) * TP + blk * 32 + hg * 16 + h2 * 8));
-          acc[b] = mfma32x32x16(kf, pb[h2], acc[b]);
+          const bf16_t* kp = Kb + (blk * 32 + 8 * h2) * KP + b * 32 + kt_off;
+          const u32x2 k0 = lds_read_tr16(kp), k1 = lds_read_tr16(kp + 4 * KP);
+          acc[b] = mfma32x32x16(as_bf16x8(u32x4{k0[0], k0[1], k1[0], k1[1]}), pb[h2], acc[b]);
         }
     }
-    if (j + 1 < walk.n) store_tile(buf ^ 1);
+    if (j + 1 < walk.n) store_tile(c_next, buf ^ 1);
     __syncthreads();
+  };
+  for (int j = 0; j < walk.n; j += 2) {
+    tile_body(j, cB, cA);
+    if (j + 1 < walk.n) tile_body(j + 1, cA, cB);
   }
   if (!qvalid) return;
   bf16_t* orow = a.dq + hb + (size_t)qrow * D;
@@ -735,19 +726,18 @@ bool softmax_bwd_mfma_ok(const Geometry& g) {
 }
 
 hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
-                                   const uint16_t* v, const uint16_t* do_hm, const uint16_t* kt,
+                                   const uint16_t* v, const uint16_t* do_hm,
                                    const uint16_t* qt, const uint16_t* dot, const float* lse,
                                    const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                                    const SoftmaxBwdText& tx, float scale, hipStream_t s) {
-  if (g.Ts > 0 && (!tx.k_text || !tx.v_text || !tx.ktt || !tx.dk_text || !tx.dv_text ||
-                   tx.tpitch < (g.Ts + 15) / 16 * 16))
+  if (g.Ts > 0 && (!tx.k_text || !tx.v_text || !tx.dk_text || !tx.dv_text))
     return hipErrorInvalidValue;
   BwdArgs a;
   a.g = g;
-  a.q = q; a.k = k; a.v = v; a.dO = do_hm; a.kt = kt; a.qt = qt; a.dOt = dot;
+  a.q = q; a.k = k; a.v = v; a.dO = do_hm; a.qt = qt; a.dOt = dot;
   a.lse = lse; a.Dq = Dq; a.dq = dq; a.dk = dk; a.dv = dv;
-  a.k_text = (const bf16_t*)tx.k_text; a.v_text = (const bf16_t*)tx.v_text; a.ktt = tx.ktt;
-  a.dk_text = (bf16_t*)tx.dk_text; a.dv_text = (bf16_t*)tx.dv_text; a.tpitch = tx.tpitch;
+  a.k_text = (const bf16_t*)tx.k_text; a.v_text = (const bf16_t*)tx.v_text;
+  a.dk_text = (bf16_t*)tx.dk_text; a.dv_text = (bf16_t*)tx.dv_text;
   a.ntext = 0;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;

@@ -125,13 +125,10 @@ Layout make_layout(const vdn::Geometry& g, int Dm, vdn_dtype dt, bool mx, Entry 
 }
 
 // Workspace of the Softmax backward: g_s * dOhat in head-major order, Dq,
-// and on the MFMA path K^T, Q^T and dO^T.
+// and on the MFMA path Q^T and dO^T.
 struct BwdLayout {
-  size_t dohm, Dq, kt, qt, dot, ktt, total;
+  size_t dohm, Dq, qt, dot, total;
 };
-
-// Row pitch of the transposed text keys of the Softmax backward.
-long long bwd_text_pitch(const vdn::Geometry& g) { return ((long long)g.Ts + 15) / 16 * 16; }
 
 BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
   const size_t es = dt == VDN_BF16 ? 2 : 4;
@@ -142,10 +139,8 @@ BwdLayout bwd_layout(const vdn::Geometry& g, vdn_dtype dt) {
   l.dohm = take(rows * g.D * es);
   l.Dq = take(rows * 4);
   const bool mf = dt == VDN_BF16 && vdn::softmax_bwd_mfma_ok(g);
-  l.kt = take(mf ? rows * g.D * es : 0);
   l.qt = take(mf ? rows * g.D * es : 0);
   l.dot = take(mf ? rows * g.D * es : 0);
-  l.ktt = take(mf && g.Ts > 0 ? (size_t)g.B * g.H * g.D * bwd_text_pitch(g) * es : 0);
   l.total = o;
   return l;
 }
@@ -906,23 +901,13 @@ vdn_status vdn_window_softmax_bwd(const void* q, const void* k, const void* v, c
                                                    dohm, Dq, dg_s, s));
     if (vdn::softmax_bwd_mfma_ok(g)) {
       const long long BH = (long long)g.B * g.H;
-      uint16_t* kt = (uint16_t*)(ws + lay.kt);
       uint16_t* qt = (uint16_t*)(ws + lay.qt);
       uint16_t* dot = (uint16_t*)(ws + lay.dot);
-      VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)k, kt, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
       VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)q, qt, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
       VDN_HIP(vdn::launch_transpose_bf16(dohm, dot, g.L, g.L, g.D, g.L, g.L * g.D, BH, s));
-      if (g.Ts > 0) {
-        uint16_t* ktt = (uint16_t*)(ws + lay.ktt);
-        const long long Tp = bwd_text_pitch(g);
-        VDN_HIP(vdn::launch_transpose_bf16((const uint16_t*)k_text, ktt, Tp, g.Ts, g.D, Tp, Tp * g.D,
-                                           BH, s));
-        tx.ktt = ktt;
-        tx.tpitch = (int)Tp;
-      }
       VDN_HIP(timer_mark(s, true));
       VDN_HIP(vdn::launch_softmax_bwd_mfma(g, (const uint16_t*)q, (const uint16_t*)k,
-                                           (const uint16_t*)v, dohm, kt, qt, dot, lse, Dq,
+                                           (const uint16_t*)v, dohm, qt, dot, lse, Dq,
                                            (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, tx, sc, s));
       VDN_HIP(timer_mark(s, false));
     } else {

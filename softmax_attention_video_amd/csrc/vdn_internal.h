@@ -144,15 +144,12 @@ hipError_t launch_softmax_bwd_prep(const Geometry& g, const T* o, const T* dout,
                                    T* do_hm, float* Dq, float* dg, hipStream_t s);
 // Text keys of the backward (g.Ts > 0): k_text, v_text [B,H,Ts,D] (storage
 // type of the call) are keys of every query; dk_text, dv_text [B,H,Ts,D]
-// receive their gradients.  The MFMA path also reads ktt = k_text^T
-// [B,H,D,tpitch], tpitch >= Ts rounded up to 16, zero columns past Ts.
+// receive their gradients.
 struct SoftmaxBwdText {
   const void* k_text = nullptr;
   const void* v_text = nullptr;
-  const uint16_t* ktt = nullptr;
   void* dk_text = nullptr;
   void* dv_text = nullptr;
-  int tpitch = 0;
 };
 // q, k, v, do_hm [B,H,L,D]; lse, Dq [B,H,L]; dq, dk, dv [B,H,L,D].
 template <typename T>
@@ -160,11 +157,10 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
                                    const T* do_hm, const float* lse, const float* Dq, T* dq, T* dk,
                                    T* dv, const SoftmaxBwdText& tx, float scale, hipStream_t s);
 
-// bf16 MFMA path (D = 64, 128; N % 16 == 0): kt, qt, dot = K^T, Q^T, dO^T [B,H,D,L].
+// bf16 MFMA path (D = 64, 128; N % 16 == 0): qt, dot = Q^T, dO^T [B,H,D,L].
 bool softmax_bwd_mfma_ok(const Geometry& g);
 hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
-                                   const uint16_t* v, const uint16_t* do_hm, const uint16_t* kt,
-                                   const uint16_t* qt, const uint16_t* dot, const float* lse,
+                                   const uint16_t* v, const uint16_t* do_hm, const uint16_t* qt, const uint16_t* dot, const float* lse,
                                    const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                                    const SoftmaxBwdText& tx, float scale, hipStream_t s);
 

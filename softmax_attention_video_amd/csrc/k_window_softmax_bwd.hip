@@ -313,8 +313,6 @@ struct BwdArgs {
   const bf16_t* k;
   const bf16_t* v;
   const bf16_t* dO;     // g_s * dOhat, [B,H,L,D]
-  const bf16_t* qt;     // Q^T  [B,H,D,L]
-  const bf16_t* dOt;    // dO^T [B,H,D,L]
   const float* lse;     // [B,H,L], natural log
   const float* Dq;      // [B,H,L]
   bf16_t* dq;
@@ -491,24 +489,22 @@ constexpr int kBwdFW = 8;          // fused dK / dV kernel: waves, 16 keys each
 //   dV^T += dO^T P,  dK^T += Q^T dS   (A: dO^T / Q^T rows from LDS, B: P / dS)
 // A lane of S holds one key and the queries 16 r + 4 (l / 16) + i of row
 // tile r = 0, 1; taken in that order as the eight contraction slots of the
-// accumulation they are its B operand directly, and the transposed tiles are
-// stored with each block's columns in the same order (two 8-byte pieces per
-// staged 16-byte chunk), so the A operand is one 16-byte read per lane.
+// accumulation they are its B operand directly, and the A operand (dO^T or
+// Q^T rows) comes from the staged row tiles with two transposing reads of
+// four queries each (16 r + 4 (l / 16) + 0..3).
 template <int D>
 __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs a) {
   constexpr int NT = kBwdFW * 64, BKEY = kBwdFW * 16, BQ = kBwdBK;
   // row pitches of 32 bytes times an odd number: the 32 lanes that one LDS
   // cycle serves (16 rows, two 16-byte column groups) then cover all banks
-  constexpr int KP = D + 16, TP = BQ + 16;
-  static_assert((KP * 2 / 32) % 2 == 1 && (TP * 2 / 32) % 2 == 1, "row pitch");
+  constexpr int KP = D + 16;
+  static_assert((KP * 2 / 32) % 2 == 1, "row pitch");
   constexpr int NKS = D / 32, NDT = D / 16, NB = BQ / 32;
-  constexpr int RCH = BQ * D / 8 / NT, TCH = D * BQ / 8 / NT;
-  static_assert(RCH * NT * 8 == BQ * D && TCH * NT * 8 == D * BQ, "tile split");
+  constexpr int RCH = BQ * D / 8 / NT;
+  static_assert(RCH * NT * 8 == BQ * D, "tile split");
   static_assert(NB == 2, "two query blocks per tile");
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * KP];
   __shared__ __attribute__((aligned(16))) bf16_t Ds[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[2][D * TP];
-  __shared__ __attribute__((aligned(16))) bf16_t Dt[2][D * TP];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Dd[2][BQ];
   const Geometry& g = a.g;
@@ -527,8 +523,6 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
   bf16_t* dVk = text ? a.dv_text : a.dv;
   const bf16_t* Q = a.q + hb;
   const bf16_t* dO = a.dO + hb;
-  const bf16_t* QT = a.qt + hb;
-  const bf16_t* dOT = a.dOt + hb;
   const float* lse = a.lse + (size_t)it.bh * L;
   const float* Dq = a.Dq + (size_t)it.bh * L;
   const int krow = k0 + wave * 16 + l16;
@@ -551,8 +545,7 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
     accV[t] = f32x4{};
   }
   const SpanWalk<BQ, 3> walk(it);
-  const uint32_t t_bytes = (uint32_t)min((long long)D * L * 2, 0x7FFFFFF0ll);
-  u32x4 c0r[2 * RCH], c1r[2 * TCH];
+  u32x4 c0r[2 * RCH];
   float cl = 0.f, cd = 0.f;
   auto load_piece0 = [&](int j) {      // Q and dO rows
     int qs, nq;
@@ -576,39 +569,15 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
       st16(&Ds[buf][off], c0r[RCH + i]);
     }
   };
-  auto load_piece1 = [&](int j) {      // Q^T and dO^T, lse and Dq
+  auto load_piece1 = [&](int j) {      // lse and Dq
     int qs, nq;
     walk.tile(j, qs, nq);
-    const rsrc_t rt = make_rsrc(QT + qs, t_bytes - (uint32_t)qs * 2);
-    const rsrc_t ru = make_rsrc(dOT + qs, t_bytes - (uint32_t)qs * 2);
-#pragma unroll
-    for (int i = 0; i < TCH; ++i) {
-      const int c = tid + NT * i;
-      const int r = c / (BQ / 8), c8 = c % (BQ / 8);
-      const uint32_t off = c8 * 8 < nq ? (uint32_t)(r * L + c8 * 8) * 2 : 0x80000000u;
-      c1r[i] = buf_ld16(rt, off);
-      c1r[TCH + i] = buf_ld16(ru, off);
-    }
     if (tid < BQ) {
       cl = tid < nq ? lse[qs + tid] * kLog2e : INFINITY;
       cd = tid < nq ? Dq[qs + tid] : 0.f;
     }
   };
-  // a staged chunk holds queries 8 m .. 8 m + 7 of a block (m = 0..3); its
-  // halves go to the slot positions 16 (m % 2) + 4 (m / 2) and that + 8
   auto store_piece1 = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < TCH; ++i) {
-      const int c = tid + NT * i;
-      const int r = c / (BQ / 8), c8 = c % (BQ / 8), m = c8 & 3;
-      const int p = r * TP + (c8 >> 2) * 32 + 16 * (m & 1) + 4 * (m >> 1);
-      const u32x2 lo = {c1r[i][0], c1r[i][1]}, hi = {c1r[i][2], c1r[i][3]};
-      *reinterpret_cast<u32x2*>(&Qt[buf][p]) = lo;
-      *reinterpret_cast<u32x2*>(&Qt[buf][p + 8]) = hi;
-      const u32x2 lo2 = {c1r[TCH + i][0], c1r[TCH + i][1]}, hi2 = {c1r[TCH + i][2], c1r[TCH + i][3]};
-      *reinterpret_cast<u32x2*>(&Dt[buf][p]) = lo2;
-      *reinterpret_cast<u32x2*>(&Dt[buf][p + 8]) = hi2;
-    }
     if (tid < BQ) {
       Ls[buf][tid] = cl;
       Dd[buf][tid] = cd;
@@ -645,12 +614,17 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
       }
     }
   };
+  // group lane l16 points at query row qb 32 + 4 grp + l16 / 4 (+ 16),
+  // channels 16 t + 4 (l16 % 4) .. + 3
+  const int tr_off = (4 * grp + (l16 >> 2)) * KP + 4 * (l16 & 3);
   auto accum = [&](int buf, int qb, const bf16x8& pb, const bf16x8& db) {
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
-      const int off = (16 * t + l16) * TP + qb * 32 + 8 * grp;
-      accV[t] = mfma16x16x32(as_bf16x8(ld16(&Dt[buf][off])), pb, accV[t]);
-      accK[t] = mfma16x16x32(as_bf16x8(ld16(&Qt[buf][off])), db, accK[t]);
+      const int off = qb * 32 * KP + 16 * t + tr_off;
+      const u32x2 d0 = lds_read_tr16(&Ds[buf][off]), d1 = lds_read_tr16(&Ds[buf][off + 16 * KP]);
+      const u32x2 q0 = lds_read_tr16(&Qs[buf][off]), q1 = lds_read_tr16(&Qs[buf][off + 16 * KP]);
+      accV[t] = mfma16x16x32(as_bf16x8(u32x4{d0[0], d0[1], d1[0], d1[1]}), pb, accV[t]);
+      accK[t] = mfma16x16x32(as_bf16x8(u32x4{q0[0], q0[1], q1[0], q1[1]}), db, accK[t]);
     }
   };
   if (walk.n > 0) {
@@ -694,13 +668,13 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
     }
 #pragma unroll
     for (int u = 0; u < 2 * NDT; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two transposing reads per product
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
 #pragma unroll
     for (int u = 0; u < 2 * NDT; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __syncthreads();
@@ -726,15 +700,14 @@ bool softmax_bwd_mfma_ok(const Geometry& g) {
 }
 
 hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
-                                   const uint16_t* v, const uint16_t* do_hm,
-                                   const uint16_t* qt, const uint16_t* dot, const float* lse,
+                                   const uint16_t* v, const uint16_t* do_hm, const float* lse,
                                    const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                                    const SoftmaxBwdText& tx, float scale, hipStream_t s) {
   if (g.Ts > 0 && (!tx.k_text || !tx.v_text || !tx.dk_text || !tx.dv_text))
     return hipErrorInvalidValue;
   BwdArgs a;
   a.g = g;
-  a.q = q; a.k = k; a.v = v; a.dO = do_hm; a.qt = qt; a.dOt = dot;
+  a.q = q; a.k = k; a.v = v; a.dO = do_hm;
   a.lse = lse; a.Dq = Dq; a.dq = dq; a.dk = dk; a.dv = dv;
   a.k_text = (const bf16_t*)tx.k_text; a.v_text = (const bf16_t*)tx.v_text;
   a.dk_text = (bf16_t*)tx.dk_text; a.dv_text = (bf16_t*)tx.dv_text;

@@ -157,10 +157,10 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
                                    const T* do_hm, const float* lse, const float* Dq, T* dq, T* dk,
                                    T* dv, const SoftmaxBwdText& tx, float scale, hipStream_t s);
 
-// bf16 MFMA path (D = 64, 128; N % 16 == 0): qt, dot = Q^T, dO^T [B,H,D,L].
+// bf16 MFMA path (D = 64, 128; N % 16 == 0).
 bool softmax_bwd_mfma_ok(const Geometry& g);
 hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const uint16_t* k,
-                                   const uint16_t* v, const uint16_t* do_hm, const uint16_t* qt, const uint16_t* dot, const float* lse,
+                                   const uint16_t* v, const uint16_t* do_hm, const float* lse,
                                    const float* Dq, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                                    const SoftmaxBwdText& tx, float scale, hipStream_t s);
 

@@ -170,23 +170,37 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
   const int bidx = bh / g.H, h = bh % g.H;
   const size_t tok0 = (size_t)bh * g.L + (size_t)t * g.N;
   // q fragments of the wave's next 32 tokens are requested while the
-  // current ones are multiplied
+  // current ones are multiplied.  Buffer loads over the frame's rows: tokens
+  // past the frame read as zeros, with no branch, so the wait counts stay
+  // exact (a load under a lane-dependent branch makes every wait after it a
+  // wait for all loads).
+  const rsrc_t qrs = make_rsrc(q + tok0 * D, (uint32_t)g.N * D * 2);
+  const rsrc_t grs = make_rsrc(g_l + (size_t)bh * g.L + (size_t)t * g.N, (uint32_t)g.N * 4);
   bf16x8 qf[NKK];
   auto load_q = [&](int n0, bf16x8* dst) {
-    const int n = n0 + l32;
+    const uint32_t off = (uint32_t)((n0 + l32) * D + hg * 8) * 2;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 v = {0, 0, 0, 0};
-      if (n < g.N) v = ld16(q + (tok0 + n) * D + kk * 16 + hg * 8);
-      dst[kk] = as_bf16x8(v);
-    }
+    for (int kk = 0; kk < NKK; ++kk) dst[kk] = as_bf16x8(buf_ld16(qrs, off + kk * 32));
   };
+  // the gate of the lane's token travels with its q fragments: a load issued
+  // and consumed in one step would wait for that step's prefetch as well
+  auto load_gate = [&](int n) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, (int)(n * 4), 0, 0));
+  };
+  // Steps alternate between two fragment sets, so the next step's loads are
+  // never copied (a copy at the end of a step would make the step wait for
+  // them); each step requests the step after next.
+  bf16x8 qb[NKK];
+  float gate_a = load_gate(wave * 32 + l32), gate_b = 0.f;
   load_q(wave * 32, qf);
-  for (int n0 = wave * 32; n0 < g.N; n0 += 128) {
+  auto step = [&](int n0, const bf16x8* cur, bf16x8* nxt, float gate_c, float& gate_nx) {
     const int n = n0 + l32;
     const bool valid = n < g.N;
-    bf16x8 qn[NKK];
-    load_q(n0 + 128, qn);
+    // M^T is read from LDS in every step: kept in registers for the frame it
+    // would take ~256 of them (one wave per SIMD), which this fence forbids
+    __asm__ volatile("" ::: "memory");
+    load_q(n0 + 128, nxt);
+    gate_nx = load_gate(n + 128);
     f32x16 o[NDB];
 #pragma unroll
     for (int b = 0; b < NDB; ++b) {
@@ -194,8 +208,8 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = (b * 32 + l32) * MP + kk * 16 + hg * 8;
-        o[b] = mfma32x32x16(as_bf16x8(ld16(&mh[off])), qf[kk], o[b]);
-        o[b] = mfma32x32x16(as_bf16x8(ld16(&ml[off])), qf[kk], o[b]);
+        o[b] = mfma32x32x16(as_bf16x8(ld16(&mh[off])), cur[kk], o[b]);
+        o[b] = mfma32x32x16(as_bf16x8(ld16(&ml[off])), cur[kk], o[b]);
       }
     }
     float ss = 0.f;
@@ -204,11 +218,9 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
 #pragma unroll
       for (int i = 0; i < 16; ++i) ss = fmaf(o[b][i], o[b][i], ss);
     ss = half_sum(ss);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = qn[kk];
-    if (!valid) continue;
+    if (!valid) return;
     const size_t l = (size_t)t * g.N + n;
-    const float sc = g_l[(size_t)bh * g.L + l] * rsqrtf(ss / (float)D + eps);
+    const float sc = gate_c * rsqrtf(ss / (float)D + eps);
     bf16_t* orow = out + (((size_t)bidx * g.L + l) * g.H + h) * D;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
@@ -220,6 +232,10 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
         pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc * gm[2], o[b][i4 * 4 + 3] * sc * gm[3]);
         *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * i4 + 4 * hg) = pk;
       }
+  };
+  for (int n0 = wave * 32; n0 < g.N; n0 += 256) {
+    step(n0, qf, qb, gate_a, gate_b);
+    if (n0 + 128 < g.N) step(n0 + 128, qb, qf, gate_b, gate_a);
   }
 }
 

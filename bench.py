@@ -317,7 +317,7 @@ def measure_bwd(cfg, t, reps: int = 3, text: bool = False) -> dict:
                 "algorithmic_flops": flops}
     return {"entry": "vdn_window_softmax_bwd (dq, dk, dv, dg_s)",
             "workload": f"{cfg.name}: Softmax branch backward, B={B} H={H} d={d} F={cfg.F} N={cfg.N}",
-            "ms": ms, "kernel": f"softmax_bwd_dq_mfma_kernel<{d}, false> + softmax_bwd_dkdv16_kernel<{d}>",
+            "ms": ms, "kernel": f"softmax_bwd_dq_mfma_kernel<{d}, false> + softmax_bwd_dkdv_mfma_kernel<{d}>",
             "kernel_ms": float(k_ms.mean()), "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flops": flops,
             "executed_mfma_flops": 1.4 * flops,

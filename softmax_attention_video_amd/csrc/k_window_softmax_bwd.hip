@@ -291,8 +291,8 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernels (D = 64, 128; N % 16 == 0) with fp32 accumulation: dQ on
-// v_mfma_f32_32x32x16_bf16, dK and dV on v_mfma_f32_16x16x32_bf16 (below).
+// bf16 MFMA kernels (D = 64, 128; N % 16 == 0) with fp32 accumulation on
+// v_mfma_f32_32x32x16_bf16.
 // Tiles are staged global -> registers -> LDS (dQ: requested two tiles
 // ahead; dK, dV: one) with one workgroup barrier per tile; rows past a
 // span's end read as zero through the buffer descriptors.
@@ -470,41 +470,38 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
     }
 }
 
-// v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies row l % 16 of A and
-// column l % 16 of B, each with contraction slots 8 (l / 16) .. 8 (l / 16) + 7;
-// the 16 x 16 result holds column l % 16, rows 4 (l / 16) .. 4 (l / 16) + 3.
-__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-constexpr int kBwdFW = 8;          // fused dK / dV kernel: waves, 16 keys each
-
-// dK and dV together (key-stationary: the item's frames are the keys, its
-// spans the queries that see them), one wave per 16 keys on
-// 16 x 16 x 32 products, so that S and dP are formed once for both
-// gradients (8 d flops per visible pair) and the wave's K and V fragments,
-// S, dP and both accumulators fit two waves per SIMD.  Per 32-query block:
-//   S  = Q K^T,  dP = dO V^T      (A: Q / dO rows from LDS, B: K / V fragments)
+// dK and dV together, one wave per 32 keys on 32 x 32 x 16 products (8
+// waves, 256 keys per workgroup, two waves per SIMD): each operand fragment
+// read from LDS then feeds a 32 x 32 block, half the LDS reads per flop of
+// 16-key waves.  Per 32-query block of a staged 64-query tile:
+//   S  = Q K^T,  dP = dO V^T      (A: Q / dO rows from LDS; B: the wave's K
+//                                  fragments in registers / its V rows in LDS)
 //   P = exp2(S scale log2e - lse log2e),  dS = P (dP - Dq)
-//   dV^T += dO^T P,  dK^T += Q^T dS   (A: dO^T / Q^T rows from LDS, B: P / dS)
-// A lane of S holds one key and the queries 16 r + 4 (l / 16) + i of row
-// tile r = 0, 1; taken in that order as the eight contraction slots of the
-// accumulation they are its B operand directly, and the A operand (dO^T or
-// Q^T rows) comes from the staged row tiles with two transposing reads of
-// four queries each (16 r + 4 (l / 16) + 0..3).
+//   dV^T += dO^T P,  dK^T += Q^T dS   (A: dO^T / Q^T from the row tiles by
+//                                      transposing reads; B: P / dS)
+// In S a lane holds one key (lane % 32) and the queries 8 a + 4 h + b of the
+// block (register 4 a + b, h = lane / 32).  Registers 8 s .. 8 s + 7 are the
+// eight contraction slots of k-step s of the accumulations; the matching A
+// operand is two transposing reads of four queries each, 16 s + 4 h + 0..3
+// and 16 s + 8 + 4 h + 0..3.  Row pitches (304 bytes at D = 128, 144 at 64)
+// keep both the 16-byte row reads of 32 rows and the transposing reads of
+// 8 rows x 64 bytes free of bank conflicts.
+constexpr int kBwdKW = 8;          // 32-key dK / dV kernel: waves
+// Operand read-ahead of the S / dP products and of the accumulations (in
+// steps); deeper read-ahead spills at D = 128.
+constexpr int kSdpAhead = 1;
+constexpr int kAccAhead = 1;
 template <int D>
-__global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs a) {
-  constexpr int NT = kBwdFW * 64, BKEY = kBwdFW * 16, BQ = kBwdBK;
-  // row pitches of 32 bytes times an odd number: the 32 lanes that one LDS
-  // cycle serves (16 rows, two 16-byte column groups) then cover all banks
-  constexpr int KP = D + 16;
-  static_assert((KP * 2 / 32) % 2 == 1, "row pitch");
-  constexpr int NKS = D / 32, NDT = D / 16, NB = BQ / 32;
+__global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
+  constexpr int NT = kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
+  constexpr int KP = D == 128 ? 152 : 72;
+  constexpr int NKK = D / 16, NDB = D / 32, NB = BQ / 32;
   constexpr int RCH = BQ * D / 8 / NT;
-  static_assert(RCH * NT * 8 == BQ * D, "tile split");
-  static_assert(NB == 2, "two query blocks per tile");
+  constexpr int VCH = 32 * D / 8 / 64;   // 16-byte chunks per lane of the wave's V rows
+  static_assert(RCH * NT * 8 == BQ * D && NB == 2, "tile split");
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * KP];
   __shared__ __attribute__((aligned(16))) bf16_t Ds[2][BQ * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vw[kBwdKW][32 * KP];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Dd[2][BQ];
   const Geometry& g = a.g;
@@ -512,10 +509,10 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
   int k0;
   bool text;
   if (!decode_key_item(g, a.w, BKEY, a.ntext, blockIdx.x, it, k0, text)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hg = lane >> 5, l32 = lane & 31;
+  const int grp = lane >> 4, l16 = lane & 15;
   const long long L = g.L;
   const size_t hb = (size_t)it.bh * L * D;
-  // the item's keys: video rows of this head, or its text keys
   const size_t hk = text ? (size_t)it.bh * g.Ts * D : hb;
   const bf16_t* Kk = text ? a.k_text : a.k;
   const bf16_t* Vk = text ? a.v_text : a.v;
@@ -525,24 +522,29 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
   const bf16_t* dO = a.dO + hb;
   const float* lse = a.lse + (size_t)it.bh * L;
   const float* Dq = a.Dq + (size_t)it.bh * L;
-  const int krow = k0 + wave * 16 + l16;
+  const int kw0 = k0 + wave * 32;   // the wave's first key
+  const int krow = kw0 + l32;
   const bool kvalid = krow < it.q_end;
-  bf16x8 kf[NKS], vf[NKS];
+  bf16x8 kf[NKK];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (kvalid) {
-      x = ld16(Kk + hk + (size_t)krow * D + ks * 32 + grp * 8);
-      y = ld16(Vk + hk + (size_t)krow * D + ks * 32 + grp * 8);
-    }
-    kf[ks] = as_bf16x8(x);
-    vf[ks] = as_bf16x8(y);
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 x = {0, 0, 0, 0};
+    if (kvalid) x = ld16(Kk + hk + (size_t)krow * D + kk * 16 + hg * 8);
+    kf[kk] = as_bf16x8(x);
   }
-  f32x4 accK[NDT], accV[NDT];
+  bf16_t* Vme = Vw[wave];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
-    accK[t] = f32x4{};
-    accV[t] = f32x4{};
+  for (int i = 0; i < VCH; ++i) {
+    const int c = lane + 64 * i, r = c / (D / 8), c8 = c % (D / 8);
+    u32x4 x = {0, 0, 0, 0};
+    if (kw0 + r < it.q_end) x = ld16(Vk + hk + (size_t)(kw0 + r) * D + c8 * 8);
+    st16(Vme + r * KP + c8 * 8, x);
+  }
+  f32x16 accK[NDB], accV[NDB];
+#pragma unroll
+  for (int t = 0; t < NDB; ++t) {
+    accK[t] = f32x16{};
+    accV[t] = f32x16{};
   }
   const SpanWalk<BQ, 3> walk(it);
   u32x4 c0r[2 * RCH];
@@ -583,48 +585,79 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
       Dd[buf][tid] = cd;
     }
   };
-  // S and dP of query block qb: row tile r holds queries qb 32 + 16 r + ...
-  auto sdp = [&](int buf, int qb, f32x4* sv, f32x4* dpv) {
+  // S and dP of query block qb.  The fragments of k-step kk + kSdpAhead are
+  // read while the products of k-step kk run.
+  auto sdp = [&](int buf, int qb, f32x16& sv, f32x16& dpv) {
+    sv = f32x16{};
+    dpv = f32x16{};
+    const bf16_t* qr = &Qs[buf][(qb * 32 + l32) * KP + hg * 8];
+    const bf16_t* dr = &Ds[buf][(qb * 32 + l32) * KP + hg * 8];
+    const bf16_t* vr = Vme + l32 * KP + hg * 8;
+    u32x4 fq[NKK], fd[NKK], fv[NKK];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      sv[r] = f32x4{};
-      dpv[r] = f32x4{};
-    }
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (kk == 0) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int off = (qb * 32 + r * 16 + l16) * KP + ks * 32 + grp * 8;
-        sv[r] = mfma16x16x32(as_bf16x8(ld16(&Qs[buf][off])), kf[ks], sv[r]);
-        dpv[r] = mfma16x16x32(as_bf16x8(ld16(&Ds[buf][off])), vf[ks], dpv[r]);
+        for (int u = 0; u < kSdpAhead; ++u) {
+          fq[u] = ld16(qr + u * 16);
+          fd[u] = ld16(dr + u * 16);
+          fv[u] = ld16(vr + u * 16);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 * kSdpAhead, 0);
       }
+      if (kk + kSdpAhead < NKK) {
+        fq[kk + kSdpAhead] = ld16(qr + (kk + kSdpAhead) * 16);
+        fd[kk + kSdpAhead] = ld16(dr + (kk + kSdpAhead) * 16);
+        fv[kk + kSdpAhead] = ld16(vr + (kk + kSdpAhead) * 16);
+      }
+      sv = mfma32x32x16(as_bf16x8(fq[kk]), kf[kk], sv);
+      dpv = mfma32x32x16(as_bf16x8(fd[kk]), as_bf16x8(fv[kk]), dpv);
+      if (kk + kSdpAhead < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
   };
-  // P and dS as bf16 operands, slot 4 r + i = query qb 32 + 16 r + 4 grp + i
-  auto probs = [&](int buf, int qb, const f32x4* sv, const f32x4* dpv, bf16x8& pb, bf16x8& db) {
+  // P and dS as bf16 operands: register r of S is query 8 (r / 4) + 4 hg + r % 4
+  auto probs = [&](int buf, int qb, const f32x16& sv, const f32x16& dpv, bf16x8* pb, bf16x8* db) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int q = qb * 32 + 16 * r + 4 * grp;
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int q = qb * 32 + 8 * a4 + 4 * hg;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][q]);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dd[buf][q]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pv = fast_exp2(fmaf(sv[r][e], a.scale_log2, -l4[e]));
-        pb[4 * r + e] = static_cast<__bf16>(pv);
-        db[4 * r + e] = static_cast<__bf16>(pv * (dpv[r][e] - d4[e]));
+        const int r = 4 * a4 + e;
+        const float pv = fast_exp2(fmaf(sv[r], a.scale_log2, -l4[e]));
+        pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
+        db[r >> 3][r & 7] = static_cast<__bf16>(pv * (dpv[r] - d4[e]));
       }
     }
   };
-  // group lane l16 points at query row qb 32 + 4 grp + l16 / 4 (+ 16),
-  // channels 16 t + 4 (l16 % 4) .. + 3
-  const int tr_off = (4 * grp + (l16 >> 2)) * KP + 4 * (l16 & 3);
-  auto accum = [&](int buf, int qb, const bf16x8& pb, const bf16x8& db) {
+  // transposing reads: group lane l16 points at query row 16 s + 4 (grp / 2)
+  // + l16 / 4 (+ 8) of the block, channels 32 t + 16 (grp % 2) + 4 (l16 % 4) .. + 3
+  const int tr_off = (4 * (grp >> 1) + (l16 >> 2)) * KP + 16 * (grp & 1) + 4 * (l16 & 3);
+  constexpr int NACC = 2 * NDB;   // accumulation steps (k-step st, row block t) per query block
+  // operands of accumulation step i = st NDB + t: dO^T and Q^T, two reads each
+  auto acc_frags = [&](int buf, int qb, int i, u32x2* f) {
+    const int st = i / NDB, t = i % NDB;
+    const int off = (qb * 32 + 16 * st) * KP + 32 * t + tr_off;
+    f[0] = lds_read_tr16(&Ds[buf][off]);
+    f[1] = lds_read_tr16(&Ds[buf][off + 8 * KP]);
+    f[2] = lds_read_tr16(&Qs[buf][off]);
+    f[3] = lds_read_tr16(&Qs[buf][off + 8 * KP]);
+  };
+  // The operands of step i + kAccAhead are read while step i runs.
+  auto accum = [&](int buf, int qb, const bf16x8* pb, const bf16x8* db) {
+    u32x2 f[NACC][4];
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-      const int off = qb * 32 * KP + 16 * t + tr_off;
-      const u32x2 d0 = lds_read_tr16(&Ds[buf][off]), d1 = lds_read_tr16(&Ds[buf][off + 16 * KP]);
-      const u32x2 q0 = lds_read_tr16(&Qs[buf][off]), q1 = lds_read_tr16(&Qs[buf][off + 16 * KP]);
-      accV[t] = mfma16x16x32(as_bf16x8(u32x4{d0[0], d0[1], d1[0], d1[1]}), pb, accV[t]);
-      accK[t] = mfma16x16x32(as_bf16x8(u32x4{q0[0], q0[1], q1[0], q1[1]}), db, accK[t]);
+    for (int i = 0; i < kAccAhead; ++i) acc_frags(buf, qb, i, f[i]);
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) {
+      if (i + kAccAhead < NACC) acc_frags(buf, qb, i + kAccAhead, f[i + kAccAhead]);
+      const int st = i / NDB, t = i % NDB;
+      accV[t] = mfma32x32x16(as_bf16x8(u32x4{f[i][0][0], f[i][0][1], f[i][1][0], f[i][1][1]}), pb[st], accV[t]);
+      accK[t] = mfma32x32x16(as_bf16x8(u32x4{f[i][2][0], f[i][2][1], f[i][3][0], f[i][3][1]}), db[st], accK[t]);
+      if (i + kAccAhead < NACC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   };
   if (walk.n > 0) {
@@ -636,63 +669,40 @@ __global__ __launch_bounds__(kBwdFW * 64) void softmax_bwd_dkdv16_kernel(BwdArgs
   __syncthreads();
   for (int j = 0; j < walk.n; ++j) {
     const int buf = j & 1;
-    // the next tile is requested now and stored at the end (into the buffer
-    // the last barrier released); the last tile restages itself there, which
-    // keeps the body one straight-line block for the issue order below
     const int jn = j + 1 < walk.n ? j + 1 : j;
     load_piece0(jn);
     load_piece1(jn);
-    f32x4 s0[2], d0[2], s1[2], d1[2];
-    bf16x8 p0, g0, p1, g1;
-    sdp(buf, 0, s0, d0);
-    sdp(buf, 1, s1, d1);
-    probs(buf, 0, s0, d0, p0, g0);
-    accum(buf, 0, p0, g0);
-    probs(buf, 1, s1, d1, p1, g1);
-    accum(buf, 1, p1, g1);
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      f32x16 sv, dpv;
+      bf16x8 pb[2], db[2];
+      sdp(buf, qb, sv, dpv);
+      __builtin_amdgcn_sched_barrier(0);
+      probs(buf, qb, sv, dpv, pb, db);
+      __builtin_amdgcn_sched_barrier(0);
+      accum(buf, qb, pb, db);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     store_piece0(buf ^ 1);
     store_piece1(buf ^ 1);
-    // issue order: block 0's S and dP; block 1's among block 0's
-    // probabilities; block 0's accumulation among block 1's probabilities;
-    // block 1's accumulation
-#pragma unroll
-    for (int u = 0; u < 4 * NKS; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 4 * NKS; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 2 * NDT; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two transposing reads per product
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 2 * NDT; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
     __syncthreads();
   }
   if (!kvalid) return;
   bf16_t* krk = dKk + hk + (size_t)krow * D;
   bf16_t* krv = dVk + hk + (size_t)krow * D;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
-    const int d = 16 * t + 4 * grp;
-    u32x2 pk, pv;
-    pk[0] = pack_bf16x2(accK[t][0] * a.scale, accK[t][1] * a.scale);
-    pk[1] = pack_bf16x2(accK[t][2] * a.scale, accK[t][3] * a.scale);
-    pv[0] = pack_bf16x2(accV[t][0], accV[t][1]);
-    pv[1] = pack_bf16x2(accV[t][2], accV[t][3]);
-    *reinterpret_cast<u32x2*>(krk + d) = pk;
-    *reinterpret_cast<u32x2*>(krv + d) = pv;
-  }
+  for (int t = 0; t < NDB; ++t)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = 32 * t + 8 * a4 + 4 * hg;
+      u32x2 pk, pv;
+      pk[0] = pack_bf16x2(accK[t][4 * a4 + 0] * a.scale, accK[t][4 * a4 + 1] * a.scale);
+      pk[1] = pack_bf16x2(accK[t][4 * a4 + 2] * a.scale, accK[t][4 * a4 + 3] * a.scale);
+      pv[0] = pack_bf16x2(accV[t][4 * a4 + 0], accV[t][4 * a4 + 1]);
+      pv[1] = pack_bf16x2(accV[t][4 * a4 + 2], accV[t][4 * a4 + 3]);
+      *reinterpret_cast<u32x2*>(krk + d) = pk;
+      *reinterpret_cast<u32x2*>(krv + d) = pv;
+    }
 }
 
 bool softmax_bwd_mfma_ok(const Geometry& g) {
@@ -716,19 +726,19 @@ hipError_t launch_softmax_bwd_mfma(const Geometry& g, const uint16_t* q, const u
   a.scale_log2 = scale * kLog2e;
   BwdArgs b = a;
   a.w = window_work(g, kBwdQW * 32);
-  b.w = window_work(g, kBwdFW * 16);
-  b.ntext = text_items_padded(g, kBwdFW * 16);
+  b.w = window_work(g, kBwdKW * 32);
+  b.ntext = text_items_padded(g, kBwdKW * 32);
   if (a.w.grid == 0) return hipSuccess;
   const unsigned gk = (unsigned)(b.ntext + b.w.grid);
   const bool tq = g.Ts > 0;
   if (g.D == 128) {
     if (tq) softmax_bwd_dq_mfma_kernel<128, true><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
     else softmax_bwd_dq_mfma_kernel<128, false><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv16_kernel<128><<<gk, kBwdFW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<128><<<gk, kBwdKW * 64, 0, s>>>(b);
   } else {
     if (tq) softmax_bwd_dq_mfma_kernel<64, true><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
     else softmax_bwd_dq_mfma_kernel<64, false><<<a.w.grid, kBwdQW * 64, 0, s>>>(a);
-    softmax_bwd_dkdv16_kernel<64><<<gk, kBwdFW * 64, 0, s>>>(b);
+    softmax_bwd_dkdv_mfma_kernel<64><<<gk, kBwdKW * 64, 0, s>>>(b);
   }
   return hipGetLastError();
 }

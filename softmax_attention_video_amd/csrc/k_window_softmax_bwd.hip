@@ -336,7 +336,13 @@ constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per st
 template <int D, bool TEXT>
 __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArgs a) {
   constexpr int NT = kBwdQW * 64, BQ = kBwdQW * 32, BK = kBwdBK;
-  constexpr int KP = D + 8;
+  // row pitch (elements): the 16-byte row reads of 32 rows and the
+  // transposing reads of 4 rows x 64 bytes per half-wave are free of bank
+  // conflicts (304 and 144 bytes)
+  constexpr int KP = D == 128 ? 152 : 72;
+  // operand read-ahead of the products, in steps (the text variant holds
+  // more registers and takes one)
+  constexpr int AH = TEXT ? 1 : 2;
   constexpr int NKK = D / 16, NDB = D / 32, NB = BK / 32;
   constexpr int RCH = BK * D / 8 / NT;   // 16-byte chunks per thread
   static_assert(RCH * NT * 8 == BK * D, "tile split");
@@ -423,14 +429,30 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
     const bf16_t* Vb = Vs[buf];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
+      // S^T and dP^T; the K and V fragments of k-step kk + AH are read while
+      // the products of k-step kk run
       f32x16 s = {}, dp = {};
       const bf16_t* kr = Kb + (blk * 32 + rperm) * KP + hg * 8;
       const bf16_t* vr = Vb + (blk * 32 + rperm) * KP + hg * 8;
+      u32x4 fk[NKK], fv[NKK];
+#pragma unroll
+      for (int kk = 0; kk < AH; ++kk) {
+        fk[kk] = ld16(kr + kk * 16);
+        fv[kk] = ld16(vr + kk * 16);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32x32x16(as_bf16x8(ld16(kr + kk * 16)), qf[kk], s);
-        dp = mfma32x32x16(as_bf16x8(ld16(vr + kk * 16)), df[kk], dp);
+        if (kk + AH < NKK) {
+          fk[kk + AH] = ld16(kr + (kk + AH) * 16);
+          fv[kk + AH] = ld16(vr + (kk + AH) * 16);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        s = mfma32x32x16(as_bf16x8(fk[kk]), qf[kk], s);
+        dp = mfma32x32x16(as_bf16x8(fv[kk]), df[kk], dp);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
       // video spans hold whole 16-key groups; the text span may end inside one
       const bool valid = blk * 32 + hg * 16 < nk;
       bf16x8 pb[2];
@@ -440,14 +462,32 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
         const float p = vk ? fast_exp2(fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
         pb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - dqv));
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // dQ^T += K^T dS^T, step i = h2 NDB + b; the operands of step i + AH
+      // are read while step i runs
+      constexpr int NS = 2 * NDB;
+      u32x2 ft[NS][2];
+      auto kt_frags = [&](int i) {
+        const int h2 = i / NDB, b = i % NDB;
+        const bf16_t* kp = Kb + (blk * 32 + 8 * h2) * KP + b * 32 + kt_off;
+        ft[i][0] = lds_read_tr16(kp);
+        ft[i][1] = lds_read_tr16(kp + 4 * KP);
+      };
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int i = 0; i < AH; ++i) kt_frags(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
 #pragma unroll
-        for (int b = 0; b < NDB; ++b) {
-          const bf16_t* kp = Kb + (blk * 32 + 8 * h2) * KP + b * 32 + kt_off;
-          const u32x2 k0 = lds_read_tr16(kp), k1 = lds_read_tr16(kp + 4 * KP);
-          acc[b] = mfma32x32x16(as_bf16x8(u32x4{k0[0], k0[1], k1[0], k1[1]}), pb[h2], acc[b]);
+      for (int i = 0; i < NS; ++i) {
+        if (i + AH < NS) {
+          kt_frags(i + AH);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+        const int h2 = i / NDB, b = i % NDB;
+        acc[b] = mfma32x32x16(as_bf16x8(u32x4{ft[i][0][0], ft[i][0][1], ft[i][1][0], ft[i][1][1]}),
+                              pb[h2], acc[b]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (j + 1 < walk.n) store_tile(c_next, buf ^ 1);
     __syncthreads();

@@ -278,7 +278,9 @@ template <int D>
 __global__ __launch_bounds__(BwdReadoutShape<D>::NW * 64) void vda_bwd_readout_mfma_kernel(VdaBwdArgs<bf16_t> a) {
   constexpr int NB = D / 32, NKK = D / 16, NW = BwdReadoutShape<D>::NW, NT = NW * 64;
   constexpr int SUBT = NW / NB, TPS = 32 * SUBT;   // token sub-tiles and tokens per step
-  constexpr int DP = D + 8;                        // pitch (bf16) of the row tiles
+  // pitch (bf16) of the row tiles: 16-byte reads of 32 rows and transposing
+  // reads of 4 rows x 64 bytes per half-wave are free of bank conflicts
+  constexpr int DP = D == 128 ? 152 : 72;
   constexpr int NGB = NB * NB / NW;                // G blocks per wave
   static_assert(NGB * NW == NB * NB && TPS == 64, "work split");
   // G goes through LDS in NPASS slices of RPP rows at the end of the frame,
@@ -1390,7 +1392,7 @@ template <int D>
 __global__ __launch_bounds__(BwdReadoutShape<D>::NW * 64) void vda_bwd_token_mfma_kernel(VdaBwdArgs<bf16_t> a) {
   constexpr int NB = D / 32, NKK = D / 16, NW = BwdReadoutShape<D>::NW, NT = NW * 64;
   constexpr int SUBT = NW / NB, TPS = 32 * SUBT;   // token sub-tiles and tokens per step
-  constexpr int MP = D + 1, DP = D + 8;
+  constexpr int MP = D + 1, DP = D == 128 ? 152 : 72;   // DP: as in the readout adjoint
   // region 0 holds dA (fp32) until dA_sym is formed, then dW hi + lo;
   // region 1 holds dA_sym hi + lo
   struct DaF32 {

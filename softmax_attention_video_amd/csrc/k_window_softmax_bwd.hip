@@ -301,10 +301,9 @@ hipError_t launch_softmax_bwd_simt(const Geometry& g, const T* q, const T* k, co
 //   S^T  = K Q^T        (A: K rows from LDS, B: the wave's Q fragments)
 //   dP^T = V dO^T       (A: V rows from LDS, B: the wave's dO fragments)
 //   dS^T = P^T (dP^T - Dq),  P^T = exp2(S^T scale log2e - lse log2e)
-//   dQ^T += K^T dS^T    (A: K^T rows from LDS, B: dS^T from registers)
-// K rows are loaded in key_perm order so a lane half holds 16 consecutive
-// keys of the block in register order, which is the B layout of the last
-// product; lse and Dq are per lane (one query per lane).
+//   dQ^T += K^T dS^T    (A: K^T by transposing reads of the K rows, B: dS^T
+//                        from registers)
+// lse and Dq are per lane (one query per lane).
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   Geometry g;
@@ -336,18 +335,20 @@ constexpr int kBwdBK = 64;         // keys per staged tile (dQ) / queries per st
 template <int D, bool TEXT>
 __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArgs a) {
   constexpr int NT = kBwdQW * 64, BQ = kBwdQW * 32, BK = kBwdBK;
-  // row pitch (elements): the 16-byte row reads of 32 rows and the
-  // transposing reads of 4 rows x 64 bytes per half-wave are free of bank
-  // conflicts (304 and 144 bytes)
-  constexpr int KP = D == 128 ? 152 : 72;
+  // tile row r starts at r (2 D + 64) + 16 (r / 8) bytes, which keeps the
+  // 16-byte row reads of 32 rows and the transposing reads of 8 consecutive
+  // rows x 64 bytes free of bank conflicts (as in the dK / dV kernel)
+  constexpr int KP = D + 32;
+  constexpr int TS = BK * KP + BK;   // tile size (elements)
+  auto rbase = [](int r) { return r * KP + (r >> 3) * 8; };
   // operand read-ahead of the products, in steps (the text variant holds
   // more registers and takes one)
   constexpr int AH = TEXT ? 1 : 2;
   constexpr int NKK = D / 16, NDB = D / 32, NB = BK / 32;
   constexpr int RCH = BK * D / 8 / NT;   // 16-byte chunks per thread
   static_assert(RCH * NT * 8 == BK * D, "tile split");
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BK * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][BK * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TS];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][TS];
   const Geometry& g = a.g;
   Item it;
   int q0;
@@ -400,17 +401,19 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = tid + NT * i;
-      const int off = (c / (D / 8)) * KP + (c % (D / 8)) * 8;
+      const int off = rbase(c / (D / 8)) + (c % (D / 8)) * 8;
       st16(&Ks[buf][off], cr[i]);
       st16(&Vs[buf][off], cr[RCH + i]);
     }
   };
-  // K^T operands of dQ^T += K^T dS^T come from the K rows through the
-  // transposing read: lane group g takes rows d = 32 b + 16 (g % 2) + 0..15
-  // and the keys 16 (g / 2) + 8 h2 + 0..7 of the block, four a read
+  // In S^T a lane holds one query (lane % 32) and the keys 8 a + 4 hg + b of
+  // the block (register 4 a + b); registers 8 h2 .. 8 h2 + 7 are the slots of
+  // k-step h2 of dQ^T += K^T dS^T, whose K^T operand comes from the K rows
+  // through the transposing read: lane group g takes rows d = 32 b + 16 (g %
+  // 2) + 0..15 and the keys 16 h2 + 8 e + 4 (g / 2) + 0..3 of the block (e =
+  // 0, 1: the two reads)
   const int grp = lane >> 4, sl = lane & 15;
-  const int kt_off = (16 * (grp >> 1) + (sl >> 2)) * KP + 16 * (grp & 1) + 4 * (sl & 3);
-  const int rperm = key_perm(l32);
+  const int kt_off = (4 * (grp >> 1) + (sl >> 2)) * KP + 16 * (grp & 1) + 4 * (sl & 3);
   // tiles are requested two ahead of their LDS store: tile j + 2 into the
   // register set of its parity at the start of tile j, tile j + 1 (requested
   // a tile earlier) stored at its end
@@ -432,8 +435,8 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
       // S^T and dP^T; the K and V fragments of k-step kk + AH are read while
       // the products of k-step kk run
       f32x16 s = {}, dp = {};
-      const bf16_t* kr = Kb + (blk * 32 + rperm) * KP + hg * 8;
-      const bf16_t* vr = Vb + (blk * 32 + rperm) * KP + hg * 8;
+      const bf16_t* kr = Kb + rbase(blk * 32 + l32) + hg * 8;
+      const bf16_t* vr = Vb + rbase(blk * 32 + l32) + hg * 8;
       u32x4 fk[NKK], fv[NKK];
 #pragma unroll
       for (int kk = 0; kk < AH; ++kk) {
@@ -453,14 +456,22 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // video spans hold whole 16-key groups; the text span may end inside one
-      const bool valid = blk * 32 + hg * 16 < nk;
+      // keys past the tile's valid ones (a partial last block) get P = 0
+      const int nvb = nk - blk * 32;
       bf16x8 pb[2];
+      if (nvb >= 32) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool vk = TEXT ? blk * 32 + hg * 16 + i < nk : valid;
-        const float p = vk ? fast_exp2(fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
-        pb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - dqv));
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
+          pb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - dqv));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool vk = 8 * (i >> 2) + 4 * hg + (i & 3) < nvb;
+          const float p = vk ? fast_exp2(fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
+          pb[i >> 3][i & 7] = static_cast<__bf16>(p * (dp[i] - dqv));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       // dQ^T += K^T dS^T, step i = h2 NDB + b; the operands of step i + AH
@@ -469,9 +480,8 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
       u32x2 ft[NS][2];
       auto kt_frags = [&](int i) {
         const int h2 = i / NDB, b = i % NDB;
-        const bf16_t* kp = Kb + (blk * 32 + 8 * h2) * KP + b * 32 + kt_off;
-        ft[i][0] = lds_read_tr16(kp);
-        ft[i][1] = lds_read_tr16(kp + 4 * KP);
+        ft[i][0] = lds_read_tr16(Kb + rbase(blk * 32 + 16 * h2) + b * 32 + kt_off);
+        ft[i][1] = lds_read_tr16(Kb + rbase(blk * 32 + 16 * h2 + 8) + b * 32 + kt_off);
       };
 #pragma unroll
       for (int i = 0; i < AH; ++i) kt_frags(i);
@@ -523,9 +533,14 @@ __global__ __launch_bounds__(kBwdQW * 64) void softmax_bwd_dq_mfma_kernel(BwdArg
 // block (register 4 a + b, h = lane / 32).  Registers 8 s .. 8 s + 7 are the
 // eight contraction slots of k-step s of the accumulations; the matching A
 // operand is two transposing reads of four queries each, 16 s + 4 h + 0..3
-// and 16 s + 8 + 4 h + 0..3.  Row pitches (304 bytes at D = 128, 144 at 64)
-// keep both the 16-byte row reads of 32 rows and the transposing reads of
-// 8 rows x 64 bytes free of bank conflicts.
+// and 16 s + 8 + 4 h + 0..3.
+// LDS banks: a transposing 8-byte read is served for all 64 lanes at once,
+// here 8 consecutive rows x 64 bytes, and a 16-byte row read per half-wave
+// (32 rows, one 16-byte chunk each).  Row r of the Q and dO tiles starts at
+// r (2 D + 64) + 16 (r / 8) bytes: 8 consecutive rows start in 8 different
+// 64-byte bank groups, and the 4 rows of a 32-row block that share one are
+// 16 bytes apart, so both reads are free of bank conflicts.  The wave's V
+// rows see only row reads (pitch 304 / 144 bytes).
 constexpr int kBwdKW = 8;          // 32-key dK / dV kernel: waves
 // Operand read-ahead of the S / dP products and of the accumulations (in
 // steps); deeper read-ahead spills at D = 128.
@@ -534,14 +549,17 @@ constexpr int kAccAhead = 1;
 template <int D>
 __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdArgs a) {
   constexpr int NT = kBwdKW * 64, BKEY = kBwdKW * 32, BQ = kBwdBK;
-  constexpr int KP = D == 128 ? 152 : 72;
+  constexpr int KP = D + 32;                 // Q / dO row tiles (elements), plus 8 per 8 rows
+  constexpr int VP = D == 128 ? 152 : 72;    // the wave's V rows
   constexpr int NKK = D / 16, NDB = D / 32, NB = BQ / 32;
   constexpr int RCH = BQ * D / 8 / NT;
   constexpr int VCH = 32 * D / 8 / 64;   // 16-byte chunks per lane of the wave's V rows
   static_assert(RCH * NT * 8 == BQ * D && NB == 2, "tile split");
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Ds[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vw[kBwdKW][32 * KP];
+  constexpr int TS = BQ * KP + BQ;           // tile size (elements)
+  auto rbase = [](int r) { return r * KP + (r >> 3) * 8; };   // start of tile row r
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][TS];
+  __shared__ __attribute__((aligned(16))) bf16_t Ds[2][TS];
+  __shared__ __attribute__((aligned(16))) bf16_t Vw[kBwdKW][32 * VP];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Dd[2][BQ];
   const Geometry& g = a.g;
@@ -578,7 +596,7 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
     const int c = lane + 64 * i, r = c / (D / 8), c8 = c % (D / 8);
     u32x4 x = {0, 0, 0, 0};
     if (kw0 + r < it.q_end) x = ld16(Vk + hk + (size_t)(kw0 + r) * D + c8 * 8);
-    st16(Vme + r * KP + c8 * 8, x);
+    st16(Vme + r * VP + c8 * 8, x);
   }
   f32x16 accK[NDB], accV[NDB];
 #pragma unroll
@@ -606,7 +624,7 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       const int c = tid + NT * i;
-      const int off = (c / (D / 8)) * KP + (c % (D / 8)) * 8;
+      const int off = rbase(c / (D / 8)) + (c % (D / 8)) * 8;
       st16(&Qs[buf][off], c0r[i]);
       st16(&Ds[buf][off], c0r[RCH + i]);
     }
@@ -630,24 +648,25 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
   auto sdp = [&](int buf, int qb, f32x16& sv, f32x16& dpv) {
     sv = f32x16{};
     dpv = f32x16{};
-    const bf16_t* qr = &Qs[buf][(qb * 32 + l32) * KP + hg * 8];
-    const bf16_t* dr = &Ds[buf][(qb * 32 + l32) * KP + hg * 8];
-    const bf16_t* vr = Vme + l32 * KP + hg * 8;
+    const bf16_t* qr = &Qs[buf][rbase(qb * 32 + l32) + hg * 8];
+    const bf16_t* dr = &Ds[buf][rbase(qb * 32 + l32) + hg * 8];
+    const bf16_t* vr = Vme + l32 * VP + hg * 8;
+    auto roff = [](int kk) { return kk * 16; };
     u32x4 fq[NKK], fd[NKK], fv[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       if (kk == 0) {
 #pragma unroll
         for (int u = 0; u < kSdpAhead; ++u) {
-          fq[u] = ld16(qr + u * 16);
-          fd[u] = ld16(dr + u * 16);
+          fq[u] = ld16(qr + roff(u));
+          fd[u] = ld16(dr + roff(u));
           fv[u] = ld16(vr + u * 16);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 3 * kSdpAhead, 0);
       }
       if (kk + kSdpAhead < NKK) {
-        fq[kk + kSdpAhead] = ld16(qr + (kk + kSdpAhead) * 16);
-        fd[kk + kSdpAhead] = ld16(dr + (kk + kSdpAhead) * 16);
+        fq[kk + kSdpAhead] = ld16(qr + roff(kk + kSdpAhead));
+        fd[kk + kSdpAhead] = ld16(dr + roff(kk + kSdpAhead));
         fv[kk + kSdpAhead] = ld16(vr + (kk + kSdpAhead) * 16);
       }
       sv = mfma32x32x16(as_bf16x8(fq[kk]), kf[kk], sv);
@@ -672,18 +691,20 @@ __global__ __launch_bounds__(kBwdKW * 64) void softmax_bwd_dkdv_mfma_kernel(BwdA
       }
     }
   };
-  // transposing reads: group lane l16 points at query row 16 s + 4 (grp / 2)
-  // + l16 / 4 (+ 8) of the block, channels 32 t + 16 (grp % 2) + 4 (l16 % 4) .. + 3
+  // transposing reads: group lane l16 points at query row 16 s + 8 e + 4 (grp
+  // / 2) + l16 / 4 of the block (e = 0, 1: the two reads), channels 32 t + 16
+  // (grp % 2) + 4 (l16 % 4) .. + 3
   const int tr_off = (4 * (grp >> 1) + (l16 >> 2)) * KP + 16 * (grp & 1) + 4 * (l16 & 3);
   constexpr int NACC = 2 * NDB;   // accumulation steps (k-step st, row block t) per query block
   // operands of accumulation step i = st NDB + t: dO^T and Q^T, two reads each
   auto acc_frags = [&](int buf, int qb, int i, u32x2* f) {
     const int st = i / NDB, t = i % NDB;
-    const int off = (qb * 32 + 16 * st) * KP + 32 * t + tr_off;
-    f[0] = lds_read_tr16(&Ds[buf][off]);
-    f[1] = lds_read_tr16(&Ds[buf][off + 8 * KP]);
-    f[2] = lds_read_tr16(&Qs[buf][off]);
-    f[3] = lds_read_tr16(&Qs[buf][off + 8 * KP]);
+    const int o0 = rbase(qb * 32 + 16 * st) + 32 * t + tr_off;
+    const int o1 = rbase(qb * 32 + 16 * st + 8) + 32 * t + tr_off;
+    f[0] = lds_read_tr16(&Ds[buf][o0]);
+    f[1] = lds_read_tr16(&Ds[buf][o1]);
+    f[2] = lds_read_tr16(&Qs[buf][o0]);
+    f[3] = lds_read_tr16(&Qs[buf][o1]);
   };
   // The operands of step i + kAccAhead are read while step i runs.
   auto accum = [&](int buf, int qb, const bf16x8* pb, const bf16x8* db) {

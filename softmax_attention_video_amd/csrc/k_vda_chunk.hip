@@ -226,23 +226,34 @@ __global__ __launch_bounds__(256 * kChainG) void vda_chain_mfma_kernel(Geometry 
     for (int j = 0; j < NK8; ++j)
       dst[j] = mw ? *reinterpret_cast<const f32x4*>(Lm + (size_t)mrow * D + 8 * j + 4 * hg) : f32x4{};
   };
-  if (nsteps > 0) load_left(L0, lf);
+  // the additive term's 32 x 32 block of this lane group, in accumulator
+  // layout; fetched one step ahead like the left factor
+  float af[16], anext[16];
+  auto load_add = [&](const float* Am, float (&dst)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      dst[i] = mw && Am ? Am[(size_t)(wave * 32 + mfma32_row(i, hg)) * D + col0 + l32] : 0.f;
+  };
+  if (nsteps > 0) {
+    load_left(L0, lf);
+    load_add(A0, af);
+  }
   for (int st = 0; st < nsteps; ++st) {
     const float* Lm = L0 + st * lstride;
-    if (st + 1 < nsteps) load_left(Lm + lstride, lnext);
+    if (st + 1 < nsteps) {
+      load_left(Lm + lstride, lnext);
+      load_add(A0 ? A0 + (st + 1) * lstride : nullptr, anext);
+    }
     __syncthreads();                      // Yt holds the current Y
     f32x16 acc = f32x16{};
     if (mw) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = af[i];
 #pragma unroll
       for (int j = 0; j < NK8; ++j) {
         const f32x4 yb = *reinterpret_cast<const f32x4*>(&Yt[l32 * YP + 8 * j + 4 * hg]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc = mfma32x32x2f32(lf[j][q], yb[q], acc);
-      }
-      if (A0) {
-        const float* Am = A0 + st * lstride;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] += Am[(size_t)(wave * 32 + mfma32_row(i, hg)) * D + col0 + l32];
       }
     }
     __syncthreads();                      // everyone has read the old Y
@@ -271,6 +282,8 @@ __global__ __launch_bounds__(256 * kChainG) void vda_chain_mfma_kernel(Geometry 
     }
 #pragma unroll
     for (int j = 0; j < NK8; ++j) lf[j] = lnext[j];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) af[i] = anext[i];
   }
   if (out_final && nsteps == 0) {   // single-frame chunk: the map itself
     __syncthreads();

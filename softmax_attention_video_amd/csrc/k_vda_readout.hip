@@ -95,14 +95,20 @@ __global__ __launch_bounds__(256) void vda_readout_simt_kernel(Geometry g, const
   }
 }
 
-// bf16 path (D = 64, 128): one workgroup per (b, h, query frame).  M_t is
-// built once in fp32, stored transposed in LDS as bf16 hi + lo parts, and
-// O_l^T = M^T Q^T runs on v_mfma_f32_32x32x16_bf16 (hi and lo products
-// accumulate in fp32, so M keeps ~16 extra mantissa bits).  A lane ends up
-// holding one token and half of its dv values: the RMS is an in-lane sum of
-// squares plus one exchange with lane ^ 32.
+// bf16 path (D = 64, 128): one workgroup of 8 waves per (b, h, query
+// frame).  M_t is built once in fp32, stored transposed in LDS as bf16 hi +
+// lo parts, and O_l^T = M^T Q^T runs on v_mfma_f32_32x32x16_bf16 (hi and lo
+// products accumulate in fp32, so M keeps ~16 extra mantissa bits: the
+// entries of M cancel in q M, and a single bf16 rounding of M is visible in
+// the output).  A lane ends up holding one token and half of its dv values:
+// the RMS is an in-lane sum of squares plus one exchange with lane ^ 32.
+// The normalised rows go through a per-wave LDS tile so that the stores
+// write whole d_v-rows of [B, L, H, d_v] (16 bytes per lane, consecutive
+// lanes along d_v): written straight from the MFMA layout, each store
+// instruction would touch 32 rows H * d_v * 2 bytes apart with 8 bytes each.
+constexpr int kReadoutNW = 8;   // waves per workgroup of the MFMA readout
 template <int D>
-__global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const bf16_t* __restrict__ q,
+__global__ __launch_bounds__(kReadoutNW * 64) void vda_readout_mfma_kernel(Geometry g, const bf16_t* __restrict__ q,
                                                                const float* __restrict__ alpha,
                                                                const float* __restrict__ P_fwd,
                                                                const float* __restrict__ P_rev,
@@ -111,8 +117,12 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
                                                                float eps, bf16_t* __restrict__ out) {
   constexpr int MP = D + 8;        // pitch of M^T (bf16)
   constexpr int NKK = D / 16, NDB = D / 32;
+  constexpr int OP = D + 8;        // pitch of the output tile (bf16)
+  constexpr int RPI = 64 / (D / 8);   // token rows per 16-byte-per-lane pass
+  constexpr int NT = kReadoutNW * 64, TSTEP = kReadoutNW * 32;
   __shared__ __attribute__((aligned(16))) bf16_t mh[D * MP];
   __shared__ __attribute__((aligned(16))) bf16_t ml[D * MP];
+  __shared__ __attribute__((aligned(16))) bf16_t ot[kReadoutNW][32 * OP];
   __shared__ float dfs[D], drs[D];
   __shared__ __attribute__((aligned(16))) float gms[D];
 
@@ -141,14 +151,14 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
     for (; f <= f1; ++f) d *= al[(size_t)f * D + k];
     (part == 0 ? dfs : drs)[k] = d;
   }
-  for (int k = tid; k < D; k += 256) gms[k] = gamma ? gamma[k] : 1.f;
+  for (int k = tid; k < D; k += NT) gms[k] = gamma ? gamma[k] : 1.f;
   __syncthreads();
   const size_t DD = (size_t)D * D;
   const float* pf = P_fwd + ((size_t)bh * (g.C + 1) + i_f) * DD;
   const float* pr = P_rev + ((size_t)bh * (g.C + 1) + i_r) * DD;
   // M^T as bf16 hi + lo: each thread forms a pair of rows k, k + 1 of M for
   // four columns and stores them as packed 32-bit pairs of M^T
-  for (int e = tid; e < (D / 2) * (D / 4); e += 256) {
+  for (int e = tid; e < (D / 2) * (D / 4); e += NT) {
     const int k = 2 * (e / (D / 4)), j0 = (e % (D / 4)) * 4;
     const f32x4 a0 = *reinterpret_cast<const f32x4*>(pf + (size_t)k * D + j0);
     const f32x4 a1 = *reinterpret_cast<const f32x4*>(pf + (size_t)(k + 1) * D + j0);
@@ -176,6 +186,11 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
   // wait for all loads).
   const rsrc_t qrs = make_rsrc(q + tok0 * D, (uint32_t)g.N * D * 2);
   const rsrc_t grs = make_rsrc(g_l + (size_t)bh * g.L + (size_t)t * g.N, (uint32_t)g.N * 4);
+  // the frame's rows of this head in [B, L, H, d_v]: row r at r * H * d_v;
+  // the descriptor ends after row N - 1, so stores of rows past it are dropped
+  const int HD = g.H * D;
+  const rsrc_t ors = make_rsrc(out + (((size_t)bidx * g.L + (size_t)t * g.N) * g.H + h) * D,
+                               (uint32_t)(((g.N - 1) * HD + D) * 2));
   bf16x8 qf[NKK];
   auto load_q = [&](int n0, bf16x8* dst) {
     const uint32_t off = (uint32_t)((n0 + l32) * D + hg * 8) * 2;
@@ -195,12 +210,11 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
   load_q(wave * 32, qf);
   auto step = [&](int n0, const bf16x8* cur, bf16x8* nxt, float gate_c, float& gate_nx) {
     const int n = n0 + l32;
-    const bool valid = n < g.N;
     // M^T is read from LDS in every step: kept in registers for the frame it
     // would take ~256 of them (one wave per SIMD), which this fence forbids
     __asm__ volatile("" ::: "memory");
-    load_q(n0 + 128, nxt);
-    gate_nx = load_gate(n + 128);
+    load_q(n0 + TSTEP, nxt);
+    gate_nx = load_gate(n + TSTEP);
     f32x16 o[NDB];
 #pragma unroll
     for (int b = 0; b < NDB; ++b) {
@@ -218,10 +232,9 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
 #pragma unroll
       for (int i = 0; i < 16; ++i) ss = fmaf(o[b][i], o[b][i], ss);
     ss = half_sum(ss);
-    if (!valid) return;
-    const size_t l = (size_t)t * g.N + n;
+    // tokens past the frame carry zeros (gate 0) and are not stored
     const float sc = gate_c * rsqrtf(ss / (float)D + eps);
-    bf16_t* orow = out + (((size_t)bidx * g.L + l) * g.H + h) * D;
+    bf16_t* tile = ot[wave];
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -230,12 +243,26 @@ __global__ __launch_bounds__(256) void vda_readout_mfma_kernel(Geometry g, const
         u32x2 pk;
         pk[0] = pack_bf16x2(o[b][i4 * 4 + 0] * sc * gm[0], o[b][i4 * 4 + 1] * sc * gm[1]);
         pk[1] = pack_bf16x2(o[b][i4 * 4 + 2] * sc * gm[2], o[b][i4 * 4 + 3] * sc * gm[3]);
-        *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * i4 + 4 * hg) = pk;
+        *reinterpret_cast<u32x2*>(&tile[l32 * OP + b * 32 + 8 * i4 + 4 * hg]) = pk;
       }
+    // the wave reads back whole token rows and stores 16 bytes per lane
+    // along d_v (a wave-scope fence orders the tile's writes and reads)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    u32x4 rows[32 / RPI];
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it)
+      rows[it] = ld16(&tile[(it * RPI + lane / (D / 8)) * OP + (lane % (D / 8)) * 8]);
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = n0 + it * RPI + lane / (D / 8);
+      __builtin_amdgcn_raw_buffer_store_b128(rows[it], ors, (int)((r * HD + (lane % (D / 8)) * 8) * 2), 0, 0);
+    }
   };
-  for (int n0 = wave * 32; n0 < g.N; n0 += 256) {
+  for (int n0 = wave * 32; n0 < g.N; n0 += 2 * TSTEP) {
     step(n0, qf, qb, gate_a, gate_b);
-    if (n0 + 128 < g.N) step(n0 + 128, qb, qf, gate_b, gate_a);
+    if (n0 + TSTEP < g.N) step(n0 + TSTEP, qb, qf, gate_b, gate_a);
   }
 }
 
@@ -259,11 +286,19 @@ hipError_t launch_vda_readout<bf16_t>(const Geometry& g, const bf16_t* q, const 
                                       const float* P_fwd, const float* P_rev, const float* g_l,
                                       const float* gamma, float eps, bf16_t* out, hipStream_t s) {
   const unsigned grid = (unsigned)(g.B * g.H * g.F);
+  // the MFMA kernel addresses one frame of all heads with 32-bit buffer offsets
+  const bool fits = (long long)g.N * g.H * g.D * 2 <= 0x7FFFFFF0ll;
   switch (g.D) {
     case 16: vda_readout_simt_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
     case 32: vda_readout_simt_kernel<bf16_t, 32><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
-    case 64: vda_readout_mfma_kernel<64><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
-    case 128: vda_readout_mfma_kernel<128><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out); break;
+    case 64:
+      if (fits) vda_readout_mfma_kernel<64><<<grid, kReadoutNW * 64, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out);
+      else vda_readout_simt_kernel<bf16_t, 64><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out);
+      break;
+    case 128:
+      if (fits) vda_readout_mfma_kernel<128><<<grid, kReadoutNW * 64, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out);
+      else vda_readout_simt_kernel<bf16_t, 128><<<grid, 256, 0, s>>>(g, q, alpha, P_fwd, P_rev, g_l, gamma, eps, out);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -11,8 +11,9 @@
 // once per call into the workspace, W^T [Dm, K]), 256 x 256 output tiles,
 // 64-deep K steps through double-buffered LDS with the next steps' global
 // loads in flight, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The
-// product is formed as out^T blocks so each lane owns 4 consecutive output
-// features of one token (8-byte stores).
+// product is formed as out^T blocks (each lane owns 4 consecutive output
+// features of one token); the finished tile is written through LDS as whole
+// row segments.
 #include "vdn_common.h"
 #include "vdn_internal.h"
 #include "gemm_nt.h"
@@ -55,8 +56,11 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
   constexpr int CH = BM * BK / 8 / 512;   // 16-byte chunks per thread per operand and K step (4)
   constexpr int NSUB = BK / 16;           // 16-deep MFMA steps per K step (4)
   static_assert(CH == NSUB, "one chunk of each operand staged per MFMA step");
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * P];
+  // buffer b: the A panel, then the W^T panel; after the K loop the whole
+  // array holds the output tile
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2][(BM + BN) * P];
+  auto As = [&](int b) { return &lds[b][0]; };
+  auto Bs = [&](int b) { return &lds[b][BM * P]; };
   // XCD-aware grouped order: XCD x owns row tiles [x rpx, (x+1) rpx) and walks
   // them in groups of kGroupRows rows, column by column inside a group.
   const int x = blockIdx.x % kNumXcd;
@@ -103,8 +107,8 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
     pb[i] = buf_ld16(second ? rb1 : rb0, voff[i], kb);
   };
   auto store_piece = [&](int i, int buf) {
-    st16(&As[buf][soff[i]], pa[i]);
-    st16(&Bs[buf][soff[i]], pb[i]);
+    st16(As(buf) + soff[i], pa[i]);
+    st16(Bs(buf) + soff[i], pb[i]);
   };
 #pragma unroll
   for (int i = 0; i < CH; ++i) load_piece(i, 0);
@@ -114,8 +118,8 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
   for (int i = 0; i < CH; ++i) load_piece(i, 1);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    const bf16_t* Ab = As[kt & 1] + (wm * 64 + l32) * P + hg * 8;
-    const bf16_t* Bb = Bs[kt & 1] + (wn * 128 + l32) * P + hg * 8;
+    const bf16_t* Ab = As(kt & 1) + (wm * 64 + l32) * P + hg * 8;
+    const bf16_t* Bb = Bs(kt & 1) + (wn * 128 + l32) * P + hg * 8;
     bf16x8 fm[2][2], fn[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) fm[0][i] = as_bf16x8(ld16(Ab + i * 32 * P));
@@ -154,21 +158,34 @@ __global__ __launch_bounds__(512) void merge_gemm_bf16_kernel(const bf16_t* __re
     }
     lds_barrier();
   }
+  // Epilogue: the 256 x 256 tile goes through LDS (the operand buffers are
+  // free after the K loop) and leaves as 512-byte row segments, 16 bytes per
+  // lane: from the MFMA layout each store would write 8 bytes into each of
+  // 32 rows D * 2 bytes apart.
+  constexpr int TP = BN + 8;   // tile pitch (bf16)
+  static_assert(BM * TP <= 2 * (BM + BN) * P, "output tile fits in the operand buffers");
+  bf16_t* tile = &lds[0][0];
+  __syncthreads();             // every wave is done with the operand tiles
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const long long m = m0 + wm * 64 + mb * 32 + l32;
-    if (m >= M) continue;
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int n = n0 + wn * 128 + nb * 32 + 8 * i4 + 4 * hg;
-        if (n >= N) continue;
         u32x2 pk;
         pk[0] = pack_bf16x2(acc[nb][mb][i4 * 4 + 0], acc[nb][mb][i4 * 4 + 1]);
         pk[1] = pack_bf16x2(acc[nb][mb][i4 * 4 + 2], acc[nb][mb][i4 * 4 + 3]);
-        *reinterpret_cast<u32x2*>(out + (size_t)m * N + n) = pk;
+        *reinterpret_cast<u32x2*>(&tile[(wm * 64 + mb * 32 + l32) * TP + wn * 128 + nb * 32 + 8 * i4 + 4 * hg]) = pk;
       }
+  __syncthreads();
+  const int c8 = (tid % (BN / 8)) * 8;
+  const bool col_ok = n0 + c8 < N;   // N % 8 == 0
+#pragma unroll 4
+  for (int it = 0; it < BM * (BN / 8) / 512; ++it) {
+    const int r = it * (512 / (BN / 8)) + tid / (BN / 8);
+    const long long m = m0 + r;
+    const u32x4 v = ld16(&tile[r * TP + c8]);
+    if (m < M && col_ok) st16(out + (size_t)m * N + n0 + c8, v);
   }
 }
 
@@ -176,6 +193,7 @@ hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const 
                                   const uint16_t* w1t, uint16_t* out, long long M, int K, int Dm,
                                   hipStream_t s) {
   if (M == 0 || Dm == 0) return hipSuccess;
+  if (Dm % 8 != 0) return hipErrorInvalidValue;   // 16-byte output rows
   const int tm = (int)((M + kGBM - 1) / kGBM), tn = (Dm + kGBN - 1) / kGBN;
   const int rpx = (tm + kNumXcd - 1) / kNumXcd;
   const int groups = (rpx + kGroupRows - 1) / kGroupRows;
@@ -188,6 +206,7 @@ hipError_t launch_merge_gemm_bf16(const uint16_t* a0, const uint16_t* a1, const 
 hipError_t launch_gemm_nt_bf16(const uint16_t* a, const uint16_t* bt, uint16_t* out, long long M,
                                long long Kc, int N, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (N % 8 != 0) return hipErrorInvalidValue;   // 16-byte output rows
   if (Kc % (2 * kGBK) != 0 || Kc / 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int K = (int)(Kc / 2);
   const int tm = (int)((M + kGBM - 1) / kGBM), tn = (N + kGBN - 1) / kGBN;

@@ -136,8 +136,11 @@ __global__ __launch_bounds__(256) void merge_gemm_mx_kernel(const uint8_t* __res
   constexpr int CH = BM * BK / 16 / 256;     // 16-byte chunks per thread per operand and K step (8)
   constexpr int NSUB = BK / 64;              // 64-deep MFMA steps per K step (2)
   constexpr int CPS = CH / NSUB;             // chunks per operand staged per MFMA step (2)
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * P];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * P];
+  // buffer b: the A panel, then the W^T panel; after the K loop the whole
+  // array holds the bf16 output tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * P];
+  auto As = [&](int b) { return &lds[b][0]; };
+  auto Bs = [&](int b) { return &lds[b][BM * P]; };
   const int x = blockIdx.x % kNumXcd;
   const int t = blockIdx.x / kNumXcd;
   const int gsz = kMxGroupRows * tiles_n;
@@ -187,8 +190,8 @@ __global__ __launch_bounds__(256) void merge_gemm_mx_kernel(const uint8_t* __res
     pb[i] = buf_ld16(rb, voff[i], kb);
   };
   auto store_piece = [&](int i, int buf) {
-    st16(&As[buf][soff[i]], pa[i]);
-    st16(&Bs[buf][soff[i]], pb[i]);
+    st16(As(buf) + soff[i], pa[i]);
+    st16(Bs(buf) + soff[i], pb[i]);
   };
   uint32_t sa[4], sb[4], sa_n[4], sb_n[4];
   auto load_scales = [&](uint32_t* da, uint32_t* db, int kt) {
@@ -211,8 +214,8 @@ __global__ __launch_bounds__(256) void merge_gemm_mx_kernel(const uint8_t* __res
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     load_scales(sa_n, sb_n, kt + 1);
-    const uint8_t* Ab = As[kt & 1] + (wm * 128 + l32) * P + hg * 16;
-    const uint8_t* Bb = Bs[kt & 1] + (wn * 128 + l32) * P + hg * 16;
+    const uint8_t* Ab = As(kt & 1) + (wm * 128 + l32) * P + hg * 16;
+    const uint8_t* Bb = Bs(kt & 1) + (wn * 128 + l32) * P + hg * 16;
     uint32_t ssa[4], ssb[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) ssa[mb] = sa[mb] >> (8 * hg);
@@ -265,21 +268,33 @@ __global__ __launch_bounds__(256) void merge_gemm_mx_kernel(const uint8_t* __res
     for (int nb = 0; nb < 4; ++nb) sb[nb] = sb_n[nb];
     lds_barrier();
   }
+  // Epilogue: the 256 x 256 bf16 tile goes through LDS (the operand buffers
+  // are free after the K loop) and leaves as 512-byte row segments, 16 bytes
+  // per lane, instead of 8 bytes into each of 32 rows D * 2 bytes apart.
+  constexpr int TP = BN + 8;   // tile pitch (bf16)
+  static_assert(BM * TP * 2 <= 2 * (BM + BN) * P, "output tile fits in the operand buffers");
+  bf16_t* tile = reinterpret_cast<bf16_t*>(&lds[0][0]);
+  __syncthreads();             // every wave is done with the operand tiles
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const long long m = m0 + wm * 128 + mb * 32 + l32;
-    if (m >= M) continue;
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int n = n0 + wn * 128 + nb * 32 + 8 * i4 + 4 * hg;
-        if (n >= N) continue;
         u32x2 pk;
         pk[0] = pack_bf16x2(acc[nb][mb][i4 * 4 + 0], acc[nb][mb][i4 * 4 + 1]);
         pk[1] = pack_bf16x2(acc[nb][mb][i4 * 4 + 2], acc[nb][mb][i4 * 4 + 3]);
-        *reinterpret_cast<u32x2*>(out + (size_t)m * N + n) = pk;
+        *reinterpret_cast<u32x2*>(&tile[(wm * 128 + mb * 32 + l32) * TP + wn * 128 + nb * 32 + 8 * i4 + 4 * hg]) = pk;
       }
+  __syncthreads();
+  const int c8 = (tid % (BN / 8)) * 8;
+  const bool col_ok = n0 + c8 < N;   // N % 8 == 0
+#pragma unroll 2
+  for (int it = 0; it < BM * (BN / 8) / 256; ++it) {
+    const int r = it * (256 / (BN / 8)) + tid / (BN / 8);
+    const long long m = m0 + r;
+    const u32x4 v = ld16(&tile[r * TP + c8]);
+    if (m < M && col_ok) st16(out + (size_t)m * N + n0 + c8, v);
   }
 }
 

@@ -28,15 +28,18 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace vdn {
 
 // ---------------------------------------------------------------------------
 // Preprocess: dO (head-major) = g * dOhat, Dq = g * rowsum(dOhat * O),
 // dg = rowsum(dOhat * O).  dOhat and O in the output layout [B,L,H,D].
 // One thread per 8 channels of a (b, l, h) row; a row's D/8 lanes reduce
-// with shuffles.
+// with shuffles.  VEC: bf16 rows read as one 16-byte access per tensor
+// (both pointers 16-byte aligned) instead of eight 2-byte loads.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void softmax_bwd_prep_kernel(Geometry g, const T* __restrict__ o,
                                                                const T* __restrict__ dout,
                                                                const float* __restrict__ g_s,
@@ -55,10 +58,25 @@ __global__ __launch_bounds__(256) void softmax_bwd_prep_kernel(Geometry g, const
   const long long b = bl / g.L, l = bl % g.L;
   const size_t src = (size_t)r * D + c8 * 8;
   float x[8], y[8];
+  if constexpr (VEC) {
+    u32x4 xv = {0, 0, 0, 0}, yv = {0, 0, 0, 0};
+    if (live) {
+      xv = ld16(dout + src);
+      yv = ld16(o + src);
+    }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[j] = live ? Elem<T>::load(dout, src + j) : 0.f;
-    y[j] = live ? Elem<T>::load(o, src + j) : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(xv[i] << 16);
+      x[2 * i + 1] = __uint_as_float(xv[i] & 0xFFFF0000u);
+      y[2 * i] = __uint_as_float(yv[i] << 16);
+      y[2 * i + 1] = __uint_as_float(yv[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = live ? Elem<T>::load(dout, src + j) : 0.f;
+      y[j] = live ? Elem<T>::load(o, src + j) : 0.f;
+    }
   }
   float part = 0.f;
 #pragma unroll
@@ -80,7 +98,14 @@ hipError_t launch_softmax_bwd_prep(const Geometry& g, const T* o, const T* dout,
                                    T* do_hm, float* Dq, float* dg, hipStream_t s) {
   const long long n = (long long)g.B * g.L * g.H * (g.D / 8);
   if (n == 0) return hipSuccess;
-  softmax_bwd_prep_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g, o, dout, g_s, do_hm, Dq, dg);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if ((((uintptr_t)o | (uintptr_t)dout) & 15) == 0) {
+      softmax_bwd_prep_kernel<T, true><<<grid, 256, 0, s>>>(g, o, dout, g_s, do_hm, Dq, dg);
+      return hipGetLastError();
+    }
+  }
+  softmax_bwd_prep_kernel<T, false><<<grid, 256, 0, s>>>(g, o, dout, g_s, do_hm, Dq, dg);
   return hipGetLastError();
 }
 

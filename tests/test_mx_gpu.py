@@ -80,8 +80,15 @@ def test_merge_fwd_mx_parity(B, L, H, d, D, F):
     want = O.merge(*ref_in)
     e_mx, e_bf = rel_l2(to_np(got), want_mx), rel_l2(to_np(ref), want)
     e_q = rel_l2(want_mx, want)
-    log(f"[mx] rel-L2 MX vs MX oracle {e_mx:.3e}, bf16 vs exact {e_bf:.3e} (MX vs exact {e_q:.3e})")
+    # per output row as well (the last, partial row and column tiles included):
+    # no row may hide in the pooled figure
+    g_bf = to_np(ref).reshape(-1, D)
+    w_bf = np.asarray(want).reshape(-1, D)
+    row_bf = np.linalg.norm(g_bf - w_bf, axis=1) / np.maximum(np.linalg.norm(w_bf, axis=1), 1e-30)
+    log(f"[mx] rel-L2 MX vs MX oracle {e_mx:.3e}, bf16 vs exact {e_bf:.3e} (MX vs exact {e_q:.3e}), "
+        f"bf16 row max {row_bf.max():.3e}")
     assert e_mx <= 1e-2 and e_bf <= 1e-2
+    assert row_bf.max() <= 3e-2, row_bf.max()
 
 
 @pytest.mark.parametrize("name", ["small", "ragged"])

@@ -530,7 +530,7 @@ def main() -> int:
         print(json.dumps(res))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); the "
               "multi-GPU (head-sharded) path is not built.", file=sys.stderr)
         return 2
 

@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on the GPU machine; here they are collected but skipped when
-    # no device is visible, so `-m gpu` on a CPU host reports skips, not errors.
+    # GPU tests need a visible gfx950 device; on a host without one they are
+    # collected but skipped, so `-m gpu` there reports skips, not errors.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

@@ -320,12 +320,10 @@ vdn_status check_merge(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt
   return VDN_OK;
 }
 
-// Merge, part 1 (may run on the linear branch's stream once Ohat_l exists):
-// transposed projections, and with MX-FP8 the W^T and Ohat_l operands.
+// Merge, part 1 (needs only the projections, so it may run on the linear
+// branch's stream): transposed projections, and with MX-FP8 their operands.
 vdn_status merge_prepare(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt, const void* W_s,
-                         const void* W_l, const void* ohl, int Dm, char* ws, const Layout& lay,
-                         hipStream_t s) {
-  const long long M = (long long)g.B * g.L;
+                         const void* W_l, int Dm, char* ws, const Layout& lay, hipStream_t s) {
   const int K = g.H * g.D;
   if (!W_s || dt != VDN_BF16) return VDN_OK;
   const bool mx = use_mx(p, dt);
@@ -339,8 +337,6 @@ vdn_status merge_prepare(const vdn::Geometry& g, const vdn_params* p, vdn_dtype 
     uint8_t* wsc = (uint8_t*)(ws + lay.mxws);
     VDN_HIP(vdn::launch_mx_quant_rows(w0t, Dm, K, wc, wsc, 2LL * K, 0, s));
     VDN_HIP(vdn::launch_mx_quant_rows(w1t, Dm, K, wc, wsc, 2LL * K, K, s));
-    VDN_HIP(vdn::launch_mx_quant_rows((const uint16_t*)ohl, M, K, (uint8_t*)(ws + lay.mxa),
-                                      (uint8_t*)(ws + lay.mxas), 2LL * K, K, s));
   }
   return VDN_OK;
 }
@@ -362,6 +358,7 @@ vdn_status merge_finish(const vdn::Geometry& g, const vdn_params* p, vdn_dtype d
     uint8_t* ac = (uint8_t*)(ws + lay.mxa);
     uint8_t* asc = (uint8_t*)(ws + lay.mxas);
     VDN_HIP(vdn::launch_mx_quant_rows((const uint16_t*)ohs, M, K, ac, asc, 2LL * K, 0, s));
+    VDN_HIP(vdn::launch_mx_quant_rows((const uint16_t*)ohl, M, K, ac, asc, 2LL * K, K, s));
     VDN_HIP(vdn::launch_merge_gemm_mx(ac, asc, (const uint8_t*)(ws + lay.mxw),
                                       (const uint8_t*)(ws + lay.mxws), (uint16_t*)out, M, 2 * K,
                                       Dm, s));
@@ -706,25 +703,21 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   float* Pf = (float*)(ws + lay.Pf);
   float* Pr = (float*)(ws + lay.Pr);
 
-  // Linear branch (a1-a6) on the side stream, forked from and joined back
-  // into the caller's stream; the window Softmax (a7) runs on the caller's
-  // stream meanwhile.  The two branches touch disjoint workspace regions.
+  // The linear branch's states (a1-a4) on the side stream, forked from and
+  // joined back into the caller's stream; the window Softmax (a7) runs on the
+  // caller's stream meanwhile.  The two touch disjoint workspace regions.
+  // The readout (a5, a6) follows the Softmax on the caller's stream: beside
+  // it each readout workgroup had to wait for a whole compute unit and then
+  // held it for a stretched span, which cost the Softmax about twice the
+  // readout's own time.
   SideStream* ss = nullptr;
   VDN_HIP(side_stream(&ss));
   VDN_HIP(hipEventRecord(ss->fork, s));
   VDN_HIP(hipStreamWaitEvent(ss->stream, ss->fork, 0));
   st = run_scan(g, p, dt, k, v, beta, alpha, k_text, v_text, beta_text, ws, lay, Pf, Pr, ss->stream);
-  if (st == VDN_OK) {
-    const hipError_t e = dt == VDN_BF16
-        ? vdn::launch_vda_readout<uint16_t>(g, (const uint16_t*)q, alpha, Pf, Pr, g_l, gamma,
-                                            p->rms_eps, (uint16_t*)ohl, ss->stream)
-        : vdn::launch_vda_readout<float>(g, (const float*)q, alpha, Pf, Pr, g_l, gamma,
-                                         p->rms_eps, (float*)ohl, ss->stream);
-    if (e != hipSuccess) st = fail(VDN_ERR_HIP, "readout launch failed: %s", hipGetErrorString(e));
-  }
-  // the merge's projection transposes (and MX-FP8 operands of W and Ohat_l)
-  // also run on the side stream, off the Softmax's path
-  if (st == VDN_OK) st = merge_prepare(g, p, dt, W_s, W_l, ohl, Dm, ws, lay, ss->stream);
+  // the merge's projection transposes (and MX-FP8 operands of W) also run
+  // on the side stream, off the Softmax's path
+  if (st == VDN_OK) st = merge_prepare(g, p, dt, W_s, W_l, Dm, ws, lay, ss->stream);
   // join is recorded even after a failure, so the caller's stream never
   // runs ahead of work already queued on the side stream
   const hipError_t ej = hipEventRecord(ss->join, ss->stream);
@@ -733,6 +726,14 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, ss->join, 0) : ej;
   if (st != VDN_OK) return st;
   if (ew != hipSuccess) return fail(VDN_ERR_HIP, "side-stream join failed: %s", hipGetErrorString(ew));
+  {
+    const hipError_t e = dt == VDN_BF16
+        ? vdn::launch_vda_readout<uint16_t>(g, (const uint16_t*)q, alpha, Pf, Pr, g_l, gamma,
+                                            p->rms_eps, (uint16_t*)ohl, s)
+        : vdn::launch_vda_readout<float>(g, (const float*)q, alpha, Pf, Pr, g_l, gamma,
+                                         p->rms_eps, (float*)ohl, s);
+    if (e != hipSuccess) return fail(VDN_ERR_HIP, "readout launch failed: %s", hipGetErrorString(e));
+  }
   // Merge (a8)
   return merge_finish(g, p, dt, W_s, W_l, ohs, ohl, out, Dm, ws, lay, s);
 }
@@ -753,7 +754,7 @@ vdn_status vdn_merge_fwd(const void* ohat_s, const void* ohat_l, const void* W_s
   if (st != VDN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  st = merge_prepare(g, p, dt, W_s, W_l, ohat_l, Dm, ws, lay, s);
+  st = merge_prepare(g, p, dt, W_s, W_l, Dm, ws, lay, s);
   if (st != VDN_OK) return st;
   return merge_finish(g, p, dt, W_s, W_l, ohat_s, ohat_l, out, Dm, ws, lay, s);
 }

@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 namespace {
@@ -318,6 +319,22 @@ vdn_status check_merge(const vdn::Geometry& g, const vdn_params* p, vdn_dtype dt
       return fail(VDN_ERR_UNSUPPORTED, "the MX-FP8 merge needs H*d_v %% 64 == 0 and D %% 8 == 0");
   }
   return VDN_OK;
+}
+
+// Whether the layer's readout runs after the Softmax rather than beside it:
+// when the Softmax's algorithmic work (4 d per visible query-key pair) is at
+// least kReadoutAfterFlops.  Side by side on one MI355X the readout after
+// the Softmax was 1% faster per layer step at 55 and 63 TFLOP of Softmax
+// work and 3% slower at 2.2 TFLOP, where beside the Softmax it is nearly
+// hidden.  Pairs from the window rule: a non-anchor query frame sees at most
+// (2 wc + 1) cf frames plus the two anchors, an anchor frame every frame.
+constexpr double kReadoutAfterFlops = 8e12;
+bool readout_after_softmax(const vdn::Geometry& g) {
+  const double win = std::min<double>(g.F, (2.0 * g.wc + 1) * g.cf + (g.anchors ? 2 : 0));
+  const double qf = g.anchors ? std::max(g.F - 2, 0) : g.F;
+  const double frame_pairs = qf * win + (g.anchors ? (double)std::min(g.F, 2) * g.F : 0.0);
+  const double pairs = (double)g.B * g.H * (double)g.N * g.N * frame_pairs;
+  return 4.0 * g.D * pairs >= kReadoutAfterFlops;
 }
 
 // Merge, part 1 (needs only the projections, so it may run on the linear
@@ -703,18 +720,28 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   float* Pf = (float*)(ws + lay.Pf);
   float* Pr = (float*)(ws + lay.Pr);
 
-  // The linear branch's states (a1-a4) on the side stream, forked from and
-  // joined back into the caller's stream; the window Softmax (a7) runs on the
+  // The linear branch (a1-a6) on the side stream, forked from and joined
+  // back into the caller's stream; the window Softmax (a7) runs on the
   // caller's stream meanwhile.  The two touch disjoint workspace regions.
-  // The readout (a5, a6) follows the Softmax on the caller's stream: beside
-  // it each readout workgroup had to wait for a whole compute unit and then
-  // held it for a stretched span, which cost the Softmax about twice the
-  // readout's own time.
+  // Beside a long Softmax each readout (a5, a6) workgroup waits for a whole
+  // compute unit and then holds it for a stretched span, which costs the
+  // Softmax about twice the readout's own time; there the readout follows
+  // the Softmax on the caller's stream instead.
+  const bool ro_after = readout_after_softmax(g);
+  auto readout = [&](hipStream_t rs) -> vdn_status {
+    const hipError_t e = dt == VDN_BF16
+        ? vdn::launch_vda_readout<uint16_t>(g, (const uint16_t*)q, alpha, Pf, Pr, g_l, gamma,
+                                            p->rms_eps, (uint16_t*)ohl, rs)
+        : vdn::launch_vda_readout<float>(g, (const float*)q, alpha, Pf, Pr, g_l, gamma,
+                                         p->rms_eps, (float*)ohl, rs);
+    return e == hipSuccess ? VDN_OK : fail(VDN_ERR_HIP, "readout launch failed: %s", hipGetErrorString(e));
+  };
   SideStream* ss = nullptr;
   VDN_HIP(side_stream(&ss));
   VDN_HIP(hipEventRecord(ss->fork, s));
   VDN_HIP(hipStreamWaitEvent(ss->stream, ss->fork, 0));
   st = run_scan(g, p, dt, k, v, beta, alpha, k_text, v_text, beta_text, ws, lay, Pf, Pr, ss->stream);
+  if (st == VDN_OK && !ro_after) st = readout(ss->stream);
   // the merge's projection transposes (and MX-FP8 operands of W) also run
   // on the side stream, off the Softmax's path
   if (st == VDN_OK) st = merge_prepare(g, p, dt, W_s, W_l, Dm, ws, lay, ss->stream);
@@ -726,13 +753,9 @@ vdn_status vdn_attn_fwd(const void* q, const void* k, const void* v, const float
   const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, ss->join, 0) : ej;
   if (st != VDN_OK) return st;
   if (ew != hipSuccess) return fail(VDN_ERR_HIP, "side-stream join failed: %s", hipGetErrorString(ew));
-  {
-    const hipError_t e = dt == VDN_BF16
-        ? vdn::launch_vda_readout<uint16_t>(g, (const uint16_t*)q, alpha, Pf, Pr, g_l, gamma,
-                                            p->rms_eps, (uint16_t*)ohl, s)
-        : vdn::launch_vda_readout<float>(g, (const float*)q, alpha, Pf, Pr, g_l, gamma,
-                                         p->rms_eps, (float*)ohl, s);
-    if (e != hipSuccess) return fail(VDN_ERR_HIP, "readout launch failed: %s", hipGetErrorString(e));
+  if (ro_after) {
+    st = readout(s);
+    if (st != VDN_OK) return st;
   }
   // Merge (a8)
   return merge_finish(g, p, dt, W_s, W_l, ohs, ohl, out, Dm, ws, lay, s);
